@@ -1,0 +1,179 @@
+"""CPU oracle for conv2d grad-input: TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding in ``conv2d_backward_implicit_amd``) never imports it, and
+this package imports nothing from the product.
+
+The arithmetic lives in ``oracle.c`` (plain loop nests in double precision,
+OpenMP over independent output elements).  This module only builds that file
+with the host C compiler and marshals numpy arrays to it.
+
+Source cited as [p3]: the docs.rs source page of meganeura 0.2.0,
+``src/shaders/conv2d_grad_input_gemm_coop.wgsl``.
+
+Functions (all take float64-convertible arrays and return float64 arrays):
+
+* ``grad_input_gather``    -- the definition ([p3] header comment, weight_T
+  staging, the stride > 1 im2col rule applied to every stride).
+* ``grad_input_gather_at`` -- the same sum at chosen flat output indices.
+* ``grad_input_scatter``   -- independent scatter form (transpose of forward).
+* ``conv2d_forward``       -- forward cross-correlation, for the adjoint check.
+
+Every function is pinned by tests/test_oracle.py to facts outside the oracle
+itself (closed forms, delta inputs, a library GEMM, torch's CPU convolution
+routines, the adjoint identity), and tests/test_oracle_mutants.py shows that
+those pins fail for planted mistakes.  No function is "parity unpinned".
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+_I64 = ctypes.c_int64
+_DP = ctypes.POINTER(ctypes.c_double)
+_IP = ctypes.POINTER(ctypes.c_int64)
+
+
+def compile_source(src: str, out: str) -> str:
+    """Compile one C file into a shared library with gcc -O2 -fopenmp."""
+    tmp = out + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           "-o", tmp, src]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, out)
+    return out
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c into liboracle.so next to it."""
+    if (not force and os.path.exists(_LIB_PATH)
+            and os.path.getmtime(_LIB_PATH) >= os.path.getmtime(SOURCE)):
+        return _LIB_PATH
+    return compile_source(SOURCE, _LIB_PATH)
+
+
+def _f64(a):
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _ptr(a):
+    return a.ctypes.data_as(_DP)
+
+
+def _dims(go_shape, w_shape, H, W, stride, padding_h, padding_w):
+    N, Co, OH, OW = (int(v) for v in go_shape)
+    Co2, Ci, KH, KW = (int(v) for v in w_shape)
+    if Co2 != Co:
+        raise ValueError("grad_out channels %d != weight out-channels %d" % (Co, Co2))
+    if stride < 1:
+        raise ValueError("stride must be >= 1")
+    return [N, Ci, int(H), int(W), Co, KH, KW, int(stride), int(padding_h),
+            int(padding_w), OH, OW]
+
+
+class Oracle:
+    """ctypes wrapper around one build of oracle.c."""
+
+    def __init__(self, path: str):
+        lib = ctypes.CDLL(path)
+        sig = [_DP, _DP, _DP] + [_I64] * 12
+        for name in ("oracle_grad_input_gather", "oracle_grad_input_scatter",
+                     "oracle_conv2d_forward"):
+            fn = getattr(lib, name)
+            fn.argtypes = sig
+            fn.restype = None
+        lib.oracle_grad_input_gather_at.argtypes = [_DP, _DP, _IP, _I64, _DP] + [_I64] * 12
+        lib.oracle_grad_input_gather_at.restype = None
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        self._lib = lib
+        self.path = path
+
+    def grad_input_gather(self, grad_out, weight, H, W, stride, padding_h, padding_w):
+        """grad_input [N, Ci, H, W] by the direct gather definition (float64)."""
+        go, w = _f64(grad_out), _f64(weight)
+        d = _dims(go.shape, w.shape, H, W, stride, padding_h, padding_w)
+        gi = np.empty((d[0], d[1], d[2], d[3]), dtype=np.float64)
+        self._lib.oracle_grad_input_gather(_ptr(go), _ptr(w), _ptr(gi), *d)
+        return gi
+
+    def grad_input_gather_at(self, grad_out, weight, H, W, stride, padding_h,
+                             padding_w, flat_idx):
+        """The gather definition evaluated at flat grad_input indices (float64)."""
+        go, w = _f64(grad_out), _f64(weight)
+        d = _dims(go.shape, w.shape, H, W, stride, padding_h, padding_w)
+        idx = np.ascontiguousarray(flat_idx, dtype=np.int64)
+        total = d[0] * d[1] * d[2] * d[3]
+        if idx.size and (idx.min() < 0 or idx.max() >= total):
+            raise IndexError("flat index out of range")
+        out = np.empty(idx.shape, dtype=np.float64)
+        self._lib.oracle_grad_input_gather_at(
+            _ptr(go), _ptr(w), idx.ctypes.data_as(_IP), int(idx.size), _ptr(out), *d)
+        return out
+
+    def grad_input_scatter(self, grad_out, weight, H, W, stride, padding_h, padding_w):
+        """grad_input [N, Ci, H, W] by the scatter formulation (float64)."""
+        go, w = _f64(grad_out), _f64(weight)
+        d = _dims(go.shape, w.shape, H, W, stride, padding_h, padding_w)
+        gi = np.empty((d[0], d[1], d[2], d[3]), dtype=np.float64)
+        self._lib.oracle_grad_input_scatter(_ptr(go), _ptr(w), _ptr(gi), *d)
+        return gi
+
+    def conv2d_forward(self, x, weight, OH, OW, stride, padding_h, padding_w):
+        """Forward cross-correlation y [N, Co, OH, OW] (float64)."""
+        xx, w = _f64(x), _f64(weight)
+        N, Ci, H, W = (int(v) for v in xx.shape)
+        Co, Ci2, KH, KW = (int(v) for v in w.shape)
+        if Ci2 != Ci:
+            raise ValueError("x channels %d != weight in-channels %d" % (Ci, Ci2))
+        y = np.empty((N, Co, int(OH), int(OW)), dtype=np.float64)
+        self._lib.oracle_conv2d_forward(_ptr(xx), _ptr(w), _ptr(y), N, Ci, H, W,
+                                        Co, KH, KW, int(stride), int(padding_h),
+                                        int(padding_w), int(OH), int(OW))
+        return y
+
+    def num_threads(self) -> int:
+        """OpenMP threads the oracle routines use in this process."""
+        return int(self._lib.oracle_num_threads())
+
+
+_default = None
+_lock = threading.Lock()
+
+
+def default() -> Oracle:
+    """The oracle built from oracle.c (built on first use if missing/stale)."""
+    global _default
+    with _lock:
+        if _default is None:
+            _default = Oracle(build(force=False))
+    return _default
+
+
+def grad_input_gather(*a, **k):
+    return default().grad_input_gather(*a, **k)
+
+
+def grad_input_gather_at(*a, **k):
+    return default().grad_input_gather_at(*a, **k)
+
+
+def grad_input_scatter(*a, **k):
+    return default().grad_input_scatter(*a, **k)
+
+
+def conv2d_forward(*a, **k):
+    return default().conv2d_forward(*a, **k)
+
+
+def num_threads() -> int:
+    return default().num_threads()

@@ -1,0 +1,208 @@
+/*
+ * CPU oracle for the convolution backward pass with respect to the input.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
+ * cpu_baseline leg of bench.py may load this code.  The product path (the HIP
+ * library under conv2d_backward_implicit_amd/csrc) never calls it, links it or
+ * shares a line with it.
+ *
+ * Source cited throughout as [p3]: the docs.rs source page of meganeura 0.2.0,
+ * "src/shaders/conv2d_grad_input_gemm_coop.wgsl".  The sections referred to
+ * are that shader's header comment, its `Params` struct, the two branches of
+ * its im2col (B-tile) staging (stride 1 and stride > 1), its weight_T (A-tile)
+ * staging and its final store to grad_input.
+ *
+ * Every routine here is a plain loop nest over the definition, accumulated in
+ * double precision, with no blocking, no reordering beyond the definition and
+ * no shared helpers with the GPU path.  Arrays are dense, row-major:
+ *   grad_out   [N, Co, OH, OW]
+ *   weight     [Co, Ci, KH, KW]
+ *   grad_input [N, Ci, H, W]
+ *   x (forward input) [N, Ci, H, W],  y (forward output) [N, Co, OH, OW]
+ * All extents are passed explicitly; OH and OW are taken as given (they bound
+ * the gather, as in [p3] `Params`), the caller decides whether they are the
+ * forward-conv extents.
+ *
+ * Parallelism: OpenMP over independent output elements only (each element is
+ * still one serial sum in the definition's loop order), so results do not
+ * depend on the thread count.
+ */
+#include <stdint.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+typedef int64_t i64;
+
+/*
+ * Direct gather (the definition).
+ *
+ * [p3] header comment: per batch item the result is the product
+ *   grad_input[ci, (ih, iw)] = sum over k = (co, kh, kw) of
+ *       weight^T[ci, k] * im2col(grad_out)[k, (ih, iw)].
+ * [p3] weight_T staging: weight^T[ci, (co, kh, kw)] = weight[co, ci, kh, kw]
+ *   (no spatial flip of the kernel).
+ * [p3] stride > 1 im2col branch: the im2col entry for pixel (ih, iw) and tap
+ *   (kh, kw) is grad_out[n, co, oh, ow] with oh = (ih + padding_h - kh) / s and
+ *   ow = (iw + padding_w - kw) / s when both numerators are non-negative and
+ *   divisible by s and oh < OH, ow < OW; otherwise the entry is zero.  This
+ *   rule is applied here for every stride, s = 1 included.  (The shader's
+ *   stride-1 branch instead offsets by kH-1-padding_h / kW-1-padding_w; the
+ *   two branches give the same entry only when padding = (k-1)/2, and only
+ *   the rule used here is the adjoint of the forward convolution below.)
+ * [p3] final store: grad_input is overwritten, every element is written.
+ */
+void oracle_grad_input_gather(const double* go, const double* w, double* gi,
+                              i64 N, i64 Ci, i64 H, i64 W, i64 Co, i64 KH,
+                              i64 KW, i64 s, i64 ph, i64 pw, i64 OH, i64 OW) {
+  i64 total = N * Ci * H * W;
+#pragma omp parallel for schedule(static)
+  for (i64 e = 0; e < total; ++e) {
+    i64 iw = e % W;
+    i64 ih = (e / W) % H;
+    i64 ci = (e / (W * H)) % Ci;
+    i64 n = e / (W * H * Ci);
+    double acc = 0.0;
+    for (i64 co = 0; co < Co; ++co) {
+      for (i64 kh = 0; kh < KH; ++kh) {
+        for (i64 kw = 0; kw < KW; ++kw) {
+          i64 th = ih + ph - kh;
+          i64 tw = iw + pw - kw;
+          if (th < 0 || tw < 0) continue;
+          if (th % s != 0 || tw % s != 0) continue;
+          i64 oh = th / s;
+          i64 ow = tw / s;
+          if (oh >= OH || ow >= OW) continue;
+          acc += go[((n * Co + co) * OH + oh) * OW + ow] *
+                 w[((co * Ci + ci) * KH + kh) * KW + kw];
+        }
+      }
+    }
+    gi[e] = acc;
+  }
+}
+
+/*
+ * The same gather, evaluated only at the listed flat grad_input indices
+ * (idx[j] in [0, N*Ci*H*W)).  Used to check outputs of full-size problems
+ * one element at a time.  Identical arithmetic to oracle_grad_input_gather.
+ */
+void oracle_grad_input_gather_at(const double* go, const double* w,
+                                 const i64* idx, i64 count, double* out,
+                                 i64 N, i64 Ci, i64 H, i64 W, i64 Co, i64 KH,
+                                 i64 KW, i64 s, i64 ph, i64 pw, i64 OH,
+                                 i64 OW) {
+  (void)N;
+#pragma omp parallel for schedule(static)
+  for (i64 j = 0; j < count; ++j) {
+    i64 e = idx[j];
+    i64 iw = e % W;
+    i64 ih = (e / W) % H;
+    i64 ci = (e / (W * H)) % Ci;
+    i64 n = e / (W * H * Ci);
+    double acc = 0.0;
+    for (i64 co = 0; co < Co; ++co) {
+      for (i64 kh = 0; kh < KH; ++kh) {
+        for (i64 kw = 0; kw < KW; ++kw) {
+          i64 th = ih + ph - kh;
+          i64 tw = iw + pw - kw;
+          if (th < 0 || tw < 0) continue;
+          if (th % s != 0 || tw % s != 0) continue;
+          i64 oh = th / s;
+          i64 ow = tw / s;
+          if (oh >= OH || ow >= OW) continue;
+          acc += go[((n * Co + co) * OH + oh) * OW + ow] *
+                 w[((co * Ci + ci) * KH + kh) * KW + kw];
+        }
+      }
+    }
+    out[j] = acc;
+  }
+}
+
+/*
+ * Scatter formulation, an independent code path for the same quantity: every
+ * grad_out element (n, co, oh, ow) is pushed back through every tap (kh, kw)
+ * to the input pixel it was computed from in the forward pass,
+ *   ih = oh*s - padding_h + kh,  iw = ow*s - padding_w + kw,
+ * and added there if that pixel lies inside the input.  This is the transpose
+ * of the forward map; it needs no divisibility test at all.
+ * Parallel over (n, ci) planes, each plane owned by one thread.
+ */
+void oracle_grad_input_scatter(const double* go, const double* w, double* gi,
+                               i64 N, i64 Ci, i64 H, i64 W, i64 Co, i64 KH,
+                               i64 KW, i64 s, i64 ph, i64 pw, i64 OH, i64 OW) {
+  i64 planes = N * Ci;
+#pragma omp parallel for schedule(static)
+  for (i64 pl = 0; pl < planes; ++pl) {
+    i64 n = pl / Ci;
+    i64 ci = pl % Ci;
+    double* dst = gi + pl * H * W;
+    for (i64 q = 0; q < H * W; ++q) dst[q] = 0.0;
+    for (i64 co = 0; co < Co; ++co) {
+      for (i64 oh = 0; oh < OH; ++oh) {
+        for (i64 ow = 0; ow < OW; ++ow) {
+          double g = go[((n * Co + co) * OH + oh) * OW + ow];
+          for (i64 kh = 0; kh < KH; ++kh) {
+            i64 ih = oh * s - ph + kh;
+            if (ih < 0 || ih >= H) continue;
+            for (i64 kw = 0; kw < KW; ++kw) {
+              i64 iw = ow * s - pw + kw;
+              if (iw < 0 || iw >= W) continue;
+              dst[ih * W + iw] += g * w[((co * Ci + ci) * KH + kh) * KW + kw];
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
+/*
+ * Forward 2-D cross-correlation (the operator whose input-gradient is the
+ * quantity above):
+ *   y[n, co, oh, ow] = sum_{ci, kh, kw} x[n, ci, oh*s - ph + kh, ow*s - pw + kw]
+ *                                        * weight[co, ci, kh, kw],
+ * with x taken as zero outside [0,H) x [0,W).  Serves the adjoint identity
+ * <grad_input(go), x> = <go, conv2d_fwd(x)>.
+ */
+void oracle_conv2d_forward(const double* x, const double* w, double* y, i64 N,
+                           i64 Ci, i64 H, i64 W, i64 Co, i64 KH, i64 KW, i64 s,
+                           i64 ph, i64 pw, i64 OH, i64 OW) {
+  i64 total = N * Co * OH * OW;
+#pragma omp parallel for schedule(static)
+  for (i64 e = 0; e < total; ++e) {
+    i64 ow = e % OW;
+    i64 oh = (e / OW) % OH;
+    i64 co = (e / (OW * OH)) % Co;
+    i64 n = e / (OW * OH * Co);
+    double acc = 0.0;
+    for (i64 ci = 0; ci < Ci; ++ci) {
+      for (i64 kh = 0; kh < KH; ++kh) {
+        i64 ih = oh * s - ph + kh;
+        if (ih < 0 || ih >= H) continue;
+        for (i64 kw = 0; kw < KW; ++kw) {
+          i64 iw = ow * s - pw + kw;
+          if (iw < 0 || iw >= W) continue;
+          acc += x[((n * Ci + ci) * H + ih) * W + iw] *
+                 w[((co * Ci + ci) * KH + kh) * KW + kw];
+        }
+      }
+    }
+    y[e] = acc;
+  }
+}
+
+/* Number of OpenMP threads the routines above will use. */
+int oracle_num_threads(void) {
+  int t = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+  {
+#pragma omp single
+    t = omp_get_num_threads();
+  }
+#endif
+  return t;
+}

@@ -1,0 +1,290 @@
+"""Pins for the CPU oracle: facts that do not come from the oracle itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` (the committed build or a
+deliberately mutated copy) and raises ``AssertionError`` when the oracle
+disagrees with the fact it checks.  tests/test_oracle.py runs them on the
+committed oracle; tests/test_oracle_mutants.py runs them on mutants and
+requires that every mutant trips at least one pin.
+
+What the pins rest on:
+* torch's CPU routines ``torch.nn.grad.conv2d_input`` and
+  ``torch.nn.functional.conv2d`` in float64 (third-party library; run, not
+  copied);
+* the adjoint identity <grad_input(g), x> = <g, conv2d(x)>, which defines the
+  input gradient of a linear map;
+* closed forms: all-ones inputs (tap counts from interval lengths), delta
+  weights and delta grad_out (placement by strided array slicing), the 1x1
+  stride-1 case as a plain matrix product (numpy matmul), exact zeros at
+  pixels no tap reaches (stride > kernel);
+* integer inputs, for which float64 sums are exact.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from conv2d_backward_implicit_amd.workloads import ConvShape, random_shape
+
+# Small random shapes used by the comparison pins (fixed seed, varied
+# strides, asymmetric padding up to the kernel size, non-square images).
+_RNG_SEED = 20261202
+_N_RANDOM = 40
+
+
+def _random_shapes(count=_N_RANDOM, seed=_RNG_SEED):
+    rng = np.random.default_rng(seed)
+    shapes = [random_shape(rng, name="rand%d" % i) for i in range(count)]
+    # always include asymmetric padding, stride > kernel and Ci != Co cases
+    shapes += [
+        ConvShape("asym", 2, 3, 7, 9, 4, 3, 5, 1, 0, 2, 5, 9, dist="uniform"),
+        ConvShape("s3k2", 1, 2, 8, 7, 3, 2, 2, 3, 1, 0, 3, 2, dist="uniform"),
+        ConvShape("s2k3p0", 1, 3, 9, 8, 2, 3, 3, 2, 0, 0, 4, 3, dist="uniform"),
+        ConvShape("k5p1", 1, 2, 9, 9, 3, 5, 5, 1, 1, 1, 7, 7, dist="uniform"),
+    ]
+    return shapes
+
+
+def _inputs(shape: ConvShape, seed: int):
+    rng = np.random.default_rng(seed)
+    go = rng.uniform(-1, 1, size=shape.go_shape)
+    w = rng.uniform(-1, 1, size=shape.w_shape)
+    return go, w
+
+
+def _gather(orc, shape, go, w):
+    return orc.grad_input_gather(go, w, shape.in_h, shape.in_w, shape.stride,
+                                 shape.padding_h, shape.padding_w)
+
+
+def _rel_err(a, b):
+    scale = max(np.max(np.abs(b)), 1e-300)
+    return float(np.max(np.abs(a - b)) / scale) if a.size else 0.0
+
+
+def pin_torch_grad_input(orc):
+    """Gather and scatter agree with torch.nn.grad.conv2d_input (float64)."""
+    import torch
+    for i, sh in enumerate(_random_shapes()):
+        go, w = _inputs(sh, i)
+        ref = torch.nn.grad.conv2d_input(
+            sh.gi_shape, torch.from_numpy(w), torch.from_numpy(go),
+            stride=sh.stride, padding=(sh.padding_h, sh.padding_w)).numpy()
+        got = _gather(orc, sh, go, w)
+        assert _rel_err(got, ref) < 1e-12, ("gather", sh, _rel_err(got, ref))
+        sc = orc.grad_input_scatter(go, w, sh.in_h, sh.in_w, sh.stride,
+                                    sh.padding_h, sh.padding_w)
+        assert _rel_err(sc, ref) < 1e-12, ("scatter", sh, _rel_err(sc, ref))
+
+
+def pin_torch_forward(orc):
+    """The forward conv agrees with torch.nn.functional.conv2d (float64)."""
+    import torch
+    for i, sh in enumerate(_random_shapes()):
+        rng = np.random.default_rng(1000 + i)
+        x = rng.uniform(-1, 1, size=sh.gi_shape)
+        w = rng.uniform(-1, 1, size=sh.w_shape)
+        ref = torch.nn.functional.conv2d(
+            torch.from_numpy(x), torch.from_numpy(w), stride=sh.stride,
+            padding=(sh.padding_h, sh.padding_w)).numpy()
+        assert ref.shape == sh.go_shape, (ref.shape, sh)
+        got = orc.conv2d_forward(x, w, sh.out_h, sh.out_w, sh.stride,
+                                 sh.padding_h, sh.padding_w)
+        assert _rel_err(got, ref) < 1e-12, (sh, _rel_err(got, ref))
+
+
+def pin_adjoint(orc):
+    """<gather(g), x> equals <g, forward(x)> to float64 rounding."""
+    for i, sh in enumerate(_random_shapes()):
+        rng = np.random.default_rng(2000 + i)
+        g = rng.uniform(-1, 1, size=sh.go_shape)
+        w = rng.uniform(-1, 1, size=sh.w_shape)
+        x = rng.uniform(-1, 1, size=sh.gi_shape)
+        lhs = float(np.sum(_gather(orc, sh, g, w) * x))
+        y = orc.conv2d_forward(x, w, sh.out_h, sh.out_w, sh.stride, sh.padding_h,
+                               sh.padding_w)
+        rhs = float(np.sum(g * y))
+        scale = float(np.sum(np.abs(g)) * np.sum(np.abs(w)) + 1.0)
+        assert abs(lhs - rhs) <= 1e-12 * scale, (sh, lhs, rhs)
+
+
+def pin_gather_vs_scatter(orc):
+    """The two independent formulations agree on every random shape."""
+    for i, sh in enumerate(_random_shapes()):
+        go, w = _inputs(sh, 3000 + i)
+        a = _gather(orc, sh, go, w)
+        b = orc.grad_input_scatter(go, w, sh.in_h, sh.in_w, sh.stride,
+                                   sh.padding_h, sh.padding_w)
+        assert _rel_err(a, b) < 1e-12, (sh, _rel_err(a, b))
+
+
+def _tap_count(i, p, k, s, o):
+    """How many kernel offsets t in [0, k) reach input index i: those with
+    i + p - t = s*m for an integer m in [0, o).  Counted as the number of m in
+    an interval: t = i + p - s*m must lie in [0, k)."""
+    m_lo = max(0, -((-(i + p - (k - 1))) // s))   # ceil((i + p - k + 1) / s)
+    m_hi = min(o - 1, (i + p) // s)                 # floor((i + p) / s)
+    return max(0, m_hi - m_lo + 1)
+
+
+def pin_all_ones(orc):
+    """All-ones inputs: grad_input = Co * Th(ih) * Tw(iw), exactly.
+
+    On the 8x8, 3x3, pad 1, stride 1 shape with 16 output channels this is
+    16*9 = 144 inside, 16*6 = 96 on edges and 16*4 = 64 at corners."""
+    tiny = ConvShape("tiny", 1, 8, 8, 8, 16, 3, 3, 1, 1, 1, 8, 8)
+    go = np.ones(tiny.go_shape)
+    w = np.ones(tiny.w_shape)
+    gi = _gather(orc, tiny, go, w)
+    assert gi[0, 0, 3, 4] == 144.0 and gi[0, 5, 0, 4] == 96.0, gi[0, 0]
+    assert gi[0, 7, 7, 7] == 64.0 and gi[0, 2, 0, 0] == 64.0, gi[0, 0]
+    for sh in _random_shapes() + [tiny]:
+        go = np.ones(sh.go_shape)
+        w = np.ones(sh.w_shape)
+        gi = _gather(orc, sh, go, w)
+        th = np.array([_tap_count(i, sh.padding_h, sh.kernel_h, sh.stride, sh.out_h)
+                       for i in range(sh.in_h)], dtype=np.float64)
+        tw = np.array([_tap_count(i, sh.padding_w, sh.kernel_w, sh.stride, sh.out_w)
+                       for i in range(sh.in_w)], dtype=np.float64)
+        exp = sh.out_channels * np.outer(th, tw)
+        assert np.array_equal(gi, np.broadcast_to(exp, gi.shape)), sh
+
+
+def _placement_slices(sh, kh, kw):
+    """For tap (kh, kw): which grad_out rows/cols land on which input
+    rows/cols, as (oh_slice, ih_slice, ow_slice, iw_slice) with in-range
+    bounds.  Input row of output row oh is oh*s - ph + kh."""
+    def axis(o, s, p, k, n):
+        pairs = [(m, m * s - p + k) for m in range(o) if 0 <= m * s - p + k < n]
+        return pairs
+    rows = axis(sh.out_h, sh.stride, sh.padding_h, kh, sh.in_h)
+    cols = axis(sh.out_w, sh.stride, sh.padding_w, kw, sh.in_w)
+    return rows, cols
+
+
+def pin_delta_weight(orc):
+    """weight = delta(co0, ci0, kh0, kw0): channel ci0 of grad_input is grad_out
+    channel co0 placed at (oh*s - ph + kh0, ow*s - pw + kw0); every other
+    channel is zero.  Pins the orientation of the kernel (no flip) and of the
+    padding of each axis."""
+    for i, sh in enumerate(_random_shapes()[:25]):
+        rng = np.random.default_rng(4000 + i)
+        go = rng.uniform(-1, 1, size=sh.go_shape)
+        co0 = int(rng.integers(sh.out_channels))
+        ci0 = int(rng.integers(sh.in_channels))
+        kh0 = int(rng.integers(sh.kernel_h))
+        kw0 = int(rng.integers(sh.kernel_w))
+        w = np.zeros(sh.w_shape)
+        w[co0, ci0, kh0, kw0] = 1.0
+        exp = np.zeros(sh.gi_shape)
+        rows, cols = _placement_slices(sh, kh0, kw0)
+        if rows and cols:
+            oh = np.array([r[0] for r in rows]); ih = np.array([r[1] for r in rows])
+            ow = np.array([c[0] for c in cols]); iw = np.array([c[1] for c in cols])
+            exp[:, ci0][:, ih[:, None], iw[None, :]] = go[:, co0][:, oh[:, None], ow[None, :]]
+        got = _gather(orc, sh, go, w)
+        assert np.array_equal(got, exp), (sh, co0, ci0, kh0, kw0)
+
+
+def pin_delta_grad_out(orc):
+    """grad_out = delta(n0, co0, oh0, ow0): grad_input[n0, :, oh0*s-ph+kh,
+    ow0*s-pw+kw] = weight[co0, :, kh, kw] at in-range positions, zero
+    elsewhere.  Pins where each kernel tap lands."""
+    for i, sh in enumerate(_random_shapes()[:25]):
+        rng = np.random.default_rng(5000 + i)
+        w = rng.uniform(-1, 1, size=sh.w_shape)
+        n0 = int(rng.integers(sh.batch))
+        co0 = int(rng.integers(sh.out_channels))
+        oh0 = int(rng.integers(sh.out_h))
+        ow0 = int(rng.integers(sh.out_w))
+        go = np.zeros(sh.go_shape)
+        go[n0, co0, oh0, ow0] = 1.0
+        exp = np.zeros(sh.gi_shape)
+        for kh in range(sh.kernel_h):
+            ih = oh0 * sh.stride - sh.padding_h + kh
+            if not 0 <= ih < sh.in_h:
+                continue
+            for kw in range(sh.kernel_w):
+                iw = ow0 * sh.stride - sh.padding_w + kw
+                if 0 <= iw < sh.in_w:
+                    exp[n0, :, ih, iw] = w[co0, :, kh, kw]
+        got = _gather(orc, sh, go, w)
+        assert np.array_equal(got, exp), (sh, n0, co0, oh0, ow0)
+
+
+def pin_pointwise_gemm(orc):
+    """1x1 kernel, stride 1, no padding: grad_input[n] = W^T @ grad_out[n]
+    (numpy matmul over channels, float64)."""
+    rng = np.random.default_rng(6000)
+    for (n, ci, co, h, w_) in [(2, 5, 7, 3, 4), (1, 16, 9, 5, 5), (3, 1, 4, 2, 6)]:
+        sh = ConvShape("pw", n, ci, h, w_, co, 1, 1, 1, 0, 0, h, w_)
+        go = rng.uniform(-1, 1, size=sh.go_shape)
+        w = rng.uniform(-1, 1, size=sh.w_shape)
+        wt = w[:, :, 0, 0].T                       # [Ci, Co]
+        exp = np.matmul(wt[None], go.reshape(n, co, h * w_)).reshape(sh.gi_shape)
+        got = _gather(orc, sh, go, w)
+        assert _rel_err(got, exp) < 1e-13, sh
+
+
+def pin_zero_structure(orc):
+    """1x1 kernel with stride 2 and no padding: only even (ih, iw) are reached
+    by a tap; odd rows/cols are exactly zero and even ones are W^T @ grad_out."""
+    rng = np.random.default_rng(7000)
+    sh = ConvShape("s2k1", 2, 3, 7, 6, 4, 1, 1, 2, 0, 0, 4, 3)
+    go = rng.uniform(-1, 1, size=sh.go_shape)
+    w = rng.uniform(-1, 1, size=sh.w_shape)
+    got = _gather(orc, sh, go, w)
+    assert np.all(got[:, :, 1::2, :] == 0.0) and np.all(got[:, :, :, 1::2] == 0.0)
+    exp = np.einsum("oc,nohw->nchw", w[:, :, 0, 0], go)
+    assert _rel_err(got[:, :, ::2, ::2], exp) < 1e-13
+
+
+def pin_gather_at(orc):
+    """Sampled evaluation returns exactly the full gather at those indices."""
+    for i, sh in enumerate(_random_shapes()[:15]):
+        go, w = _inputs(sh, 8000 + i)
+        full = _gather(orc, sh, go, w).ravel()
+        rng = np.random.default_rng(8000 + i)
+        idx = rng.integers(0, full.size, size=min(64, full.size))
+        got = orc.grad_input_gather_at(go, w, sh.in_h, sh.in_w, sh.stride,
+                                       sh.padding_h, sh.padding_w, idx)
+        assert np.array_equal(got, full[idx]), sh
+
+
+def pin_integer_exact(orc):
+    """Integer inputs give the same exact integers as torch's float64 routine
+    (all partial sums are small integers, so every order is exact)."""
+    import torch
+    for i, sh in enumerate(_random_shapes()[:20]):
+        rng = np.random.default_rng(9000 + i)
+        go = rng.integers(-4, 5, size=sh.go_shape).astype(np.float64)
+        w = rng.integers(-4, 5, size=sh.w_shape).astype(np.float64)
+        ref = torch.nn.grad.conv2d_input(
+            sh.gi_shape, torch.from_numpy(w), torch.from_numpy(go),
+            stride=sh.stride, padding=(sh.padding_h, sh.padding_w)).numpy()
+        got = _gather(orc, sh, go, w)
+        assert np.array_equal(got, ref), sh
+        assert np.array_equal(got, np.round(got)), sh
+
+
+def pin_degenerate(orc):
+    """No output channels: the sum is empty and grad_input is all zeros."""
+    sh = ConvShape("co0", 1, 3, 5, 5, 0, 3, 3, 1, 1, 1, 5, 5)
+    go = np.zeros(sh.go_shape)
+    w = np.zeros(sh.w_shape)
+    got = _gather(orc, sh, go, w)
+    assert got.shape == sh.gi_shape and np.all(got == 0.0)
+
+
+ALL_PINS = [
+    pin_torch_grad_input,
+    pin_torch_forward,
+    pin_adjoint,
+    pin_gather_vs_scatter,
+    pin_all_ones,
+    pin_delta_weight,
+    pin_delta_grad_out,
+    pin_pointwise_gemm,
+    pin_zero_structure,
+    pin_gather_at,
+    pin_integer_exact,
+    pin_degenerate,
+]

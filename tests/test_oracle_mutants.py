@@ -1,0 +1,77 @@
+"""Planted mistakes in the oracle must trip at least one pin.
+
+Each mutant is a copy of oracle/oracle.c with one plausible slip (a flipped
+kernel, a wrong sign, swapped paddings, a transposed weight, a dropped tap or
+divisibility test, a shifted bound, a wrong initial value), compiled on the
+CPU into a temporary library.  The committed oracle passes every pin (see
+test_oracle.py); each mutant must fail at least one.
+"""
+import os
+
+import pytest
+
+import oracle
+from tests import oracle_pins
+
+# (name, function the slip goes into, text to replace, replacement)
+MUTANTS = [
+    ("gather_flipped_kernel", "oracle_grad_input_gather",
+     "w[((co * Ci + ci) * KH + kh) * KW + kw]",
+     "w[((co * Ci + ci) * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)]"),
+    ("gather_sign_h", "oracle_grad_input_gather",
+     "i64 th = ih + ph - kh;", "i64 th = ih - ph + kh;"),
+    ("gather_padding_swapped", "oracle_grad_input_gather",
+     "i64 tw = iw + pw - kw;", "i64 tw = iw + ph - kw;"),
+    ("gather_weight_transposed", "oracle_grad_input_gather",
+     "w[((co * Ci + ci)", "w[((ci * Co + co)"),
+    ("gather_no_divisibility", "oracle_grad_input_gather",
+     "if (th % s != 0 || tw % s != 0) continue;", ""),
+    ("gather_last_row_dropped", "oracle_grad_input_gather",
+     "if (oh >= OH || ow >= OW) continue;", "if (oh >= OH - 1 || ow >= OW) continue;"),
+    ("gather_last_tap_dropped", "oracle_grad_input_gather",
+     "kw < KW; ++kw", "kw < KW - 1; ++kw"),
+    ("gather_no_stride_divide", "oracle_grad_input_gather",
+     "i64 oh = th / s;", "i64 oh = th;"),
+    ("gather_bad_init", "oracle_grad_input_gather",
+     "double acc = 0.0;", "double acc = 1e-3;"),
+    ("gather_at_sign_w", "oracle_grad_input_gather_at",
+     "i64 tw = iw + pw - kw;", "i64 tw = iw - pw + kw;"),
+    ("scatter_sign_h", "oracle_grad_input_scatter",
+     "i64 ih = oh * s - ph + kh;", "i64 ih = oh * s + ph - kh;"),
+    ("scatter_flipped_kernel", "oracle_grad_input_scatter",
+     "w[((co * Ci + ci) * KH + kh) * KW + kw]",
+     "w[((co * Ci + ci) * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)]"),
+    ("forward_padding_swapped", "oracle_conv2d_forward",
+     "i64 iw = ow * s - pw + kw;", "i64 iw = ow * s - ph + kw;"),
+    ("forward_flipped_kernel", "oracle_conv2d_forward",
+     "w[((co * Ci + ci) * KH + kh) * KW + kw]",
+     "w[((co * Ci + ci) * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)]"),
+]
+
+
+def _mutate(src, func, old, new):
+    start = src.index("void %s(" % func)
+    nxt = src.find("\nvoid ", start + 1)
+    end = len(src) if nxt < 0 else nxt
+    body = src[start:end]
+    assert old in body, (func, old)
+    return src[:start] + body.replace(old, new, 1) + src[end:]
+
+
+@pytest.mark.parametrize("mutant", MUTANTS, ids=lambda m: m[0])
+def test_mutant_is_caught(mutant, tmp_path):
+    name, func, old, new = mutant
+    with open(oracle.SOURCE) as f:
+        src = f.read()
+    path = os.path.join(str(tmp_path), name + ".c")
+    with open(path, "w") as f:
+        f.write(_mutate(src, func, old, new))
+    lib = oracle.compile_source(path, os.path.join(str(tmp_path), name + ".so"))
+    orc = oracle.Oracle(lib)
+    tripped = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except AssertionError:
+            tripped.append(pin.__name__)
+    assert tripped, "mutant %s passed every pin" % name
