@@ -1,0 +1,182 @@
+#!/usr/bin/env python3
+"""Throughput of the conv2d input-gradient HIP path on one MI355X.
+
+One step = one conv2d_grad_input call over the whole workload (all batch
+items, all stride classes), inputs already resident in HBM.  Prints one JSON
+line with useful TFLOP/s (2*N*Co*out_h*out_w*Ci*kH*kW per second), the
+roofline of the kernel (timed with HIP events on the stream it runs on) and
+the CPU oracle timed on the host cores on the same workload.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--f16 | --fp32] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "conv2d grad-input useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
+# MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}
+PEAK_HBM_GBS = 8000.0
+KERNEL_SOURCES = ["conv2d_backward_implicit_amd/csrc/kernels.hip",
+                  "conv2d_backward_implicit_amd/csrc/tile_index.hpp",
+                  "conv2d_backward_implicit_amd/csrc/plan.hpp",
+                  "conv2d_backward_implicit_amd/csrc/plan.cpp"]
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_tag: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources; else None."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel_tag, workload))
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"^source_digest:\s*(\S+)", text, re.M)
+    m_val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
+    if not m_sha or not m_val or m_sha.group(1) != source_digest():
+        return None
+    return float(m_val.group(1))
+
+
+def cpu_baseline(shape, go, w):
+    """The oracle as it stands, on the whole workload, on this host's cores."""
+    import numpy as np
+    import oracle
+
+    go64 = np.ascontiguousarray(go, dtype=np.float64)
+    w64 = np.ascontiguousarray(w, dtype=np.float64)
+    orc = oracle.default()
+    t0 = time.perf_counter()
+    orc.grad_input_gather(go64, w64, shape.in_h, shape.in_w, shape.stride,
+                          shape.padding_h, shape.padding_w)
+    dt = time.perf_counter() - t0
+    return {"value": shape.useful_flops / dt / 1e12, "unit": "TFLOP/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": "whole workload (%d images), one pass, %.2f s" % (shape.batch, dt)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=None, help="workload name (default: headline)")
+    g = ap.add_mutually_exclusive_group()
+    g.add_argument("--f16", action="store_true", help="f16-staged path")
+    g.add_argument("--fp32", action="store_true", help="fp32 path")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each GPU would run its own batch shard with no exchange); "
+              "run with --gpus 1", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import conv2d_backward_implicit_amd as c2b
+    from conv2d_backward_implicit_amd.workloads import CONFIGS, HEADLINE, by_name, draw
+
+    shape = by_name(args.workload) if args.workload else CONFIGS[HEADLINE]
+    f16 = shape.f16_staged if not (args.f16 or args.fp32) else args.f16
+    dtype = "f16" if f16 else "f32"
+    seed = CONFIGS.index(shape)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    go, w = draw(shape, seed)
+    tgo = torch.from_numpy(go).to(dev)
+    tw = torch.from_numpy(w).to(dev)
+    gi = torch.empty(shape.gi_shape, dtype=torch.float32, device=dev)
+    p = c2b.make_params(shape.batch, shape.in_channels, shape.in_h, shape.in_w,
+                        shape.out_channels, shape.kernel_h, shape.kernel_w, shape.stride,
+                        shape.padding_h, shape.padding_w, shape.out_h, shape.out_w)
+    plan = c2b.describe_plan(p, f16)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, each bracketed by HIP events on the kernel's stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ev_avg_s = sum(ev_ms) / len(ev_ms) / 1e3
+
+    value = shape.useful_flops * args.steps / wall / 1e12
+    achieved = shape.useful_flops / ev_avg_s / 1e12
+    kernel_tag = "grad_input_%s" % dtype
+    traffic = measured_traffic(kernel_tag, shape.name)
+    # bound: compare the workload's arithmetic intensity (useful flops per
+    # compulsory byte) with the ridge point of the path's matrix peak
+    intensity = shape.useful_flops / shape.compulsory_bytes
+    ridge = PEAK_TFLOPS[dtype] * 1e12 / (PEAK_HBM_GBS * 1e9)
+    if intensity >= ridge:
+        roofline = {"bound": "mfma", "achieved": round(achieved, 3),
+                    "peak": PEAK_TFLOPS[dtype], "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_TFLOPS[dtype], 4), "traffic": traffic}
+    else:
+        gbs = shape.compulsory_bytes / ev_avg_s / 1e9
+        roofline = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                    "traffic": traffic}
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": dtype, "data": "synthetic",
+        "config": {"workload": shape.name, "batch": shape.batch,
+                   "in_channels": shape.in_channels, "out_channels": shape.out_channels,
+                   "in_hw": [shape.in_h, shape.in_w], "kernel": [shape.kernel_h, shape.kernel_w],
+                   "stride": shape.stride, "padding": [shape.padding_h, shape.padding_w],
+                   "out_hw": [shape.out_h, shape.out_w], "path": dtype},
+        "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS[dtype], 2),
+        "kernel_avg_us": round(ev_avg_s * 1e6, 3),
+        "compulsory_hbm_GBps": round(shape.compulsory_bytes / ev_avg_s / 1e9, 1),
+        "plan": plan,
+        "roofline": roofline,
+        "source_digest": source_digest(),
+    }
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(shape, go, w)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

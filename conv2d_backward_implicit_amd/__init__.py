@@ -1,0 +1,233 @@
+"""MI355X (gfx950) convolution input-gradient as an implicit GEMM.
+
+Thin Python binding over the C ABI of ``libconv2d_bwd.so`` (declared in
+``include/conv2d_bwd.h``).  Every step of the computation runs in the HIP
+kernels of that library; this module only marshals arguments (device
+pointers of torch tensors, the shape struct, torch's current HIP stream).
+If the library has not been built, every call raises -- there is no CPU
+fallback.
+
+    import conv2d_backward_implicit_amd as c2b
+    gi = c2b.grad_input(grad_out, weight, in_h=56, in_w=56, stride=1,
+                        padding_h=1, padding_w=1)          # fp32 path
+    gi = c2b.grad_input(..., f16=True)                     # f16-staged path
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "Conv2dParams", "Conv2dError", "PlanInfo", "grad_input", "grad_input_into",
+    "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
+    "describe_plan", "check_indexing", "status_string", "library_path", "load_library",
+    "make_params", "EXPORTED_SYMBOLS",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "libconv2d_bwd.so")
+
+# every extern "C" symbol include/conv2d_bwd.h declares
+EXPORTED_SYMBOLS = (
+    "conv2d_grad_input",
+    "conv2d_grad_input_f16",
+    "conv2d_check_params",
+    "conv2d_status_string",
+    "conv2d_describe_plan",
+    "conv2d_check_indexing",
+)
+
+CONV2D_OK = 0
+STATUS_NAMES = {
+    0: "CONV2D_OK",
+    -1: "CONV2D_ERR_NULL_PTR",
+    -2: "CONV2D_ERR_BAD_SHAPE",
+    -3: "CONV2D_ERR_ALIAS",
+    -4: "CONV2D_ERR_OVERFLOW",
+    -5: "CONV2D_ERR_UNSUPPORTED",
+    -6: "CONV2D_ERR_HIP",
+}
+
+
+class Conv2dParams(ctypes.Structure):
+    """Mirror of ``conv2d_params`` (12 x uint32, header field order)."""
+    _fields_ = [(name, ctypes.c_uint32) for name in (
+        "batch", "in_channels", "in_h", "in_w", "out_channels", "kernel_h",
+        "kernel_w", "stride", "padding_h", "padding_w", "out_h", "out_w")]
+
+    def as_tuple(self):
+        return tuple(getattr(self, f) for f, _ in self._fields_)
+
+    def __repr__(self):
+        return "Conv2dParams(%s)" % ", ".join(
+            "%s=%d" % (f, getattr(self, f)) for f, _ in self._fields_)
+
+
+class PlanInfo(ctypes.Structure):
+    """Mirror of ``conv2d_plan_info``."""
+    _fields_ = [(name, ctypes.c_int64) for name in (
+        "launches", "tiles", "phases", "zero_phases", "macs", "useful_macs")]
+
+    def as_dict(self):
+        return {f: int(getattr(self, f)) for f, _ in self._fields_}
+
+
+class Conv2dError(RuntimeError):
+    def __init__(self, status: int, what: str = ""):
+        self.status = int(status)
+        name = STATUS_NAMES.get(self.status, str(status))
+        msg = "%s (%s)" % (name, status_string(self.status))
+        super().__init__(msg + (": " + what if what else ""))
+
+
+_lib = None
+_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libconv2d_bwd.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(_LIB_PATH):
+            raise RuntimeError(
+                "libconv2d_bwd.so is not built; run "
+                "`python -m conv2d_backward_implicit_amd.build` (or "
+                "__graft_entry__.build()) first")
+        lib = ctypes.CDLL(_LIB_PATH)
+        P = ctypes.POINTER(Conv2dParams)
+        for name in ("conv2d_grad_input", "conv2d_grad_input_f16"):
+            fn = getattr(lib, name)
+            fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, P,
+                           ctypes.c_void_p]
+            fn.restype = ctypes.c_int
+        lib.conv2d_check_params.argtypes = [P]
+        lib.conv2d_check_params.restype = ctypes.c_int
+        lib.conv2d_status_string.argtypes = [ctypes.c_int]
+        lib.conv2d_status_string.restype = ctypes.c_char_p
+        lib.conv2d_describe_plan.argtypes = [P, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+        lib.conv2d_describe_plan.restype = ctypes.c_int
+        lib.conv2d_check_indexing.argtypes = [P, ctypes.c_int, ctypes.c_char_p,
+                                              ctypes.c_size_t]
+        lib.conv2d_check_indexing.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def make_params(batch, in_channels, in_h, in_w, out_channels, kernel_h, kernel_w,
+                stride=1, padding_h=0, padding_w=0, out_h=None, out_w=None):
+    """Fill a Conv2dParams; out_h/out_w default to the forward extents
+    floor((in + 2*pad - k) / stride) + 1."""
+    if out_h is None:
+        out_h = (in_h + 2 * padding_h - kernel_h) // stride + 1 if stride else 0
+    if out_w is None:
+        out_w = (in_w + 2 * padding_w - kernel_w) // stride + 1 if stride else 0
+    vals = (batch, in_channels, in_h, in_w, out_channels, kernel_h, kernel_w, stride,
+            padding_h, padding_w, out_h, out_w)
+    for v in vals:
+        if not 0 <= int(v) < 2 ** 32:
+            raise Conv2dError(-4, "field out of uint32 range: %r" % (v,))
+    return Conv2dParams(*(int(v) for v in vals))
+
+
+def status_string(status: int) -> str:
+    return load_library().conv2d_status_string(int(status)).decode()
+
+
+def check_params(p: Conv2dParams) -> int:
+    """Status of conv2d_check_params (pure host code, no device needed)."""
+    return int(load_library().conv2d_check_params(ctypes.byref(p)))
+
+
+def describe_plan(p: Conv2dParams, f16: bool = False) -> dict:
+    """Launch plan of a shape (pure host code).  Raises on a bad shape."""
+    info = PlanInfo()
+    rc = load_library().conv2d_describe_plan(ctypes.byref(p), int(bool(f16)),
+                                             ctypes.byref(info))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return info.as_dict()
+
+
+def check_indexing(p: Conv2dParams, f16: bool = False) -> tuple:
+    """Host replay of the kernels' addressing for a shape (no device needed).
+    Returns (status, message); status 0 means every check passed."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().conv2d_check_indexing(ctypes.byref(p), int(bool(f16)), buf,
+                                              len(buf))
+    return int(rc), buf.value.decode()
+
+
+def conv2d_grad_input(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,
+                      p: Conv2dParams, stream: int = 0) -> int:
+    """Raw C-ABI call with integer device pointers; returns the status."""
+    return int(load_library().conv2d_grad_input(
+        ctypes.c_void_p(grad_out_ptr), ctypes.c_void_p(weight_ptr),
+        ctypes.c_void_p(grad_input_ptr), ctypes.byref(p), ctypes.c_void_p(stream)))
+
+
+def conv2d_grad_input_f16(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,
+                          p: Conv2dParams, stream: int = 0) -> int:
+    """Raw C-ABI call of the f16-staged path; returns the status."""
+    return int(load_library().conv2d_grad_input_f16(
+        ctypes.c_void_p(grad_out_ptr), ctypes.c_void_p(weight_ptr),
+        ctypes.c_void_p(grad_input_ptr), ctypes.byref(p), ctypes.c_void_p(stream)))
+
+
+def _check_tensor(t, name, shape):
+    import torch
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.dtype != torch.float32:
+        raise TypeError("%s must be float32, got %s" % (name, t.dtype))
+    if t.device.type != "cuda":
+        raise ValueError("%s must be on a GPU device, got %s" % (name, t.device))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), shape))
+
+
+def grad_input_into(grad_input, grad_out, weight, p: Conv2dParams, f16=False,
+                    stream=None):
+    """Write the input gradient into ``grad_input`` on torch's current stream
+    (or ``stream``, a torch.cuda.Stream).  Raises Conv2dError on a bad status."""
+    import torch
+    _check_tensor(grad_out, "grad_out", (p.batch, p.out_channels, p.out_h, p.out_w))
+    _check_tensor(weight, "weight", (p.out_channels, p.in_channels, p.kernel_h,
+                                     p.kernel_w))
+    _check_tensor(grad_input, "grad_input", (p.batch, p.in_channels, p.in_h, p.in_w))
+    if not (grad_out.device == weight.device == grad_input.device):
+        raise ValueError("all tensors must be on the same device")
+    with torch.cuda.device(grad_input.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        fn = conv2d_grad_input_f16 if f16 else conv2d_grad_input
+        rc = fn(grad_out.data_ptr(), weight.data_ptr(), grad_input.data_ptr(), p,
+                int(s.cuda_stream))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return grad_input
+
+
+def grad_input(grad_out, weight, in_h, in_w, stride=1, padding_h=0, padding_w=0,
+               f16=False, out=None, stream=None):
+    """Input gradient of conv2d for NCHW ``grad_out`` and [Co, Ci, kH, kW]
+    ``weight`` (float32 GPU tensors).  Returns a new [N, Ci, in_h, in_w]
+    tensor (or fills ``out``)."""
+    import torch
+    n, co, oh, ow = (int(v) for v in grad_out.shape)
+    co2, ci, kh, kw = (int(v) for v in weight.shape)
+    if co2 != co:
+        raise ValueError("grad_out has %d channels, weight has %d" % (co, co2))
+    p = make_params(n, ci, in_h, in_w, co, kh, kw, stride, padding_h, padding_w,
+                    oh, ow)
+    if out is None:
+        out = torch.empty((n, ci, in_h, in_w), dtype=torch.float32,
+                          device=grad_out.device)
+    return grad_input_into(out, grad_out, weight, p, f16=f16, stream=stream)

@@ -1,0 +1,288 @@
+// Convolution input-gradient as an implicit GEMM on CDNA4 (gfx950) matrix
+// cores, and the C-ABI entry points that launch it.
+//
+// What is computed (meganeura 0.2.0, conv2d_grad_input_gemm_coop.wgsl, header
+// comment): per batch item, C[Ci, H*W] = A[Ci, K] x B[K, H*W] with
+// K = Co*kH*kW, A[ci, (co,kh,kw)] = weight[co, ci, kh, kw] (weight_T staging)
+// and B the im2col of grad_out under the stride > 1 gather rule.
+//
+// How it is computed here (a re-design for gfx950, not the shader's scheme):
+//  * Stride-residue classes (plan.hpp): every class is a dense stride-1
+//    problem on a sub-image, so no structural zero is staged or multiplied.
+//  * One workgroup = 4 waves owns a 64-channel x 256-pixel output tile of one
+//    class; pixels are consecutive (row-major) positions of one band of the
+//    class sub-image of one image.  Batch, class and band are all folded into
+//    the one-dimensional grid.
+//  * B is never materialised: per stage the workgroup copies the grad_out
+//    window its pixels read (band rows plus the kernel halo, zero outside the
+//    image) into LDS once, coalesced along rows; every tap then reads the
+//    window at a fixed offset, so each grad_out element crosses from L2/HBM
+//    once per stage instead of once per tap.
+//  * A (the stage's weights) is copied to LDS with a channel-fastest layout.
+//  * Register-staged prefetch: the global loads of stage s+1 are issued
+//    before the matrix instructions of stage s.
+//  * Matrix cores: fp32 path v_mfma_f32_32x32x2_f32, f16-staged path
+//    v_mfma_f32_32x32x16_f16 (operands rounded to f16 on the way into LDS);
+//    each wave owns 2 x 2 blocks of 32x32 with fp32 accumulators.
+//  * Epilogue: masked stores straight to NCHW grad_input; every pixel of a
+//    class is owned by exactly one tile, so grad_input is overwritten once,
+//    with no race between workgroups.
+#include <hip/hip_runtime.h>
+
+#include "tile_index.hpp"
+
+namespace c2b {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct alignas(16) Half8 {
+  _Float16 v[8];
+};
+
+// f32 -> f16 with round-to-nearest-even (the hardware conversion in the
+// default rounding mode), 8 values into one 16-byte LDS cell.
+__device__ __forceinline__ Half8 pack8(const float (&x)[8]) {
+  Half8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r.v[i] = (_Float16)x[i];
+  return r;
+}
+
+template <bool F16>
+struct Cell;
+template <>
+struct Cell<false> {
+  using type = float;
+  static constexpr int kChannels = 1;   // output channels per LDS cell
+  static constexpr int kKPerStep = 2;   // k values per matrix instruction
+};
+template <>
+struct Cell<true> {
+  using type = Half8;
+  static constexpr int kChannels = 8;
+  static constexpr int kKPerStep = 16;
+};
+
+// A/B operands of one k-step for both 32-pixel blocks, then the 2 x 2 block
+// products.  NB = number of pixel blocks of this wave that hold a pixel.
+template <bool F16, int NB>
+__device__ __forceinline__ void mma_step(const typename Cell<F16>::type* sA,
+                                         const typename Cell<F16>::type* sH, int ai,
+                                         const int (&bi)[2], f32x16 (&acc)[2][2]) {
+  if constexpr (!F16) {
+    const float a0 = sA[ai], a1 = sA[ai + 32];
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const float b = sH[bi[nb]];
+      acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0][nb], 0, 0, 0);
+      acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1][nb], 0, 0, 0);
+    }
+  } else {
+    const f16x8 a0 = __builtin_bit_cast(f16x8, sA[ai]);
+    const f16x8 a1 = __builtin_bit_cast(f16x8, sA[ai + 32]);
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const f16x8 b = __builtin_bit_cast(f16x8, sH[bi[nb]]);
+      acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b, acc[0][nb], 0, 0, 0);
+      acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b, acc[1][nb], 0, 0, 0);
+    }
+  }
+}
+
+template <bool F16, int MT, int NT, int CK, int TAPS, int SLAB>
+__global__ __launch_bounds__(kThreads) void grad_input_kernel(const LaunchArgs a) {
+  using T = typename Cell<F16>::type;
+  using G = KernelGeom<F16, MT, CK, TAPS, SLAB>;
+  static_assert(MT == 64 && NT == 256, "4 waves x 2x2 blocks of 32x32");
+  static_assert(G::kCPC == Cell<F16>::kChannels && G::kKPerStep == Cell<F16>::kKPerStep,
+                "cell geometry");
+  constexpr int CPC = G::kCPC;
+  constexpr int NCG = G::kNCG;
+  constexpr int KSTEPS = G::kKSteps;
+  constexpr int PITCH = G::kPitch;
+  constexpr int HS = G::kHS;
+  constexpr int AE = G::kAE;
+  constexpr int WS = G::kWS;
+  static_assert(SLAB % 64 == 32 || F16, "fp32 window pitch keeps half-waves 32 banks apart");
+  __shared__ T sA[G::kLdsA];
+  __shared__ T sH[G::kLdsH];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const TileCtx c = decode_tile<MT, CK>(a, blockIdx.x);
+  const PhaseDesc& P = c.P;
+  const int OHOW = a.OH * a.OW;
+  const int cstride = a.Ci * a.KH * a.KW;   // weight distance between channels
+  const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
+
+  int goff[HS];
+#pragma unroll
+  for (int k = 0; k < HS; ++k) goff[k] = window_slot_offset(c, a, tid + kThreads * k);
+
+  // pixel blocks of this wave holding at least one pixel (wave-uniform)
+  const int first = wave * 64;
+  const int nact = first >= c.npx ? 0 : (first + 32 >= c.npx ? 1 : 2);
+  int bbase[2];
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) bbase[nb] = h * SLAB + window_base(c, first + nb * 32 + l32);
+  const int abase = h * PITCH + l32;
+
+  int woff[WS];
+  int wgroup = -1;
+  float hreg[CK][HS];
+  float wreg[WS][CPC];
+  auto load_stage = [&](int st) {
+    int co0, g;
+    stage_split(c, CK, st, &co0, &g);
+    if (g != wgroup) {
+#pragma unroll
+      for (int k = 0; k < WS; ++k)
+        woff[k] = weight_cell_offset<MT, NCG, TAPS, CPC>(c, a, tid + kThreads * k, g);
+      wgroup = g;
+    }
+#pragma unroll
+    for (int co = 0; co < CK; ++co) {
+      const bool cv = co0 + co < a.Co;
+      const float* src = go_n + (size_t)(co0 + co) * OHOW;
+#pragma unroll
+      for (int k = 0; k < HS; ++k) hreg[co][k] = (cv && goff[k] >= 0) ? src[goff[k]] : 0.0f;
+    }
+    const float* wsrc = a.w + (size_t)co0 * cstride;
+#pragma unroll
+    for (int k = 0; k < WS; ++k) {
+      const int cc = co0 + weight_cell_channel<MT, NCG, CPC>(tid + kThreads * k);
+#pragma unroll
+      for (int v = 0; v < CPC; ++v)
+        wreg[k][v] = (woff[k] >= 0 && cc + v < a.Co) ? wsrc[woff[k] + v * cstride] : 0.0f;
+    }
+  };
+  auto store_stage = [&]() {
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int k = 0; k < HS; ++k) {
+        const int f = tid + kThreads * k;
+        if (f < SLAB) {
+          if constexpr (F16) {
+            float x[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) x[v] = hreg[cg * 8 + v][k];
+            sH[cg * SLAB + f] = pack8(x);
+          } else {
+            sH[cg * SLAB + f] = hreg[cg][k];
+          }
+        }
+      }
+#pragma unroll
+    for (int k = 0; k < WS; ++k) {
+      const int e = tid + kThreads * k;
+      if (e < AE) {
+        if constexpr (F16)
+          sA[weight_cell_lds<MT, NCG, PITCH>(e)] = pack8(wreg[k]);
+        else
+          sA[weight_cell_lds<MT, NCG, PITCH>(e)] = wreg[k][0];
+      }
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // taps of stage st: k-step ks of tap tt uses cell group 2*ks + h
+  auto compute_stage = [&](auto nb_tag, int st) {
+    constexpr int NB = decltype(nb_tag)::value;
+    int co0, g;
+    stage_split(c, CK, st, &co0, &g);
+    const int tap0 = g * TAPS;
+    const int ntg = imin(TAPS, c.ntaps - tap0);
+    int j = tap0 / P.tw;
+    int l = tap0 - j * P.tw;
+    for (int tt = 0; tt < ntg; ++tt) {
+      const int boff = tap_window_offset(c, j, l);
+      const int bi0[2] = {bbase[0] + boff, bbase[1] + boff};
+#pragma unroll
+      for (int ks = 0; ks < KSTEPS; ++ks) {
+        const int ai = abase + (tt * NCG + 2 * ks) * PITCH;
+        const int bi[2] = {bi0[0] + 2 * ks * SLAB, bi0[1] + 2 * ks * SLAB};
+        mma_step<F16, NB>(sA, sH, ai, bi, acc);
+      }
+      if (++l == P.tw) {
+        l = 0;
+        ++j;
+      }
+    }
+  };
+
+  if (c.nstages > 0) load_stage(0);
+  for (int st = 0; st < c.nstages; ++st) {
+    __syncthreads();
+    store_stage();
+    __syncthreads();
+    if (st + 1 < c.nstages) load_stage(st + 1);
+    if (nact == 2)
+      compute_stage(std::integral_constant<int, 2>(), st);
+    else if (nact == 1)
+      compute_stage(std::integral_constant<int, 1>(), st);
+  }
+
+  float* gi_n = a.gi + (size_t)c.n * a.Ci * (a.H * a.W);
+  const size_t HW = (size_t)a.H * a.W;
+#pragma unroll
+  for (int nb = 0; nb < 2; ++nb) {
+    const int po = output_offset(c, a, first + nb * 32 + l32);
+    if (po < 0) continue;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int ci = c.ci0 + mb * 32 + acc_row(r, h);
+        if (ci < a.Ci) gi_n[ci * HW + po] = acc[mb][nb][r];
+      }
+  }
+}
+
+template <bool F16>
+constexpr TileShape tile_of() {
+  return F16 ? kF16Tile : kF32Tile;
+}
+
+template <bool F16>
+int launch(const float* go, const float* w, float* gi, const conv2d_params* p, void* stream) {
+  constexpr TileShape ts = tile_of<F16>();
+  int rc = validate_shape(p);
+  if (rc != CONV2D_OK) return rc;
+  rc = check_pointers(go, w, gi, p);
+  if (rc != CONV2D_OK) return rc;
+  std::vector<LaunchArgs> launches;
+  rc = build_plan(p, ts, &launches, nullptr);
+  if (rc != CONV2D_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (LaunchArgs& la : launches) {
+    la.go = go;
+    la.w = w;
+    la.gi = gi;
+    if (la.total_tiles == 0) continue;
+    hipLaunchKernelGGL((grad_input_kernel<F16, ts.mt, ts.nt, ts.ck, ts.taps, ts.slab>),
+                       dim3(la.total_tiles), dim3(kThreads), 0, st, la);
+  }
+  if (hipGetLastError() != hipSuccess) return CONV2D_ERR_HIP;
+  return CONV2D_OK;
+}
+
+}  // namespace c2b
+
+extern "C" int conv2d_grad_input(const float* grad_out, const float* weight, float* grad_input,
+                                 const conv2d_params* p, void* stream) {
+  return c2b::launch<false>(grad_out, weight, grad_input, p, stream);
+}
+
+extern "C" int conv2d_grad_input_f16(const float* grad_out, const float* weight,
+                                     float* grad_input, const conv2d_params* p, void* stream) {
+  return c2b::launch<true>(grad_out, weight, grad_input, p, stream);
+}

@@ -1,0 +1,93 @@
+// Launch planning for the conv2d input-gradient kernels (internal header).
+//
+// The planner is plain host C++: it validates a conv2d_params, splits the
+// problem into stride-residue phases and tiles, and fills the by-value
+// argument block each kernel launch receives.  The kernels only decode their
+// tile from that block.
+//
+// Stride-residue phases.  In the gather rule of the shader's stride > 1
+// im2col branch (meganeura 0.2.0, conv2d_grad_input_gemm_coop.wgsl), a tap
+// (kh, kw) contributes to input pixel (ih, iw) only if ih + padding_h - kh and
+// iw + padding_w - kw are both multiples of s.  Grouping input rows by
+// rh = (ih + padding_h) mod s and kernel rows by kh mod s, only kernel rows
+// with kh = rh (mod s) ever reach the rows of class rh (likewise for columns).
+// Each class (rh, rw) is therefore a dense stride-1 problem on the sub-image
+//   ih = ih0 + s*i',  iw = iw0 + s*j'
+// with the sub-kernel kh = rh + s*j, kw = rw + s*l (j < th, l < tw), and the
+// grad_out row it reads is oh = i' + ch - j (column ow = j' + cw - l), where
+// ch = (ih0 + padding_h - rh) / s.  For s = 1 there is one class.  No
+// structural zero is ever multiplied; classes that no tap reaches (s > kernel)
+// are written as zeros.
+#pragma once
+
+#include <stdint.h>
+
+namespace c2b {
+
+constexpr int kMaxPhasesPerLaunch = 16;
+
+// One stride-residue class and its tiling.
+struct PhaseDesc {
+  int32_t rh, rw;      // residues of (ih + padding_h), (iw + padding_w) mod s
+  int32_t ih0, iw0;    // first input row / column of the class
+  int32_t hp, wp;      // rows / columns of the class sub-image
+  int32_t th, tw;      // sub-kernel taps per axis (0: class gets zeros)
+  int32_t ch, cw;      // grad_out row = i' + ch - j, column = j' + cw - l
+  int32_t wb;          // band width: sub-image columns per band
+  int32_t nbands;      // bands per sub-image row, ceil(wp / wb)
+  int32_t ntv;         // pixels per tile (<= the kernel's lane tile)
+  int32_t ptiles;      // tiles per (image, band): ceil(hp * wb / ntv)
+  int32_t ngroups;     // tap groups: ceil(th * tw / taps per stage)
+  int32_t tiles;       // tiles of this class in the launch
+  int32_t tile_begin;  // first workgroup index of this class in the launch
+  int32_t pad_;
+};
+
+// By-value kernel argument block of one launch.
+struct LaunchArgs {
+  const float* go;
+  const float* w;
+  float* gi;
+  int32_t N, Ci, H, W, Co, KH, KW, S, PH, PW, OH, OW;
+  int32_t ciblocks;    // ceil(Ci / channel tile)
+  int32_t nphases;     // classes in this launch, heaviest first
+  int32_t total_tiles; // workgroups in this launch
+  int32_t pad_;
+  PhaseDesc ph[kMaxPhasesPerLaunch];
+};
+
+// Compile-time tile shape of one kernel variant, as the planner sees it.
+struct TileShape {
+  int mt;     // input channels per workgroup
+  int nt;     // pixel lanes per workgroup
+  int ck;     // output channels staged per stage
+  int taps;   // kernel taps staged per stage
+  int slab;   // staged grad_out elements per output channel (halo window)
+};
+
+}  // namespace c2b
+
+#include <vector>
+
+#include "../../include/conv2d_bwd.h"
+
+namespace c2b {
+
+// Tile shapes of the two kernel families (the kernels static_assert that
+// their template arguments match these).
+constexpr TileShape kF32Tile{64, 256, 8, 9, 608};
+constexpr TileShape kF16Tile{64, 256, 16, 9, 608};
+
+// Shape checks shared by every entry point (no pointer is looked at).
+int validate_shape(const conv2d_params* p);
+
+// Full plan for one tile shape: validate, split into classes and tiles, and
+// append one LaunchArgs per launch (pointers left null).  `info` may be null.
+int build_plan(const conv2d_params* p, const TileShape& ts,
+               std::vector<LaunchArgs>* launches, conv2d_plan_info* info);
+
+// Pointer checks: NULL inputs of non-empty tensors and output/input overlap.
+int check_pointers(const float* go, const float* w, const float* gi,
+                   const conv2d_params* p);
+
+}  // namespace c2b

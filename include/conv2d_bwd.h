@@ -1,0 +1,166 @@
+/*
+ * conv2d_bwd.h -- C ABI of the MI355X (gfx950) convolution input-gradient
+ * library (libconv2d_bwd.so).
+ *
+ * Operation.  For a 2-D cross-correlation y = conv2d(x, weight) with one
+ * stride s for both axes and separate paddings padding_h / padding_w, the
+ * library computes the gradient with respect to the input:
+ *
+ *   grad_input[n, ci, ih, iw] =
+ *       sum over co, kh, kw with  th = ih + padding_h - kh >= 0,
+ *                                 tw = iw + padding_w - kw >= 0,
+ *                                 th % s == 0, tw % s == 0,
+ *                                 th / s < out_h,  tw / s < out_w
+ *       of grad_out[n, co, th / s, tw / s] * weight[co, ci, kh, kw].
+ *
+ * Source: the docs.rs source page of meganeura 0.2.0,
+ * src/shaders/conv2d_grad_input_gemm_coop.wgsl.  Its header comment defines
+ * the per-item product C[Ci, H*W] = A[Ci, Co*kH*kW] x B[Co*kH*kW, H*W] with
+ * A = weight transposed and B = im2col(grad_out) transposed; its weight_T
+ * staging fixes the weight index (no kernel flip); its stride > 1 im2col
+ * branch fixes the divisibility rule above, used here for every stride; its
+ * `Params` struct fixes the twelve shape fields (reordered below) and its
+ * final store overwrites grad_input.
+ *
+ * Layouts (all dense, row-major, fp32 in device memory):
+ *   grad_out   [batch, out_channels, out_h, out_w]
+ *   weight     [out_channels, in_channels, kernel_h, kernel_w]
+ *   grad_input [batch, in_channels, in_h, in_w]
+ *
+ * Ownership.  The caller owns all three device buffers and keeps them alive
+ * until the work enqueued on `stream` has completed.  `p` is read during the
+ * call only.  The library keeps no per-call state and allocates nothing, so
+ * calls are reentrant; calls on different streams that write the same
+ * grad_input race like any other kernels would.
+ *
+ * Semantics.  grad_input is fully overwritten (elements no tap reaches are
+ * set to 0).  grad_out and weight are only read.  grad_input must not overlap
+ * either input.  The call is asynchronous on `stream` (a hipStream_t; NULL
+ * means the null stream); execution faults surface at the caller's next
+ * synchronisation.
+ *
+ * Errors.  Every entry point returns an int status: CONV2D_OK (0) or a
+ * negative CONV2D_ERR_* code.  On any validation error nothing is enqueued and
+ * nothing is written.  Nothing is printed and no exception crosses the ABI.
+ */
+#ifndef CONV2D_BWD_H_
+#define CONV2D_BWD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* The twelve shape fields of the shader's `Params` uniform, in the order
+ * batch, in_channels, in_h, in_w, out_channels, kernel_h, kernel_w, stride,
+ * padding_h, padding_w, out_h, out_w (the shader itself stores padding_w
+ * last).  48 bytes. */
+typedef struct conv2d_params {
+  uint32_t batch;
+  uint32_t in_channels;
+  uint32_t in_h;
+  uint32_t in_w;
+  uint32_t out_channels;
+  uint32_t kernel_h;
+  uint32_t kernel_w;
+  uint32_t stride;
+  uint32_t padding_h;
+  uint32_t padding_w;
+  uint32_t out_h;
+  uint32_t out_w;
+} conv2d_params;
+
+enum {
+  CONV2D_OK = 0,
+  CONV2D_ERR_NULL_PTR = -1,    /* a required pointer is NULL                 */
+  CONV2D_ERR_BAD_SHAPE = -2,   /* stride/kernel 0, input smaller than kernel
+                                  after padding, or out_h/out_w differ from
+                                  floor((in + 2*pad - k) / stride) + 1       */
+  CONV2D_ERR_ALIAS = -3,       /* grad_input overlaps grad_out or weight     */
+  CONV2D_ERR_OVERFLOW = -4,    /* a per-image plane or the weight has
+                                  >= 2^31 elements, or the tile count does   */
+  CONV2D_ERR_UNSUPPORTED = -5, /* one kernel tap window of one stride phase
+                                  does not fit the on-chip staging tile
+                                  (kernel_h*kernel_w / stride^2 too large)   */
+  CONV2D_ERR_HIP = -6          /* the HIP runtime reported an error at
+                                  launch (hipGetLastError)                   */
+};
+
+/*
+ * fp32 path: operands staged in fp32, products on the fp32 matrix cores
+ * (v_mfma_f32_32x32x2_f32), fp32 accumulation.
+ *   grad_out, weight: device pointers to the inputs (layouts above).
+ *   grad_input:       device pointer to the output, fully overwritten.
+ *   p:                host pointer to the shape.
+ *   stream:           hipStream_t to enqueue on (NULL: null stream).
+ * Returns CONV2D_OK or a CONV2D_ERR_* code.
+ */
+int conv2d_grad_input(const float* grad_out, const float* weight,
+                      float* grad_input, const conv2d_params* p, void* stream);
+
+/*
+ * f16-staged path: the same operation and contract.  Storage stays fp32;
+ * both operands are rounded to f16 (round to nearest even) as they are
+ * staged on chip, products run on the f16 matrix cores
+ * (v_mfma_f32_32x32x16_f16) and accumulate in fp32.  This is the shader's
+ * $ENABLE_F16 specialisation: f16 workgroup tiles, fp32 buffers and store.
+ */
+int conv2d_grad_input_f16(const float* grad_out, const float* weight,
+                          float* grad_input, const conv2d_params* p,
+                          void* stream);
+
+/*
+ * Validate a shape without touching any device or pointer (pure host code).
+ * Returns CONV2D_OK, CONV2D_ERR_NULL_PTR (p == NULL), CONV2D_ERR_BAD_SHAPE,
+ * CONV2D_ERR_OVERFLOW or CONV2D_ERR_UNSUPPORTED, exactly as the compute entry
+ * points would for this shape.
+ */
+int conv2d_check_params(const conv2d_params* p);
+
+/* Static English description of a status code (never NULL). */
+const char* conv2d_status_string(int status);
+
+/*
+ * Launch plan of a shape, for inspection and host-side tests (pure host
+ * code).  `f16` selects the plan of conv2d_grad_input_f16.  Fills `out`:
+ *   out->launches      kernel launches the call would make
+ *   out->tiles         workgroups over all launches
+ *   out->phases        stride-residue phases with at least one pixel
+ *   out->zero_phases   of those, phases no kernel tap reaches (written as 0)
+ *   out->macs          multiply-adds issued, counting padded tile lanes
+ *   out->useful_macs   N*Co*out_h*out_w*Ci*kH*kW
+ * Returns the status conv2d_check_params returns.
+ */
+typedef struct conv2d_plan_info {
+  int64_t launches;
+  int64_t tiles;
+  int64_t phases;
+  int64_t zero_phases;
+  int64_t macs;
+  int64_t useful_macs;
+} conv2d_plan_info;
+
+int conv2d_describe_plan(const conv2d_params* p, int f16,
+                         conv2d_plan_info* out);
+
+/*
+ * Host-side replay of the kernels' addressing for a shape (pure host code,
+ * no device needed).  Walks every workgroup and thread of every launch that
+ * conv2d_grad_input (f16 == 0) or conv2d_grad_input_f16 (f16 != 0) would
+ * make and checks that every global and LDS access is in bounds, that every
+ * tap reads the grad_out and weight elements of the gather rule above, and
+ * that each grad_input element is written exactly once.  Returns CONV2D_OK,
+ * a CONV2D_ERR_* code of conv2d_check_params, or 1 on a failed check, with a
+ * description in `msg` (NUL-terminated, at most msg_len bytes; may be NULL).
+ * Cost is proportional to the problem's multiply-adds / 64.
+ */
+int conv2d_check_indexing(const conv2d_params* p, int f16, char* msg,
+                          size_t msg_len);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONV2D_BWD_H_ */

@@ -1,0 +1,56 @@
+"""Helpers for the GPU tests: run the HIP path through the C ABI on seeded
+host arrays, with a NaN-filled output (every element must be written) framed
+by guard bands (no element outside grad_input may change)."""
+from __future__ import annotations
+
+import numpy as np
+
+import conv2d_backward_implicit_amd as c2b
+from conv2d_backward_implicit_amd.workloads import ConvShape
+
+GUARD = 1024          # float32 elements of canary before and after grad_input
+CANARY = -12345.678   # any value the kernels never produce from these inputs
+
+TOL = {False: 1e-4, True: 2e-2}   # max|gpu - ref| / max|ref|, fp32 / f16-staged
+
+
+def params_of(sh: ConvShape):
+    return c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w,
+                           sh.out_channels, sh.kernel_h, sh.kernel_w, sh.stride,
+                           sh.padding_h, sh.padding_w, sh.out_h, sh.out_w)
+
+
+def run_gpu(sh: ConvShape, go: np.ndarray, w: np.ndarray, f16: bool = False,
+            stream=None, check_guards: bool = True) -> np.ndarray:
+    """grad_input of the HIP path, as a float32 numpy array."""
+    import torch
+    dev = torch.device("cuda", 0)
+    tgo = torch.from_numpy(np.ascontiguousarray(go, dtype=np.float32)).to(dev)
+    tw = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev)
+    n = int(np.prod(sh.gi_shape))
+    buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=torch.float32, device=dev)
+    buf[:GUARD] = CANARY
+    buf[GUARD + n:] = CANARY
+    gi = buf[GUARD:GUARD + n].view(sh.gi_shape)
+    c2b.grad_input_into(gi, tgo, tw, params_of(sh), f16=f16, stream=stream)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    if check_guards:
+        assert np.all(host[:GUARD] == np.float32(CANARY)), "write before grad_input"
+        assert np.all(host[GUARD + n:] == np.float32(CANARY)), "write after grad_input"
+    return host[GUARD:GUARD + n].reshape(sh.gi_shape)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    if ref.size == 0:
+        return 0.0
+    scale = float(np.max(np.abs(ref)))
+    diff = float(np.max(np.abs(got.astype(np.float64) - ref)))
+    if scale == 0.0:
+        return diff
+    return diff / scale
+
+
+def round_f16(a: np.ndarray) -> np.ndarray:
+    """float32 -> nearest float16 (ties to even, numpy's cast) -> float64."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float64)

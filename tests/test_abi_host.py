@@ -1,0 +1,188 @@
+"""Host-side checks of the C ABI: no GPU needed, no kernel is launched.
+
+The library must load on a machine without a GPU, export every function the
+header declares, and turn every invalid argument into its status code before
+any HIP call is made.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import conv2d_backward_implicit_amd as c2b
+from conv2d_backward_implicit_amd.workloads import CONFIGS
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "conv2d_bwd.h")
+
+OK, NULL, BAD, ALIAS, OVF, UNSUP = 0, -1, -2, -3, -4, -5
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv2d_\w+)\s*\(",
+                                 text, flags=re.M)))
+
+
+def _p(**kw):
+    base = dict(batch=1, in_channels=3, in_h=8, in_w=8, out_channels=4,
+                kernel_h=3, kernel_w=3, stride=1, padding_h=1, padding_w=1)
+    base.update(kw)
+    return c2b.make_params(**base)
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    lib = c2b.load_library()
+    declared = _header_functions()
+    assert declared == sorted(c2b.EXPORTED_SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_params_struct_layout_matches_header():
+    assert ctypes.sizeof(c2b.Conv2dParams) == 48
+    text = open(HEADER).read()
+    body = re.search(r"typedef struct conv2d_params \{(.*?)\} conv2d_params;", text,
+                     re.S).group(1)
+    fields = re.findall(r"uint32_t (\w+);", body)
+    assert fields == [f for f, _ in c2b.Conv2dParams._fields_]
+    assert ctypes.sizeof(c2b.PlanInfo) == 48
+
+
+def test_status_strings():
+    for code in (OK, NULL, BAD, ALIAS, OVF, UNSUP, -6):
+        s = c2b.status_string(code)
+        assert s and s != "unknown status", code
+    assert c2b.status_string(12345) == "unknown status"
+
+
+def test_valid_shapes_ok():
+    for cfg in CONFIGS:
+        p = c2b.make_params(cfg.batch, cfg.in_channels, cfg.in_h, cfg.in_w,
+                            cfg.out_channels, cfg.kernel_h, cfg.kernel_w, cfg.stride,
+                            cfg.padding_h, cfg.padding_w, cfg.out_h, cfg.out_w)
+        assert c2b.check_params(p) == OK, cfg.name
+
+
+def test_null_params():
+    lib = c2b.load_library()
+    assert lib.conv2d_check_params(None) == NULL
+    info = c2b.PlanInfo()
+    assert lib.conv2d_describe_plan(None, 0, ctypes.byref(info)) == NULL
+    assert lib.conv2d_describe_plan(ctypes.byref(_p()), 0, None) == NULL
+
+
+@pytest.mark.parametrize("kw", [
+    dict(stride=0, out_h=1, out_w=1),
+    dict(kernel_h=0, out_h=10),
+    dict(kernel_w=0, out_w=10),
+    dict(out_h=7),                       # forward extent is 8
+    dict(out_w=9),
+    dict(in_h=1, padding_h=0, out_h=1),  # padded input smaller than kernel
+    dict(in_w=2, padding_w=0, kernel_w=3, out_w=1),
+])
+def test_bad_shape(kw):
+    assert c2b.check_params(_p(**kw)) == BAD
+
+
+def test_padding_axes_are_separate():
+    # out_h follows padding_h and out_w follows padding_w
+    p = _p(in_h=9, in_w=9, padding_h=0, padding_w=2, out_h=7, out_w=11)
+    assert c2b.check_params(p) == OK
+    p = _p(in_h=9, in_w=9, padding_h=0, padding_w=2, out_h=11, out_w=7)
+    assert c2b.check_params(p) == BAD
+
+
+def test_overflow():
+    # per-image grad_input plane of 2^31 elements
+    p = _p(in_channels=2 ** 11, in_h=2 ** 10, in_w=2 ** 10)
+    assert c2b.check_params(p) == OVF
+    # weight of 2^31 elements
+    p = _p(in_channels=2 ** 16, out_channels=2 ** 15, kernel_h=1, kernel_w=1,
+           padding_h=0, padding_w=0)
+    assert c2b.check_params(p) == OVF
+    # a large batch alone is fine (64-bit batch offsets)
+    p = _p(batch=2 ** 20)
+    assert c2b.check_params(p) == OK
+
+
+def test_unsupported_kernel_window():
+    # a 40x40 stride-1 kernel window cannot be staged on chip
+    p = _p(in_h=64, in_w=64, kernel_h=40, kernel_w=40, padding_h=0, padding_w=0)
+    assert c2b.check_params(p) == UNSUP
+    # the same kernel with stride 4 splits into 16 classes of 10x10 taps
+    p = _p(in_h=64, in_w=64, kernel_h=40, kernel_w=40, padding_h=0, padding_w=0,
+           stride=4)
+    assert c2b.check_params(p) == OK
+
+
+def test_degenerate_sizes_ok():
+    for kw in (dict(batch=0), dict(in_channels=0), dict(out_channels=0),
+               dict(in_h=0, padding_h=1, kernel_h=1, out_h=2)):
+        assert c2b.check_params(_p(**kw)) == OK, kw
+    info = c2b.describe_plan(_p(batch=0))
+    assert info["tiles"] == 0 and info["launches"] == 0
+
+
+def _call(fn, go, w, gi, p):
+    return fn(go, w, gi, p, 0)
+
+
+@pytest.mark.parametrize("fn", [c2b.conv2d_grad_input, c2b.conv2d_grad_input_f16])
+def test_entry_points_reject_before_any_device_call(fn):
+    p = _p()
+    # shape errors come first
+    assert _call(fn, 0x1000, 0x2000, 0x3000, _p(stride=0, out_h=1, out_w=1)) == BAD
+    # null pointers of non-empty tensors
+    assert _call(fn, 0, 0x2000, 0x100000, p) == NULL
+    assert _call(fn, 0x1000, 0, 0x100000, p) == NULL
+    assert _call(fn, 0x1000, 0x2000, 0, p) == NULL
+    # grad_input overlapping grad_out or weight
+    gi_bytes = 1 * 3 * 8 * 8 * 4
+    assert _call(fn, 0x100000, 0x900000, 0x100000, p) == ALIAS
+    assert _call(fn, 0x100000 + gi_bytes - 4, 0x900000, 0x100000, p) == ALIAS
+    assert _call(fn, 0x100000, 0x900000 + 4, 0x900000, p) == ALIAS
+    lib = c2b.load_library()
+    assert getattr(lib, fn.__name__)(ctypes.c_void_p(1), ctypes.c_void_p(2),
+                                     ctypes.c_void_p(3), None, None) == NULL
+
+
+def test_plan_phases_and_work():
+    by = {c.name.split("_")[0]: c for c in CONFIGS}
+    def plan(c, f16=False):
+        p = c2b.make_params(c.batch, c.in_channels, c.in_h, c.in_w, c.out_channels,
+                            c.kernel_h, c.kernel_w, c.stride, c.padding_h,
+                            c.padding_w, c.out_h, c.out_w)
+        return c2b.describe_plan(p, f16)
+    # stride 1: one class; stride 2: four classes, none empty for 3x3 / 7x7
+    assert plan(by["resnet"])["phases"] == 1
+    assert plan(by["strided"])["phases"] == 4
+    assert plan(by["stem"])["phases"] == 4
+    for c in CONFIGS:
+        info = plan(c, c.f16_staged)
+        assert info["zero_phases"] == 0
+        assert info["useful_macs"] * 2 == c.useful_flops
+        # the residue split never issues the 4x structural-zero work of a
+        # dense im2col GEMM: issued MACs stay within tile padding of useful
+        assert info["macs"] >= info["useful_macs"]
+    # ResNet stage-1: 32 images x ceil(3136 / 256) tiles, 64 channels = 1 tile
+    r = plan(by["resnet"])
+    assert r["tiles"] == 32 * 13 and r["launches"] == 1
+    # strided: issued work within 1.25x of useful (no 4x zero work)
+    s = plan(by["strided"])
+    assert s["macs"] <= 1.25 * s["useful_macs"]
+
+
+def test_plan_zero_classes_when_stride_exceeds_kernel():
+    # 1x1 kernel, stride 2: only the class (0, 0) is reached by a tap
+    p = _p(in_h=7, in_w=6, kernel_h=1, kernel_w=1, padding_h=0, padding_w=0,
+           stride=2, out_h=4, out_w=3)
+    info = c2b.describe_plan(p)
+    assert info["phases"] == 4 and info["zero_phases"] == 3
+    # stride 3 with a 2x2 kernel: 9 classes, 5 of them without taps
+    p = _p(in_h=8, in_w=7, kernel_h=2, kernel_w=2, padding_h=1, padding_w=0,
+           stride=3, out_h=3, out_w=2)
+    info = c2b.describe_plan(p)
+    assert info["phases"] == 9 and info["zero_phases"] == 5

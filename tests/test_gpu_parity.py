@@ -1,0 +1,208 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bar: max|gpu - oracle| / max|oracle| <= 1e-4 for the fp32 path and <= 2e-2
+for the f16-staged path; integer-valued inputs must match bit for bit on both
+paths; every grad_input element is written (NaN pre-fill) and nothing outside
+it is (guard canaries).
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw,
+                                                    draw_integers, random_shape)
+from tests.gpu_helpers import TOL, rel_err, round_f16, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+
+
+def _oracle(sh, go, w):
+    return oracle.grad_input_gather(go, w, sh.in_h, sh.in_w, sh.stride,
+                                    sh.padding_h, sh.padding_w)
+
+
+def _reduced(sh: ConvShape, batch: int) -> ConvShape:
+    d = sh.as_dict()
+    d["batch"] = batch
+    d["name"] = sh.name + "_b%d" % batch
+    return ConvShape(**d)
+
+
+# ---- the five workloads, full oracle at reduced batch -----------------------
+@pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_config_reduced_batch(idx, f16):
+    cfg = CONFIGS[idx]
+    sh = cfg if cfg.batch <= 2 else _reduced(cfg, 2 if idx != 2 else 1)
+    _say("case", sh.name, "f16" if f16 else "fp32")
+    go, w = draw(sh, idx)
+    ref = _oracle(sh, go, w)
+    got = run_gpu(sh, go, w, f16=f16)
+    assert not np.any(np.isnan(got)), "unwritten grad_input elements"
+    err = rel_err(got, ref)
+    _say("  rel err", err)
+    assert err <= TOL[f16], err
+    if f16:
+        # the f16-staged path is the exact sum of f16-rounded operands, up to
+        # fp32 accumulation rounding
+        ref16 = _oracle(sh, round_f16(go), round_f16(w))
+        assert rel_err(got, ref16) <= 1e-5, rel_err(got, ref16)
+
+
+@pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_config_integer_inputs_bit_exact(idx, f16):
+    cfg = CONFIGS[idx]
+    sh = cfg if cfg.batch <= 2 else _reduced(cfg, 1)
+    _say("case int", sh.name, "f16" if f16 else "fp32")
+    go, w = draw_integers(sh, 100 + idx)
+    ref = _oracle(sh, go, w)
+    got = run_gpu(sh, go, w, f16=f16)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+# ---- the five workloads at full size, sampled against the oracle ------------
+def _sample_indices(sh, rng, count=3000):
+    n = int(np.prod(sh.gi_shape))
+    idx = list(rng.integers(0, n, size=count))
+    # every border row/column of the first and last image of a few channels
+    N, C, H, W = sh.gi_shape
+    for nn in (0, N - 1):
+        for cc in sorted({0, C // 2, C - 1}):
+            base = (nn * C + cc) * H * W
+            for x in range(W):
+                idx += [base + x, base + (H - 1) * W + x]
+            for y in range(H):
+                idx += [base + y * W, base + y * W + W - 1]
+    return np.unique(np.array(idx, dtype=np.int64))
+
+
+@pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
+def test_config_full_size_sampled(idx):
+    sh = CONFIGS[idx]
+    f16 = sh.f16_staged
+    _say("case full", sh.name, "f16" if f16 else "fp32")
+    go, w = draw(sh, idx)
+    got = run_gpu(sh, go, w, f16=f16)
+    assert not np.any(np.isnan(got)), "unwritten grad_input elements"
+    rng = np.random.default_rng(idx)
+    sel = _sample_indices(sh, rng)
+    ref = oracle.grad_input_gather_at(go, w, sh.in_h, sh.in_w, sh.stride,
+                                      sh.padding_h, sh.padding_w, sel)
+    scale = float(np.max(np.abs(ref)))
+    err = float(np.max(np.abs(got.ravel()[sel].astype(np.float64) - ref))) / scale
+    _say("  sampled rel err", err, "over", sel.size)
+    assert err <= TOL[f16], err
+    if f16:
+        ref16 = oracle.grad_input_gather_at(round_f16(go), round_f16(w), sh.in_h,
+                                            sh.in_w, sh.stride, sh.padding_h,
+                                            sh.padding_w, sel)
+        err16 = float(np.max(np.abs(got.ravel()[sel] - ref16))) / scale
+        assert err16 <= 1e-5, err16
+    # the f32 path of the f16 workload, and the f16 path of the others
+    other = run_gpu(sh, go, w, f16=not f16)
+    err2 = float(np.max(np.abs(other.ravel()[sel].astype(np.float64) - ref))) / scale
+    _say("  other path sampled rel err", err2)
+    assert err2 <= TOL[not f16], err2
+
+
+# ---- random small shapes: strides 1-3, asymmetric padding, ragged tiles ----
+RANDOM = [random_shape(np.random.default_rng(500 + i), max_n=3, max_c=9, max_hw=23,
+                       max_k=7, max_s=4, name="r%d" % i) for i in range(60)]
+
+
+@pytest.mark.parametrize("sh", RANDOM, ids=[s.name for s in RANDOM])
+def test_random_small_shapes(sh):
+    _say("case", sh)
+    rng = np.random.default_rng(hash(sh.name) % 2 ** 32)
+    go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+    ref = _oracle(sh, go, w)
+    for f16 in (False, True):
+        got = run_gpu(sh, go, w, f16=f16)
+        assert not np.any(np.isnan(got))
+        assert rel_err(got, ref) <= TOL[f16], (f16, rel_err(got, ref))
+
+
+# ---- edge cases --------------------------------------------------------------
+EDGE = [
+    # channels not a multiple of the 64-channel tile; pixel tails
+    ConvShape("ci65_co3", 2, 65, 9, 11, 3, 3, 3, 1, 1, 1, 9, 11, dist="uniform"),
+    ConvShape("ci130_s2", 1, 130, 10, 9, 17, 3, 3, 2, 1, 1, 5, 5, dist="uniform"),
+    ConvShape("ci3_stem_small", 2, 3, 30, 30, 8, 7, 7, 2, 3, 3, 15, 15, dist="uniform"),
+    # very wide rows (band split) and a one-column image (tall halo)
+    ConvShape("wide", 1, 4, 5, 700, 5, 3, 7, 1, 1, 3, 5, 700, dist="uniform"),
+    ConvShape("one_col", 1, 3, 300, 1, 4, 3, 3, 1, 1, 1, 300, 1, dist="uniform"),
+    ConvShape("one_px", 3, 5, 1, 1, 6, 1, 1, 1, 0, 0, 1, 1, dist="uniform"),
+    # padding larger than the kernel; stride larger than the kernel
+    ConvShape("pad_gt_k", 1, 3, 6, 6, 4, 2, 3, 1, 3, 4, 11, 12, dist="uniform"),
+    ConvShape("s3_k2", 2, 4, 13, 11, 5, 2, 2, 3, 1, 0, 5, 4, dist="uniform"),
+    ConvShape("s4_k1", 1, 6, 15, 17, 7, 1, 1, 4, 0, 0, 4, 5, dist="uniform"),
+    # large kernel at stride 1 (several tap groups per stage)
+    ConvShape("k11", 1, 5, 20, 20, 9, 11, 11, 1, 5, 5, 20, 20, dist="uniform"),
+    # output channels not a multiple of the stage depth
+    ConvShape("co13", 1, 7, 12, 12, 13, 3, 3, 1, 1, 1, 12, 12, dist="uniform"),
+    # zero output channels: grad_input must be all zeros
+    ConvShape("co0", 2, 5, 7, 7, 0, 3, 3, 1, 1, 1, 7, 7, dist="uniform"),
+]
+
+
+@pytest.mark.parametrize("sh", EDGE, ids=[s.name for s in EDGE])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_edge_shapes(sh, f16):
+    _say("case", sh.name, "f16" if f16 else "fp32")
+    rng = np.random.default_rng(7)
+    go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+    ref = _oracle(sh, go, w)
+    got = run_gpu(sh, go, w, f16=f16)
+    assert not np.any(np.isnan(got))
+    if sh.out_channels == 0:
+        assert np.all(got == 0.0)
+    assert rel_err(got, ref) <= TOL[f16], rel_err(got, ref)
+
+
+def test_empty_batch_is_noop():
+    import torch
+    import conv2d_backward_implicit_amd as c2b
+    dev = torch.device("cuda", 0)
+    go = torch.zeros((0, 4, 5, 5), device=dev)
+    w = torch.zeros((4, 3, 3, 3), device=dev)
+    gi = c2b.grad_input(go, w, 5, 5, 1, 1, 1)
+    torch.cuda.synchronize()
+    assert gi.shape == (0, 3, 5, 5)
+
+
+def test_deterministic_and_on_side_stream():
+    import torch
+    sh = _reduced(CONFIGS[2], 1)
+    go, w = draw(sh, 2)
+    a = run_gpu(sh, go, w)
+    s = torch.cuda.Stream()
+    b = run_gpu(sh, go, w, stream=s)
+    assert np.array_equal(a, b)
+
+
+def test_bad_status_raises():
+    import torch
+    import conv2d_backward_implicit_amd as c2b
+    dev = torch.device("cuda", 0)
+    go = torch.zeros((1, 4, 5, 5), device=dev)
+    w = torch.zeros((4, 3, 3, 3), device=dev)
+    p = c2b.make_params(1, 3, 5, 5, 4, 3, 3, 1, 1, 1, 5, 5)
+    with pytest.raises(c2b.Conv2dError):
+        c2b.grad_input_into(go.view(1, 4, 5, 5)[:, :3], go, w, p)  # alias

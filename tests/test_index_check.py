@@ -1,0 +1,47 @@
+"""Host replay of the kernels' addressing (conv2d_check_indexing), CPU only.
+
+For each shape the library walks every workgroup and thread it would launch
+and checks bounds of every global/LDS access, that every tap reads the
+grad_out and weight element of the gather rule, and that each grad_input
+element is written exactly once.  Runs on the shapes the GPU tests and the
+benchmark use, before any of them touches a GPU.
+"""
+import numpy as np
+import pytest
+
+import conv2d_backward_implicit_amd as c2b
+from conv2d_backward_implicit_amd.workloads import CONFIGS, ConvShape, random_shape
+from tests.gpu_helpers import params_of
+from tests.test_gpu_parity import EDGE, RANDOM
+
+
+def _check(sh, f16):
+    rc, msg = c2b.check_indexing(params_of(sh), f16)
+    assert rc == 0, (sh, f16, rc, msg)
+
+
+@pytest.mark.parametrize("sh", CONFIGS, ids=[c.name for c in CONFIGS])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_workloads(sh, f16):
+    _check(sh, f16)
+
+
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_gpu_test_shapes(f16):
+    for sh in EDGE + RANDOM:
+        _check(sh, f16)
+
+
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_random_stress(f16):
+    rng = np.random.default_rng(99)
+    for i in range(150):
+        sh = random_shape(rng, max_n=3, max_c=140, max_hw=70, max_k=9, max_s=5,
+                          name="s%d" % i)
+        _check(sh, f16)
+
+
+def test_checker_rejects_bad_shape():
+    p = c2b.make_params(1, 3, 8, 8, 4, 3, 3, 1, 1, 1, 7, 8)
+    rc, _ = c2b.check_indexing(p)
+    assert rc == -2
