@@ -72,6 +72,22 @@ def cpu_baseline(shape, go, w):
             "sample": "whole workload (%d images), one pass, %.2f s" % (shape.batch, dt)}
 
 
+def copy_calibration(mib: int, steps: int) -> int:
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE per dispatch
+    (KiB) against the true bytes gives the scale for the byte counters."""
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n * 4, "copy_bytes_written": n * 4,
+                      "dispatches": steps}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -82,7 +98,12 @@ def main() -> int:
     g.add_argument("--f16", action="store_true", help="f16-staged path")
     g.add_argument("--fp32", action="store_true", help="fp32 path")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead: run --steps plain device-to-device copies of MIB "
+                         "MiB (reference kernel for HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        return copy_calibration(args.copy_calibration, args.steps)
 
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "

@@ -13,6 +13,7 @@
 #include <cstdio>
 #include <cstring>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "tile_index.hpp"
@@ -45,7 +46,7 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
   const int64_t HW = int64_t(a.H) * a.W;
 
   for (int bid = 0; bid < a.total_tiles; ++bid) {
-    const TileCtx c = decode_tile<MT, CK>(a, bid);
+    const TileCtx c = decode_tile<MT>(a, bid, CK);
     const PhaseDesc& P = c.P;
     C2B_REQUIRE(c.n >= 0 && c.n < a.N, "bid %d n %d", bid, c.n);
     C2B_REQUIRE(c.band >= 0 && c.band < P.nbands, "bid %d band %d", bid, c.band);
@@ -167,15 +168,162 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
   }
 }
 
+// fp32 family (grad_input_f32_kernel<WM, NBW>): window and weights are
+// copied by buffer loads that write LDS directly (64 consecutive floats per
+// wave-instruction), double-buffered.
+template <int WM, int NBW>
+void check_launch_f32(const LaunchArgs& a, std::vector<unsigned char>& written) {
+  using G = F32Geom<WM, NBW>;
+  constexpr int MT = G::kMT, WN = G::kWN, NT = G::kThreads, CH = kF32StageCh;
+  const int64_t OHOW = int64_t(a.OH) * a.OW;
+  const int64_t go_size = int64_t(a.N) * a.Co * OHOW;
+  const int64_t KHW = int64_t(a.KH) * a.KW;
+  const int64_t cstride = int64_t(a.Ci) * KHW;
+  const int64_t w_size = int64_t(a.Co) * cstride;
+  const int64_t HW = int64_t(a.H) * a.W;
+
+  for (int bid = 0; bid < a.total_tiles; ++bid) {
+    const TileCtx c = decode_tile<MT>(a, bid, 0);
+    const PhaseDesc& P = c.P;
+    C2B_REQUIRE(c.n >= 0 && c.n < a.N, "bid %d n %d", bid, c.n);
+    C2B_REQUIRE(c.band >= 0 && c.band < P.nbands, "bid %d band %d", bid, c.band);
+    C2B_REQUIRE(c.ci0 >= 0 && c.ci0 < a.Ci, "bid %d ci0 %d", bid, c.ci0);
+    C2B_REQUIRE(c.npx >= 1 && c.npx <= P.ntv && P.ntv <= G::kNTL, "bid %d npx %d", bid, c.npx);
+    const int SLOTS = P.slabr, CP = P.cp, TG = P.tg;
+    const int fcount = CH * SLOTS, ecount = CH * CP;
+    const int wt0 = 2 * CH * SLOTS;
+    if (c.ntaps > 0) {
+      C2B_REQUIRE(P.ckr == CH && TG >= 1 && TG <= kF32StageTaps, "stage shape");
+      C2B_REQUIRE(c.R * c.roww <= SLOTS && SLOTS <= kF32MaxSlots && SLOTS % 4 == 0,
+                  "bid %d window %d > %d", bid, c.R * c.roww, SLOTS);
+      C2B_REQUIRE(CP >= MT * TG && CP % 16 == 4 && CP <= kF32MaxCP, "weight pitch %d", CP);
+      C2B_REQUIRE(2 * (fcount + ecount) <= kF32LdsFloats, "LDS %d", 2 * (fcount + ecount));
+      C2B_REQUIRE(fcount % 64 == 0 && ecount % 64 == 0, "whole wave-instructions");
+      C2B_REQUIRE(int64_t(CH) * OHOW * 4 < (int64_t(1) << 31) &&
+                      int64_t(CH) * cstride * 4 < (int64_t(1) << 31),
+                  "stage byte range");
+    }
+    for (int tid = 0; tid < NT; ++tid) {
+      const int lane = tid & 63, wave = tid >> 6;
+      const int mg = wave % WM, ng = wave / WM, g = lane >> 4, c16 = lane & 15;
+      for (int st = 0; st < c.nstages; ++st) {
+        int co0, grp;
+        stage_split(c, CH, st, &co0, &grp);
+        const int nco = imin(CH, a.Co - co0);
+        C2B_REQUIRE(nco >= 1, "stage %d without channels", st);
+        // window cells
+        for (int k = 0; k < G::kHS; ++k) {
+          const int f0 = wave * 64 + NT * k, f = tid + NT * k;
+          if (f0 >= fcount) continue;
+          C2B_REQUIRE(f == f0 + lane && f < fcount, "window lds %d", f);
+          const int o = f32_window_cell(c, a, f);
+          if (o < 0 || int64_t(o) >= int64_t(nco) * OHOW) continue;   // reads 0
+          const int cq = f / (4 * SLOTS), r = f % (4 * SLOTS);
+          const int slot = r / 4, ch = 4 * cq + r % 4;
+          C2B_REQUIRE(ch < nco && slot < c.R * c.roww, "cell %d", f);
+          const int oh = c.oh_base + slot / c.roww, ow = c.ow_base + slot % c.roww;
+          C2B_REQUIRE(o == ch * OHOW + int64_t(oh) * a.OW + ow, "window element");
+          const int64_t gi = int64_t(c.n) * a.Co * OHOW + int64_t(co0) * OHOW + o;
+          C2B_REQUIRE(gi >= 0 && gi < go_size, "grad_out read %lld", (long long)gi);
+        }
+        const int tap0 = grp * TG;
+        const int ntg = imin(TG, c.ntaps - tap0);
+        C2B_REQUIRE(ntg >= 1, "stage without taps");
+        // weight cells
+        for (int k = 0; k < G::kWS; ++k) {
+          const int e0 = wave * 64 + NT * k, e = tid + NT * k;
+          if (e0 >= ecount) continue;
+          C2B_REQUIRE(e == e0 + lane && wt0 + CH * CP + e < kF32LdsFloats, "weight lds %d", e);
+          const int o = f32_weight_cell<MT>(c, a, e, grp);
+          if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) continue;  // reads 0
+          const int co = e / CP, r = e % CP, ci = r / TG, t = r % TG;
+          C2B_REQUIRE(co < nco && ci < MT && t < ntg, "weight cell %d", e);
+          const int64_t want = (int64_t(co0 + co) * a.Ci + c.ci0 + ci) * KHW +
+                               tap_kidx(P, a, tap0 + t);
+          const int64_t wi = int64_t(co0) * cstride + o;
+          C2B_REQUIRE(wi == want && wi >= 0 && wi < w_size, "weight element");
+        }
+        // contraction reads
+        int j = tap0 / P.tw, l = tap0 % P.tw;
+        for (int tt = 0; tt < ntg; ++tt) {
+          C2B_REQUIRE(j * P.tw + l == tap0 + tt, "tap order");
+          for (int q = 0; q < 4; ++q) {
+            const int ai = 4 * g * CP + (mg * 16 + c16) * TG + q * CP + tt;
+            C2B_REQUIRE(ai >= 0 && ai < ecount, "weight read %d", ai);
+            C2B_REQUIRE(ai / CP == 4 * g + q && (ai % CP) / TG == mg * 16 + c16 &&
+                            (ai % CP) % TG == tt,
+                        "weight of k-step");
+          }
+          for (int b = 0; b < NBW; ++b) {
+            const int local = f32_local(b, ng, c16, WN);
+            const int base = window_base(c, local);
+            const int slot = base + tap_window_offset(c, j, l);
+            const int byte = (g * SLOTS + base) * 16 + tap_window_offset(c, j, l) * 16;
+            C2B_REQUIRE(byte >= 0 && byte % 16 == 0 && byte + 16 <= fcount * 4, "window read %d",
+                        byte);
+            C2B_REQUIRE(slot >= 0 && slot < SLOTS && byte / 16 == g * SLOTS + slot,
+                        "slot %d", slot);
+            if (local < c.npx) {
+              C2B_REQUIRE(slot < c.R * c.roww, "slot beyond window");
+              const int qq = c.p0 + local, ip = qq / P.wb, jj = c.band * P.wb + qq % P.wb;
+              C2B_REQUIRE(c.oh_base + slot / c.roww == ip + P.ch - j &&
+                              c.ow_base + slot % c.roww == jj + P.cw - l,
+                          "tap (%d,%d) reads the wrong grad_out element", j, l);
+            }
+          }
+          if (++l == P.tw) {
+            l = 0;
+            ++j;
+          }
+        }
+      }
+      // epilogue
+      for (int b = 0; b < NBW; ++b) {
+        const int po = output_offset(c, a, f32_local(b, ng, c16, WN));
+        if (po < 0) continue;
+        const int ih = po / a.W, iw = po % a.W;
+        C2B_REQUIRE(((ih + a.PH) % a.S) == P.rh && ((iw + a.PW) % a.S) == P.rw,
+                    "pixel (%d,%d) outside class", ih, iw);
+        for (int r = 0; r < 4; ++r) {
+          const int cc = c.ci0 + mg * 16 + 4 * g + r;
+          if (cc >= a.Ci) continue;
+          const int64_t gi = int64_t(c.n) * a.Ci * HW + int64_t(cc) * HW + po;
+          C2B_REQUIRE(gi >= 0 && gi < int64_t(written.size()), "grad_input write");
+          C2B_REQUIRE(written[gi] == 0, "grad_input element %lld written twice", (long long)gi);
+          written[gi] = 1;
+        }
+      }
+    }
+  }
+}
+
+template <int V>
+void check_f32_variant(const LaunchArgs& la, std::vector<unsigned char>& written) {
+  constexpr F32Variant v = kF32Variants[V];
+  check_launch_f32<v.wm, v.nbw>(la, written);
+}
+
+template <int... Vs>
+void check_f32_dispatch(const LaunchArgs& la, std::vector<unsigned char>& written,
+                        std::integer_sequence<int, Vs...>) {
+  ((la.variant == Vs ? check_f32_variant<Vs>(la, written) : void()), ...);
+}
+
 template <bool F16>
 int check_all(const conv2d_params* p, char* msg, size_t len) {
   std::vector<LaunchArgs> launches;
-  int rc = build_plan(p, F16 ? kF16Tile : kF32Tile, &launches, nullptr);
+  int rc = F16 ? build_plan(p, kF16Tile, &launches, nullptr)
+               : build_plan_f32(p, kF32DefaultCUs, &launches, nullptr);
   if (rc != CONV2D_OK) return rc;
   const int64_t n_gi = int64_t(p->batch) * p->in_channels * p->in_h * p->in_w;
   std::vector<unsigned char> written(size_t(n_gi), 0);
   try {
-    for (const LaunchArgs& la : launches) check_launch<F16>(la, written);
+    for (const LaunchArgs& la : launches) {
+      if (F16)
+        check_launch<true>(la, written);
+      else
+        check_f32_dispatch(la, written, std::make_integer_sequence<int, kNumF32Variants>());
+    }
     for (int64_t i = 0; i < n_gi; ++i)
       C2B_REQUIRE(written[i] == 1, "grad_input element %lld never written", (long long)i);
   } catch (const Failure& f) {

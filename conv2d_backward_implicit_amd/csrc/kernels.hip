@@ -29,6 +29,8 @@
 //    with no race between workgroups.
 #include <hip/hip_runtime.h>
 
+#include <utility>
+
 #include "tile_index.hpp"
 
 namespace c2b {
@@ -110,7 +112,7 @@ __global__ __launch_bounds__(kThreads) void grad_input_kernel(const LaunchArgs a
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const TileCtx c = decode_tile<MT, CK>(a, blockIdx.x);
+  const TileCtx c = decode_tile<MT>(a, blockIdx.x, CK);
   const PhaseDesc& P = c.P;
   const int OHOW = a.OH * a.OW;
   const int cstride = a.Ci * a.KH * a.KW;   // weight distance between channels
@@ -247,6 +249,205 @@ __global__ __launch_bounds__(kThreads) void grad_input_kernel(const LaunchArgs a
   }
 }
 
+// Word 3 of a raw (untyped, unswizzled) buffer resource: 32-bit data format.
+constexpr int kRawBufferFlags = 0x00020000;
+// A byte offset past every buffer's range: such loads return 0.
+constexpr unsigned kOutOfRange = 0xFFFFFFFFu;
+
+__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
+// Wait until this wave's outstanding vector-memory operations (including
+// loads that write LDS directly) have completed.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// ---------------------------------------------------------------------------
+// fp32 family: 8 waves, v_mfma_f32_16x16x4_f32 (layouts: see F32Geom).
+// Stage s+1 (window and weights) is copied into the second LDS buffers while
+// stage s is multiplied; one barrier per stage.  Per tap, a wave reads one
+// 16-byte window cell per 16-pixel block and 4 weights, then issues
+// 4 x NBW matrix instructions.
+template <int WM, int NBW>
+__global__ __launch_bounds__(kF32Threads) void grad_input_f32_kernel(const LaunchArgs a) {
+  using G = F32Geom<WM, NBW>;
+  constexpr int MT = G::kMT, WN = G::kWN, HS = G::kHS, WS = G::kWS, NT = G::kThreads;
+  constexpr int TGM = kF32StageTaps, CH = kF32StageCh;
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  __shared__ f32x4 lds4[kF32LdsFloats / 4];
+  float* lds = reinterpret_cast<float*>(lds4);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int mg = wave % WM, ng = wave / WM;
+  const int g = lane >> 4, c16 = lane & 15;
+  const TileCtx c = decode_tile<MT>(a, blockIdx.x, 0);
+  const PhaseDesc& P = c.P;
+  const int OHOW = a.OH * a.OW;
+  const int cstride = a.Ci * a.KH * a.KW;
+  const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
+  const int SLOTS = P.slabr, CP = P.cp, TG = P.tg;
+  // LDS float offsets of the two window and the two weight buffers
+  const int win0 = 0, win1 = CH * SLOTS, wt0 = 2 * CH * SLOTS, wt1 = wt0 + CH * CP;
+
+  unsigned gbyte[HS];
+#pragma unroll
+  for (int k = 0; k < HS; ++k) {
+    const int o = f32_window_cell(c, a, tid + NT * k);
+    gbyte[k] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
+  }
+  unsigned wbyte[WS];
+  int wgroup = -1;
+  const int fcount = CH * SLOTS;   // multiple of 64
+  const int ecount = CH * CP;      // multiple of 64
+  auto issue_stage = [&](int st, int buf) {
+    int co0, grp;
+    stage_split(c, CH, st, &co0, &grp);
+    if (grp != wgroup) {
+#pragma unroll
+      for (int k = 0; k < WS; ++k) {
+        const int o = f32_weight_cell<MT>(c, a, tid + NT * k, grp);
+        wbyte[k] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
+      }
+      wgroup = grp;
+    }
+    const int nco = imin(CH, a.Co - co0);
+    const auto rg = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(go_n + (size_t)co0 * OHOW), 0, nco * OHOW * 4, kRawBufferFlags);
+    float* wdst = lds + (buf ? win1 : win0);
+#pragma unroll
+    for (int k = 0; k < HS; ++k) {
+      const int f0 = wave * 64 + NT * k;
+      if (f0 < fcount)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, lds_ptr(wdst + f0), 4, gbyte[k], 0, 0, 0);
+    }
+    const auto rw = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.w + (size_t)co0 * cstride), 0, nco * cstride * 4, kRawBufferFlags);
+    float* adst = lds + (buf ? wt1 : wt0);
+#pragma unroll
+    for (int k = 0; k < WS; ++k) {
+      const int e0 = wave * 64 + NT * k;
+      if (e0 < ecount)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(adst + e0), 4, wbyte[k], 0, 0, 0);
+    }
+  };
+
+  const int nst = c.nstages;
+  if (nst > 0) issue_stage(0, 0);
+  if (nst > 1) issue_stage(1, 1);
+
+  // byte offsets within a window buffer of each block's cell for the class's
+  // first tap, and within a weight buffer of this lane's weights
+  int bb[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b)
+    bb[b] = (g * SLOTS + window_base(c, f32_local(b, ng, c16, WN))) * 16;
+  const int ab = (4 * g * CP + (mg * 16 + c16) * TG) * 4;
+
+  f32x4 acc[NBW];
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+  auto compute = [&](int st, int buf) {
+    int co0, grp;
+    stage_split(c, CH, st, &co0, &grp);
+    const int tap0 = grp * TG;
+    const int ntg = imin(TG, c.ntaps - tap0);
+    const char* Hb = reinterpret_cast<const char*>(lds + (buf ? win1 : win0));
+    const char* Ab = reinterpret_cast<const char*>(lds + (buf ? wt1 : wt0)) + ab;
+    int j = tap0 / P.tw, l = tap0 - (tap0 / P.tw) * P.tw;
+#pragma unroll
+    for (int tt = 0; tt < TGM; ++tt) {
+      if (tt < ntg) {
+        const int boff = tap_window_offset(c, j, l) * 16;
+        f32x4 bv[NBW];
+#pragma unroll
+        for (int b = 0; b < NBW; ++b) bv[b] = *reinterpret_cast<const f32x4*>(Hb + bb[b] + boff);
+        float aw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) aw[q] = *reinterpret_cast<const float*>(Ab + (q * CP + tt) * 4);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int b = 0; b < NBW; ++b)
+            acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[q], bv[b][q], acc[b], 0, 0, 0);
+        if (++l == P.tw) {
+          l = 0;
+          ++j;
+        }
+      }
+    }
+  };
+
+  wait_vmem();
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    compute(st, st & 1);
+    wait_vmem();          // this wave's copies of stage st+1 have landed
+    __syncthreads();      // ... everyone's, and buffer st&1 is free again
+    if (st + 2 < nst) issue_stage(st + 2, st & 1);
+  }
+
+  // epilogue: register r of block b holds channel mg*16 + 4g + r, pixel
+  // (b*WN + ng)*16 + c16
+  float* gi_n = a.gi + (size_t)c.n * a.Ci * (a.H * a.W);
+  const size_t HW = (size_t)a.H * a.W;
+#pragma unroll
+  for (int b = 0; b < NBW; ++b) {
+    const int po = output_offset(c, a, f32_local(b, ng, c16, WN));
+    if (po < 0) continue;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int cc = c.ci0 + mg * 16 + 4 * g + r;
+      if (cc < a.Ci) gi_n[cc * HW + po] = acc[b][r];
+    }
+  }
+}
+
+template <int V>
+void launch_f32_variant(const LaunchArgs& la, hipStream_t st) {
+  constexpr F32Variant v = kF32Variants[V];
+  hipLaunchKernelGGL((grad_input_f32_kernel<v.wm, v.nbw>), dim3(la.total_tiles),
+                     dim3(kF32Threads), 0, st, la);
+}
+
+template <int... Vs>
+void launch_f32_dispatch(const LaunchArgs& la, hipStream_t st,
+                         std::integer_sequence<int, Vs...>) {
+  ((la.variant == Vs ? launch_f32_variant<Vs>(la, st) : void()), ...);
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kF32DefaultCUs;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < 1)
+    return kF32DefaultCUs;
+  return cus;
+}
+
+int launch_f32(const float* go, const float* w, float* gi, const conv2d_params* p,
+               void* stream) {
+  int rc = validate_shape(p);
+  if (rc != CONV2D_OK) return rc;
+  rc = check_pointers(go, w, gi, p);
+  if (rc != CONV2D_OK) return rc;
+  std::vector<LaunchArgs> launches;
+  rc = build_plan_f32(p, device_cus(), &launches, nullptr);
+  if (rc != CONV2D_OK) return rc;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  for (LaunchArgs& la : launches) {
+    la.go = go;
+    la.w = w;
+    la.gi = gi;
+    if (la.total_tiles == 0) continue;
+    launch_f32_dispatch(la, st, std::make_integer_sequence<int, kNumF32Variants>());
+  }
+  if (hipGetLastError() != hipSuccess) return CONV2D_ERR_HIP;
+  return CONV2D_OK;
+}
+
 template <bool F16>
 constexpr TileShape tile_of() {
   return F16 ? kF16Tile : kF32Tile;
@@ -279,7 +480,7 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, v
 
 extern "C" int conv2d_grad_input(const float* grad_out, const float* weight, float* grad_input,
                                  const conv2d_params* p, void* stream) {
-  return c2b::launch<false>(grad_out, weight, grad_input, p, stream);
+  return c2b::launch_f32(grad_out, weight, grad_input, p, stream);
 }
 
 extern "C" int conv2d_grad_input_f16(const float* grad_out, const float* weight,

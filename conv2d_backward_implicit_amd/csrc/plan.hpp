@@ -40,7 +40,17 @@ struct PhaseDesc {
   int32_t ngroups;     // tap groups: ceil(th * tw / taps per stage)
   int32_t tiles;       // tiles of this class in the launch
   int32_t tile_begin;  // first workgroup index of this class in the launch
-  int32_t pad_;
+  int32_t ckr;         // output channels per stage (fp32 kernel)
+  int32_t tg;          // taps per stage (fp32 kernel)
+  int32_t slabr;       // window slots per channel in LDS (fp32 kernel)
+  int32_t cp;          // LDS floats per output channel of staged weights (fp32 kernel)
+  // reciprocals for per-lane division: m = ceil(2^31 / d), see fast_div
+  uint32_t m_roww;     // d = wb + tw - 1
+  uint32_t m_wb;       // d = wb
+  uint32_t m_tw;       // d = tw
+  uint32_t m_slots4;   // d = 4 * slabr
+  uint32_t m_cp;       // d = cp
+  uint32_t m_tg;       // d = tg
 };
 
 // By-value kernel argument block of one launch.
@@ -52,7 +62,7 @@ struct LaunchArgs {
   int32_t ciblocks;    // ceil(Ci / channel tile)
   int32_t nphases;     // classes in this launch, heaviest first
   int32_t total_tiles; // workgroups in this launch
-  int32_t pad_;
+  int32_t variant;     // kernel instantiation (host side only)
   PhaseDesc ph[kMaxPhasesPerLaunch];
 };
 
@@ -83,8 +93,33 @@ int validate_shape(const conv2d_params* p);
 
 // Full plan for one tile shape: validate, split into classes and tiles, and
 // append one LaunchArgs per launch (pointers left null).  `info` may be null.
+// Used by the f16-staged kernel.
 int build_plan(const conv2d_params* p, const TileShape& ts,
                std::vector<LaunchArgs>* launches, conv2d_plan_info* info);
+
+// fp32 kernel family: 8 waves, 16x16x4 fp32 matrix instructions; each wave
+// owns 16 input channels x NBW blocks of 16 pixels.  Variants differ in the
+// waves along channels (WM) and the blocks per wave (NBW).
+struct F32Variant {
+  int wm;    // waves along channels: 4 (64-channel tiles) or 8 (128)
+  int nbw;   // 16-pixel blocks per wave
+};
+constexpr F32Variant kF32Variants[] = {{4, 4}, {4, 8}, {4, 10}, {4, 13},
+                                       {8, 4}, {8, 8}, {8, 10}, {8, 13}};
+constexpr int kNumF32Variants = int(sizeof(kF32Variants) / sizeof(kF32Variants[0]));
+constexpr int kF32Threads = 512;
+constexpr int kF32StageCh = 16;     // output channels per stage
+constexpr int kF32MaxSlots = 672;   // window slots per channel (multiple of 4)
+constexpr int kF32MaxCP = 608;      // staged weight floats per channel
+constexpr int kF32LdsFloats = 40960;  // 160 KiB: 2 x 16 x (slots + cp) floats at most
+constexpr int kF32StageTaps = 9;    // kernel taps per stage
+constexpr int kF32DefaultCUs = 256;
+
+// Plan for the fp32 kernel family on a device with `num_cus` compute units:
+// chooses the variant, tile sizes and stage depths per class (balancing the
+// tiles over the compute units, heaviest first).
+int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>* launches,
+                   conv2d_plan_info* info);
 
 // Pointer checks: NULL inputs of non-empty tensors and output/input overlap.
 int check_pointers(const float* go, const float* w, const float* gi,

@@ -33,6 +33,22 @@ struct TileCtx {
 
 C2B_HD int imin(int a, int b) { return a < b ? a : b; }
 
+// floor(n / d) as one multiply-high: m = ceil(2^31 / d) (fast_div_magic),
+// exact whenever n * d < 2^31 (n*m/2^31 exceeds n/d by less than n/2^31,
+// which cannot reach the next multiple of 1/d).  The planner bounds every
+// numerator it is used with.
+C2B_HD int fast_div(int n, uint32_t m) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return int(__umulhi(uint32_t(n) << 1, m));
+#else
+  return int((uint64_t(uint32_t(n) << 1) * m) >> 32);
+#endif
+}
+
+C2B_HD uint32_t fast_div_magic(uint32_t d) {
+  return uint32_t(((uint64_t(1) << 31) + d - 1) / d);
+}
+
 // Index of the class of workgroup `bid` within the launch.
 C2B_HD int phase_of(const LaunchArgs& a, int bid) {
   int pi = 0;
@@ -45,8 +61,9 @@ C2B_HD int phase_of(const LaunchArgs& a, int bid) {
 // x mod 8 (one XCD: the dispatcher deals workgroups round-robin over the 8
 // XCDs) take one contiguous run of tiles, channel tile fastest, so tiles
 // that share grad_out rows and weights share that XCD's L2.
-template <int MT, int CK>
-C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
+// ck: output channels per stage (0: the class's own stage depth, P.ckr).
+template <int MT>
+C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid, int ck) {
   TileCtx c;
   c.P = a.ph[phase_of(a, bid)];
   const PhaseDesc& P = c.P;
@@ -68,7 +85,8 @@ C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   const int pend = imin(c.p0 + P.ntv, bandpix);
   c.npx = pend - c.p0;
   c.ntaps = P.th * P.tw;
-  c.nstages = c.ntaps > 0 ? ((a.Co + CK - 1) / CK) * P.ngroups : 0;
+  if (ck == 0) ck = P.ckr;
+  c.nstages = c.ntaps > 0 ? ((a.Co + ck - 1) / ck) * P.ngroups : 0;
   c.i_start = c.p0 / P.wb;
   c.R = (pend - 1) / P.wb - c.i_start + P.th;
   c.roww = P.wb + P.tw - 1;
@@ -81,7 +99,7 @@ C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
 // -1 if the slot is outside the image (zero padding) or outside the window.
 C2B_HD int window_slot_offset(const TileCtx& c, const LaunchArgs& a, int f) {
   if (c.ntaps == 0 || f >= c.R * c.roww) return -1;
-  const int r = f / c.roww;
+  const int r = fast_div(f, c.P.m_roww);
   const int col = f - r * c.roww;
   const int oh = c.oh_base + r;
   const int ow = c.ow_base + col;
@@ -96,10 +114,11 @@ C2B_HD int window_base(const TileCtx& c, int local) {
   const PhaseDesc& P = c.P;
   if (c.ntaps == 0) return 0;
   if (local >= c.npx) return (P.th - 1) * c.roww + P.tw - 1;
-  const int q = c.p0 + local;
-  const int ip = q / P.wb;
-  const int jb = q - ip * P.wb;
-  return (ip - c.i_start + P.th - 1) * c.roww + jb + P.tw - 1;
+  // row within the tile's first row: (p0 mod wb + local) / wb
+  const int q0 = c.p0 - c.i_start * P.wb + local;
+  const int dr = fast_div(q0, P.m_wb);
+  const int jb = q0 - dr * P.wb;
+  return (dr + P.th - 1) * c.roww + jb + P.tw - 1;
 }
 
 // Window slot offset of tap (j, l) relative to window_base.
@@ -109,9 +128,10 @@ C2B_HD int tap_window_offset(const TileCtx& c, int j, int l) { return -(j * c.ro
 C2B_HD int output_offset(const TileCtx& c, const LaunchArgs& a, int local) {
   const PhaseDesc& P = c.P;
   if (local >= c.npx) return -1;
-  const int q = c.p0 + local;
-  const int ip = q / P.wb;
-  const int jj = c.band * P.wb + (q - ip * P.wb);
+  const int q0 = c.p0 - c.i_start * P.wb + local;
+  const int dr = fast_div(q0, P.m_wb);
+  const int ip = c.i_start + dr;
+  const int jj = c.band * P.wb + (q0 - dr * P.wb);
   if (jj >= P.wp) return -1;
   const int ih = P.ih0 + a.S * ip;
   const int iw = P.iw0 + a.S * jj;
@@ -120,7 +140,7 @@ C2B_HD int output_offset(const TileCtx& c, const LaunchArgs& a, int local) {
 
 // Flat weight index kh*KW + kw of the tap-th tap of the class.
 C2B_HD int tap_kidx(const PhaseDesc& P, const LaunchArgs& a, int tap) {
-  const int j = tap / P.tw;
+  const int j = fast_div(tap, P.m_tw);
   const int l = tap - j * P.tw;
   return (P.rh + a.S * j) * a.KW + (P.rw + a.S * l);
 }
@@ -181,6 +201,70 @@ struct KernelGeom {
   static_assert(CK % (2 * kCPC) == 0, "a k-step takes one cell group per half-wave");
   static_assert(kKSteps * 2 == kNCG, "k-steps cover the stage's cell groups");
 };
+
+// ---------------------------------------------------------------------------
+// fp32 kernel family (8 waves, 16x16x4 fp32 matrix instructions).
+//   wave w: channel group mg = w % WM (16 input channels), pixel group
+//   ng = w / WM; lane: k group g = lane / 16, c16 = lane % 16;
+//   block b of the wave covers tile-local pixels (b*WN + ng)*16 + [0, 16);
+//   k-step q (0..3) of a tap: lane group g supplies output channel 4g + q.
+// A stage is 16 output channels x up to tg taps.  LDS per buffer (two
+// buffers of each):
+//   window  [quad cq = 0..3][slot][4 channels]  (16*slots floats): a lane
+//           reads its group's 4 channels with one 16-byte read, 16 lanes read
+//           16 consecutive 16-byte cells (every bank once), and a tap shift
+//           is a plain subtraction of slots;
+//   weights [co][ci][t] with channel pitch cp (= 4 mod 16 floats, so the
+//           four lane groups, 4*cp apart, sit 16 banks apart).
+// Both are filled by buffer loads that write LDS directly: each
+// wave-instruction fills 64 consecutive floats, which here come from 16
+// consecutive pixels of 4 channels, or from consecutive weights of one
+// channel -- a few cache lines per instruction.
+template <int WM, int NBW>
+struct F32Geom {
+  static constexpr int kThreads = kF32Threads;
+  static constexpr int kWN = 8 / WM;                  // waves along pixels
+  static constexpr int kMT = 16 * WM;                 // channels per tile
+  static constexpr int kNTL = 16 * NBW * kWN;         // pixel lanes per tile
+  static constexpr int kHS = kF32StageCh * kF32MaxSlots / kThreads;  // window cells / thread
+  static constexpr int kWS = kF32StageCh * kF32MaxCP / kThreads;     // weight cells / thread
+  static_assert(WM * kWN == 8, "8 waves");
+  static_assert(kF32StageCh * kF32MaxSlots % kThreads == 0 &&
+                    kF32StageCh * kF32MaxCP % kThreads == 0, "whole cells per thread");
+  static_assert(2 * kF32StageCh * (kF32MaxSlots + kF32MaxCP) <= kF32LdsFloats, "LDS");
+};
+
+// Tile-local pixel of block b of pixel group ng, lane c16.
+C2B_HD int f32_local(int b, int ng, int c16, int wn) { return (b * wn + ng) * 16 + c16; }
+
+// Window cell f = (cq*slots + slot)*4 + c of a stage: grad_out offset
+// ch*OH*OW + oh*OW + ow (ch = 4cq + c) relative to the stage's first channel,
+// or -1 if the cell is padding (outside the image or the window).
+C2B_HD int f32_window_cell(const TileCtx& c, const LaunchArgs& a, int f) {
+  const int slots = c.P.slabr;
+  if (c.ntaps == 0 || f >= kF32StageCh * slots) return -1;
+  const int cq = fast_div(f, c.P.m_slots4);
+  const int r = f - cq * 4 * slots;
+  const int slot = r >> 2, ch = 4 * cq + (r & 3);
+  const int off = window_slot_offset(c, a, slot);
+  return off < 0 ? -1 : ch * (a.OH * a.OW) + off;
+}
+
+// Weight cell e = co*cp + ci*tg + t of stage tap group `grp`: offset of
+// weight[co, ci0 + ci, tap] relative to the stage's first output channel,
+// or -1 if padding.
+template <int MT>
+C2B_HD int f32_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0 || e >= kF32StageCh * P.cp) return -1;
+  const int co = fast_div(e, P.m_cp);
+  const int r = e - co * P.cp;
+  if (r >= MT * P.tg) return -1;
+  const int ci = fast_div(r, P.m_tg), t = r - ci * P.tg;
+  const int tap = grp * P.tg + t;
+  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return -1;
+  return (co * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
+}
 
 // Accumulator register r of lane half h in a 32x32 block holds block row
 // 8*(r/4) + 4*h + r%4 (column = lane mod 32) -- the C/D layout of the
