@@ -21,7 +21,8 @@ import threading
 __all__ = [
     "Conv2dParams", "Conv2dError", "PlanInfo", "grad_input", "grad_input_into",
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
-    "describe_plan", "check_indexing", "status_string", "library_path", "load_library",
+    "describe_plan", "check_indexing", "check_indexing_variant", "num_f32_variants",
+    "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
 
@@ -36,6 +37,8 @@ EXPORTED_SYMBOLS = (
     "conv2d_status_string",
     "conv2d_describe_plan",
     "conv2d_check_indexing",
+    "conv2d_check_indexing_variant",
+    "conv2d_num_f32_variants",
 )
 
 CONV2D_OK = 0
@@ -116,6 +119,11 @@ def load_library():
         lib.conv2d_check_indexing.argtypes = [P, ctypes.c_int, ctypes.c_char_p,
                                               ctypes.c_size_t]
         lib.conv2d_check_indexing.restype = ctypes.c_int
+        lib.conv2d_check_indexing_variant.argtypes = [P, ctypes.c_int, ctypes.c_char_p,
+                                                      ctypes.c_size_t]
+        lib.conv2d_check_indexing_variant.restype = ctypes.c_int
+        lib.conv2d_num_f32_variants.argtypes = []
+        lib.conv2d_num_f32_variants.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -162,6 +170,18 @@ def check_indexing(p: Conv2dParams, f16: bool = False) -> tuple:
     rc = load_library().conv2d_check_indexing(ctypes.byref(p), int(bool(f16)), buf,
                                               len(buf))
     return int(rc), buf.value.decode()
+
+
+def check_indexing_variant(p: Conv2dParams, variant: int) -> tuple:
+    """check_indexing with the fp32 kernel variant forced (host only)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().conv2d_check_indexing_variant(ctypes.byref(p), int(variant), buf,
+                                                      len(buf))
+    return int(rc), buf.value.decode()
+
+
+def num_f32_variants() -> int:
+    return int(load_library().conv2d_num_f32_variants())
 
 
 def conv2d_grad_input(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,

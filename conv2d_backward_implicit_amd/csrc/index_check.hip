@@ -171,10 +171,10 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
 // fp32 family (grad_input_f32_kernel<WM, NBW>): window and weights are
 // copied by buffer loads that write LDS directly (64 consecutive floats per
 // wave-instruction), double-buffered.
-template <int WM, int NBW>
+template <int WM, int WN, int NBW>
 void check_launch_f32(const LaunchArgs& a, std::vector<unsigned char>& written) {
-  using G = F32Geom<WM, NBW>;
-  constexpr int MT = G::kMT, WN = G::kWN, NT = G::kThreads, CH = kF32StageCh;
+  using G = F32Geom<WM, WN, NBW>;
+  constexpr int MT = G::kMT, NT = G::kThreads, CH = kF32StageCh;
   const int64_t OHOW = int64_t(a.OH) * a.OW;
   const int64_t go_size = int64_t(a.N) * a.Co * OHOW;
   const int64_t KHW = int64_t(a.KH) * a.KW;
@@ -191,14 +191,12 @@ void check_launch_f32(const LaunchArgs& a, std::vector<unsigned char>& written) 
     C2B_REQUIRE(c.npx >= 1 && c.npx <= P.ntv && P.ntv <= G::kNTL, "bid %d npx %d", bid, c.npx);
     const int SLOTS = P.slabr, CP = P.cp, TG = P.tg;
     const int fcount = CH * SLOTS, ecount = CH * CP;
-    const int wt0 = 2 * CH * SLOTS;
     if (c.ntaps > 0) {
       C2B_REQUIRE(P.ckr == CH && TG >= 1 && TG <= kF32StageTaps, "stage shape");
-      C2B_REQUIRE(c.R * c.roww <= SLOTS && SLOTS <= kF32MaxSlots && SLOTS % 4 == 0,
+      C2B_REQUIRE(c.R * c.roww <= SLOTS && SLOTS <= kF32MaxSlots && SLOTS % 16 == 0,
                   "bid %d window %d > %d", bid, c.R * c.roww, SLOTS);
       C2B_REQUIRE(CP >= MT * TG && CP % 16 == 4 && CP <= kF32MaxCP, "weight pitch %d", CP);
-      C2B_REQUIRE(2 * (fcount + ecount) <= kF32LdsFloats, "LDS %d", 2 * (fcount + ecount));
-      C2B_REQUIRE(fcount % 64 == 0 && ecount % 64 == 0, "whole wave-instructions");
+      C2B_REQUIRE(fcount <= kF32WinFloats && ecount <= kF32WtFloats, "stage exceeds buffers");
       C2B_REQUIRE(int64_t(CH) * OHOW * 4 < (int64_t(1) << 31) &&
                       int64_t(CH) * cstride * 4 < (int64_t(1) << 31),
                   "stage byte range");
@@ -214,9 +212,10 @@ void check_launch_f32(const LaunchArgs& a, std::vector<unsigned char>& written) 
         // window cells
         for (int k = 0; k < G::kHS; ++k) {
           const int f0 = wave * 64 + NT * k, f = tid + NT * k;
-          if (f0 >= fcount) continue;
-          C2B_REQUIRE(f == f0 + lane && f < fcount, "window lds %d", f);
+          if (f0 >= kF32WinFloats) continue;            // instruction not issued
+          C2B_REQUIRE(f == f0 + lane && f < kF32WinFloats, "window lds %d", f);
           const int o = f32_window_cell(c, a, f);
+          if (f >= fcount) C2B_REQUIRE(o < 0, "cell past the window reads memory");
           if (o < 0 || int64_t(o) >= int64_t(nco) * OHOW) continue;   // reads 0
           const int cq = f / (4 * SLOTS), r = f % (4 * SLOTS);
           const int slot = r / 4, ch = 4 * cq + r % 4;
@@ -232,9 +231,10 @@ void check_launch_f32(const LaunchArgs& a, std::vector<unsigned char>& written) 
         // weight cells
         for (int k = 0; k < G::kWS; ++k) {
           const int e0 = wave * 64 + NT * k, e = tid + NT * k;
-          if (e0 >= ecount) continue;
-          C2B_REQUIRE(e == e0 + lane && wt0 + CH * CP + e < kF32LdsFloats, "weight lds %d", e);
+          if (e0 >= kF32WtFloats) continue;             // instruction not issued
+          C2B_REQUIRE(e == e0 + lane && e < kF32WtFloats, "weight lds %d", e);
           const int o = f32_weight_cell<MT>(c, a, e, grp);
+          if (e >= ecount) C2B_REQUIRE(o < 0, "cell past the weights reads memory");
           if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) continue;  // reads 0
           const int co = e / CP, r = e % CP, ci = r / TG, t = r % TG;
           C2B_REQUIRE(co < nco && ci < MT && t < ntg, "weight cell %d", e);
@@ -300,7 +300,7 @@ void check_launch_f32(const LaunchArgs& a, std::vector<unsigned char>& written) 
 template <int V>
 void check_f32_variant(const LaunchArgs& la, std::vector<unsigned char>& written) {
   constexpr F32Variant v = kF32Variants[V];
-  check_launch_f32<v.wm, v.nbw>(la, written);
+  check_launch_f32<v.wm, v.wn, v.nbw>(la, written);
 }
 
 template <int... Vs>
@@ -310,10 +310,10 @@ void check_f32_dispatch(const LaunchArgs& la, std::vector<unsigned char>& writte
 }
 
 template <bool F16>
-int check_all(const conv2d_params* p, char* msg, size_t len) {
+int check_all(const conv2d_params* p, char* msg, size_t len, int variant) {
   std::vector<LaunchArgs> launches;
   int rc = F16 ? build_plan(p, kF16Tile, &launches, nullptr)
-               : build_plan_f32(p, kF32DefaultCUs, &launches, nullptr);
+               : build_plan_f32(p, kF32DefaultCUs, &launches, nullptr, variant);
   if (rc != CONV2D_OK) return rc;
   const int64_t n_gi = int64_t(p->batch) * p->in_channels * p->in_h * p->in_w;
   std::vector<unsigned char> written(size_t(n_gi), 0);
@@ -342,5 +342,14 @@ int check_all(const conv2d_params* p, char* msg, size_t len) {
 
 extern "C" int conv2d_check_indexing(const conv2d_params* p, int f16, char* msg,
                                      size_t msg_len) {
-  return f16 ? c2b::check_all<true>(p, msg, msg_len) : c2b::check_all<false>(p, msg, msg_len);
+  return f16 ? c2b::check_all<true>(p, msg, msg_len, -1)
+             : c2b::check_all<false>(p, msg, msg_len, -1);
 }
+
+extern "C" int conv2d_check_indexing_variant(const conv2d_params* p, int variant, char* msg,
+                                             size_t msg_len) {
+  if (variant < 0 || variant >= c2b::kNumF32Variants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::check_all<false>(p, msg, msg_len, variant);
+}
+
+extern "C" int conv2d_num_f32_variants(void) { return c2b::kNumF32Variants; }

@@ -268,11 +268,14 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // stage s is multiplied; one barrier per stage.  Per tap, a wave reads one
 // 16-byte window cell per 16-pixel block and 4 weights, then issues
 // 4 x NBW matrix instructions.
-template <int WM, int NBW>
-__global__ __launch_bounds__(kF32Threads) void grad_input_f32_kernel(const LaunchArgs a) {
-  using G = F32Geom<WM, NBW>;
-  constexpr int MT = G::kMT, WN = G::kWN, HS = G::kHS, WS = G::kWS, NT = G::kThreads;
+template <int WM, int WN, int NBW>
+__global__ __launch_bounds__(64 * WM * WN) void grad_input_f32_kernel(const LaunchArgs a) {
+  using G = F32Geom<WM, WN, NBW>;
+  constexpr int MT = G::kMT, HS = G::kHS, WS = G::kWS, NT = G::kThreads;
   constexpr int TGM = kF32StageTaps, CH = kF32StageCh;
+  // fixed LDS regions (floats): two window buffers, then two weight buffers
+  constexpr int kWin0 = 0, kWin1 = kF32WinFloats, kWt0 = 2 * kF32WinFloats,
+                kWt1 = 2 * kF32WinFloats + kF32WtFloats;
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ f32x4 lds4[kF32LdsFloats / 4];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -288,54 +291,71 @@ __global__ __launch_bounds__(kF32Threads) void grad_input_f32_kernel(const Launc
   const int cstride = a.Ci * a.KH * a.KW;
   const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
   const int SLOTS = P.slabr, CP = P.cp, TG = P.tg;
-  // LDS float offsets of the two window and the two weight buffers
-  const int win0 = 0, win1 = CH * SLOTS, wt0 = 2 * CH * SLOTS, wt1 = wt0 + CH * CP;
 
+  // copy cells: thread tid holds cells tid + NT*k of the window and of the
+  // weights; every wave-instruction writes 64 consecutive floats inside its
+  // fixed buffer, cells past the stage's data read 0
   unsigned gbyte[HS];
 #pragma unroll
   for (int k = 0; k < HS; ++k) {
-    const int o = f32_window_cell(c, a, tid + NT * k);
+    const int f = tid + NT * k;
+    const int o = f < kF32WinFloats ? f32_window_cell(c, a, f) : -1;
     gbyte[k] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
   }
   unsigned wbyte[WS];
   int wgroup = -1;
-  const int fcount = CH * SLOTS;   // multiple of 64
-  const int ecount = CH * CP;      // multiple of 64
-  auto issue_stage = [&](int st, int buf) {
+  struct StageCopy {
+    __amdgpu_buffer_rsrc_t rg, rw;
+    int buf;
+  };
+  auto begin_stage_copy = [&](int st, int buf) {
     int co0, grp;
     stage_split(c, CH, st, &co0, &grp);
     if (grp != wgroup) {
 #pragma unroll
       for (int k = 0; k < WS; ++k) {
-        const int o = f32_weight_cell<MT>(c, a, tid + NT * k, grp);
+        const int e = tid + NT * k;
+        const int o = e < kF32WtFloats ? f32_weight_cell<MT>(c, a, e, grp) : -1;
         wbyte[k] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
       }
       wgroup = grp;
     }
     const int nco = imin(CH, a.Co - co0);
-    const auto rg = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(go_n + (size_t)co0 * OHOW), 0, nco * OHOW * 4, kRawBufferFlags);
-    float* wdst = lds + (buf ? win1 : win0);
+    StageCopy sc;
+    sc.rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(go_n + (size_t)co0 * OHOW), 0,
+                                              nco * OHOW * 4, kRawBufferFlags);
+    sc.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.w + (size_t)co0 * cstride), 0,
+                                              nco * cstride * 4, kRawBufferFlags);
+    sc.buf = buf;
+    return sc;
+  };
+  // copy instructions [lo, hi) of a stage (window ones first); lo and hi are
+  // compile-time constants here, so the range test folds away
+  auto copy_chunk = [&](const StageCopy& sc, int lo, int hi) {
 #pragma unroll
-    for (int k = 0; k < HS; ++k) {
-      const int f0 = wave * 64 + NT * k;
-      if (f0 < fcount)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, lds_ptr(wdst + f0), 4, gbyte[k], 0, 0, 0);
-    }
-    const auto rw = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<float*>(a.w + (size_t)co0 * cstride), 0, nco * cstride * 4, kRawBufferFlags);
-    float* adst = lds + (buf ? wt1 : wt0);
-#pragma unroll
-    for (int k = 0; k < WS; ++k) {
-      const int e0 = wave * 64 + NT * k;
-      if (e0 < ecount)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rw, lds_ptr(adst + e0), 4, wbyte[k], 0, 0, 0);
+    for (int i = 0; i < HS + WS; ++i) {
+      if (i < lo || i >= hi) continue;
+      if (i < HS) {
+        const int f0 = wave * 64 + NT * i;
+        if (HS * NT == kF32WinFloats || f0 < kF32WinFloats)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              sc.rg, lds_ptr(lds + (sc.buf ? kWin1 : kWin0) + f0), 4, gbyte[i], 0, 0, 0);
+      } else {
+        const int k = i - HS;
+        const int e0 = wave * 64 + NT * k;
+        if (WS * NT == kF32WtFloats || e0 < kF32WtFloats)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              sc.rw, lds_ptr(lds + (sc.buf ? kWt1 : kWt0) + e0), 4, wbyte[k], 0, 0, 0);
+      }
     }
   };
+  constexpr int kCopies = HS + WS;
 
   const int nst = c.nstages;
-  if (nst > 0) issue_stage(0, 0);
-  if (nst > 1) issue_stage(1, 1);
+  if (nst > 0) {
+    const StageCopy sc0 = begin_stage_copy(0, 0);
+    copy_chunk(sc0, 0, kCopies);
+  }
 
   // byte offsets within a window buffer of each block's cell for the class's
   // first tap, and within a weight buffer of this lane's weights
@@ -343,39 +363,73 @@ __global__ __launch_bounds__(kF32Threads) void grad_input_f32_kernel(const Launc
 #pragma unroll
   for (int b = 0; b < NBW; ++b)
     bb[b] = (g * SLOTS + window_base(c, f32_local(b, ng, c16, WN))) * 16;
-  const int ab = (4 * g * CP + (mg * 16 + c16) * TG) * 4;
+  // byte offsets of this lane's weights of channel 4g + q, tap 0
+  int aq[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) aq[q] = ((4 * g + q) * CP + (mg * 16 + c16) * TG) * 4;
 
   f32x4 acc[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  auto compute = [&](int st, int buf) {
+  // multiply stage st out of buffer st&1; the copies of stage st+1 (if any)
+  // go out into the other buffer during the first tap.  Tap tt reads the
+  // window at a fixed slot offset and weight t = tt of channel 4g + q.
+  auto tap_mma = [&](const char* Hb, const char* Ab, int boff) {
+    // all addresses, then all reads, then (in the caller) the products: the
+    // scheduling barriers keep the compiler from recycling a read's target
+    // register as the next address, which would serialise the reads
+    const f32x4* ba[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) ba[b] = reinterpret_cast<const f32x4*>(Hb + bb[b] + boff);
+    const float* aa[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) aa[q] = reinterpret_cast<const float*>(Ab + aq[q]);
+    __builtin_amdgcn_sched_barrier(0);
+    float aw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) aw[q] = *aa[q];
+    f32x4 bv[NBW];
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) bv[b] = *ba[b];
+    __builtin_amdgcn_sched_barrier(0);
+    return [&, bv, aw]() mutable {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int b = 0; b < NBW; ++b)
+          acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[q], bv[b][q], acc[b], 0, 0, 0);
+    };
+  };
+  auto compute = [&](int st) {
+    const int buf = st & 1;
     int co0, grp;
     stage_split(c, CH, st, &co0, &grp);
     const int tap0 = grp * TG;
     const int ntg = imin(TG, c.ntaps - tap0);
-    const char* Hb = reinterpret_cast<const char*>(lds + (buf ? win1 : win0));
-    const char* Ab = reinterpret_cast<const char*>(lds + (buf ? wt1 : wt0)) + ab;
+    const char* Hb = reinterpret_cast<const char*>(lds + (buf ? kWin1 : kWin0));
+    const char* Ab = reinterpret_cast<const char*>(lds + (buf ? kWt1 : kWt0));
     int j = tap0 / P.tw, l = tap0 - (tap0 / P.tw) * P.tw;
-#pragma unroll
-    for (int tt = 0; tt < TGM; ++tt) {
-      if (tt < ntg) {
-        const int boff = tap_window_offset(c, j, l) * 16;
-        f32x4 bv[NBW];
-#pragma unroll
-        for (int b = 0; b < NBW; ++b) bv[b] = *reinterpret_cast<const f32x4*>(Hb + bb[b] + boff);
-        float aw[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) aw[q] = *reinterpret_cast<const float*>(Ab + (q * CP + tt) * 4);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-#pragma unroll
-          for (int b = 0; b < NBW; ++b)
-            acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[q], bv[b][q], acc[b], 0, 0, 0);
-        if (++l == P.tw) {
-          l = 0;
-          ++j;
-        }
+    // first tap, with the copies of the next stage
+    {
+      auto mma = tap_mma(Hb, Ab, tap_window_offset(c, j, l) * 16);
+      if (st + 1 < nst) {
+        const StageCopy sc = begin_stage_copy(st + 1, buf ^ 1);
+        copy_chunk(sc, 0, kCopies);
+      }
+      mma();
+      if (++l == P.tw) {
+        l = 0;
+        ++j;
+      }
+    }
+    for (int tt = 1; tt < ntg; ++tt) {
+      Ab += 4;   // weight t = tt
+      auto mma = tap_mma(Hb, Ab, tap_window_offset(c, j, l) * 16);
+      mma();
+      if (++l == P.tw) {
+        l = 0;
+        ++j;
       }
     }
   };
@@ -383,10 +437,9 @@ __global__ __launch_bounds__(kF32Threads) void grad_input_f32_kernel(const Launc
   wait_vmem();
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
-    compute(st, st & 1);
+    compute(st);
     wait_vmem();          // this wave's copies of stage st+1 have landed
-    __syncthreads();      // ... everyone's, and buffer st&1 is free again
-    if (st + 2 < nst) issue_stage(st + 2, st & 1);
+    __syncthreads();      // ... everyone's, and buffer st&1 may be refilled
   }
 
   // epilogue: register r of block b holds channel mg*16 + 4g + r, pixel
@@ -408,8 +461,8 @@ __global__ __launch_bounds__(kF32Threads) void grad_input_f32_kernel(const Launc
 template <int V>
 void launch_f32_variant(const LaunchArgs& la, hipStream_t st) {
   constexpr F32Variant v = kF32Variants[V];
-  hipLaunchKernelGGL((grad_input_f32_kernel<v.wm, v.nbw>), dim3(la.total_tiles),
-                     dim3(kF32Threads), 0, st, la);
+  hipLaunchKernelGGL((grad_input_f32_kernel<v.wm, v.wn, v.nbw>), dim3(la.total_tiles),
+                     dim3(64 * v.wm * v.wn), 0, st, la);
 }
 
 template <int... Vs>

@@ -297,8 +297,7 @@ bool tile_class_f32(PhaseDesc* d, int64_t ntl, int64_t mt) {
   while (tg > 1 && weight_pitch(mt, tg) > kF32MaxCP) --tg;
   const int64_t cp = weight_pitch(mt, tg);
   if (cp > kF32MaxCP) return false;
-  const int64_t max_slots = std::min<int64_t>(kF32MaxSlots,
-                                              (kF32LdsFloats / (2 * kF32StageCh) - cp) / 4 * 4);
+  const int64_t max_slots = kF32MaxSlots;
   int64_t last_wb = -1;
   for (int64_t nb = 1; nb <= wp; ++nb) {
     const int64_t wb = ceil_div(wp, nb);
@@ -310,7 +309,9 @@ bool tile_class_f32(PhaseDesc* d, int64_t ntl, int64_t mt) {
     for (int64_t cap = ntl;; cap = (cap + 1) / 2) {
       const int64_t ntv = ceil_div(bp, ceil_div(bp, cap));
       const int64_t rows = max_rows_spanned(wb, ntv, bp) + th - 1;
-      const int64_t slots = ceil_div(rows * roww, 4) * 4;
+      // the four channel quads of a window start 16*slots floats apart; a
+      // multiple of 256 bytes keeps 16-byte reads free of bank conflicts
+      const int64_t slots = ceil_div(rows * roww, 16) * 16;
       if (slots <= max_slots) {
         d->wb = int32_t(wb);
         d->nbands = int32_t(ceil_div(wp, wb));
@@ -330,16 +331,22 @@ bool tile_class_f32(PhaseDesc* d, int64_t ntl, int64_t mt) {
   return false;
 }
 
-// Relative cost of one tile: matrix work of every wave (NBW blocks x padded
-// k values) plus a per-stage and per-tile overhead.
-double tile_cost_f32(const PhaseDesc& d, int64_t Co, int nbw) {
-  const double tile_overhead = 4000.0;                // cycles: set-up, epilogue
+// Matrix-unit efficiency reached with `wn` waves per SIMD (measured on the
+// tap loop: more waves hide more of the LDS latency between taps).
+double simd_efficiency(int wn) { return wn >= 4 ? 0.88 : wn == 3 ? 0.85 : wn == 2 ? 0.75 : 0.6; }
+
+// Relative cost of one tile: matrix work of the waves sharing a SIMD (wn
+// waves x NBW blocks x padded k values / efficiency) plus per-stage and
+// per-tile overheads.
+double tile_cost_f32(const PhaseDesc& d, int64_t Co, const F32Variant& v) {
+  const double tile_overhead = 20000.0;               // cycles: set-up, epilogue
   if (d.th == 0) return tile_overhead;
   const int64_t ntaps = int64_t(d.th) * d.tw;
   const int64_t kpad = ceil_div(Co, d.ckr) * d.ckr * ntaps;
   const int64_t stages = ceil_div(Co, d.ckr) * d.ngroups;
-  // two waves share a SIMD's matrix unit; 16x16x4 fp32 takes 32 cycles
-  return 2.0 * nbw * (kpad / 4) * 32.0 + stages * 600.0 + tile_overhead;
+  // 16x16x4 fp32 takes 32 cycles of a SIMD's matrix unit
+  return double(v.wn) * v.nbw * (kpad / 4) * 32.0 / simd_efficiency(v.wn) + stages * 600.0 +
+         tile_overhead;
 }
 
 // Largest-first makespan of the tiles over `cus` compute units.
@@ -373,7 +380,7 @@ double lpt_makespan(const std::vector<PhaseDesc>& phases, int64_t per_class_mult
 }  // namespace
 
 int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>* launches,
-                   conv2d_plan_info* info) {
+                   conv2d_plan_info* info, int force_variant) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
   if (info) std::memset(info, 0, sizeof(*info));
@@ -386,28 +393,26 @@ int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>*
   std::vector<PhaseDesc> classes;
   make_classes(p, &classes);
   const int wm = Ci > 64 ? 8 : 4;
-  const int64_t mt = 16 * wm;
-  const int64_t ciblocks = ceil_div(Ci, mt);
 
   int best_v = -1;
   F32Choice best;
   for (int v = 0; v < kNumF32Variants; ++v) {
-    if (kF32Variants[v].wm != wm) continue;
-    const int nbw = kF32Variants[v].nbw;
-    const int64_t ntl = 16 * nbw * (8 / wm);
+    if (force_variant >= 0 ? v != force_variant : kF32Variants[v].wm != wm) continue;
+    const int64_t vmt = 16 * int64_t(kF32Variants[v].wm);
+    const int64_t ntl = 16 * int64_t(kF32Variants[v].nbw) * kF32Variants[v].wn;
     F32Choice ch;
     ch.phases = classes;
     bool ok = true;
     std::vector<double> costs;
     for (PhaseDesc& d : ch.phases) {
-      if (!tile_class_f32(&d, ntl, mt)) {
+      if (!tile_class_f32(&d, ntl, vmt)) {
         ok = false;
         break;
       }
-      costs.push_back(tile_cost_f32(d, Co, nbw));
+      costs.push_back(tile_cost_f32(d, Co, kF32Variants[v]));
     }
     if (!ok) continue;
-    ch.cost = lpt_makespan(ch.phases, N * ciblocks, costs, num_cus);
+    ch.cost = lpt_makespan(ch.phases, N * ceil_div(Ci, vmt), costs, num_cus);
     if (best_v < 0 || ch.cost < best.cost * 0.999) {
       best_v = v;
       best = ch;
@@ -415,26 +420,28 @@ int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>*
   }
   if (best_v < 0) return CONV2D_ERR_UNSUPPORTED;
 
-  const int nbw = kF32Variants[best_v].nbw;
+  const F32Variant bv = kF32Variants[best_v];
+  const int64_t bmt = 16 * int64_t(bv.wm);
+  const int64_t bci = ceil_div(Ci, bmt);
   for (PhaseDesc& d : best.phases) {
-    const int64_t tiles = N * d.nbands * int64_t(d.ptiles) * ciblocks;
+    const int64_t tiles = N * d.nbands * int64_t(d.ptiles) * bci;
     if (tiles >= kI31) return CONV2D_ERR_OVERFLOW;
     d.tiles = int32_t(tiles);
     if (info) {
       info->phases += 1;
       if (d.th == 0) info->zero_phases += 1;
       if (d.th > 0) {
-        const int64_t lanes = 16 * int64_t(nbw) * (8 / wm);
+        const int64_t lanes = 16 * int64_t(bv.nbw) * bv.wn;
         const int64_t kpad = ceil_div(Co, d.ckr) * d.ckr * int64_t(d.th) * d.tw;
-        info->macs += tiles * lanes * mt * kpad;
+        info->macs += tiles * lanes * bmt * kpad;
       }
     }
   }
   std::stable_sort(best.phases.begin(), best.phases.end(),
                    [&](const PhaseDesc& a, const PhaseDesc& b) {
-                     return tile_cost_f32(a, Co, nbw) > tile_cost_f32(b, Co, nbw);
+                     return tile_cost_f32(a, Co, bv) > tile_cost_f32(b, Co, bv);
                    });
-  return emit_launches(p, ciblocks, best_v, best.phases, launches, info);
+  return emit_launches(p, bci, best_v, best.phases, launches, info);
 }
 
 }  // namespace c2b

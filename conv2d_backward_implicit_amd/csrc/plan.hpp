@@ -97,29 +97,35 @@ int validate_shape(const conv2d_params* p);
 int build_plan(const conv2d_params* p, const TileShape& ts,
                std::vector<LaunchArgs>* launches, conv2d_plan_info* info);
 
-// fp32 kernel family: 8 waves, 16x16x4 fp32 matrix instructions; each wave
-// owns 16 input channels x NBW blocks of 16 pixels.  Variants differ in the
-// waves along channels (WM) and the blocks per wave (NBW).
+// fp32 kernel family: WM x WN waves, 16x16x4 fp32 matrix instructions; each
+// wave owns 16 input channels x NBW blocks of 16 pixels.  WM waves along
+// channels (64- or 128-channel tiles), WN waves along pixels (2, 3 or 4 waves
+// per SIMD).
 struct F32Variant {
   int wm;    // waves along channels: 4 (64-channel tiles) or 8 (128)
+  int wn;    // waves along pixels
   int nbw;   // 16-pixel blocks per wave
 };
-constexpr F32Variant kF32Variants[] = {{4, 4}, {4, 8}, {4, 10}, {4, 13},
-                                       {8, 4}, {8, 8}, {8, 10}, {8, 13}};
+constexpr F32Variant kF32Variants[] = {{4, 2, 4}, {4, 2, 8}, {4, 2, 13}, {4, 3, 9},
+                                       {4, 4, 7}, {8, 1, 4}, {8, 1, 8}, {8, 1, 13},
+                                       {8, 2, 7}};
 constexpr int kNumF32Variants = int(sizeof(kF32Variants) / sizeof(kF32Variants[0]));
-constexpr int kF32Threads = 512;
 constexpr int kF32StageCh = 16;     // output channels per stage
-constexpr int kF32MaxSlots = 672;   // window slots per channel (multiple of 4)
+constexpr int kF32MaxSlots = 640;   // window slots per channel (multiple of 16)
 constexpr int kF32MaxCP = 608;      // staged weight floats per channel
-constexpr int kF32LdsFloats = 40960;  // 160 KiB: 2 x 16 x (slots + cp) floats at most
+constexpr int kF32WinFloats = kF32StageCh * kF32MaxSlots;   // one window buffer
+constexpr int kF32WtFloats = kF32StageCh * kF32MaxCP;       // one weight buffer
+constexpr int kF32LdsFloats = 2 * (kF32WinFloats + kF32WtFloats);   // 156 KiB
 constexpr int kF32StageTaps = 9;    // kernel taps per stage
 constexpr int kF32DefaultCUs = 256;
 
 // Plan for the fp32 kernel family on a device with `num_cus` compute units:
 // chooses the variant, tile sizes and stage depths per class (balancing the
 // tiles over the compute units, heaviest first).
+// force_variant >= 0 plans with that variant only (CONV2D_ERR_UNSUPPORTED if
+// it cannot tile the shape); used by host-side checks of every variant.
 int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>* launches,
-                   conv2d_plan_info* info);
+                   conv2d_plan_info* info, int force_variant = -1);
 
 // Pointer checks: NULL inputs of non-empty tensors and output/input overlap.
 int check_pointers(const float* go, const float* w, const float* gi,

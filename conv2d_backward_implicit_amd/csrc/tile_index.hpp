@@ -205,11 +205,11 @@ struct KernelGeom {
 // ---------------------------------------------------------------------------
 // fp32 kernel family (8 waves, 16x16x4 fp32 matrix instructions).
 //   wave w: channel group mg = w % WM (16 input channels), pixel group
-//   ng = w / WM; lane: k group g = lane / 16, c16 = lane % 16;
+//   ng = w / WM (WN groups); lane: k group g = lane / 16, c16 = lane % 16;
 //   block b of the wave covers tile-local pixels (b*WN + ng)*16 + [0, 16);
 //   k-step q (0..3) of a tap: lane group g supplies output channel 4g + q.
-// A stage is 16 output channels x up to tg taps.  LDS per buffer (two
-// buffers of each):
+// A stage is 16 output channels x up to tg taps.  LDS (two buffers of each,
+// at fixed offsets):
 //   window  [quad cq = 0..3][slot][4 channels]  (16*slots floats): a lane
 //           reads its group's 4 channels with one 16-byte read, 16 lanes read
 //           16 consecutive 16-byte cells (every bank once), and a tap shift
@@ -220,18 +220,17 @@ struct KernelGeom {
 // wave-instruction fills 64 consecutive floats, which here come from 16
 // consecutive pixels of 4 channels, or from consecutive weights of one
 // channel -- a few cache lines per instruction.
-template <int WM, int NBW>
+template <int WM, int WN, int NBW>
 struct F32Geom {
-  static constexpr int kThreads = kF32Threads;
-  static constexpr int kWN = 8 / WM;                  // waves along pixels
+  static constexpr int kThreads = 64 * WM * WN;
+  static constexpr int kWN = WN;                      // waves along pixels
   static constexpr int kMT = 16 * WM;                 // channels per tile
-  static constexpr int kNTL = 16 * NBW * kWN;         // pixel lanes per tile
-  static constexpr int kHS = kF32StageCh * kF32MaxSlots / kThreads;  // window cells / thread
-  static constexpr int kWS = kF32StageCh * kF32MaxCP / kThreads;     // weight cells / thread
-  static_assert(WM * kWN == 8, "8 waves");
-  static_assert(kF32StageCh * kF32MaxSlots % kThreads == 0 &&
-                    kF32StageCh * kF32MaxCP % kThreads == 0, "whole cells per thread");
-  static_assert(2 * kF32StageCh * (kF32MaxSlots + kF32MaxCP) <= kF32LdsFloats, "LDS");
+  static constexpr int kNTL = 16 * NBW * WN;          // pixel lanes per tile
+  // copy wave-instructions per wave and stage: every one is issued; cells
+  // past the stage's window or weights read 0 and land inside the buffer
+  static constexpr int kHS = (kF32WinFloats + kThreads - 1) / kThreads;
+  static constexpr int kWS = (kF32WtFloats + kThreads - 1) / kThreads;
+  static_assert(kF32WinFloats % 64 == 0 && kF32WtFloats % 64 == 0, "whole instructions");
 };
 
 // Tile-local pixel of block b of pixel group ng, lane c16.

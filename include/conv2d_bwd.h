@@ -159,6 +159,19 @@ int conv2d_describe_plan(const conv2d_params* p, int f16,
 int conv2d_check_indexing(const conv2d_params* p, int f16, char* msg,
                           size_t msg_len);
 
+/*
+ * The same replay for the fp32 path with its kernel variant forced to
+ * `variant` (0 <= variant < conv2d_num_f32_variants()) instead of the one
+ * the planner would pick, so every variant can be checked on any shape.
+ * Returns as conv2d_check_indexing, or CONV2D_ERR_UNSUPPORTED if the
+ * variant index is out of range or the variant cannot tile the shape.
+ */
+int conv2d_check_indexing_variant(const conv2d_params* p, int variant,
+                                  char* msg, size_t msg_len);
+
+/* Number of fp32 kernel variants (tile shapes) the library carries. */
+int conv2d_num_f32_variants(void);
+
 #ifdef __cplusplus
 }
 #endif
