@@ -33,11 +33,21 @@ KERNEL_SOURCES = ["conv2d_backward_implicit_amd/csrc/kernels.hip",
                   "conv2d_backward_implicit_amd/csrc/plan.cpp"]
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source with comments and blank lines removed (string literals in
+    these sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def source_digest() -> str:
+    """Digest of the code (not the comments) of the kernel sources: a counter
+    summary taken on other code is stale."""
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

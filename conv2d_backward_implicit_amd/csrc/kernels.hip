@@ -9,21 +9,28 @@
 // How it is computed here (a re-design for gfx950, not the shader's scheme):
 //  * Stride-residue classes (plan.hpp): every class is a dense stride-1
 //    problem on a sub-image, so no structural zero is staged or multiplied.
-//  * One workgroup = 4 waves owns a 64-channel x 256-pixel output tile of one
-//    class; pixels are consecutive (row-major) positions of one band of the
-//    class sub-image of one image.  Batch, class and band are all folded into
-//    the one-dimensional grid.
-//  * B is never materialised: per stage the workgroup copies the grad_out
+//    Batch, class, pixel band and channel block are folded into one
+//    one-dimensional grid.  Workgroups are dealt to the 8 XCDs round robin,
+//    so the tile index is remapped (decode_tile) to give each XCD one
+//    contiguous run of tiles: neighbours that share halo rows and weights
+//    then meet in the same L2.
+//  * B is never materialised: per stage a workgroup copies the grad_out
 //    window its pixels read (band rows plus the kernel halo, zero outside the
-//    image) into LDS once, coalesced along rows; every tap then reads the
-//    window at a fixed offset, so each grad_out element crosses from L2/HBM
-//    once per stage instead of once per tap.
-//  * A (the stage's weights) is copied to LDS with a channel-fastest layout.
-//  * Register-staged prefetch: the global loads of stage s+1 are issued
-//    before the matrix instructions of stage s.
-//  * Matrix cores: fp32 path v_mfma_f32_32x32x2_f32, f16-staged path
-//    v_mfma_f32_32x32x16_f16 (operands rounded to f16 on the way into LDS);
-//    each wave owns 2 x 2 blocks of 32x32 with fp32 accumulators.
+//    image) into LDS once, then every tap reads that window at a fixed
+//    offset, so each grad_out element crosses from L2/HBM once per stage
+//    instead of once per tap.
+//  * fp32 path (grad_input_f32_kernel): WM x WN waves, v_mfma_f32_16x16x4_f32.
+//    Window and weights go straight from global memory into LDS with buffer
+//    loads that write LDS (no register round trip); reads past a tensor's
+//    extent return 0, which supplies the padding halo.  Two LDS buffers per
+//    operand: the copies of stage s+1 are issued during the first tap of
+//    stage s, one barrier per stage.  The planner picks the wave shape
+//    (channel blocks x pixel blocks) per problem from a cost model of the
+//    schedule over all CUs.
+//  * f16-staged path (grad_input_kernel<true, ...>): 4 waves own a
+//    64-channel x 256-pixel tile, operands are staged through registers and
+//    rounded to f16 (round to nearest even) on their way into LDS, products
+//    on v_mfma_f32_32x32x16_f16 with fp32 accumulators.
 //  * Epilogue: masked stores straight to NCHW grad_input; every pixel of a
 //    class is owned by exactly one tile, so grad_input is overwritten once,
 //    with no race between workgroups.

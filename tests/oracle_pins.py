@@ -16,9 +16,12 @@ What the pins rest on:
   weights and delta grad_out (placement by strided array slicing), the 1x1
   stride-1 case as a plain matrix product (numpy matmul), exact zeros at
   pixels no tap reaches (stride > kernel);
-* integer inputs, for which float64 sums are exact.
+* integer inputs, for which float64 sums are exact;
+* hand-worked tap-count tables under tests/golden/ (no program made them).
 """
 from __future__ import annotations
+
+import os
 
 import numpy as np
 
@@ -265,6 +268,35 @@ def pin_integer_exact(orc):
         assert np.array_equal(got, np.round(got)), sh
 
 
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_tap_count_tables(path=os.path.join(GOLDEN_DIR, "all_ones_tap_counts.txt")):
+    """(ConvShape, row counts, column counts) for every case in the table."""
+    cases, cur = [], {}
+    for line in open(path):
+        line = line.split("#", 1)[0].split()
+        if not line:
+            continue
+        cur[line[0]] = [int(v) for v in line[1:]]
+        if line[0] == "cols":
+            sh = ConvShape("golden%d" % len(cases), *cur["shape"])
+            assert len(cur["rows"]) == sh.in_h and len(cur["cols"]) == sh.in_w
+            cases.append((sh, cur["rows"], cur["cols"]))
+            cur = {}
+    return cases
+
+
+def pin_golden_tap_counts(orc):
+    """All-ones inputs against the hand-worked tables: Co * rows[ih] * cols[iw]."""
+    cases = load_tap_count_tables()
+    assert len(cases) == 4
+    for sh, rows, cols in cases:
+        gi = _gather(orc, sh, np.ones(sh.go_shape), np.ones(sh.w_shape))
+        exp = sh.out_channels * np.outer(np.array(rows, float), np.array(cols, float))
+        assert np.array_equal(gi, np.broadcast_to(exp, gi.shape)), (sh, gi[0, 0], exp)
+
+
 def pin_degenerate(orc):
     """No output channels: the sum is empty and grad_input is all zeros."""
     sh = ConvShape("co0", 1, 3, 5, 5, 0, 3, 3, 1, 1, 1, 5, 5)
@@ -280,6 +312,7 @@ ALL_PINS = [
     pin_adjoint,
     pin_gather_vs_scatter,
     pin_all_ones,
+    pin_golden_tap_counts,
     pin_delta_weight,
     pin_delta_grad_out,
     pin_pointwise_gemm,
