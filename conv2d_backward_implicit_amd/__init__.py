@@ -21,7 +21,8 @@ import threading
 __all__ = [
     "Conv2dParams", "Conv2dError", "PlanInfo", "grad_input", "grad_input_into",
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
-    "describe_plan", "check_indexing", "check_indexing_variant", "num_f32_variants",
+    "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
+    "variant_is_f16", "conv2d_grad_input_variant",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -37,8 +38,10 @@ EXPORTED_SYMBOLS = (
     "conv2d_status_string",
     "conv2d_describe_plan",
     "conv2d_check_indexing",
+    "conv2d_num_variants",
+    "conv2d_variant_is_f16",
+    "conv2d_grad_input_variant",
     "conv2d_check_indexing_variant",
-    "conv2d_num_f32_variants",
 )
 
 CONV2D_OK = 0
@@ -122,8 +125,14 @@ def load_library():
         lib.conv2d_check_indexing_variant.argtypes = [P, ctypes.c_int, ctypes.c_char_p,
                                                       ctypes.c_size_t]
         lib.conv2d_check_indexing_variant.restype = ctypes.c_int
-        lib.conv2d_num_f32_variants.argtypes = []
-        lib.conv2d_num_f32_variants.restype = ctypes.c_int
+        lib.conv2d_num_variants.argtypes = []
+        lib.conv2d_num_variants.restype = ctypes.c_int
+        lib.conv2d_variant_is_f16.argtypes = [ctypes.c_int]
+        lib.conv2d_variant_is_f16.restype = ctypes.c_int
+        lib.conv2d_grad_input_variant.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                                  ctypes.c_void_p, P, ctypes.c_int,
+                                                  ctypes.c_void_p]
+        lib.conv2d_grad_input_variant.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -173,15 +182,20 @@ def check_indexing(p: Conv2dParams, f16: bool = False) -> tuple:
 
 
 def check_indexing_variant(p: Conv2dParams, variant: int) -> tuple:
-    """check_indexing with the fp32 kernel variant forced (host only)."""
+    """check_indexing with the kernel variant forced (host only)."""
     buf = ctypes.create_string_buffer(512)
     rc = load_library().conv2d_check_indexing_variant(ctypes.byref(p), int(variant), buf,
                                                       len(buf))
     return int(rc), buf.value.decode()
 
 
-def num_f32_variants() -> int:
-    return int(load_library().conv2d_num_f32_variants())
+def num_variants() -> int:
+    return int(load_library().conv2d_num_variants())
+
+
+def variant_is_f16(variant: int) -> int:
+    """1 (f16-staged), 0 (fp32) or a negative status for a bad index."""
+    return int(load_library().conv2d_variant_is_f16(int(variant)))
 
 
 def conv2d_grad_input(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,
@@ -200,6 +214,15 @@ def conv2d_grad_input_f16(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: in
         ctypes.c_void_p(grad_input_ptr), ctypes.byref(p), ctypes.c_void_p(stream)))
 
 
+def conv2d_grad_input_variant(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,
+                              p: Conv2dParams, variant: int, stream: int = 0) -> int:
+    """Raw C-ABI call with the kernel variant forced; returns the status."""
+    return int(load_library().conv2d_grad_input_variant(
+        ctypes.c_void_p(grad_out_ptr), ctypes.c_void_p(weight_ptr),
+        ctypes.c_void_p(grad_input_ptr), ctypes.byref(p), ctypes.c_int(int(variant)),
+        ctypes.c_void_p(stream)))
+
+
 def _check_tensor(t, name, shape):
     import torch
     if not isinstance(t, torch.Tensor):
@@ -215,9 +238,11 @@ def _check_tensor(t, name, shape):
 
 
 def grad_input_into(grad_input, grad_out, weight, p: Conv2dParams, f16=False,
-                    stream=None):
+                    stream=None, variant=None):
     """Write the input gradient into ``grad_input`` on torch's current stream
-    (or ``stream``, a torch.cuda.Stream).  Raises Conv2dError on a bad status."""
+    (or ``stream``, a torch.cuda.Stream).  ``variant`` forces a kernel
+    variant (its path overrides ``f16``).  Raises Conv2dError on a bad
+    status."""
     import torch
     _check_tensor(grad_out, "grad_out", (p.batch, p.out_channels, p.out_h, p.out_w))
     _check_tensor(weight, "weight", (p.out_channels, p.in_channels, p.kernel_h,
@@ -227,9 +252,14 @@ def grad_input_into(grad_input, grad_out, weight, p: Conv2dParams, f16=False,
         raise ValueError("all tensors must be on the same device")
     with torch.cuda.device(grad_input.device):
         s = stream if stream is not None else torch.cuda.current_stream()
-        fn = conv2d_grad_input_f16 if f16 else conv2d_grad_input
-        rc = fn(grad_out.data_ptr(), weight.data_ptr(), grad_input.data_ptr(), p,
-                int(s.cuda_stream))
+        if variant is not None:
+            rc = conv2d_grad_input_variant(grad_out.data_ptr(), weight.data_ptr(),
+                                           grad_input.data_ptr(), p, variant,
+                                           int(s.cuda_stream))
+        else:
+            fn = conv2d_grad_input_f16 if f16 else conv2d_grad_input
+            rc = fn(grad_out.data_ptr(), weight.data_ptr(), grad_input.data_ptr(), p,
+                    int(s.cuda_stream))
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return grad_input

@@ -19,242 +19,37 @@
 //    image) into LDS once, then every tap reads that window at a fixed
 //    offset, so each grad_out element crosses from L2/HBM once per stage
 //    instead of once per tap.
-//  * fp32 path (grad_input_f32_kernel): WM x WN waves, v_mfma_f32_16x16x4_f32.
-//    Window and weights go straight from global memory into LDS with buffer
+//  * Window and weights go straight from global memory into LDS with buffer
 //    loads that write LDS (no register round trip); reads past a tensor's
-//    extent return 0, which supplies the padding halo.  Two LDS buffers per
-//    operand: the copies of stage s+1 are issued during the first tap of
-//    stage s, one barrier per stage.  The planner picks the wave shape
-//    (channel blocks x pixel blocks) per problem from a cost model of the
+//    extent return 0, which supplies the padding halo.  Two stage buffers:
+//    the copies of stage s+1 are issued during the first unit of stage s,
+//    one barrier per stage.  The planner picks the wave shape and the stage
+//    shape (channel groups x taps) per problem from a cost model of the
 //    schedule over all CUs.
-//  * f16-staged path (grad_input_kernel<true, ...>): 4 waves own a
-//    64-channel x 256-pixel tile, operands are staged through registers and
-//    rounded to f16 (round to nearest even) on their way into LDS, products
-//    on v_mfma_f32_32x32x16_f16 with fp32 accumulators.
+//  * fp32 path: v_mfma_f32_16x16x4_f32, four per (unit, block).  f16-staged
+//    path: the same fp32 data in LDS, rounded to f16 (round to nearest even)
+//    as it is read into registers -- every operand element is rounded exactly
+//    once before it is multiplied -- and two units (32 values of k) per
+//    v_mfma_f32_16x16x32_f16 (a lone last unit on v_mfma_f32_16x16x16_f16),
+//    fp32 accumulators.
 //  * Epilogue: masked stores straight to NCHW grad_input; every pixel of a
 //    class is owned by exactly one tile, so grad_input is overwritten once,
 //    with no race between workgroups.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <cstring>
+#include <mutex>
 #include <utility>
+#include <vector>
 
 #include "tile_index.hpp"
 
 namespace c2b {
 
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-
-struct alignas(16) Half8 {
-  _Float16 v[8];
-};
-
-// f32 -> f16 with round-to-nearest-even (the hardware conversion in the
-// default rounding mode), 8 values into one 16-byte LDS cell.
-__device__ __forceinline__ Half8 pack8(const float (&x)[8]) {
-  Half8 r;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) r.v[i] = (_Float16)x[i];
-  return r;
-}
-
-template <bool F16>
-struct Cell;
-template <>
-struct Cell<false> {
-  using type = float;
-  static constexpr int kChannels = 1;   // output channels per LDS cell
-  static constexpr int kKPerStep = 2;   // k values per matrix instruction
-};
-template <>
-struct Cell<true> {
-  using type = Half8;
-  static constexpr int kChannels = 8;
-  static constexpr int kKPerStep = 16;
-};
-
-// A/B operands of one k-step for both 32-pixel blocks, then the 2 x 2 block
-// products.  NB = number of pixel blocks of this wave that hold a pixel.
-template <bool F16, int NB>
-__device__ __forceinline__ void mma_step(const typename Cell<F16>::type* sA,
-                                         const typename Cell<F16>::type* sH, int ai,
-                                         const int (&bi)[2], f32x16 (&acc)[2][2]) {
-  if constexpr (!F16) {
-    const float a0 = sA[ai], a1 = sA[ai + 32];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const float b = sH[bi[nb]];
-      acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a0, b, acc[0][nb], 0, 0, 0);
-      acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x2f32(a1, b, acc[1][nb], 0, 0, 0);
-    }
-  } else {
-    const f16x8 a0 = __builtin_bit_cast(f16x8, sA[ai]);
-    const f16x8 a1 = __builtin_bit_cast(f16x8, sA[ai + 32]);
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const f16x8 b = __builtin_bit_cast(f16x8, sH[bi[nb]]);
-      acc[0][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0, b, acc[0][nb], 0, 0, 0);
-      acc[1][nb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1, b, acc[1][nb], 0, 0, 0);
-    }
-  }
-}
-
-template <bool F16, int MT, int NT, int CK, int TAPS, int SLAB>
-__global__ __launch_bounds__(kThreads) void grad_input_kernel(const LaunchArgs a) {
-  using T = typename Cell<F16>::type;
-  using G = KernelGeom<F16, MT, CK, TAPS, SLAB>;
-  static_assert(MT == 64 && NT == 256, "4 waves x 2x2 blocks of 32x32");
-  static_assert(G::kCPC == Cell<F16>::kChannels && G::kKPerStep == Cell<F16>::kKPerStep,
-                "cell geometry");
-  constexpr int CPC = G::kCPC;
-  constexpr int NCG = G::kNCG;
-  constexpr int KSTEPS = G::kKSteps;
-  constexpr int PITCH = G::kPitch;
-  constexpr int HS = G::kHS;
-  constexpr int AE = G::kAE;
-  constexpr int WS = G::kWS;
-  static_assert(SLAB % 64 == 32 || F16, "fp32 window pitch keeps half-waves 32 banks apart");
-  __shared__ T sA[G::kLdsA];
-  __shared__ T sH[G::kLdsH];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6, h = lane >> 5, l32 = lane & 31;
-  const TileCtx c = decode_tile<MT>(a, blockIdx.x, CK);
-  const PhaseDesc& P = c.P;
-  const int OHOW = a.OH * a.OW;
-  const int cstride = a.Ci * a.KH * a.KW;   // weight distance between channels
-  const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
-
-  int goff[HS];
-#pragma unroll
-  for (int k = 0; k < HS; ++k) goff[k] = window_slot_offset(c, a, tid + kThreads * k);
-
-  // pixel blocks of this wave holding at least one pixel (wave-uniform)
-  const int first = wave * 64;
-  const int nact = first >= c.npx ? 0 : (first + 32 >= c.npx ? 1 : 2);
-  int bbase[2];
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) bbase[nb] = h * SLAB + window_base(c, first + nb * 32 + l32);
-  const int abase = h * PITCH + l32;
-
-  int woff[WS];
-  int wgroup = -1;
-  float hreg[CK][HS];
-  float wreg[WS][CPC];
-  auto load_stage = [&](int st) {
-    int co0, g;
-    stage_split(c, CK, st, &co0, &g);
-    if (g != wgroup) {
-#pragma unroll
-      for (int k = 0; k < WS; ++k)
-        woff[k] = weight_cell_offset<MT, NCG, TAPS, CPC>(c, a, tid + kThreads * k, g);
-      wgroup = g;
-    }
-#pragma unroll
-    for (int co = 0; co < CK; ++co) {
-      const bool cv = co0 + co < a.Co;
-      const float* src = go_n + (size_t)(co0 + co) * OHOW;
-#pragma unroll
-      for (int k = 0; k < HS; ++k) hreg[co][k] = (cv && goff[k] >= 0) ? src[goff[k]] : 0.0f;
-    }
-    const float* wsrc = a.w + (size_t)co0 * cstride;
-#pragma unroll
-    for (int k = 0; k < WS; ++k) {
-      const int cc = co0 + weight_cell_channel<MT, NCG, CPC>(tid + kThreads * k);
-#pragma unroll
-      for (int v = 0; v < CPC; ++v)
-        wreg[k][v] = (woff[k] >= 0 && cc + v < a.Co) ? wsrc[woff[k] + v * cstride] : 0.0f;
-    }
-  };
-  auto store_stage = [&]() {
-#pragma unroll
-    for (int cg = 0; cg < NCG; ++cg)
-#pragma unroll
-      for (int k = 0; k < HS; ++k) {
-        const int f = tid + kThreads * k;
-        if (f < SLAB) {
-          if constexpr (F16) {
-            float x[8];
-#pragma unroll
-            for (int v = 0; v < 8; ++v) x[v] = hreg[cg * 8 + v][k];
-            sH[cg * SLAB + f] = pack8(x);
-          } else {
-            sH[cg * SLAB + f] = hreg[cg][k];
-          }
-        }
-      }
-#pragma unroll
-    for (int k = 0; k < WS; ++k) {
-      const int e = tid + kThreads * k;
-      if (e < AE) {
-        if constexpr (F16)
-          sA[weight_cell_lds<MT, NCG, PITCH>(e)] = pack8(wreg[k]);
-        else
-          sA[weight_cell_lds<MT, NCG, PITCH>(e)] = wreg[k][0];
-      }
-    }
-  };
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
-
-  // taps of stage st: k-step ks of tap tt uses cell group 2*ks + h
-  auto compute_stage = [&](auto nb_tag, int st) {
-    constexpr int NB = decltype(nb_tag)::value;
-    int co0, g;
-    stage_split(c, CK, st, &co0, &g);
-    const int tap0 = g * TAPS;
-    const int ntg = imin(TAPS, c.ntaps - tap0);
-    int j = tap0 / P.tw;
-    int l = tap0 - j * P.tw;
-    for (int tt = 0; tt < ntg; ++tt) {
-      const int boff = tap_window_offset(c, j, l);
-      const int bi0[2] = {bbase[0] + boff, bbase[1] + boff};
-#pragma unroll
-      for (int ks = 0; ks < KSTEPS; ++ks) {
-        const int ai = abase + (tt * NCG + 2 * ks) * PITCH;
-        const int bi[2] = {bi0[0] + 2 * ks * SLAB, bi0[1] + 2 * ks * SLAB};
-        mma_step<F16, NB>(sA, sH, ai, bi, acc);
-      }
-      if (++l == P.tw) {
-        l = 0;
-        ++j;
-      }
-    }
-  };
-
-  if (c.nstages > 0) load_stage(0);
-  for (int st = 0; st < c.nstages; ++st) {
-    __syncthreads();
-    store_stage();
-    __syncthreads();
-    if (st + 1 < c.nstages) load_stage(st + 1);
-    if (nact == 2)
-      compute_stage(std::integral_constant<int, 2>(), st);
-    else if (nact == 1)
-      compute_stage(std::integral_constant<int, 1>(), st);
-  }
-
-  float* gi_n = a.gi + (size_t)c.n * a.Ci * (a.H * a.W);
-  const size_t HW = (size_t)a.H * a.W;
-#pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int po = output_offset(c, a, first + nb * 32 + l32);
-    if (po < 0) continue;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int ci = c.ci0 + mb * 32 + acc_row(r, h);
-        if (ci < a.Ci) gi_n[ci * HW + po] = acc[mb][nb][r];
-      }
-  }
-}
 
 // Word 3 of a raw (untyped, unswizzled) buffer resource: 32-bit data format.
 constexpr int kRawBufferFlags = 0x00020000;
@@ -269,22 +64,18 @@ __device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float
 // loads that write LDS directly) have completed.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// ---------------------------------------------------------------------------
-// fp32 family: 8 waves, v_mfma_f32_16x16x4_f32 (layouts: see F32Geom).
-// Stage s+1 (window and weights) is copied into the second LDS buffers while
-// stage s is multiplied; one barrier per stage.  Per tap, a wave reads one
-// 16-byte window cell per 16-pixel block and 4 weights, then issues
-// 4 x NBW matrix instructions.
-template <int WM, int WN, int NBW>
-__global__ __launch_bounds__(64 * WM * WN) void grad_input_f32_kernel(const LaunchArgs a) {
-  using G = F32Geom<WM, WN, NBW>;
-  constexpr int MT = G::kMT, HS = G::kHS, WS = G::kWS, NT = G::kThreads;
-  constexpr int TGM = kF32StageTaps, CH = kF32StageCh;
-  // fixed LDS regions (floats): two window buffers, then two weight buffers
-  constexpr int kWin0 = 0, kWin1 = kF32WinFloats, kWt0 = 2 * kF32WinFloats,
-                kWt1 = 2 * kF32WinFloats + kF32WtFloats;
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ f32x4 lds4[kF32LdsFloats / 4];
+// Four fp32 values rounded to f16 (round to nearest even).
+__device__ __forceinline__ f16x4 to_f16(f32x4 x) { return __builtin_convertvector(x, f16x4); }
+
+__device__ __forceinline__ f16x8 join(f16x4 lo, f16x4 hi) {
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+template <bool F16, int WM, int WN, int MB, int NBW>
+__global__ __launch_bounds__(64 * WM * WN) void grad_input_mm_kernel(const LaunchArgs a) {
+  using G = MMGeom<WM, WN, MB, NBW>;
+  constexpr int MT = G::kMT, NT = G::kThreads, NC = G::kCopies;
+  __shared__ f32x4 lds4[2 * kStageFloats / 4];
   float* lds = reinterpret_cast<float*>(lds4);
 
   const int tid = threadIdx.x;
@@ -292,151 +83,229 @@ __global__ __launch_bounds__(64 * WM * WN) void grad_input_f32_kernel(const Laun
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mg = wave % WM, ng = wave / WM;
   const int g = lane >> 4, c16 = lane & 15;
-  const TileCtx c = decode_tile<MT>(a, blockIdx.x, 0);
+  const TileCtx c = decode_tile<MT>(a, blockIdx.x);
   const PhaseDesc& P = c.P;
   const int OHOW = a.OH * a.OW;
   const int cstride = a.Ci * a.KH * a.KW;
   const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
-  const int SLOTS = P.slabr, CP = P.cp, TG = P.tg;
+  const int nst = c.nstages;
 
-  // copy cells: thread tid holds cells tid + NT*k of the window and of the
-  // weights; every wave-instruction writes 64 consecutive floats inside its
-  // fixed buffer, cells past the stage's data read 0
-  unsigned gbyte[HS];
+  // copy offsets: instruction i of this wave fills stage-buffer floats
+  // f0 = i*NT + 64*wave + [0, 64); window cells are the same for every stage,
+  // weight cells change with the tap group
+  unsigned off[NC];
 #pragma unroll
-  for (int k = 0; k < HS; ++k) {
-    const int f = tid + NT * k;
-    const int o = f < kF32WinFloats ? f32_window_cell(c, a, f) : -1;
-    gbyte[k] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
+  for (int i = 0; i < NC; ++i) {
+    const int f0 = i * NT + wave * 64;
+    const int o = f0 < P.wfl ? mm_window_cell(c, a, f0 + lane) : -1;
+    off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
   }
-  unsigned wbyte[WS];
   int wgroup = -1;
   struct StageCopy {
     __amdgpu_buffer_rsrc_t rg, rw;
-    int buf;
+    int base;
   };
-  auto begin_stage_copy = [&](int st, int buf) {
+  // (Every lambda here is forced inline: an outlined one becomes a real call
+  // with its own stack frame.)
+  auto begin_stage_copy = [&](int st, int buf) __attribute__((always_inline)) {
     int co0, grp;
-    stage_split(c, CH, st, &co0, &grp);
-    if (grp != wgroup) {
-#pragma unroll
-      for (int k = 0; k < WS; ++k) {
-        const int e = tid + NT * k;
-        const int o = e < kF32WtFloats ? f32_weight_cell<MT>(c, a, e, grp) : -1;
-        wbyte[k] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
-      }
-      wgroup = grp;
-    }
-    const int nco = imin(CH, a.Co - co0);
+    stage_split(c, st, &co0, &grp);
+    const int nco = imin(16 * P.cg, a.Co - co0);
     StageCopy sc;
     sc.rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(go_n + (size_t)co0 * OHOW), 0,
                                               nco * OHOW * 4, kRawBufferFlags);
     sc.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.w + (size_t)co0 * cstride), 0,
                                               nco * cstride * 4, kRawBufferFlags);
-    sc.buf = buf;
+    sc.base = buf * kStageFloats;
     return sc;
   };
-  // copy instructions [lo, hi) of a stage (window ones first); lo and hi are
-  // compile-time constants here, so the range test folds away
-  auto copy_chunk = [&](const StageCopy& sc, int lo, int hi) {
+  // Weight copy offsets for the tap group of stage st, recomputed between
+  // stages (no operand registers live) and only when the group changes.
+  // The empty asm makes the cell index opaque, so the compiler cannot hoist
+  // the group-independent part of every cell out of the stage loop (that
+  // would hold two more registers per copy instruction).
+  auto update_weight_offsets = [&](int st) __attribute__((always_inline)) {
+    if (st >= nst) return;
+    int co0, grp;
+    stage_split(c, st, &co0, &grp);
+    if (grp == wgroup) return;
 #pragma unroll
-    for (int i = 0; i < HS + WS; ++i) {
-      if (i < lo || i >= hi) continue;
-      if (i < HS) {
-        const int f0 = wave * 64 + NT * i;
-        if (HS * NT == kF32WinFloats || f0 < kF32WinFloats)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              sc.rg, lds_ptr(lds + (sc.buf ? kWin1 : kWin0) + f0), 4, gbyte[i], 0, 0, 0);
-      } else {
-        const int k = i - HS;
-        const int e0 = wave * 64 + NT * k;
-        if (WS * NT == kF32WtFloats || e0 < kF32WtFloats)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              sc.rw, lds_ptr(lds + (sc.buf ? kWt1 : kWt0) + e0), 4, wbyte[k], 0, 0, 0);
+    for (int i = 0; i < NC; ++i) {
+      const int f0 = i * NT + wave * 64;
+      if (f0 >= P.wfl) {
+        int e = f0 + lane - P.wfl;
+        asm volatile("" : "+v"(e));
+        const int o = mm_weight_cell<MT>(c, a, e, grp);
+        off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
       }
     }
+    wgroup = grp;
   };
-  constexpr int kCopies = HS + WS;
+  // Every instruction of the stage buffer is issued (cells past `used` read
+  // 0); the buffer resource is picked per instruction, uniformly per wave.
+  auto copy_stage = [&](const StageCopy& sc) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int f0 = i * NT + wave * 64;   // wave-uniform
+      if (i * NT + 64 * (NT / 64 - 1) >= kStageFloats && f0 >= kStageFloats) continue;
+      const __amdgpu_buffer_rsrc_t rs = f0 < P.wfl ? sc.rg : sc.rw;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(lds + sc.base + f0), 4, off[i], 0,
+                                               0, 0);
+    }
+  };
 
-  const int nst = c.nstages;
-  if (nst > 0) {
-    const StageCopy sc0 = begin_stage_copy(0, 0);
-    copy_chunk(sc0, 0, kCopies);
-  }
+  update_weight_offsets(0);
+  if (nst > 0) copy_stage(begin_stage_copy(0, 0));
 
-  // byte offsets within a window buffer of each block's cell for the class's
-  // first tap, and within a weight buffer of this lane's weights
+  // byte offsets within a stage buffer: block b's window cell (quad g,
+  // first tap of the class), and block m's weights (quad g, t = 0) within
+  // the weight region
   int bb[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b)
-    bb[b] = (g * SLOTS + window_base(c, f32_local(b, ng, c16, WN))) * 16;
-  // byte offsets of this lane's weights of channel 4g + q, tap 0
-  int aq[4];
+    bb[b] = (g * P.slots + window_base(c, mm_local(b, ng, c16, WN))) * 16;
+  int aq[MB];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) aq[q] = ((4 * g + q) * CP + (mg * 16 + c16) * TG) * 4;
+  for (int m = 0; m < MB; ++m) aq[m] = (g * P.qp + mm_channel(m, mg, c16, MB) * 4 * P.pt) * 4;
 
-  f32x4 acc[NBW];
+  f32x4 acc[MB][NBW];
 #pragma unroll
-  for (int b = 0; b < NBW; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int m = 0; m < MB; ++m)
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) acc[m][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  // multiply stage st out of buffer st&1; the copies of stage st+1 (if any)
-  // go out into the other buffer during the first tap.  Tap tt reads the
-  // window at a fixed slot offset and weight t = tt of channel 4g + q.
-  auto tap_mma = [&](const char* Hb, const char* Ab, int boff) {
-    // all addresses, then all reads, then (in the caller) the products: the
-    // scheduling barriers keep the compiler from recycling a read's target
-    // register as the next address, which would serialise the reads
+  // All addresses, then all reads of one unit: the scheduling barriers keep
+  // the compiler from recycling a read's target register as the next
+  // address, which would serialise the reads.
+  auto read_unit = [&](const char* Hb, const char* Ab, int wo, int ao, f32x4(&bv)[NBW],
+                       f32x4(&aw)[MB]) __attribute__((always_inline)) {
     const f32x4* ba[NBW];
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) ba[b] = reinterpret_cast<const f32x4*>(Hb + bb[b] + boff);
-    const float* aa[4];
+    for (int b = 0; b < NBW; ++b) ba[b] = reinterpret_cast<const f32x4*>(Hb + bb[b] + wo);
+    const f32x4* aa[MB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) aa[q] = reinterpret_cast<const float*>(Ab + aq[q]);
+    for (int m = 0; m < MB; ++m) aa[m] = reinterpret_cast<const f32x4*>(Ab + aq[m] + ao);
     __builtin_amdgcn_sched_barrier(0);
-    float aw[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) aw[q] = *aa[q];
-    f32x4 bv[NBW];
+    for (int m = 0; m < MB; ++m) aw[m] = *aa[m];
 #pragma unroll
     for (int b = 0; b < NBW; ++b) bv[b] = *ba[b];
     __builtin_amdgcn_sched_barrier(0);
-    return [&, bv, aw]() mutable {
+  };
+  auto mma_f32 = [&](const f32x4(&bv)[NBW], const f32x4(&aw)[MB]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int b = 0; b < NBW; ++b)
-          acc[b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[q], bv[b][q], acc[b], 0, 0, 0);
-    };
+          acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[b][q], acc[m][b], 0, 0, 0);
   };
-  auto compute = [&](int st) {
+  auto mma_f16_pair = [&](const f32x4(&bv0)[NBW], const f32x4(&aw0)[MB],
+                          const f32x4(&bv1)[NBW],
+                          const f32x4(&aw1)[MB]) __attribute__((always_inline)) {
+    f16x8 ah[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) ah[m] = join(to_f16(aw0[m]), to_f16(aw1[m]));
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const f16x8 bh = join(to_f16(bv0[b]), to_f16(bv1[b]));
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[m], bh, acc[m][b], 0, 0, 0);
+    }
+  };
+  auto mma_f16_single = [&](const f32x4(&bv)[NBW],
+                            const f32x4(&aw)[MB]) __attribute__((always_inline)) {
+    f16x4 ah[MB];
+#pragma unroll
+    for (int m = 0; m < MB; ++m) ah[m] = to_f16(aw[m]);
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const f16x4 bh = to_f16(bv[b]);
+#pragma unroll
+      for (int m = 0; m < MB; ++m)
+        acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x16f16(ah[m], bh, acc[m][b], 0, 0, 0);
+    }
+  };
+
+  // Multiply stage st out of buffer st&1; the copies of stage st+1 (if any)
+  // go out into the other buffer during the first unit.  Units run channel
+  // group by channel group, taps in class order inside a group.
+  auto compute = [&](int st) __attribute__((always_inline)) {
     const int buf = st & 1;
     int co0, grp;
-    stage_split(c, CH, st, &co0, &grp);
-    const int tap0 = grp * TG;
-    const int ntg = imin(TG, c.ntaps - tap0);
-    const char* Hb = reinterpret_cast<const char*>(lds + (buf ? kWin1 : kWin0));
-    const char* Ab = reinterpret_cast<const char*>(lds + (buf ? kWt1 : kWt0));
-    int j = tap0 / P.tw, l = tap0 - (tap0 / P.tw) * P.tw;
-    // first tap, with the copies of the next stage
-    {
-      auto mma = tap_mma(Hb, Ab, tap_window_offset(c, j, l) * 16);
-      if (st + 1 < nst) {
-        const StageCopy sc = begin_stage_copy(st + 1, buf ^ 1);
-        copy_chunk(sc, 0, kCopies);
-      }
-      mma();
-      if (++l == P.tw) {
+    stage_split(c, st, &co0, &grp);
+    const int tap0 = grp * P.tg;
+    const int ntg = imin(P.tg, c.ntaps - tap0);
+    const int units = P.cg * ntg;
+    const char* Hb = reinterpret_cast<const char*>(lds + buf * kStageFloats);
+    const char* Ab = Hb + P.wfl * 4;
+    const int j0 = tap0 / P.tw, l0 = tap0 - j0 * P.tw;
+    int cgi = 0, t = 0, j = j0, l = l0;
+    auto wo = [&]() __attribute__((always_inline)) {
+      return cgi * P.slots * 64 + tap_window_offset(c, j, l) * 16;
+    };
+    auto ao = [&]() __attribute__((always_inline)) { return cgi * P.qp * 16 + t * 16; };
+    auto advance = [&]() __attribute__((always_inline)) {
+      if (++t == ntg) {
+        t = 0;
+        ++cgi;
+        j = j0;
+        l = l0;
+      } else if (++l == P.tw) {
         l = 0;
         ++j;
       }
-    }
-    for (int tt = 1; tt < ntg; ++tt) {
-      Ab += 4;   // weight t = tt
-      auto mma = tap_mma(Hb, Ab, tap_window_offset(c, j, l) * 16);
-      mma();
-      if (++l == P.tw) {
-        l = 0;
-        ++j;
+    };
+    auto issue_next = [&]() __attribute__((always_inline)) {
+      if (st + 1 < nst) copy_stage(begin_stage_copy(st + 1, buf ^ 1));
+    };
+    if constexpr (!F16) {
+      {
+        f32x4 bv[NBW], aw[MB];
+        read_unit(Hb, Ab, wo(), ao(), bv, aw);
+        issue_next();
+        mma_f32(bv, aw);
+        advance();
+      }
+      for (int u = 1; u < units; ++u) {
+        f32x4 bv[NBW], aw[MB];
+        read_unit(Hb, Ab, wo(), ao(), bv, aw);
+        mma_f32(bv, aw);
+        advance();
+      }
+    } else {
+      int u = 0;
+      if (units >= 2) {
+        f32x4 bv0[NBW], aw0[MB], bv1[NBW], aw1[MB];
+        read_unit(Hb, Ab, wo(), ao(), bv0, aw0);
+        advance();
+        read_unit(Hb, Ab, wo(), ao(), bv1, aw1);
+        advance();
+        issue_next();
+        mma_f16_pair(bv0, aw0, bv1, aw1);
+        u = 2;
+      } else {
+        f32x4 bv[NBW], aw[MB];
+        read_unit(Hb, Ab, wo(), ao(), bv, aw);
+        issue_next();
+        mma_f16_single(bv, aw);
+        advance();
+        u = 1;
+      }
+      for (; u + 2 <= units; u += 2) {
+        f32x4 bv0[NBW], aw0[MB], bv1[NBW], aw1[MB];
+        read_unit(Hb, Ab, wo(), ao(), bv0, aw0);
+        advance();
+        read_unit(Hb, Ab, wo(), ao(), bv1, aw1);
+        advance();
+        mma_f16_pair(bv0, aw0, bv1, aw1);
+      }
+      if (u < units) {
+        f32x4 bv[NBW], aw[MB];
+        read_unit(Hb, Ab, wo(), ao(), bv, aw);
+        mma_f16_single(bv, aw);
       }
     }
   };
@@ -444,84 +313,107 @@ __global__ __launch_bounds__(64 * WM * WN) void grad_input_f32_kernel(const Laun
   wait_vmem();
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
+    update_weight_offsets(st + 1);
     compute(st);
     wait_vmem();          // this wave's copies of stage st+1 have landed
     __syncthreads();      // ... everyone's, and buffer st&1 may be refilled
   }
 
-  // epilogue: register r of block b holds channel mg*16 + 4g + r, pixel
-  // (b*WN + ng)*16 + c16
+  // epilogue: register r of block (m, b) holds input channel
+  // (mg*MB + m)*16 + 4g + r, pixel (b*WN + ng)*16 + c16
   float* gi_n = a.gi + (size_t)c.n * a.Ci * (a.H * a.W);
   const size_t HW = (size_t)a.H * a.W;
 #pragma unroll
   for (int b = 0; b < NBW; ++b) {
-    const int po = output_offset(c, a, f32_local(b, ng, c16, WN));
+    const int po = output_offset(c, a, mm_local(b, ng, c16, WN));
     if (po < 0) continue;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int cc = c.ci0 + mg * 16 + 4 * g + r;
-      if (cc < a.Ci) gi_n[cc * HW + po] = acc[b][r];
-    }
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int cc = c.ci0 + (mg * MB + m) * 16 + 4 * g + r;
+        if (cc < a.Ci) gi_n[cc * HW + po] = acc[m][b][r];
+      }
   }
 }
 
 template <int V>
-void launch_f32_variant(const LaunchArgs& la, hipStream_t st) {
-  constexpr F32Variant v = kF32Variants[V];
-  hipLaunchKernelGGL((grad_input_f32_kernel<v.wm, v.wn, v.nbw>), dim3(la.total_tiles),
-                     dim3(64 * v.wm * v.wn), 0, st, la);
+void launch_variant(const LaunchArgs& la, hipStream_t st) {
+  constexpr Variant v = kVariants[V];
+  hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw>),
+                     dim3(la.total_tiles), dim3(64 * v.wm * v.wn), 0, st, la);
 }
 
 template <int... Vs>
-void launch_f32_dispatch(const LaunchArgs& la, hipStream_t st,
-                         std::integer_sequence<int, Vs...>) {
-  ((la.variant == Vs ? launch_f32_variant<Vs>(la, st) : void()), ...);
+void launch_dispatch(const LaunchArgs& la, hipStream_t st, std::integer_sequence<int, Vs...>) {
+  ((la.variant == Vs ? launch_variant<Vs>(la, st) : void()), ...);
 }
 
+// Compute units of the current device, read once per device.
 int device_cus() {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return kF32DefaultCUs;
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cus_of[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return kDefaultCUs;
+  if (dev >= 0 && dev < kMaxDevices) {
+    const int known = cus_of[dev].load(std::memory_order_relaxed);
+    if (known > 0) return known;
+  }
+  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       cus < 1)
-    return kF32DefaultCUs;
+    return kDefaultCUs;
+  if (dev >= 0 && dev < kMaxDevices) cus_of[dev].store(cus, std::memory_order_relaxed);
   return cus;
 }
 
-int launch_f32(const float* go, const float* w, float* gi, const conv2d_params* p,
-               void* stream) {
-  int rc = validate_shape(p);
-  if (rc != CONV2D_OK) return rc;
-  rc = check_pointers(go, w, gi, p);
-  if (rc != CONV2D_OK) return rc;
+// Launch plans of recent shapes (host memory only), so that a repeated call
+// skips the planner's search.  Keyed by the shape, the path, the forced
+// variant and the CU count; at most kPlanCacheSize entries, oldest evicted.
+struct PlanKey {
+  conv2d_params p;
+  int f16, variant, cus;
+};
+struct PlanEntry {
+  PlanKey key;
   std::vector<LaunchArgs> launches;
-  rc = build_plan_f32(p, device_cus(), &launches, nullptr);
-  if (rc != CONV2D_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  for (LaunchArgs& la : launches) {
-    la.go = go;
-    la.w = w;
-    la.gi = gi;
-    if (la.total_tiles == 0) continue;
-    launch_f32_dispatch(la, st, std::make_integer_sequence<int, kNumF32Variants>());
+};
+constexpr size_t kPlanCacheSize = 64;
+
+int cached_plan(const conv2d_params* p, int f16, int variant, int cus,
+                std::vector<LaunchArgs>* out) {
+  static std::mutex mu;
+  static std::vector<PlanEntry> cache;
+  PlanKey key;
+  std::memset(&key, 0, sizeof(key));
+  key.p = *p;
+  key.f16 = f16;
+  key.variant = variant;
+  key.cus = cus;
+  {
+    std::lock_guard<std::mutex> lock(mu);
+    for (const PlanEntry& e : cache)
+      if (std::memcmp(&e.key, &key, sizeof(key)) == 0) {
+        *out = e.launches;
+        return CONV2D_OK;
+      }
   }
-  if (hipGetLastError() != hipSuccess) return CONV2D_ERR_HIP;
+  const int rc = build_plan(p, f16, cus, out, nullptr, variant);
+  if (rc != CONV2D_OK) return rc;
+  std::lock_guard<std::mutex> lock(mu);
+  if (cache.size() >= kPlanCacheSize) cache.erase(cache.begin());
+  cache.push_back(PlanEntry{key, *out});
   return CONV2D_OK;
 }
 
-template <bool F16>
-constexpr TileShape tile_of() {
-  return F16 ? kF16Tile : kF32Tile;
-}
-
-template <bool F16>
-int launch(const float* go, const float* w, float* gi, const conv2d_params* p, void* stream) {
-  constexpr TileShape ts = tile_of<F16>();
+int launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
+           int variant, void* stream) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
   rc = check_pointers(go, w, gi, p);
   if (rc != CONV2D_OK) return rc;
   std::vector<LaunchArgs> launches;
-  rc = build_plan(p, ts, &launches, nullptr);
+  rc = cached_plan(p, f16, variant, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
   hipStream_t st = static_cast<hipStream_t>(stream);
   for (LaunchArgs& la : launches) {
@@ -529,8 +421,7 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, v
     la.w = w;
     la.gi = gi;
     if (la.total_tiles == 0) continue;
-    hipLaunchKernelGGL((grad_input_kernel<F16, ts.mt, ts.nt, ts.ck, ts.taps, ts.slab>),
-                       dim3(la.total_tiles), dim3(kThreads), 0, st, la);
+    launch_dispatch(la, st, std::make_integer_sequence<int, kNumVariants>());
   }
   if (hipGetLastError() != hipSuccess) return CONV2D_ERR_HIP;
   return CONV2D_OK;
@@ -540,10 +431,19 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, v
 
 extern "C" int conv2d_grad_input(const float* grad_out, const float* weight, float* grad_input,
                                  const conv2d_params* p, void* stream) {
-  return c2b::launch_f32(grad_out, weight, grad_input, p, stream);
+  return c2b::launch(grad_out, weight, grad_input, p, 0, -1, stream);
 }
 
 extern "C" int conv2d_grad_input_f16(const float* grad_out, const float* weight,
                                      float* grad_input, const conv2d_params* p, void* stream) {
-  return c2b::launch<true>(grad_out, weight, grad_input, p, stream);
+  return c2b::launch(grad_out, weight, grad_input, p, 1, -1, stream);
+}
+
+extern "C" int conv2d_grad_input_variant(const float* grad_out, const float* weight,
+                                         float* grad_input, const conv2d_params* p, int variant,
+                                         void* stream) {
+  if (p == nullptr) return CONV2D_ERR_NULL_PTR;
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::launch(grad_out, weight, grad_input, p, c2b::kVariants[variant].f16, variant,
+                     stream);
 }

@@ -25,32 +25,6 @@ int64_t first_of_class(int64_t r, int64_t pad, int64_t s) {
   return (((r - pad) % s) + s) % s;
 }
 
-// Choose band width and pixels per tile for a class whose halo window must
-// fit `slab` elements per output channel.  Rows spanned by `ntv` consecutive
-// pixels of a band `wb` wide are at most floor((wb + ntv - 2) / wb) + 1; the
-// window adds th - 1 rows above and tw - 1 columns to the left.
-bool choose_band(int64_t wp, int64_t th, int64_t tw, const TileShape& ts,
-                 int64_t* wb_out, int64_t* ntv_out) {
-  for (int64_t ntv = ts.nt; ntv >= 1; ntv /= 2) {
-    // fewest bands first; ceil(wp / nb) keeps bands nearly equal
-    int64_t last_wb = -1;
-    for (int64_t nb = 1; nb <= wp; ++nb) {
-      int64_t wb = ceil_div(wp, nb);
-      if (wb == last_wb) continue;
-      last_wb = wb;
-      int64_t rows = (wb + ntv - 2) / wb + th;
-      int64_t roww = wb + tw - 1;
-      if (rows * roww <= ts.slab) {
-        *wb_out = wb;
-        *ntv_out = ntv;
-        return true;
-      }
-      if (wb == 1) break;
-    }
-  }
-  return false;
-}
-
 }  // namespace
 
 int validate_shape(const conv2d_params* p) {
@@ -148,26 +122,28 @@ static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks) {
   return la;
 }
 
+
 // Reciprocals of a class's per-lane divisors, and the bounds under which the
-// kernels' fast_div is exact (numerator x divisor < 2^31): numerators are
-// window cells (< 16 * slots or the tile window), taps, and positions inside
-// a band row plus one tile of pixels.
+// kernel's fast_div is exact (numerator x divisor < 2^31): numerators are
+// stage-buffer cells (< kStageFloats), window slots (< slots), taps, and
+// positions inside a band row plus one tile of pixels.
 static int finalize_divisors(PhaseDesc* d) {
-  const int64_t roww = int64_t(d->wb) + d->tw - 1;
   const int64_t lim = int64_t(1) << 31;
+  const int64_t roww = std::max<int64_t>(int64_t(d->wb) + d->tw - 1, 1);
   const int64_t wb = d->wb, tw = std::max(d->tw, 1);
-  const int64_t slots4 = std::max<int64_t>(4 * int64_t(d->slabr), 1);
-  const int64_t cp = std::max(d->cp, 1), tg = std::max(d->tg, 1);
-  const int64_t win = std::max<int64_t>(int64_t(kF32StageCh) * d->slabr, 4096);
-  if (roww >= 1 && win * roww >= lim) return CONV2D_ERR_OVERFLOW;
+  const int64_t slots4 = std::max<int64_t>(4 * int64_t(d->slots), 1);
+  const int64_t qp = std::max(d->qp, 1), pt4 = std::max<int64_t>(4 * int64_t(d->pt), 1);
+  if (int64_t(kStageFloats) * std::max<int64_t>(slots4, qp) >= lim) return CONV2D_ERR_OVERFLOW;
+  if (int64_t(std::max(d->slots, 4096)) * roww >= lim) return CONV2D_ERR_OVERFLOW;
+  if (qp * pt4 >= lim) return CONV2D_ERR_OVERFLOW;
   if ((wb + d->ntv + 1024) * wb >= lim) return CONV2D_ERR_OVERFLOW;
   if (int64_t(d->th) * d->tw * tw >= lim) return CONV2D_ERR_OVERFLOW;
-  d->m_roww = fast_div_magic(uint32_t(std::max<int64_t>(roww, 1)));
+  d->m_roww = fast_div_magic(uint32_t(roww));
   d->m_wb = fast_div_magic(uint32_t(wb));
   d->m_tw = fast_div_magic(uint32_t(tw));
   d->m_slots4 = fast_div_magic(uint32_t(slots4));
-  d->m_cp = fast_div_magic(uint32_t(cp));
-  d->m_tg = fast_div_magic(uint32_t(tg));
+  d->m_qp = fast_div_magic(uint32_t(qp));
+  d->m_pt4 = fast_div_magic(uint32_t(pt4));
   return CONV2D_OK;
 }
 
@@ -200,104 +176,38 @@ static int emit_launches(const conv2d_params* p, int64_t ciblocks, int variant,
   return CONV2D_OK;
 }
 
-int build_plan(const conv2d_params* p, const TileShape& ts,
-               std::vector<LaunchArgs>* launches, conv2d_plan_info* info) {
-  int rc = validate_shape(p);
-  if (rc != CONV2D_OK) return rc;
-  if (info) std::memset(info, 0, sizeof(*info));
-
-  const int64_t N = p->batch, Ci = p->in_channels, H = p->in_h, W = p->in_w;
-  const int64_t Co = p->out_channels;
-  if (info) info->useful_macs = N * Co * p->out_h * p->out_w * Ci * p->kernel_h * p->kernel_w;
-  if (N == 0 || Ci == 0 || H == 0 || W == 0) return CONV2D_OK;  // nothing to write
-
-  const int64_t ciblocks = ceil_div(Ci, ts.mt);
-  std::vector<PhaseDesc> phases;
-  make_classes(p, &phases);
-  for (PhaseDesc& d : phases) {
-    const int64_t th = d.th, tw = d.tw, hp = d.hp, wp = d.wp;
-    int64_t wb = wp, ntv = ts.nt;
-    if (th > 0) {
-      if (!choose_band(wp, th, tw, ts, &wb, &ntv)) return CONV2D_ERR_UNSUPPORTED;
-      d.ngroups = int32_t(ceil_div(th * tw, ts.taps));
-    }
-    d.wb = int32_t(wb);
-    d.nbands = int32_t(ceil_div(wp, wb));
-    d.ntv = int32_t(ntv);
-    const int64_t ptiles = ceil_div(hp * wb, ntv);
-    const int64_t tiles = N * d.nbands * ptiles * ciblocks;
-    if (ptiles >= kI31 || tiles >= kI31) return CONV2D_ERR_OVERFLOW;
-    d.ptiles = int32_t(ptiles);
-    d.tiles = int32_t(tiles);
-    if (info) {
-      info->phases += 1;
-      if (d.th == 0) info->zero_phases += 1;
-      // issued MACs: whole channel tiles, 32-pixel blocks, whole stages
-      const int64_t band_px = hp * wb;
-      const int64_t full = band_px / ntv, rem = band_px % ntv;
-      const int64_t lanes = full * ceil_div(ntv, 32) * 32 + ceil_div(rem, 32) * 32;
-      const int64_t kk = ceil_div(Co, ts.ck) * ts.ck * th * tw;
-      info->macs += N * d.nbands * lanes * ciblocks * ts.mt * kk;
-    }
-  }
-  // heaviest classes first: they start first and the light ones fill the tail
-  std::stable_sort(phases.begin(), phases.end(), [](const PhaseDesc& a, const PhaseDesc& b) {
-    return int64_t(a.th) * a.tw > int64_t(b.th) * b.tw;
-  });
-  return emit_launches(p, ciblocks, 0, phases, launches, info);
-}
-
-// ---------------------------------------------------------------------------
-// fp32 kernel family planning.
-
 namespace {
 
 // Most grad_out rows a run of `ntv` consecutive pixels touches in a band
-// `wb` wide, over all tiles p0 = k*ntv of a band of `bp` pixels.
+// `wb` wide, over all tiles p0 = k*ntv of a band of `bp` pixels.  The row
+// phase p0 mod wb repeats with period wb / gcd(ntv, wb), so one period of
+// full-length tiles covers every case (a shorter last tile spans no more
+// rows than a full one at the same phase).
 int64_t max_rows_spanned(int64_t wb, int64_t ntv, int64_t bp) {
   if (ntv % wb == 0) return ntv / wb;               // tiles start on row starts
   const int64_t tiles = ceil_div(bp, ntv);
+  int64_t a = ntv, b = wb;
+  while (b) {
+    const int64_t t = a % b;
+    a = b;
+    b = t;
+  }
+  const int64_t period = wb / a;
   int64_t best = 0;
-  if (tiles <= 4096) {
-    for (int64_t t = 0; t < tiles; ++t) {
-      const int64_t p0 = t * ntv, p1 = std::min(p0 + ntv, bp) - 1;
-      best = std::max(best, p1 / wb - p0 / wb + 1);
-    }
-    return best;
+  for (int64_t t = 0; t < std::min(tiles, period); ++t) {
+    const int64_t p0 = t * ntv, p1 = p0 + ntv - 1;
+    best = std::max(best, p1 / wb - p0 / wb + 1);
   }
-  return (wb + ntv - 2) / wb + 1;                    // worst case over starts
+  return best;
 }
 
-struct F32Choice {
-  std::vector<PhaseDesc> phases;
-  double cost = 0.0;
-};
-
-// LDS floats per output channel of staged weights for mt channels x tg
-// taps: at least mt*tg, = 4 mod 16.
-int64_t weight_pitch(int64_t mt, int64_t tg) {
-  int64_t x = mt * tg;
-  return x + ((4 - x % 16) + 16) % 16;
-}
-
-// Tile one class for a variant; false if no band/tile size fits LDS.
-bool tile_class_f32(PhaseDesc* d, int64_t ntl, int64_t mt) {
-  const int64_t th = d->th, tw = d->tw, hp = d->hp, wp = d->wp;
-  if (th == 0) {                                      // zero class: stores only
-    d->wb = d->wp;
-    d->nbands = 1;
-    d->ntv = int32_t(std::min<int64_t>(ntl, hp * wp));
-    d->ptiles = int32_t(ceil_div(hp * wp, d->ntv));
-    d->ngroups = d->ckr = d->tg = d->slabr = d->cp = 0;
-    return true;
-  }
-  const int64_t ntaps = th * tw;
-  // taps per stage: as many as fit, the weights of a stage in LDS
-  int64_t tg = std::min<int64_t>(ntaps, kF32StageTaps);
-  while (tg > 1 && weight_pitch(mt, tg) > kF32MaxCP) --tg;
-  const int64_t cp = weight_pitch(mt, tg);
-  if (cp > kF32MaxCP) return false;
-  const int64_t max_slots = kF32MaxSlots;
+// Band width and pixels per tile for a class whose window must fit
+// `max_slots` slots per channel (slots rounded up to a multiple of 16).
+// Fewest bands first; for each band width, equal tiles of at most ntl
+// pixels, halving the tile until the window fits.
+bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* wb_out,
+                   int64_t* ntv_out, int64_t* slots_out) {
+  const int64_t th = d.th, tw = d.tw, hp = d.hp, wp = d.wp;
   int64_t last_wb = -1;
   for (int64_t nb = 1; nb <= wp; ++nb) {
     const int64_t wb = ceil_div(wp, nb);
@@ -305,23 +215,14 @@ bool tile_class_f32(PhaseDesc* d, int64_t ntl, int64_t mt) {
     last_wb = wb;
     const int64_t bp = hp * wb;
     const int64_t roww = wb + tw - 1;
-    // equal tiles of at most ntl pixels first, then halve the tile
     for (int64_t cap = ntl;; cap = (cap + 1) / 2) {
       const int64_t ntv = ceil_div(bp, ceil_div(bp, cap));
       const int64_t rows = max_rows_spanned(wb, ntv, bp) + th - 1;
-      // the four channel quads of a window start 16*slots floats apart; a
-      // multiple of 256 bytes keeps 16-byte reads free of bank conflicts
       const int64_t slots = ceil_div(rows * roww, 16) * 16;
       if (slots <= max_slots) {
-        d->wb = int32_t(wb);
-        d->nbands = int32_t(ceil_div(wp, wb));
-        d->ntv = int32_t(ntv);
-        d->ptiles = int32_t(ceil_div(bp, ntv));
-        d->slabr = int32_t(slots);
-        d->cp = int32_t(cp);
-        d->ckr = kF32StageCh;
-        d->tg = int32_t(tg);
-        d->ngroups = int32_t(ceil_div(ntaps, tg));
+        *wb_out = wb;
+        *ntv_out = ntv;
+        *slots_out = slots;
         return true;
       }
       if (cap <= 1 || ntv <= wb / 4) break;           // more tiles will not help
@@ -331,22 +232,98 @@ bool tile_class_f32(PhaseDesc* d, int64_t ntl, int64_t mt) {
   return false;
 }
 
-// Matrix-unit efficiency reached with `wn` waves per SIMD (measured on the
+// Matrix-unit efficiency reached with `wps` waves per SIMD (measured on the
 // tap loop: more waves hide more of the LDS latency between taps).
-double simd_efficiency(int wn) { return wn >= 4 ? 0.88 : wn == 3 ? 0.85 : wn == 2 ? 0.75 : 0.6; }
+double simd_efficiency(int wps) {
+  return wps >= 4 ? 0.88 : wps == 3 ? 0.85 : wps == 2 ? 0.75 : 0.6;
+}
 
-// Relative cost of one tile: matrix work of the waves sharing a SIMD (wn
-// waves x NBW blocks x padded k values / efficiency) plus per-stage and
-// per-tile overheads.
-double tile_cost_f32(const PhaseDesc& d, int64_t Co, const F32Variant& v) {
-  const double tile_overhead = 20000.0;               // cycles: set-up, epilogue
-  if (d.th == 0) return tile_overhead;
+constexpr double kStageCycles = 1500.0;   // barrier, copy issue and wait per stage
+constexpr double kTileCycles = 20000.0;   // set-up, first copies, epilogue
+
+// Relative cost (SIMD cycles) of one tile of class d with variant v.
+//   matrix: per unit (16 k values), each wave issues MB x NBW blocks of
+//   4 fp32 instructions of 32 cycles, or half an f16 pair instruction of
+//   16 cycles; waves of a SIMD add up;
+//   LDS: per unit each wave reads NBW window and MB weight vectors of 1 KiB,
+//   at 128 bytes per cycle per CU;
+// the larger of the two, over the padded units of all stages.
+double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v) {
+  if (d.th == 0) return kTileCycles;
   const int64_t ntaps = int64_t(d.th) * d.tw;
-  const int64_t kpad = ceil_div(Co, d.ckr) * d.ckr * ntaps;
-  const int64_t stages = ceil_div(Co, d.ckr) * d.ngroups;
-  // 16x16x4 fp32 takes 32 cycles of a SIMD's matrix unit
-  return double(v.wn) * v.nbw * (kpad / 4) * 32.0 / simd_efficiency(v.wn) + stages * 600.0 +
-         tile_overhead;
+  const int64_t nstages = int64_t(d.nchunks) * d.ngroups;
+  int64_t unit_slots = 0;   // units issued per channel chunk over all tap groups
+  for (int64_t g = 0; g < d.ngroups; ++g) {
+    const int64_t ntg = std::min<int64_t>(d.tg, ntaps - g * d.tg);
+    const int64_t u = int64_t(d.cg) * ntg;
+    unit_slots += v.f16 ? 2 * ceil_div(u, 2) : u;
+  }
+  const int64_t units = unit_slots * d.nchunks;
+  const int wps = std::max(1, v.wm * v.wn / 4);
+  const double mfma = double(wps) * v.mb * v.nbw * (v.f16 ? 8.0 : 128.0);
+  const double lds = 8.0 * v.wm * v.wn * (v.nbw + v.mb);
+  (void)Co;
+  return double(units) * std::max(mfma, lds) / simd_efficiency(wps) + nstages * kStageCycles +
+         kTileCycles;
+}
+
+// Stage shape and tiling of one class for variant v: the (taps, channel
+// groups) per stage and the band/tile sizes that fit the LDS stage buffer
+// with the lowest cost per pixel.  False if nothing fits.
+bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_t cstride) {
+  const int64_t ntl = 16 * int64_t(v.nbw) * v.wn, mt = 16 * int64_t(v.wm) * v.mb;
+  if (d->th == 0) {                                   // zero class: stores only
+    d->wb = d->wp;
+    d->nbands = 1;
+    d->ntv = int32_t(std::min<int64_t>(ntl, int64_t(d->hp) * d->wp));
+    d->ptiles = int32_t(ceil_div(int64_t(d->hp) * d->wp, d->ntv));
+    d->cg = d->tg = d->ngroups = d->nchunks = d->slots = d->pt = d->qp = d->wfl = d->used = 0;
+    return true;
+  }
+  const int64_t ntaps = int64_t(d->th) * d->tw;
+  const int64_t cg_useful = std::max<int64_t>(1, ceil_div(Co, 16));
+  bool found = false;
+  double best = 0.0;
+  PhaseDesc out = *d;
+  int64_t last_tg = -1;
+  for (int64_t ng = ceil_div(ntaps, kMaxStageTaps); ng <= ntaps; ++ng) {
+    const int64_t tg = ceil_div(ntaps, ng);         // fewest taps for this group count
+    if (tg == last_tg) continue;
+    last_tg = tg;
+    const int64_t pt = tg | 1;
+    const int64_t qp = ceil_div(mt * pt * 4, 64) * 64;
+    for (int64_t cg = 1; cg <= std::min<int64_t>(kMaxStageGroups, cg_useful); ++cg) {
+      // byte ranges of a stage's buffer resources stay below 2^31
+      if (16 * cg * OHOW * 4 >= kI31 || 16 * cg * cstride * 4 >= kI31) break;
+      const int64_t wt = 4 * cg * qp;
+      const int64_t max_slots = (kStageFloats - wt) / (16 * cg) / 16 * 16;
+      if (max_slots < 16) break;
+      PhaseDesc c = *d;
+      int64_t wb, ntv, slots;
+      if (!choose_tiling(c, ntl, max_slots, &wb, &ntv, &slots)) continue;
+      c.wb = int32_t(wb);
+      c.nbands = int32_t(ceil_div(c.wp, wb));
+      c.ntv = int32_t(ntv);
+      c.ptiles = int32_t(ceil_div(int64_t(c.hp) * wb, ntv));
+      c.cg = int32_t(cg);
+      c.tg = int32_t(tg);
+      c.ngroups = int32_t(ceil_div(ntaps, tg));
+      c.nchunks = int32_t(ceil_div(Co, 16 * cg));
+      c.slots = int32_t(slots);
+      c.pt = int32_t(pt);
+      c.qp = int32_t(qp);
+      c.wfl = int32_t(16 * cg * slots);
+      c.used = int32_t(16 * cg * slots + wt);
+      const double per_px = tile_cost(c, Co, v) / double(ntv);
+      if (!found || per_px < best * 0.999) {
+        found = true;
+        best = per_px;
+        out = c;
+      }
+    }
+  }
+  if (found) *d = out;
+  return found;
 }
 
 // Largest-first makespan of the tiles over `cus` compute units.
@@ -364,7 +341,8 @@ double lpt_makespan(const std::vector<PhaseDesc>& phases, int64_t per_class_mult
   std::vector<double> load(size_t(cus), 0.0);   // min-heap of CU loads
   std::vector<size_t> order(phases.size());
   for (size_t i = 0; i < order.size(); ++i) order[i] = i;
-  std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) { return costs[a] > costs[b]; });
+  std::stable_sort(order.begin(), order.end(),
+                   [&](size_t a, size_t b) { return costs[a] > costs[b]; });
   auto cmp = [](double a, double b) { return a > b; };
   for (size_t oi : order) {
     const int64_t t = int64_t(phases[oi].ptiles) * phases[oi].nbands * per_class_mult;
@@ -379,51 +357,56 @@ double lpt_makespan(const std::vector<PhaseDesc>& phases, int64_t per_class_mult
 
 }  // namespace
 
-int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>* launches,
-                   conv2d_plan_info* info, int force_variant) {
+int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchArgs>* launches,
+               conv2d_plan_info* info, int force_variant) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
   if (info) std::memset(info, 0, sizeof(*info));
   const int64_t N = p->batch, Ci = p->in_channels, H = p->in_h, W = p->in_w;
   const int64_t Co = p->out_channels;
-  if (info) info->useful_macs = N * Co * p->out_h * p->out_w * Ci * p->kernel_h * p->kernel_w;
+  const int64_t KHW = int64_t(p->kernel_h) * p->kernel_w;
+  if (info) info->useful_macs = N * Co * p->out_h * p->out_w * Ci * KHW;
+  if (force_variant >= kNumVariants || (force_variant >= 0 && kVariants[force_variant].f16 != (f16 ? 1 : 0)))
+    return CONV2D_ERR_UNSUPPORTED;
   if (N == 0 || Ci == 0 || H == 0 || W == 0) return CONV2D_OK;
-  if (num_cus < 1) num_cus = kF32DefaultCUs;
+  if (num_cus < 1) num_cus = kDefaultCUs;
+  const int64_t OHOW = int64_t(p->out_h) * p->out_w;
+  const int64_t cstride = Ci * KHW;
 
   std::vector<PhaseDesc> classes;
   make_classes(p, &classes);
-  const int wm = Ci > 64 ? 8 : 4;
 
   int best_v = -1;
-  F32Choice best;
-  for (int v = 0; v < kNumF32Variants; ++v) {
-    if (force_variant >= 0 ? v != force_variant : kF32Variants[v].wm != wm) continue;
-    const int64_t vmt = 16 * int64_t(kF32Variants[v].wm);
-    const int64_t ntl = 16 * int64_t(kF32Variants[v].nbw) * kF32Variants[v].wn;
-    F32Choice ch;
-    ch.phases = classes;
-    bool ok = true;
+  double best_cost = 0.0;
+  std::vector<PhaseDesc> best;
+  for (int v = 0; v < kNumVariants; ++v) {
+    const Variant& var = kVariants[v];
+    if (force_variant >= 0 ? v != force_variant : var.f16 != (f16 ? 1 : 0)) continue;
+    const int64_t vmt = 16 * int64_t(var.wm) * var.mb;
+    std::vector<PhaseDesc> phases = classes;
     std::vector<double> costs;
-    for (PhaseDesc& d : ch.phases) {
-      if (!tile_class_f32(&d, ntl, vmt)) {
+    bool ok = true;
+    for (PhaseDesc& d : phases) {
+      if (!tile_class(&d, var, Co, OHOW, cstride)) {
         ok = false;
         break;
       }
-      costs.push_back(tile_cost_f32(d, Co, kF32Variants[v]));
+      costs.push_back(tile_cost(d, Co, var));
     }
     if (!ok) continue;
-    ch.cost = lpt_makespan(ch.phases, N * ceil_div(Ci, vmt), costs, num_cus);
-    if (best_v < 0 || ch.cost < best.cost * 0.999) {
+    const double cost = lpt_makespan(phases, N * ceil_div(Ci, vmt), costs, num_cus);
+    if (best_v < 0 || cost < best_cost * 0.999) {
       best_v = v;
-      best = ch;
+      best_cost = cost;
+      best = phases;
     }
   }
   if (best_v < 0) return CONV2D_ERR_UNSUPPORTED;
 
-  const F32Variant bv = kF32Variants[best_v];
-  const int64_t bmt = 16 * int64_t(bv.wm);
+  const Variant& bv = kVariants[best_v];
+  const int64_t bmt = 16 * int64_t(bv.wm) * bv.mb;
   const int64_t bci = ceil_div(Ci, bmt);
-  for (PhaseDesc& d : best.phases) {
+  for (PhaseDesc& d : best) {
     const int64_t tiles = N * d.nbands * int64_t(d.ptiles) * bci;
     if (tiles >= kI31) return CONV2D_ERR_OVERFLOW;
     d.tiles = int32_t(tiles);
@@ -432,31 +415,36 @@ int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>*
       if (d.th == 0) info->zero_phases += 1;
       if (d.th > 0) {
         const int64_t lanes = 16 * int64_t(bv.nbw) * bv.wn;
-        const int64_t kpad = ceil_div(Co, d.ckr) * d.ckr * int64_t(d.th) * d.tw;
+        const int64_t kpad = int64_t(d.nchunks) * 16 * d.cg * int64_t(d.th) * d.tw;
         info->macs += tiles * lanes * bmt * kpad;
       }
     }
   }
-  std::stable_sort(best.phases.begin(), best.phases.end(),
-                   [&](const PhaseDesc& a, const PhaseDesc& b) {
-                     return tile_cost_f32(a, Co, bv) > tile_cost_f32(b, Co, bv);
-                   });
-  return emit_launches(p, bci, best_v, best.phases, launches, info);
+  std::stable_sort(best.begin(), best.end(), [&](const PhaseDesc& a, const PhaseDesc& b) {
+    return tile_cost(a, Co, bv) > tile_cost(b, Co, bv);
+  });
+  return emit_launches(p, bci, best_v, best, launches, info);
 }
 
 }  // namespace c2b
 
 extern "C" int conv2d_check_params(const conv2d_params* p) {
-  int rc = c2b::build_plan_f32(p, c2b::kF32DefaultCUs, nullptr, nullptr);
+  int rc = c2b::build_plan(p, 0, c2b::kDefaultCUs, nullptr, nullptr);
   if (rc != CONV2D_OK) return rc;
-  return c2b::build_plan(p, c2b::kF16Tile, nullptr, nullptr);
+  return c2b::build_plan(p, 1, c2b::kDefaultCUs, nullptr, nullptr);
 }
 
 extern "C" int conv2d_describe_plan(const conv2d_params* p, int f16,
                                     conv2d_plan_info* out) {
   if (out == nullptr) return CONV2D_ERR_NULL_PTR;
-  if (f16) return c2b::build_plan(p, c2b::kF16Tile, nullptr, out);
-  return c2b::build_plan_f32(p, c2b::kF32DefaultCUs, nullptr, out);
+  return c2b::build_plan(p, f16 ? 1 : 0, c2b::kDefaultCUs, nullptr, out);
+}
+
+extern "C" int conv2d_num_variants(void) { return c2b::kNumVariants; }
+
+extern "C" int conv2d_variant_is_f16(int variant) {
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::kVariants[variant].f16;
 }
 
 extern "C" const char* conv2d_status_string(int status) {
@@ -469,7 +457,8 @@ extern "C" const char* conv2d_status_string(int status) {
     case CONV2D_ERR_ALIAS: return "grad_input overlaps grad_out or weight";
     case CONV2D_ERR_OVERFLOW: return "size exceeds 32-bit per-image indexing";
     case CONV2D_ERR_UNSUPPORTED:
-      return "kernel window of one stride phase too large for the staging tile";
+      return "kernel window of one stride phase too large for the staging tile, "
+             "or kernel variant not available for this path";
     case CONV2D_ERR_HIP: return "HIP runtime error at launch";
     default: return "unknown status";
   }

@@ -18,6 +18,13 @@
 // ch = (ih0 + padding_h - rh) / s.  For s = 1 there is one class.  No
 // structural zero is ever multiplied; classes that no tap reaches (s > kernel)
 // are written as zeros.
+//
+// Stages.  A tile's contraction runs in stages; a stage is cg groups of 16
+// output channels times up to tg taps of the class (a "unit" is one group at
+// one tap: 16 values of k).  Its grad_out halo window and its weights are
+// copied into one of two LDS stage buffers while the other buffer is
+// multiplied.  Stages run tap-group-major: for each tap group, every chunk of
+// 16*cg output channels.
 #pragma once
 
 #include <stdint.h>
@@ -25,6 +32,12 @@
 namespace c2b {
 
 constexpr int kMaxPhasesPerLaunch = 16;
+
+// LDS floats of one stage buffer (two per workgroup: 156 KiB of the 160 KiB).
+constexpr int kStageFloats = 19968;
+constexpr int kMaxStageTaps = 9;    // taps per stage
+constexpr int kMaxStageGroups = 8;  // 16-channel groups per stage
+constexpr int kDefaultCUs = 256;
 
 // One stride-residue class and its tiling.
 struct PhaseDesc {
@@ -37,20 +50,24 @@ struct PhaseDesc {
   int32_t nbands;      // bands per sub-image row, ceil(wp / wb)
   int32_t ntv;         // pixels per tile (<= the kernel's lane tile)
   int32_t ptiles;      // tiles per (image, band): ceil(hp * wb / ntv)
-  int32_t ngroups;     // tap groups: ceil(th * tw / taps per stage)
   int32_t tiles;       // tiles of this class in the launch
   int32_t tile_begin;  // first workgroup index of this class in the launch
-  int32_t ckr;         // output channels per stage (fp32 kernel)
-  int32_t tg;          // taps per stage (fp32 kernel)
-  int32_t slabr;       // window slots per channel in LDS (fp32 kernel)
-  int32_t cp;          // LDS floats per output channel of staged weights (fp32 kernel)
+  int32_t cg;          // 16-channel groups per stage
+  int32_t tg;          // taps per stage
+  int32_t ngroups;     // tap groups, ceil(th * tw / tg)
+  int32_t nchunks;     // output-channel chunks, ceil(Co / (16 * cg))
+  int32_t slots;       // window slots per channel (multiple of 16)
+  int32_t pt;          // weight pitch per input channel, in taps (odd, >= tg)
+  int32_t qp;          // weight floats per channel quad (multiple of 64)
+  int32_t wfl;         // window floats of a stage buffer: 16 * cg * slots
+  int32_t used;        // floats of a stage buffer copied: wfl + 4 * cg * qp
   // reciprocals for per-lane division: m = ceil(2^31 / d), see fast_div
   uint32_t m_roww;     // d = wb + tw - 1
   uint32_t m_wb;       // d = wb
   uint32_t m_tw;       // d = tw
-  uint32_t m_slots4;   // d = 4 * slabr
-  uint32_t m_cp;       // d = cp
-  uint32_t m_tg;       // d = tg
+  uint32_t m_slots4;   // d = 4 * slots
+  uint32_t m_qp;       // d = qp
+  uint32_t m_pt4;      // d = 4 * pt
 };
 
 // By-value kernel argument block of one launch.
@@ -66,14 +83,26 @@ struct LaunchArgs {
   PhaseDesc ph[kMaxPhasesPerLaunch];
 };
 
-// Compile-time tile shape of one kernel variant, as the planner sees it.
-struct TileShape {
-  int mt;     // input channels per workgroup
-  int nt;     // pixel lanes per workgroup
-  int ck;     // output channels staged per stage
-  int taps;   // kernel taps staged per stage
-  int slab;   // staged grad_out elements per output channel (halo window)
+// One instantiation of the kernel family: WM x WN waves; wave (mg, ng) owns
+// MB blocks of 16 input channels x NBW blocks of 16 pixels.  fp32 variants
+// multiply on v_mfma_f32_16x16x4_f32, f16 variants on
+// v_mfma_f32_16x16x32_f16 (pairs of units) and v_mfma_f32_16x16x16_f16.
+struct Variant {
+  int f16;   // 0: fp32 path, 1: f16-staged path
+  int wm;    // waves along channels
+  int wn;    // waves along pixels
+  int mb;    // 16-channel blocks per wave
+  int nbw;   // 16-pixel blocks per wave
 };
+
+constexpr Variant kVariants[] = {
+    // fp32
+    {0, 4, 2, 1, 4}, {0, 4, 2, 1, 8}, {0, 4, 2, 1, 13}, {0, 4, 3, 1, 9}, {0, 4, 4, 1, 7},
+    {0, 8, 1, 1, 4}, {0, 8, 1, 1, 8}, {0, 8, 1, 1, 13}, {0, 8, 2, 1, 7},
+    // f16-staged
+    {1, 4, 2, 1, 8}, {1, 2, 4, 2, 4}, {1, 1, 8, 4, 2}, {1, 2, 4, 4, 2}, {1, 2, 4, 4, 4},
+    {1, 4, 2, 2, 4}, {1, 2, 6, 2, 3}};
+constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b
 
@@ -83,49 +112,17 @@ struct TileShape {
 
 namespace c2b {
 
-// Tile shapes of the two kernel families (the kernels static_assert that
-// their template arguments match these).
-constexpr TileShape kF32Tile{64, 256, 8, 9, 608};
-constexpr TileShape kF16Tile{64, 256, 16, 9, 608};
-
 // Shape checks shared by every entry point (no pointer is looked at).
 int validate_shape(const conv2d_params* p);
 
-// Full plan for one tile shape: validate, split into classes and tiles, and
-// append one LaunchArgs per launch (pointers left null).  `info` may be null.
-// Used by the f16-staged kernel.
-int build_plan(const conv2d_params* p, const TileShape& ts,
-               std::vector<LaunchArgs>* launches, conv2d_plan_info* info);
-
-// fp32 kernel family: WM x WN waves, 16x16x4 fp32 matrix instructions; each
-// wave owns 16 input channels x NBW blocks of 16 pixels.  WM waves along
-// channels (64- or 128-channel tiles), WN waves along pixels (2, 3 or 4 waves
-// per SIMD).
-struct F32Variant {
-  int wm;    // waves along channels: 4 (64-channel tiles) or 8 (128)
-  int wn;    // waves along pixels
-  int nbw;   // 16-pixel blocks per wave
-};
-constexpr F32Variant kF32Variants[] = {{4, 2, 4}, {4, 2, 8}, {4, 2, 13}, {4, 3, 9},
-                                       {4, 4, 7}, {8, 1, 4}, {8, 1, 8}, {8, 1, 13},
-                                       {8, 2, 7}};
-constexpr int kNumF32Variants = int(sizeof(kF32Variants) / sizeof(kF32Variants[0]));
-constexpr int kF32StageCh = 16;     // output channels per stage
-constexpr int kF32MaxSlots = 640;   // window slots per channel (multiple of 16)
-constexpr int kF32MaxCP = 608;      // staged weight floats per channel
-constexpr int kF32WinFloats = kF32StageCh * kF32MaxSlots;   // one window buffer
-constexpr int kF32WtFloats = kF32StageCh * kF32MaxCP;       // one weight buffer
-constexpr int kF32LdsFloats = 2 * (kF32WinFloats + kF32WtFloats);   // 156 KiB
-constexpr int kF32StageTaps = 9;    // kernel taps per stage
-constexpr int kF32DefaultCUs = 256;
-
-// Plan for the fp32 kernel family on a device with `num_cus` compute units:
-// chooses the variant, tile sizes and stage depths per class (balancing the
-// tiles over the compute units, heaviest first).
+// Plan for the fp32 (f16 == 0) or f16-staged path on a device with
+// `num_cus` compute units: chooses the variant, tile sizes and stage shapes
+// per class (balancing the tiles over the compute units, heaviest first) and
+// appends one LaunchArgs per launch (pointers left null).  `info` may be null.
 // force_variant >= 0 plans with that variant only (CONV2D_ERR_UNSUPPORTED if
-// it cannot tile the shape); used by host-side checks of every variant.
-int build_plan_f32(const conv2d_params* p, int num_cus, std::vector<LaunchArgs>* launches,
-                   conv2d_plan_info* info, int force_variant = -1);
+// it belongs to the other path or cannot tile the shape).
+int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchArgs>* launches,
+               conv2d_plan_info* info, int force_variant = -1);
 
 // Pointer checks: NULL inputs of non-empty tensors and output/input overlap.
 int check_pointers(const float* go, const float* w, const float* gi,

@@ -1,13 +1,13 @@
-// Index arithmetic of the input-gradient kernels, shared by the kernels and
-// by the host-side index checker (index_check.hip), so that the checker
-// replays exactly the addresses the kernels form.
+// Index arithmetic of the input-gradient kernel, shared by the kernel and by
+// the host-side index checker (index_check.hip), so that the checker replays
+// exactly the addresses the kernel forms.
 //
-// Terms (see plan.hpp for the stride-residue classes):
-//  * tile: 64 input channels x up to 256 consecutive pixels of one band of
+// Terms (see plan.hpp for the stride-residue classes and stages):
+//  * tile: MT input channels x up to NTL consecutive pixels of one band of
 //    one class sub-image of one image;
 //  * window: the grad_out rows/columns a tile's pixels read through all taps
 //    of the class, R rows of roww elements, staged in LDS per output channel;
-//  * stage: CK output channels x up to TAPS taps of the class.
+//  * stage: 16*cg output channels x up to tg taps of the class.
 #pragma once
 
 #include "plan.hpp"
@@ -20,8 +20,6 @@
 #endif
 
 namespace c2b {
-
-constexpr int kThreads = 256;
 
 // Everything one workgroup derives from its index.
 struct TileCtx {
@@ -61,9 +59,8 @@ C2B_HD int phase_of(const LaunchArgs& a, int bid) {
 // x mod 8 (one XCD: the dispatcher deals workgroups round-robin over the 8
 // XCDs) take one contiguous run of tiles, channel tile fastest, so tiles
 // that share grad_out rows and weights share that XCD's L2.
-// ck: output channels per stage (0: the class's own stage depth, P.ckr).
 template <int MT>
-C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid, int ck) {
+C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   TileCtx c;
   c.P = a.ph[phase_of(a, bid)];
   const PhaseDesc& P = c.P;
@@ -85,8 +82,7 @@ C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid, int ck) {
   const int pend = imin(c.p0 + P.ntv, bandpix);
   c.npx = pend - c.p0;
   c.ntaps = P.th * P.tw;
-  if (ck == 0) ck = P.ckr;
-  c.nstages = c.ntaps > 0 ? ((a.Co + ck - 1) / ck) * P.ngroups : 0;
+  c.nstages = c.ntaps > 0 ? P.nchunks * P.ngroups : 0;
   c.i_start = c.p0 / P.wb;
   c.R = (pend - 1) / P.wb - c.i_start + P.th;
   c.roww = P.wb + P.tw - 1;
@@ -145,129 +141,77 @@ C2B_HD int tap_kidx(const PhaseDesc& P, const LaunchArgs& a, int tap) {
   return (P.rh + a.S * j) * a.KW + (P.rw + a.S * l);
 }
 
-// Stage st -> (first output channel, tap group).
-C2B_HD void stage_split(const TileCtx& c, int ck, int st, int* co0, int* g) {
-  const int cchunk = st / c.P.ngroups;
-  *g = st - cchunk * c.P.ngroups;
-  *co0 = cchunk * ck;
+// Stage st -> (first output channel, tap group); tap-group-major.
+C2B_HD void stage_split(const TileCtx& c, int st, int* co0, int* grp) {
+  *grp = st / c.P.nchunks;
+  *co0 = (st - *grp * c.P.nchunks) * 16 * c.P.cg;
 }
-
-// Weight staging cell e = (t, cg, ci), t-major, ci fastest; each cell holds
-// CPC consecutive output channels (1 for fp32, 8 for f16).  Returns the offset
-// of weight[cg*CPC, ci0 + ci, tap] relative to the stage's first output
-// channel, or -1 if the cell is padding (no tap / channel beyond Ci).
-template <int MT, int NCG, int TAPS, int CPC>
-C2B_HD int weight_cell_offset(const TileCtx& c, const LaunchArgs& a, int e, int g) {
-  constexpr int AE = TAPS * NCG * MT;
-  if (e >= AE) return -1;
-  const int t = e / (NCG * MT);
-  const int cg = (e / MT) % NCG;
-  const int ci = e % MT;
-  const int tap = g * TAPS + t;
-  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return -1;
-  return (cg * CPC * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(c.P, a, tap);
-}
-
-// First output channel (relative to the stage) of weight cell e.
-template <int MT, int NCG, int CPC>
-C2B_HD int weight_cell_channel(int e) { return ((e / MT) % NCG) * CPC; }
-
-// LDS index of weight cell e: cells are stored [t][cg][pitch], ci fastest.
-template <int MT, int NCG, int PITCH>
-C2B_HD int weight_cell_lds(int e) {
-  const int t = e / (NCG * MT);
-  const int cg = (e / MT) % NCG;
-  const int ci = e % MT;
-  return (t * NCG + cg) * PITCH + ci;
-}
-
-// Compile-time geometry of one kernel instantiation.
-//   fp32: one output channel per LDS cell, 2 k values per matrix instruction,
-//         A rows padded by 32 floats so the two half-waves of a read sit 32
-//         banks apart;
-//   f16:  8 output channels per 16-byte cell, 16 k values per instruction.
-template <bool F16, int MT, int CK, int TAPS, int SLAB>
-struct KernelGeom {
-  static constexpr int kCPC = F16 ? 8 : 1;               // channels per cell
-  static constexpr int kKPerStep = F16 ? 16 : 2;         // k per instruction
-  static constexpr int kNCG = CK / kCPC;                 // cell groups / stage
-  static constexpr int kKSteps = CK / kKPerStep;         // k-steps per tap
-  static constexpr int kPitch = F16 ? MT : MT + 32;      // A row pitch, cells
-  static constexpr int kHS = (SLAB + kThreads - 1) / kThreads;  // window slots
-  static constexpr int kAE = TAPS * kNCG * MT;           // A cells per stage
-  static constexpr int kWS = (kAE + kThreads - 1) / kThreads;   // A slots
-  static constexpr int kLdsA = TAPS * kNCG * kPitch;     // A cells in LDS
-  static constexpr int kLdsH = kNCG * SLAB;              // window cells in LDS
-  static_assert(CK % (2 * kCPC) == 0, "a k-step takes one cell group per half-wave");
-  static_assert(kKSteps * 2 == kNCG, "k-steps cover the stage's cell groups");
-};
 
 // ---------------------------------------------------------------------------
-// fp32 kernel family (8 waves, 16x16x4 fp32 matrix instructions).
-//   wave w: channel group mg = w % WM (16 input channels), pixel group
-//   ng = w / WM (WN groups); lane: k group g = lane / 16, c16 = lane % 16;
-//   block b of the wave covers tile-local pixels (b*WN + ng)*16 + [0, 16);
-//   k-step q (0..3) of a tap: lane group g supplies output channel 4g + q.
-// A stage is 16 output channels x up to tg taps.  LDS (two buffers of each,
-// at fixed offsets):
-//   window  [quad cq = 0..3][slot][4 channels]  (16*slots floats): a lane
-//           reads its group's 4 channels with one 16-byte read, 16 lanes read
-//           16 consecutive 16-byte cells (every bank once), and a tap shift
-//           is a plain subtraction of slots;
-//   weights [co][ci][t] with channel pitch cp (= 4 mod 16 floats, so the
-//           four lane groups, 4*cp apart, sit 16 banks apart).
-// Both are filled by buffer loads that write LDS directly: each
-// wave-instruction fills 64 consecutive floats, which here come from 16
-// consecutive pixels of 4 channels, or from consecutive weights of one
-// channel -- a few cache lines per instruction.
-template <int WM, int WN, int NBW>
-struct F32Geom {
+// Kernel geometry.
+//   wave w: channel group mg = w % WM, pixel group ng = w / WM; lane: k group
+//   g = lane / 16, c16 = lane % 16.  Channel block m of the wave covers input
+//   channels (mg*MB + m)*16 + [0, 16); pixel block b covers tile-local pixels
+//   (b*WN + ng)*16 + [0, 16).  In every unit (16 output channels at one tap)
+//   lane group g supplies output channels 4g .. 4g+3 of the unit's group.
+// A stage buffer (kStageFloats floats, two of them at fixed offsets) holds:
+//   window  [quad cq < 4cg][slot < slots][4 channels] at float 0: a lane
+//           reads its 4 channels of one slot with one 16-byte read; slots is
+//           a multiple of 16, so the four lane groups sit a multiple of
+//           256 bytes apart, and a tap shift is a plain subtraction of slots;
+//   weights [quad cq][ci < MT][t < pt][4 channels] at float wfl, quads qp
+//           floats apart (a multiple of 64): a lane reads the 4 channels of
+//           one (ci, tap) with one 16-byte read; pt is odd, so the 16 lanes
+//           of a group (consecutive ci) hit 16 disjoint sets of 4 banks.
+// Both are filled by buffer loads that write LDS directly: copy instruction
+// i of wave w fills floats i*threads + 64w + [0, 64) of the stage buffer.
+// wfl and used are multiples of 64, so one instruction never mixes window
+// and weights.
+template <int WM, int WN, int MB, int NBW>
+struct MMGeom {
   static constexpr int kThreads = 64 * WM * WN;
-  static constexpr int kWN = WN;                      // waves along pixels
-  static constexpr int kMT = 16 * WM;                 // channels per tile
+  static constexpr int kMT = 16 * WM * MB;            // channels per tile
   static constexpr int kNTL = 16 * NBW * WN;          // pixel lanes per tile
-  // copy wave-instructions per wave and stage: every one is issued; cells
-  // past the stage's window or weights read 0 and land inside the buffer
-  static constexpr int kHS = (kF32WinFloats + kThreads - 1) / kThreads;
-  static constexpr int kWS = (kF32WtFloats + kThreads - 1) / kThreads;
-  static_assert(kF32WinFloats % 64 == 0 && kF32WtFloats % 64 == 0, "whole instructions");
+  static constexpr int kCopies = (kStageFloats + kThreads - 1) / kThreads;
+  static_assert(kStageFloats % 64 == 0, "whole copy instructions");
 };
 
 // Tile-local pixel of block b of pixel group ng, lane c16.
-C2B_HD int f32_local(int b, int ng, int c16, int wn) { return (b * wn + ng) * 16 + c16; }
+C2B_HD int mm_local(int b, int ng, int c16, int wn) { return (b * wn + ng) * 16 + c16; }
 
-// Window cell f = (cq*slots + slot)*4 + c of a stage: grad_out offset
-// ch*OH*OW + oh*OW + ow (ch = 4cq + c) relative to the stage's first channel,
-// or -1 if the cell is padding (outside the image or the window).
-C2B_HD int f32_window_cell(const TileCtx& c, const LaunchArgs& a, int f) {
-  const int slots = c.P.slabr;
-  if (c.ntaps == 0 || f >= kF32StageCh * slots) return -1;
-  const int cq = fast_div(f, c.P.m_slots4);
-  const int r = f - cq * 4 * slots;
+// Tile-local input channel of block m of channel group mg, lane c16.
+C2B_HD int mm_channel(int m, int mg, int c16, int mb) { return (mg * mb + m) * 16 + c16; }
+
+// Window cell f = (cq*slots + slot)*4 + c of a stage buffer: grad_out offset
+// ch*OH*OW + oh*OW + ow (ch = 4cq + c) relative to the stage's first output
+// channel, or -1 if the cell is padding (outside the image or the window).
+C2B_HD int mm_window_cell(const TileCtx& c, const LaunchArgs& a, int f) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0 || f >= P.wfl) return -1;
+  const int cq = fast_div(f, P.m_slots4);
+  const int r = f - cq * 4 * P.slots;
   const int slot = r >> 2, ch = 4 * cq + (r & 3);
   const int off = window_slot_offset(c, a, slot);
   return off < 0 ? -1 : ch * (a.OH * a.OW) + off;
 }
 
-// Weight cell e = co*cp + ci*tg + t of stage tap group `grp`: offset of
-// weight[co, ci0 + ci, tap] relative to the stage's first output channel,
-// or -1 if padding.
+// Weight cell e = cq*qp + (ci*pt + t)*4 + c (e counted from the start of the
+// weight region) of tap group `grp`: offset of weight[co = 4cq + c, ci0 + ci,
+// tap grp*tg + t] relative to the stage's first output channel, or -1 if the
+// cell is padding.
 template <int MT>
-C2B_HD int f32_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp) {
+C2B_HD int mm_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp) {
   const PhaseDesc& P = c.P;
-  if (c.ntaps == 0 || e >= kF32StageCh * P.cp) return -1;
-  const int co = fast_div(e, P.m_cp);
-  const int r = e - co * P.cp;
-  if (r >= MT * P.tg) return -1;
-  const int ci = fast_div(r, P.m_tg), t = r - ci * P.tg;
+  if (c.ntaps == 0 || e < 0 || e >= 4 * P.cg * P.qp) return -1;
+  const int cq = fast_div(e, P.m_qp);
+  const int r = e - cq * P.qp;
+  const int ci = fast_div(r, P.m_pt4);
+  const int r2 = r - ci * 4 * P.pt;
+  const int t = r2 >> 2, co = 4 * cq + (r2 & 3);
+  if (ci >= MT || t >= P.tg) return -1;
   const int tap = grp * P.tg + t;
   if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return -1;
   return (co * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
 }
-
-// Accumulator register r of lane half h in a 32x32 block holds block row
-// 8*(r/4) + 4*h + r%4 (column = lane mod 32) -- the C/D layout of the
-// 32x32 matrix instructions used here.
-C2B_HD int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
 }  // namespace c2b

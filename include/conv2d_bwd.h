@@ -29,9 +29,11 @@
  *
  * Ownership.  The caller owns all three device buffers and keeps them alive
  * until the work enqueued on `stream` has completed.  `p` is read during the
- * call only.  The library keeps no per-call state and allocates nothing, so
- * calls are reentrant; calls on different streams that write the same
- * grad_input race like any other kernels would.
+ * call only.  The library allocates no device memory and keeps no per-call
+ * state; it keeps a small host-side cache of launch plans (at most 64
+ * shapes, guarded by a mutex), so calls are reentrant and thread-safe.
+ * Calls on different streams that write the same grad_input race like any
+ * other kernels would.
  *
  * Semantics.  grad_input is fully overwritten (elements no tap reaches are
  * set to 0).  grad_out and weight are only read.  grad_input must not overlap
@@ -83,14 +85,16 @@ enum {
                                   >= 2^31 elements, or the tile count does   */
   CONV2D_ERR_UNSUPPORTED = -5, /* one kernel tap window of one stride phase
                                   does not fit the on-chip staging tile
-                                  (kernel_h*kernel_w / stride^2 too large)   */
+                                  (kernel_h*kernel_w / stride^2 too large),
+                                  or a forced kernel variant is out of range
+                                  or cannot tile the shape                  */
   CONV2D_ERR_HIP = -6          /* the HIP runtime reported an error at
                                   launch (hipGetLastError)                   */
 };
 
 /*
  * fp32 path: operands staged in fp32, products on the fp32 matrix cores
- * (v_mfma_f32_32x32x2_f32), fp32 accumulation.
+ * (v_mfma_f32_16x16x4_f32), fp32 accumulation.
  *   grad_out, weight: device pointers to the inputs (layouts above).
  *   grad_input:       device pointer to the output, fully overwritten.
  *   p:                host pointer to the shape.
@@ -102,10 +106,11 @@ int conv2d_grad_input(const float* grad_out, const float* weight,
 
 /*
  * f16-staged path: the same operation and contract.  Storage stays fp32;
- * both operands are rounded to f16 (round to nearest even) as they are
- * staged on chip, products run on the f16 matrix cores
- * (v_mfma_f32_32x32x16_f16) and accumulate in fp32.  This is the shader's
- * $ENABLE_F16 specialisation: f16 workgroup tiles, fp32 buffers and store.
+ * every operand element is rounded to f16 (round to nearest even) exactly
+ * once, on its way from on-chip staging into the matrix cores
+ * (v_mfma_f32_16x16x32_f16, v_mfma_f32_16x16x16_f16), with fp32
+ * accumulation and an fp32 store.  This is the shader's $ENABLE_F16
+ * specialisation: f16 tiles, fp32 buffers and store.
  */
 int conv2d_grad_input_f16(const float* grad_out, const float* weight,
                           float* grad_input, const conv2d_params* p,
@@ -160,17 +165,38 @@ int conv2d_check_indexing(const conv2d_params* p, int f16, char* msg,
                           size_t msg_len);
 
 /*
- * The same replay for the fp32 path with its kernel variant forced to
- * `variant` (0 <= variant < conv2d_num_f32_variants()) instead of the one
- * the planner would pick, so every variant can be checked on any shape.
- * Returns as conv2d_check_indexing, or CONV2D_ERR_UNSUPPORTED if the
- * variant index is out of range or the variant cannot tile the shape.
+ * Kernel variants.  Both paths run one kernel family; a variant fixes its
+ * wave layout (waves along channels and pixels, 16-channel and 16-pixel
+ * blocks per wave) and whether it is an fp32 or an f16-staged instance.
+ * The compute entry points let the planner pick the variant; the calls
+ * below force one, so that tests and tuning can reach every variant.
+ */
+
+/* Number of kernel variants the library carries (indices 0 .. n-1). */
+int conv2d_num_variants(void);
+
+/* 1 if `variant` is an f16-staged instance, 0 if fp32,
+ * CONV2D_ERR_UNSUPPORTED if the index is out of range. */
+int conv2d_variant_is_f16(int variant);
+
+/*
+ * conv2d_grad_input (or conv2d_grad_input_f16, as the variant's path
+ * dictates) with the kernel variant forced to `variant`.  Same contract and
+ * results (up to summation order); returns CONV2D_ERR_UNSUPPORTED, with
+ * nothing enqueued, if the index is out of range or the variant cannot tile
+ * the shape.
+ */
+int conv2d_grad_input_variant(const float* grad_out, const float* weight,
+                              float* grad_input, const conv2d_params* p,
+                              int variant, void* stream);
+
+/*
+ * conv2d_check_indexing for the launches conv2d_grad_input_variant would
+ * make.  Returns as conv2d_check_indexing, or CONV2D_ERR_UNSUPPORTED as
+ * conv2d_grad_input_variant does.
  */
 int conv2d_check_indexing_variant(const conv2d_params* p, int variant,
                                   char* msg, size_t msg_len);
-
-/* Number of fp32 kernel variants (tile shapes) the library carries. */
-int conv2d_num_f32_variants(void);
 
 #ifdef __cplusplus
 }

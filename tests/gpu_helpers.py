@@ -21,8 +21,9 @@ def params_of(sh: ConvShape):
 
 
 def run_gpu(sh: ConvShape, go: np.ndarray, w: np.ndarray, f16: bool = False,
-            stream=None, check_guards: bool = True) -> np.ndarray:
-    """grad_input of the HIP path, as a float32 numpy array."""
+            stream=None, check_guards: bool = True, variant=None) -> np.ndarray:
+    """grad_input of the HIP path, as a float32 numpy array (``variant``
+    forces a kernel variant through conv2d_grad_input_variant)."""
     import torch
     dev = torch.device("cuda", 0)
     tgo = torch.from_numpy(np.ascontiguousarray(go, dtype=np.float32)).to(dev)
@@ -32,13 +33,26 @@ def run_gpu(sh: ConvShape, go: np.ndarray, w: np.ndarray, f16: bool = False,
     buf[:GUARD] = CANARY
     buf[GUARD + n:] = CANARY
     gi = buf[GUARD:GUARD + n].view(sh.gi_shape)
-    c2b.grad_input_into(gi, tgo, tw, params_of(sh), f16=f16, stream=stream)
+    c2b.grad_input_into(gi, tgo, tw, params_of(sh), f16=f16, stream=stream, variant=variant)
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     if check_guards:
         assert np.all(host[:GUARD] == np.float32(CANARY)), "write before grad_input"
         assert np.all(host[GUARD + n:] == np.float32(CANARY)), "write after grad_input"
     return host[GUARD:GUARD + n].reshape(sh.gi_shape)
+
+
+# Shapes every kernel variant is run on (GPU) and replayed on (CPU): ragged
+# channel and pixel tiles, deep stages of a 1x1 kernel with a ragged last
+# channel chunk, stride-2 classes with 1, 2 and 4 taps, a Ci = 3 stem, a
+# 5x5 kernel with asymmetric padding.
+VARIANT_SHAPES = [
+    ConvShape("v_3x3_ragged", 2, 70, 13, 17, 40, 3, 3, 1, 1, 1, 13, 17, dist="uniform"),
+    ConvShape("v_1x1_deep", 2, 33, 9, 10, 300, 1, 1, 1, 0, 0, 9, 10, dist="uniform"),
+    ConvShape("v_3x3_s2", 1, 20, 15, 14, 37, 3, 3, 2, 1, 1, 8, 7, dist="uniform"),
+    ConvShape("v_7x7_s2_ci3", 1, 3, 22, 19, 19, 7, 7, 2, 3, 3, 11, 10, dist="uniform"),
+    ConvShape("v_5x5_asym", 1, 17, 11, 12, 21, 5, 5, 1, 2, 1, 11, 10, dist="uniform"),
+]
 
 
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:

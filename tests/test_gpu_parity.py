@@ -14,7 +14,7 @@ import pytest
 import oracle
 from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw,
                                                     draw_integers, random_shape)
-from tests.gpu_helpers import TOL, rel_err, round_f16, run_gpu
+from tests.gpu_helpers import TOL, VARIANT_SHAPES, rel_err, round_f16, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -206,3 +206,33 @@ def test_bad_status_raises():
     p = c2b.make_params(1, 3, 5, 5, 4, 3, 3, 1, 1, 1, 5, 5)
     with pytest.raises(c2b.Conv2dError):
         c2b.grad_input_into(go.view(1, 4, 5, 5)[:, :3], go, w, p)  # alias
+
+
+# ---- every kernel variant, forced through conv2d_grad_input_variant ---------
+def _num_variants():
+    import conv2d_backward_implicit_amd as c2b
+    return c2b.num_variants()
+
+
+@pytest.mark.parametrize("variant", range(16))
+def test_every_variant(variant):
+    import conv2d_backward_implicit_amd as c2b
+    assert _num_variants() == 16
+    f16 = bool(c2b.variant_is_f16(variant))
+    for sh in VARIANT_SHAPES:
+        _say("case variant", variant, sh.name)
+        rng = np.random.default_rng(11)
+        go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+        w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+        ref = _oracle(sh, go, w)
+        got = run_gpu(sh, go, w, variant=variant)
+        assert not np.any(np.isnan(got)), "unwritten grad_input elements"
+        err = rel_err(got, ref)
+        assert err <= TOL[f16], (sh.name, err)
+        if f16:
+            err16 = rel_err(got, _oracle(sh, round_f16(go), round_f16(w)))
+            assert err16 <= 1e-5, (sh.name, err16)
+        # integer inputs: exact on every path and in any summation order
+        gi_, wi_ = draw_integers(sh, 3)
+        got_i = run_gpu(sh, gi_, wi_, variant=variant)
+        assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_)), sh.name

@@ -11,7 +11,7 @@ import pytest
 
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import CONFIGS, ConvShape, random_shape
-from tests.gpu_helpers import params_of
+from tests.gpu_helpers import VARIANT_SHAPES, params_of
 from tests.test_gpu_parity import EDGE, RANDOM
 
 
@@ -39,6 +39,24 @@ def test_random_stress(f16):
         sh = random_shape(rng, max_n=3, max_c=140, max_hw=70, max_k=9, max_s=5,
                           name="s%d" % i)
         _check(sh, f16)
+
+
+@pytest.mark.parametrize("variant", range(16))
+def test_every_variant_replay(variant):
+    assert c2b.num_variants() == 16
+    shapes = list(VARIANT_SHAPES) + [CONFIGS[0]]
+    for sh in shapes:
+        rc, msg = c2b.check_indexing_variant(params_of(sh), variant)
+        assert rc == 0, (variant, sh.name, rc, msg)
+
+
+def test_variant_queries():
+    n = c2b.num_variants()
+    kinds = [c2b.variant_is_f16(v) for v in range(n)]
+    assert set(kinds) == {0, 1}
+    assert c2b.variant_is_f16(-1) == -5 and c2b.variant_is_f16(n) == -5
+    p = params_of(VARIANT_SHAPES[0])
+    assert c2b.check_indexing_variant(p, n)[0] == -5
 
 
 def test_checker_rejects_bad_shape():
