@@ -88,11 +88,13 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
         // copies
         for (int i = 0; i < NC; ++i) {
           const int f0 = i * NT + wave * 64, f = f0 + lane;
-          if (f0 >= P.used) continue;                    // not issued
+          if (f0 >= kStageFloats) continue;              // not issued
           C2B_REQUIRE(f < kStageFloats, "copy lds %d", f);
           if (f0 < P.wfl) {
             C2B_REQUIRE(f0 + 64 <= P.wfl, "copy instruction straddles regions");
             const int o = mm_window_cell(c, a, f);
+            C2B_REQUIRE(mm_window_cell_at(c, a, f0, lane) == o, "window cell %d (per instruction)",
+                        f);
             if (o < 0 || int64_t(o) >= int64_t(nco) * OHOW) continue;   // reads 0
             const int cq = f / (4 * SLOTS), r = f % (4 * SLOTS);
             const int slot = r / 4, ch = 4 * cq + r % 4;
@@ -102,10 +104,16 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
             C2B_REQUIRE(o == ch * OHOW + int64_t(oh) * a.OW + ow, "window element");
             const int64_t gi = int64_t(c.n) * a.Co * OHOW + int64_t(co0) * OHOW + o;
             C2B_REQUIRE(gi >= 0 && gi < go_size, "grad_out read %lld", (long long)gi);
+          } else if (f0 >= P.used) {
+            // issued past the stage's data: every lane must read nothing
+            C2B_REQUIRE(mm_weight_cell_at<MT>(c, a, f0 - P.wfl, lane, grp) < 0,
+                        "copy past the stage's data reads memory");
           } else {
             C2B_REQUIRE(f0 + 64 <= P.used, "copy instruction straddles regions");
             const int e = f - P.wfl;
             const int o = mm_weight_cell<MT>(c, a, e, grp);
+            C2B_REQUIRE(mm_weight_cell_at<MT>(c, a, f0 - P.wfl, lane, grp) == o,
+                        "weight cell %d (per instruction)", e);
             if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) continue;  // reads 0
             const int cq = e / QP, r = e % QP, ci = r / (4 * PT), t = (r % (4 * PT)) / 4;
             const int co = 4 * cq + r % 4;

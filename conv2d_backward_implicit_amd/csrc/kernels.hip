@@ -92,14 +92,9 @@ __global__ __launch_bounds__(64 * WM * WN) void grad_input_mm_kernel(const Launc
 
   // copy offsets: instruction i of this wave fills stage-buffer floats
   // f0 = i*NT + 64*wave + [0, 64); window cells are the same for every stage,
-  // weight cells change with the tap group
+  // weight cells change with the tap group (filled below, together with the
+  // first stage's copies)
   unsigned off[NC];
-#pragma unroll
-  for (int i = 0; i < NC; ++i) {
-    const int f0 = i * NT + wave * 64;
-    const int o = f0 < P.wfl ? mm_window_cell(c, a, f0 + lane) : -1;
-    off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
-  }
   int wgroup = -1;
   struct StageCopy {
     __amdgpu_buffer_rsrc_t rg, rw;
@@ -123,7 +118,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grad_input_mm_kernel(const Launc
   // stages (no operand registers live) and only when the group changes.
   // The empty asm makes the cell index opaque, so the compiler cannot hoist
   // the group-independent part of every cell out of the stage loop (that
-  // would hold two more registers per copy instruction).
+  // would hold more vector and scalar registers per copy instruction).
   auto update_weight_offsets = [&](int st) __attribute__((always_inline)) {
     if (st >= nst) return;
     int co0, grp;
@@ -133,29 +128,48 @@ __global__ __launch_bounds__(64 * WM * WN) void grad_input_mm_kernel(const Launc
     for (int i = 0; i < NC; ++i) {
       const int f0 = i * NT + wave * 64;
       if (f0 >= P.wfl) {
-        int e = f0 + lane - P.wfl;
-        asm volatile("" : "+v"(e));
-        const int o = mm_weight_cell<MT>(c, a, e, grp);
+        int e0 = f0 - P.wfl, ln = lane;
+        asm volatile("" : "+s"(e0), "+v"(ln));
+        const int o = mm_weight_cell_at<MT>(c, a, e0, ln, grp);
         off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
       }
     }
     wgroup = grp;
   };
-  // Every instruction of the stage buffer is issued (cells past `used` read
-  // 0); the buffer resource is picked per instruction, uniformly per wave.
+  // Every instruction of the stage buffer is issued (cells past the stage's
+  // data read 0: a branch per instruction costs more scalar registers than
+  // the idle loads cost); the buffer resource is picked per instruction,
+  // uniformly per wave.
+  auto copy_one = [&](const StageCopy& sc, int i) __attribute__((always_inline)) {
+    const int f0 = i * NT + wave * 64;   // wave-uniform
+    const __amdgpu_buffer_rsrc_t rs = f0 < P.wfl ? sc.rg : sc.rw;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(lds + sc.base + f0), 4, off[i], 0, 0, 0);
+  };
   auto copy_stage = [&](const StageCopy& sc) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int f0 = i * NT + wave * 64;   // wave-uniform
-      if (i * NT + 64 * (NT / 64 - 1) >= kStageFloats && f0 >= kStageFloats) continue;
-      const __amdgpu_buffer_rsrc_t rs = f0 < P.wfl ? sc.rg : sc.rw;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(lds + sc.base + f0), 4, off[i], 0,
-                                               0, 0);
-    }
+    for (int i = 0; i < NC; ++i)
+      if (i * NT + 64 * (NT / 64 - 1) < kStageFloats || i * NT + wave * 64 < kStageFloats)
+        copy_one(sc, i);
   };
 
-  update_weight_offsets(0);
-  if (nst > 0) copy_stage(begin_stage_copy(0, 0));
+  // First stage: each copy goes out as soon as its offset is known, so the
+  // first loads overlap the offsets still being computed.
+  {
+    const StageCopy sc0 = begin_stage_copy(0, 0);
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const int f0 = i * NT + wave * 64;
+      int o;
+      if (f0 < P.wfl)
+        o = mm_window_cell_at(c, a, f0, lane);
+      else
+        o = mm_weight_cell_at<MT>(c, a, f0 - P.wfl, lane, 0);
+      off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
+      if (nst > 0 && (i * NT + 64 * (NT / 64 - 1) < kStageFloats || f0 < kStageFloats))
+        copy_one(sc0, i);
+    }
+    wgroup = 0;
+  }
 
   // byte offsets within a stage buffer: block b's window cell (quad g,
   // first tap of the class), and block m's weights (quad g, t = 0) within

@@ -232,39 +232,45 @@ bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* 
   return false;
 }
 
-// Matrix-unit efficiency reached with `wps` waves per SIMD (measured on the
-// tap loop: more waves hide more of the LDS latency between taps).
-double simd_efficiency(int wps) {
-  return wps >= 4 ? 0.88 : wps == 3 ? 0.85 : wps == 2 ? 0.75 : 0.6;
+// Matrix-unit efficiency of a variant, fitted to measurements on MI355X:
+// occupancy (waves per SIMD hide each other's LDS latency) times a term for
+// the LDS latency a wave exposes between units when it issues few matrix
+// instructions per unit (`unit_cycles` per SIMD per unit).
+double simd_efficiency(int wps, double unit_cycles) {
+  const double occ = wps >= 4 ? 0.95 : wps == 3 ? 0.9 : wps == 2 ? 0.7 : 0.5;
+  return occ * unit_cycles / (unit_cycles + 600.0);
 }
 
-constexpr double kStageCycles = 1500.0;   // barrier, copy issue and wait per stage
-constexpr double kTileCycles = 20000.0;   // set-up, first copies, epilogue
+constexpr double kStageCycles = 4800.0;    // barrier, copy issue and wait per stage
+constexpr double kTileCycles = 25000.0;    // set-up, first copies, epilogue
+constexpr double kCopyBytesPerCycle = 12.0;   // gathered copies into LDS, per CU
 
-// Relative cost (SIMD cycles) of one tile of class d with variant v.
+// Relative cost (CU cycles) of one tile of class d with variant v.
 //   matrix: per unit (16 k values), each wave issues MB x NBW blocks of
 //   4 fp32 instructions of 32 cycles, or half an f16 pair instruction of
 //   16 cycles; waves of a SIMD add up;
 //   LDS: per unit each wave reads NBW window and MB weight vectors of 1 KiB,
 //   at 128 bytes per cycle per CU;
-// the larger of the two, over the padded units of all stages.
+//   copies: a stage's buffer (all of it is issued) at kCopyBytesPerCycle,
+//   overlapped with the stage's products;
+// plus per-stage and per-tile overheads.
 double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v) {
+  (void)Co;
   if (d.th == 0) return kTileCycles;
   const int64_t ntaps = int64_t(d.th) * d.tw;
-  const int64_t nstages = int64_t(d.nchunks) * d.ngroups;
-  int64_t unit_slots = 0;   // units issued per channel chunk over all tap groups
-  for (int64_t g = 0; g < d.ngroups; ++g) {
-    const int64_t ntg = std::min<int64_t>(d.tg, ntaps - g * d.tg);
-    const int64_t u = int64_t(d.cg) * ntg;
-    unit_slots += v.f16 ? 2 * ceil_div(u, 2) : u;
-  }
-  const int64_t units = unit_slots * d.nchunks;
   const int wps = std::max(1, v.wm * v.wn / 4);
   const double mfma = double(wps) * v.mb * v.nbw * (v.f16 ? 8.0 : 128.0);
   const double lds = 8.0 * v.wm * v.wn * (v.nbw + v.mb);
-  (void)Co;
-  return double(units) * std::max(mfma, lds) / simd_efficiency(wps) + nstages * kStageCycles +
-         kTileCycles;
+  const double unit = std::max(mfma, lds) / simd_efficiency(wps, mfma);
+  const double copy = double(kStageFloats) * 4.0 / kCopyBytesPerCycle;
+  double cycles = kTileCycles;
+  for (int64_t g = 0; g < d.ngroups; ++g) {
+    const int64_t ntg = std::min<int64_t>(d.tg, ntaps - g * d.tg);
+    const int64_t u = int64_t(d.cg) * ntg;
+    const double units = v.f16 ? 2.0 * double(ceil_div(u, 2)) : double(u);
+    cycles += double(d.nchunks) * (std::max(units * unit, copy) + kStageCycles);
+  }
+  return cycles;
 }
 
 // Stage shape and tiling of one class for variant v: the (taps, channel

@@ -214,4 +214,36 @@ C2B_HD int mm_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp)
   return (co * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
 }
 
+// The same cells as mm_window_cell / mm_weight_cell for lane `lane` of the
+// copy instruction whose 64 floats start at f0 (window) or e0 (weights), a
+// multiple of 64: such an instruction never crosses a channel quad (4*slots
+// and qp are multiples of 64), so the quad and the instruction's first slot
+// or weight are wave-uniform and computed once, on the scalar unit.
+C2B_HD int mm_window_cell_at(const TileCtx& c, const LaunchArgs& a, int f0, int lane) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0 || f0 >= P.wfl) return -1;
+  const int cq = fast_div(f0, P.m_slots4);
+  const int slot = ((f0 - cq * 4 * P.slots) >> 2) + (lane >> 2);
+  if (slot >= c.R * c.roww) return -1;
+  const int r = fast_div(slot, P.m_roww);
+  const int oh = c.oh_base + r, ow = c.ow_base + (slot - r * c.roww);
+  if ((unsigned)oh >= (unsigned)a.OH || (unsigned)ow >= (unsigned)a.OW) return -1;
+  return (4 * cq + (lane & 3)) * (a.OH * a.OW) + oh * a.OW + ow;
+}
+
+template <int MT>
+C2B_HD int mm_weight_cell_at(const TileCtx& c, const LaunchArgs& a, int e0, int lane, int grp) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0 || e0 < 0 || e0 >= 4 * P.cg * P.qp) return -1;
+  const int cq = fast_div(e0, P.m_qp);
+  const int r = e0 - cq * P.qp + lane;
+  const int ci = fast_div(r, P.m_pt4);
+  const int r2 = r - ci * 4 * P.pt;
+  const int t = r2 >> 2;
+  if (ci >= MT || t >= P.tg) return -1;
+  const int tap = grp * P.tg + t;
+  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return -1;
+  return ((4 * cq + (r2 & 3)) * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
+}
+
 }  // namespace c2b
