@@ -106,6 +106,14 @@ def load_library():
                 "libconv2d_bwd.so is not built; run "
                 "`python -m conv2d_backward_implicit_amd.build` (or "
                 "__graft_entry__.build()) first")
+        # torch carries its own HIP runtime: load it before this library so
+        # that the library's kernels are registered with the runtime torch's
+        # streams and allocations belong to (loaded the other way round, every
+        # launch on a torch stream fails)
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.POINTER(Conv2dParams)
         for name in ("conv2d_grad_input", "conv2d_grad_input_f16"):

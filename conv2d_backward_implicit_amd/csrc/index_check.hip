@@ -34,9 +34,10 @@ struct Failure {
     }                                                           \
   } while (0)
 
-template <int WM, int WN, int MB, int NBW>
+template <int WM, int WN, int MB, int NBW, int SF>
 void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
-  using G = MMGeom<WM, WN, MB, NBW>;
+  using G = MMGeom<WM, WN, MB, NBW, SF>;
+  constexpr int kStageFloats = SF;
   constexpr int MT = G::kMT, NT = G::kThreads, NC = G::kCopies;
   const int64_t OHOW = int64_t(a.OH) * a.OW;
   const int64_t go_size = int64_t(a.N) * a.Co * OHOW;
@@ -191,7 +192,7 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
 template <int V>
 void check_variant(const LaunchArgs& la, std::vector<unsigned char>& written) {
   constexpr Variant v = kVariants[V];
-  check_launch<v.wm, v.wn, v.mb, v.nbw>(la, written);
+  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v)>(la, written);
 }
 
 template <int... Vs>

@@ -71,11 +71,13 @@ __device__ __forceinline__ f16x8 join(f16x4 lo, f16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <bool F16, int WM, int WN, int MB, int NBW>
-__global__ __launch_bounds__(64 * WM * WN) void grad_input_mm_kernel(const LaunchArgs a) {
-  using G = MMGeom<WM, WN, MB, NBW>;
+template <bool F16, int WM, int WN, int MB, int NBW, int SF>
+__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
+    const LaunchArgs a) {
+  using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int MT = G::kMT, NT = G::kThreads, NC = G::kCopies;
-  __shared__ f32x4 lds4[2 * kStageFloats / 4];
+  constexpr int kStageFloats = SF;   // this instance's stage buffer
+  __shared__ f32x4 lds4[2 * SF / 4];
   float* lds = reinterpret_cast<float*>(lds4);
 
   const int tid = threadIdx.x;
@@ -354,7 +356,7 @@ __global__ __launch_bounds__(64 * WM * WN) void grad_input_mm_kernel(const Launc
 template <int V>
 void launch_variant(const LaunchArgs& la, hipStream_t st) {
   constexpr Variant v = kVariants[V];
-  hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw>),
+  hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw, stage_floats(v)>),
                      dim3(la.total_tiles), dim3(64 * v.wm * v.wn), 0, st, la);
 }
 

@@ -232,43 +232,44 @@ bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* 
   return false;
 }
 
-// Matrix-unit efficiency of a variant, fitted to measurements on MI355X:
-// occupancy (waves per SIMD hide each other's LDS latency) times a term for
-// the LDS latency a wave exposes between units when it issues few matrix
-// instructions per unit (`unit_cycles` per SIMD per unit).
-double simd_efficiency(int wps, double unit_cycles) {
-  const double occ = wps >= 4 ? 0.95 : wps == 3 ? 0.9 : wps == 2 ? 0.7 : 0.5;
-  return occ * unit_cycles / (unit_cycles + 600.0);
-}
+// Cost model of one tile, in CU cycles, with constants fitted (least squares
+// on log time) to forced-variant timings of every kernel variant on the four
+// large workloads on MI355X:
+//   matrix: per unit (16 k values) each wave issues MB x NBW blocks of four
+//   fp32 instructions of 32 cycles (or half an f16 pair instruction of 16
+//   cycles); the waves of a SIMD add up, at an efficiency set by how many
+//   waves share the SIMD, plus the LDS latency the SIMD's waves cannot hide;
+//   copies: a stage's buffer at kCopyBytesPerCycle, overlapped with the
+//   stage's products;
+//   fixed costs per stage (barrier, copy issue and wait) and per tile (set-up,
+//   first copies, epilogue).
+// A two-per-CU variant that shares its CU (share = 2) gets half of every
+// SIMD, and part of its stage overheads hides behind the other workgroup.
+double simd_efficiency(int wps) { return wps >= 3 ? 1.0 : wps == 2 ? 0.9 : 0.4; }
 
-constexpr double kStageCycles = 4800.0;    // barrier, copy issue and wait per stage
-constexpr double kTileCycles = 25000.0;    // set-up, first copies, epilogue
+constexpr double kUnitLatency = 500.0;        // exposed LDS latency per unit and SIMD
+constexpr double kStageCycles = 2000.0;       // barrier, copy issue and wait per stage
+constexpr double kTileCycles = 45000.0;       // set-up, first copies, epilogue
 constexpr double kCopyBytesPerCycle = 12.0;   // gathered copies into LDS, per CU
+constexpr double kSharedStageVisible = 0.4;   // stage overhead left when sharing a CU
 
-// Relative cost (CU cycles) of one tile of class d with variant v.
-//   matrix: per unit (16 k values), each wave issues MB x NBW blocks of
-//   4 fp32 instructions of 32 cycles, or half an f16 pair instruction of
-//   16 cycles; waves of a SIMD add up;
-//   LDS: per unit each wave reads NBW window and MB weight vectors of 1 KiB,
-//   at 128 bytes per cycle per CU;
-//   copies: a stage's buffer (all of it is issued) at kCopyBytesPerCycle,
-//   overlapped with the stage's products;
-// plus per-stage and per-tile overheads.
-double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v) {
+double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v, int share) {
   (void)Co;
   if (d.th == 0) return kTileCycles;
   const int64_t ntaps = int64_t(d.th) * d.tw;
-  const int wps = std::max(1, v.wm * v.wn / 4);
-  const double mfma = double(wps) * v.mb * v.nbw * (v.f16 ? 8.0 : 128.0);
-  const double lds = 8.0 * v.wm * v.wn * (v.nbw + v.mb);
-  const double unit = std::max(mfma, lds) / simd_efficiency(wps, mfma);
-  const double copy = double(kStageFloats) * 4.0 / kCopyBytesPerCycle;
+  const double wps = v.wm * v.wn / 4.0;
+  const double mfma = wps * v.mb * v.nbw * (v.f16 ? 8.0 : 128.0) * share;
+  const double lds = 8.0 * v.wm * v.wn * (v.nbw + v.mb) * share;
+  const double unit = std::max(mfma, lds) / simd_efficiency(int(wps * share)) +
+                      kUnitLatency / std::max(1.0, wps * share);
+  const double copy = double(stage_floats(v)) * 4.0 / kCopyBytesPerCycle * share;
+  const double stage = kStageCycles * (share == 2 ? kSharedStageVisible : 1.0);
   double cycles = kTileCycles;
   for (int64_t g = 0; g < d.ngroups; ++g) {
     const int64_t ntg = std::min<int64_t>(d.tg, ntaps - g * d.tg);
     const int64_t u = int64_t(d.cg) * ntg;
     const double units = v.f16 ? 2.0 * double(ceil_div(u, 2)) : double(u);
-    cycles += double(d.nchunks) * (std::max(units * unit, copy) + kStageCycles);
+    cycles += double(d.nchunks) * (std::max(units * unit, copy) + stage);
   }
   return cycles;
 }
@@ -302,7 +303,7 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
       // byte ranges of a stage's buffer resources stay below 2^31
       if (16 * cg * OHOW * 4 >= kI31 || 16 * cg * cstride * 4 >= kI31) break;
       const int64_t wt = 4 * cg * qp;
-      const int64_t max_slots = (kStageFloats - wt) / (16 * cg) / 16 * 16;
+      const int64_t max_slots = (stage_floats(v) - wt) / (16 * cg) / 16 * 16;
       if (max_slots < 16) break;
       PhaseDesc c = *d;
       int64_t wb, ntv, slots;
@@ -320,7 +321,7 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
       c.qp = int32_t(qp);
       c.wfl = int32_t(16 * cg * slots);
       c.used = int32_t(16 * cg * slots + wt);
-      const double per_px = tile_cost(c, Co, v) / double(ntv);
+      const double per_px = tile_cost(c, Co, v, v.half ? 2 : 1) / double(ntv);
       if (!found || per_px < best * 0.999) {
         found = true;
         best = per_px;
@@ -390,17 +391,22 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     if (force_variant >= 0 ? v != force_variant : var.f16 != (f16 ? 1 : 0)) continue;
     const int64_t vmt = 16 * int64_t(var.wm) * var.mb;
     std::vector<PhaseDesc> phases = classes;
-    std::vector<double> costs;
     bool ok = true;
-    for (PhaseDesc& d : phases) {
+    for (PhaseDesc& d : phases)
       if (!tile_class(&d, var, Co, OHOW, cstride)) {
         ok = false;
         break;
       }
-      costs.push_back(tile_cost(d, Co, var));
-    }
     if (!ok) continue;
-    const double cost = lpt_makespan(phases, N * ceil_div(Ci, vmt), costs, num_cus);
+    // a two-per-CU variant only shares its CU when there are more tiles
+    // than CUs
+    int64_t ntiles = 0;
+    for (const PhaseDesc& d : phases)
+      ntiles += N * d.nbands * int64_t(d.ptiles) * ceil_div(Ci, vmt);
+    const int share = (var.half && ntiles > num_cus) ? 2 : 1;
+    std::vector<double> costs;
+    for (const PhaseDesc& d : phases) costs.push_back(tile_cost(d, Co, var, share));
+    const double cost = lpt_makespan(phases, N * ceil_div(Ci, vmt), costs, num_cus * share);
     if (best_v < 0 || cost < best_cost * 0.999) {
       best_v = v;
       best_cost = cost;
@@ -427,7 +433,7 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     }
   }
   std::stable_sort(best.begin(), best.end(), [&](const PhaseDesc& a, const PhaseDesc& b) {
-    return tile_cost(a, Co, bv) > tile_cost(b, Co, bv);
+    return tile_cost(a, Co, bv, 1) > tile_cost(b, Co, bv, 1);
   });
   return emit_launches(p, bci, best_v, best, launches, info);
 }

@@ -33,8 +33,11 @@ namespace c2b {
 
 constexpr int kMaxPhasesPerLaunch = 16;
 
-// LDS floats of one stage buffer (two per workgroup: 156 KiB of the 160 KiB).
+// LDS floats of one stage buffer: two per workgroup, 156 KiB of the 160 KiB
+// (kStageFloats), or half of that for variants that run two workgroups per
+// CU (kStageFloatsHalf).
 constexpr int kStageFloats = 19968;
+constexpr int kStageFloatsHalf = 9984;
 constexpr int kMaxStageTaps = 9;    // taps per stage
 constexpr int kMaxStageGroups = 8;  // 16-channel groups per stage
 constexpr int kDefaultCUs = 256;
@@ -93,15 +96,22 @@ struct Variant {
   int wn;    // waves along pixels
   int mb;    // 16-channel blocks per wave
   int nbw;   // 16-pixel blocks per wave
+  int half;  // 1: half-size stage buffers, two workgroups per CU
 };
 
+// Floats of one stage buffer of a variant.
+constexpr int stage_floats(const Variant& v) { return v.half ? kStageFloatsHalf : kStageFloats; }
+
 constexpr Variant kVariants[] = {
-    // fp32
-    {0, 4, 2, 1, 4}, {0, 4, 2, 1, 8}, {0, 4, 2, 1, 13}, {0, 4, 3, 1, 9}, {0, 4, 4, 1, 7},
-    {0, 8, 1, 1, 4}, {0, 8, 1, 1, 8}, {0, 8, 1, 1, 13}, {0, 8, 2, 1, 7},
-    // f16-staged
-    {1, 4, 2, 1, 8}, {1, 2, 4, 2, 4}, {1, 1, 8, 4, 2}, {1, 2, 4, 4, 2}, {1, 2, 4, 4, 4},
-    {1, 4, 2, 2, 4}, {1, 2, 6, 2, 3}};
+    // fp32, one workgroup per CU
+    {0, 4, 2, 1, 4, 0}, {0, 4, 2, 1, 8, 0}, {0, 4, 2, 1, 13, 0}, {0, 4, 3, 1, 9, 0},
+    {0, 4, 4, 1, 7, 0}, {0, 8, 1, 1, 4, 0}, {0, 8, 1, 1, 8, 0}, {0, 8, 1, 1, 13, 0},
+    {0, 8, 2, 1, 7, 0},
+    // f16-staged, one workgroup per CU
+    {1, 4, 2, 1, 8, 0}, {1, 2, 4, 2, 4, 0}, {1, 1, 8, 4, 2, 0}, {1, 2, 4, 4, 2, 0},
+    {1, 2, 4, 4, 4, 0}, {1, 4, 2, 2, 4, 0}, {1, 2, 6, 2, 3, 0},
+    // fp32, two workgroups per CU
+    {0, 4, 2, 1, 7, 1}, {0, 4, 2, 1, 5, 1}, {0, 4, 2, 1, 8, 1}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b

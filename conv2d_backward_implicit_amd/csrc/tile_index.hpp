@@ -154,7 +154,7 @@ C2B_HD void stage_split(const TileCtx& c, int st, int* co0, int* grp) {
 //   channels (mg*MB + m)*16 + [0, 16); pixel block b covers tile-local pixels
 //   (b*WN + ng)*16 + [0, 16).  In every unit (16 output channels at one tap)
 //   lane group g supplies output channels 4g .. 4g+3 of the unit's group.
-// A stage buffer (kStageFloats floats, two of them at fixed offsets) holds:
+// A stage buffer (SF floats, two of them at fixed offsets) holds:
 //   window  [quad cq < 4cg][slot < slots][4 channels] at float 0: a lane
 //           reads its 4 channels of one slot with one 16-byte read; slots is
 //           a multiple of 16, so the four lane groups sit a multiple of
@@ -167,13 +167,14 @@ C2B_HD void stage_split(const TileCtx& c, int st, int* co0, int* grp) {
 // i of wave w fills floats i*threads + 64w + [0, 64) of the stage buffer.
 // wfl and used are multiples of 64, so one instruction never mixes window
 // and weights.
-template <int WM, int WN, int MB, int NBW>
+template <int WM, int WN, int MB, int NBW, int SF>
 struct MMGeom {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kMT = 16 * WM * MB;            // channels per tile
   static constexpr int kNTL = 16 * NBW * WN;          // pixel lanes per tile
-  static constexpr int kCopies = (kStageFloats + kThreads - 1) / kThreads;
-  static_assert(kStageFloats % 64 == 0, "whole copy instructions");
+  static constexpr int kSF = SF;                      // floats per stage buffer
+  static constexpr int kCopies = (SF + kThreads - 1) / kThreads;
+  static_assert(SF % 64 == 0, "whole copy instructions");
 };
 
 // Tile-local pixel of block b of pixel group ng, lane c16.

@@ -41,9 +41,8 @@ def test_random_stress(f16):
         _check(sh, f16)
 
 
-@pytest.mark.parametrize("variant", range(16))
+@pytest.mark.parametrize("variant", range(c2b.num_variants()))
 def test_every_variant_replay(variant):
-    assert c2b.num_variants() == 16
     shapes = list(VARIANT_SHAPES) + [CONFIGS[0]]
     for sh in shapes:
         rc, msg = c2b.check_indexing_variant(params_of(sh), variant)
