@@ -112,8 +112,9 @@ constexpr Variant kVariants[] = {
     {1, 2, 4, 4, 4, 0}, {1, 4, 2, 2, 4, 0}, {1, 2, 6, 2, 3, 0},
     // fp32, two workgroups per CU
     {0, 4, 2, 1, 7, 1}, {0, 4, 2, 1, 5, 1}, {0, 4, 2, 1, 8, 1},
-    // fp32, one 16-channel block per tile (few input channels)
-    {0, 1, 8, 1, 7, 0}, {0, 1, 12, 1, 5, 0}, {0, 1, 16, 1, 4, 0}};
+    // one 16-channel block per tile (few input channels)
+    {0, 1, 8, 1, 7, 0}, {0, 1, 12, 1, 5, 0}, {0, 1, 16, 1, 4, 0}, {1, 1, 12, 1, 5, 0},
+    {1, 1, 8, 1, 7, 0}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b
