@@ -188,3 +188,28 @@ def test_plan_zero_classes_when_stride_exceeds_kernel():
            stride=3, out_h=3, out_w=2)
     info = c2b.describe_plan(p)
     assert info["phases"] == 9 and info["zero_phases"] == 5
+
+
+def test_library_shares_torchs_hip_runtime():
+    """Loaded first thing in a fresh process, the library must still bind to
+    the HIP runtime torch carries: with two runtimes in one process, every
+    launch on a torch stream fails."""
+    import subprocess
+    import sys
+    code = (
+        "import conv2d_backward_implicit_amd as c2b\n"
+        "c2b.load_library()\n"
+        "paths = set()\n"
+        "for line in open('/proc/self/maps'):\n"
+        "    if 'libamdhip64' in line:\n"
+        "        paths.add(line.split()[-1])\n"
+        "print(len(paths))\n"
+        "print('\\n'.join(sorted(paths)))\n")
+    out = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True,
+                         cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                         timeout=300)
+    assert out.returncode == 0, out.stderr[-2000:]
+    lines = out.stdout.split()
+    assert lines[0] == "1", out.stdout
+    import torch
+    assert os.path.dirname(torch.__file__) in lines[1], out.stdout
