@@ -3,8 +3,10 @@
 // launch the plan makes and checks, with the same index functions the kernel
 // uses (tile_index.hpp):
 //  * every copy instruction fills 64 consecutive floats inside one region
-//    (window or weights) of its stage buffer, and every global element it
-//    reads lies inside its tensor and is the one the gather rule asks for;
+//    (window or weights) of its stage buffer, every global element it reads
+//    lies inside its tensor and is the one the gather rule asks for, and
+//    every padding cell's offset lies beyond its buffer's range (so it reads
+//    0) without wrapping;
 //  * every LDS read lies inside its region, and for a real pixel the window
 //    cell a unit reads holds grad_out[oh = i' + ch - j, ow = j' + cw - l] of
 //    the unit's output channels, while the weight cell it is multiplied with
@@ -38,7 +40,7 @@ template <int WM, int WN, int MB, int NBW, int SF>
 void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int kStageFloats = SF;
-  constexpr int MT = G::kMT, NT = G::kThreads, NC = G::kCopies;
+  constexpr int MT = G::kMT, NT = G::kThreads, NW = G::kWaves, NJ = G::kBatches;
   const int64_t OHOW = int64_t(a.OH) * a.OW;
   const int64_t go_size = int64_t(a.N) * a.Co * OHOW;
   const int64_t KHW = int64_t(a.KH) * a.KW;
@@ -71,6 +73,7 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
                       int64_t(CH) * cstride * 4 < (int64_t(1) << 31),
                   "stage byte range");
     }
+    std::vector<unsigned char> covered(size_t(c.nstages) * size_t(c.ntaps > 0 ? P.used : 0), 0);
     for (int tid = 0; tid < NT; ++tid) {
       const int lane = tid & 63, wave = tid >> 6;
       const int mg = wave % WM, ng = wave / WM, g = lane >> 4, c16 = lane & 15;
@@ -86,43 +89,69 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
         const int tap0 = grp * TG;
         const int ntg = imin(TG, c.ntaps - tap0);
         C2B_REQUIRE(ntg >= 1 && grp < P.ngroups, "stage %d without taps", st);
-        // copies
-        for (int i = 0; i < NC; ++i) {
-          const int f0 = i * NT + wave * 64, f = f0 + lane;
-          if (f0 >= kStageFloats) continue;              // not issued
-          C2B_REQUIRE(f < kStageFloats, "copy lds %d", f);
-          if (f0 < P.wfl) {
-            C2B_REQUIRE(f0 + 64 <= P.wfl, "copy instruction straddles regions");
-            const int o = mm_window_cell(c, a, f);
-            C2B_REQUIRE(mm_window_cell_at(c, a, f0, lane) == o, "window cell %d (per instruction)",
-                        f);
-            if (o < 0 || int64_t(o) >= int64_t(nco) * OHOW) continue;   // reads 0
-            const int cq = f / (4 * SLOTS), r = f % (4 * SLOTS);
-            const int slot = r / 4, ch = 4 * cq + r % 4;
-            C2B_REQUIRE(ch < nco && slot < c.R * c.roww, "window cell %d", f);
-            const int oh = c.oh_base + slot / c.roww, ow = c.ow_base + slot % c.roww;
-            C2B_REQUIRE(oh >= 0 && oh < a.OH && ow >= 0 && ow < a.OW, "window pixel");
-            C2B_REQUIRE(o == ch * OHOW + int64_t(oh) * a.OW + ow, "window element");
-            const int64_t gi = int64_t(c.n) * a.Co * OHOW + int64_t(co0) * OHOW + o;
-            C2B_REQUIRE(gi >= 0 && gi < go_size, "grad_out read %lld", (long long)gi);
-          } else if (f0 >= P.used) {
-            // issued past the stage's data: every lane must read nothing
-            C2B_REQUIRE(mm_weight_cell_at<MT>(c, a, f0 - P.wfl, lane, grp) < 0,
-                        "copy past the stage's data reads memory");
-          } else {
-            C2B_REQUIRE(f0 + 64 <= P.used, "copy instruction straddles regions");
-            const int e = f - P.wfl;
-            const int o = mm_weight_cell<MT>(c, a, e, grp);
-            C2B_REQUIRE(mm_weight_cell_at<MT>(c, a, f0 - P.wfl, lane, grp) == o,
-                        "weight cell %d (per instruction)", e);
-            if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) continue;  // reads 0
-            const int cq = e / QP, r = e % QP, ci = r / (4 * PT), t = (r % (4 * PT)) / 4;
-            const int co = 4 * cq + r % 4;
-            C2B_REQUIRE(co < nco && ci < MT && t < ntg, "weight cell %d", e);
-            const int64_t want = (int64_t(co0 + co) * a.Ci + c.ci0 + ci) * KHW +
-                                 tap_kidx(P, a, tap0 + t);
-            const int64_t wi = int64_t(co0) * cstride + o;
-            C2B_REQUIRE(wi == want && wi >= 0 && wi < w_size, "weight element");
+        // copies: batch wave + NW*j of this wave (tile_index.hpp); every
+        // stage-buffer cell below `used` must be written by exactly one lane
+        // of one wave per stage (checked after the last thread below)
+        const int NB = stage_batches(P), WB = window_blocks(P);
+        C2B_REQUIRE(NB <= NW * NJ, "bid %d: %d copy batches for %d waves", bid, NB, NW);
+        for (int j = 0; j < NJ; ++j) {
+          const int k = wave + NW * j;
+          if (k >= NB) break;
+          int block, quad;
+          batch_split(P, k, &block, &quad);
+          C2B_REQUIRE(block >= 0 && block < copy_blocks(P) && quad >= 0 && quad < 4 * CG,
+                      "batch %d split", k);
+          const bool win = block < WB;
+          const uint32_t off = win ? window_lane_offset(c, a, block, lane)
+                                   : weight_lane_offset<MT>(c, a, block - WB, lane, grp);
+          const uint32_t ch = win ? window_channel_bytes(a) : weight_channel_bytes(a);
+          const int64_t range = win ? int64_t(nco) * OHOW * 4 : int64_t(nco) * cstride * 4;
+          C2B_REQUIRE(off == kPadOffset || off % 4 == 0, "unaligned copy offset");
+          const int f = batch_lds_float(P, block, quad, lane);
+          if (f < 0) continue;                               // lane writes nothing
+          C2B_REQUIRE(f % 4 == 0 && f + 4 <= (win ? P.wfl : P.used) && (win || f >= P.wfl),
+                      "batch %d lane %d writes float %d outside its region", k, lane, f);
+          for (int q = 0; q < 4; ++q) {
+            const int cell = f + q;
+            unsigned char& cov = covered[size_t(st) * size_t(P.used) + size_t(cell)];
+            C2B_REQUIRE(cov == 0, "stage %d cell %d written twice", st, cell);
+            cov = 1;
+            const uint64_t o64 = uint64_t(off) + uint64_t(4 * quad + q) * ch;
+            C2B_REQUIRE(o64 < (uint64_t(1) << 32), "copy offset wraps");
+            const bool pad = off == kPadOffset;
+            C2B_REQUIRE(!pad || int64_t(o64) >= range, "padding cell inside the range");
+            const bool reads = !pad && int64_t(o64) < range;
+            if (win) {
+              const int o = mm_window_cell(c, a, cell);
+              if (o < 0 || int64_t(o) >= int64_t(nco) * OHOW) {
+                C2B_REQUIRE(!reads, "window cell %d should read 0", cell);
+                continue;
+              }
+              C2B_REQUIRE(reads && int64_t(o64) == int64_t(o) * 4, "window cell %d offset", cell);
+              const int cq2 = cell / (4 * SLOTS), r = cell % (4 * SLOTS);
+              const int slot = r / 4, chn = 4 * cq2 + r % 4;
+              C2B_REQUIRE(chn < nco && slot < c.R * c.roww, "window cell %d", cell);
+              const int oh = c.oh_base + slot / c.roww, ow = c.ow_base + slot % c.roww;
+              C2B_REQUIRE(oh >= 0 && oh < a.OH && ow >= 0 && ow < a.OW, "window pixel");
+              C2B_REQUIRE(o == chn * OHOW + int64_t(oh) * a.OW + ow, "window element");
+              const int64_t gi = int64_t(c.n) * a.Co * OHOW + int64_t(co0) * OHOW + o;
+              C2B_REQUIRE(gi >= 0 && gi < go_size, "grad_out read %lld", (long long)gi);
+            } else {
+              const int e = cell - P.wfl;
+              const int o = mm_weight_cell<MT>(c, a, e, grp);
+              if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) {
+                C2B_REQUIRE(!reads, "weight cell %d should read 0", e);
+                continue;
+              }
+              C2B_REQUIRE(reads && int64_t(o64) == int64_t(o) * 4, "weight cell %d offset", e);
+              const int cq2 = e / QP, r = e % QP, ci = r / (4 * PT), t = (r % (4 * PT)) / 4;
+              const int co = 4 * cq2 + r % 4;
+              C2B_REQUIRE(co < nco && ci < MT && t < ntg, "weight cell %d", e);
+              const int64_t want = (int64_t(co0 + co) * a.Ci + c.ci0 + ci) * KHW +
+                                   tap_kidx(P, a, tap0 + t);
+              const int64_t wi = int64_t(co0) * cstride + o;
+              C2B_REQUIRE(wi == want && wi >= 0 && wi < w_size, "weight element");
+            }
           }
         }
         // unit reads, in the kernel's order
@@ -186,6 +215,9 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
           }
       }
     }
+    for (size_t i = 0; i < covered.size(); ++i)
+      C2B_REQUIRE(covered[i] == 1, "bid %d: stage %d cell %d never copied", bid,
+                  int(i / size_t(P.used)), int(i % size_t(P.used)));
   }
 }
 

@@ -21,9 +21,14 @@
 //    instead of once per tap.
 //  * Window and weights go straight from global memory into LDS with buffer
 //    loads that write LDS (no register round trip); reads past a tensor's
-//    extent return 0, which supplies the padding halo.  Two stage buffers:
-//    the copies of stage s+1 are issued during the first unit of stage s,
-//    one barrier per stage.  The planner picks the wave shape and the stage
+//    extent return 0, which supplies the padding halo.  Copies go through
+//    registers (tile_index.hpp, copy batches): each load instruction reads
+//    64 consecutive cells of one channel, and each lane writes the 4
+//    channels of one cell to LDS with one 16-byte store.  (Loads that write
+//    LDS directly were measured to stall the matrix cores' LDS reads for the
+//    whole time they land.)  Two stage buffers: at the end of stage s the
+//    lanes write stage s+1 (loaded a stage earlier) into the buffer stage
+//    s-1 used and issue the loads of stage s+2; one barrier per stage.  The planner picks the wave shape and the stage
 //    shape (channel groups x taps) per problem from a cost model of the
 //    schedule over all CUs.
 //  * fp32 path: v_mfma_f32_16x16x4_f32, four per (unit, block).  f16-staged
@@ -53,16 +58,11 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 // Word 3 of a raw (untyped, unswizzled) buffer resource: 32-bit data format.
 constexpr int kRawBufferFlags = 0x00020000;
-// A byte offset past every buffer's range: such loads return 0.
-constexpr unsigned kOutOfRange = 0xFFFFFFFFu;
-
-__device__ __forceinline__ __attribute__((address_space(3))) void* lds_ptr(float* p) {
-  return (__attribute__((address_space(3))) void*)p;
+// One fp32 value from a buffer (0 if `byte_offset` is past the range); the
+// builtin returns the raw 32 bits.
+__device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t byte_offset) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rs, byte_offset, 0, 0));
 }
-
-// Wait until this wave's outstanding vector-memory operations (including
-// loads that write LDS directly) have completed.
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // Four fp32 values rounded to f16 (round to nearest even).
 __device__ __forceinline__ f16x4 to_f16(f32x4 x) { return __builtin_convertvector(x, f16x4); }
@@ -75,7 +75,7 @@ template <bool F16, int WM, int WN, int MB, int NBW, int SF>
 __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
     const LaunchArgs a) {
   using G = MMGeom<WM, WN, MB, NBW, SF>;
-  constexpr int MT = G::kMT, NT = G::kThreads, NC = G::kCopies;
+  constexpr int MT = G::kMT, NW = G::kWaves, NJ = G::kBatches;
   constexpr int kStageFloats = SF;   // this instance's stage buffer
   __shared__ f32x4 lds4[2 * SF / 4];
   float* lds = reinterpret_cast<float*>(lds4);
@@ -91,86 +91,99 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
   const int cstride = a.Ci * a.KH * a.KW;
   const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
   const int nst = c.nstages;
+  // copy batches (tile_index.hpp): batch wave + NW*j of every stage is this
+  // wave's j-th; its 64 lanes load 4 channels each and write 16 bytes to LDS
+  const int NB = stage_batches(P);
+  const int WB = window_blocks(P);
+  const uint32_t wch = window_channel_bytes(a), tch = weight_channel_bytes(a);
 
-  // copy offsets: instruction i of this wave fills stage-buffer floats
-  // f0 = i*NT + 64*wave + [0, 64); window cells are the same for every stage,
-  // weight cells change with the tap group (filled below, together with the
-  // first stage's copies)
-  unsigned off[NC];
-  int wgroup = -1;
-  struct StageCopy {
+  uint32_t off[NJ];   // per-lane source offsets of this wave's batches
+  f32x4 stg[NJ];      // a stage's batches between their loads and LDS writes
+  int wgroup = -1;    // tap group the weight offsets are for
+  struct StageSrc {
     __amdgpu_buffer_rsrc_t rg, rw;
-    int base;
   };
   // (Every lambda here is forced inline: an outlined one becomes a real call
   // with its own stack frame.)
-  auto begin_stage_copy = [&](int st, int buf) __attribute__((always_inline)) {
+  auto stage_src = [&](int st) __attribute__((always_inline)) {
     int co0, grp;
     stage_split(c, st, &co0, &grp);
     const int nco = imin(16 * P.cg, a.Co - co0);
-    StageCopy sc;
+    StageSrc sc;
     sc.rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(go_n + (size_t)co0 * OHOW), 0,
                                               nco * OHOW * 4, kRawBufferFlags);
     sc.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.w + (size_t)co0 * cstride), 0,
                                               nco * cstride * 4, kRawBufferFlags);
-    sc.base = buf * kStageFloats;
     return sc;
   };
-  // Weight copy offsets for the tap group of stage st, recomputed between
-  // stages (no operand registers live) and only when the group changes.
-  // The empty asm makes the cell index opaque, so the compiler cannot hoist
-  // the group-independent part of every cell out of the stage loop (that
-  // would hold more vector and scalar registers per copy instruction).
-  auto update_weight_offsets = [&](int st) __attribute__((always_inline)) {
-    if (st >= nst) return;
-    int co0, grp;
-    stage_split(c, st, &co0, &grp);
-    if (grp == wgroup) return;
+  // Source offsets of this wave's batches: window blocks once per tile,
+  // weight blocks whenever the tap group changes.  The empty asm makes the
+  // lane index opaque, so the compiler cannot hoist the group-independent
+  // part of every offset out of the stage loop (that would hold more
+  // registers per batch).
+  auto set_offsets = [&](int grp, bool window_too) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int f0 = i * NT + wave * 64;
-      if (f0 >= P.wfl) {
-        int e0 = f0 - P.wfl, ln = lane;
-        asm volatile("" : "+s"(e0), "+v"(ln));
-        const int o = mm_weight_cell_at<MT>(c, a, e0, ln, grp);
-        off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
+    for (int j = 0; j < NJ; ++j) {
+      const int k = wave + NW * j;
+      if (k >= NB) break;
+      int block, quad;
+      batch_split(P, k, &block, &quad);
+      if (block < WB) {
+        if (window_too) off[j] = window_lane_offset(c, a, block, lane);
+      } else {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        off[j] = weight_lane_offset<MT>(c, a, block - WB, ln, grp);
       }
     }
     wgroup = grp;
   };
-  // Every instruction of the stage buffer is issued (cells past the stage's
-  // data read 0: a branch per instruction costs more scalar registers than
-  // the idle loads cost); the buffer resource is picked per instruction,
-  // uniformly per wave.
-  auto copy_one = [&](const StageCopy& sc, int i) __attribute__((always_inline)) {
-    const int f0 = i * NT + wave * 64;   // wave-uniform
-    const __amdgpu_buffer_rsrc_t rs = f0 < P.wfl ? sc.rg : sc.rw;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(lds + sc.base + f0), 4, off[i], 0, 0, 0);
+  auto update_weight_offsets = [&](int st) __attribute__((always_inline)) {
+    int co0, grp;
+    stage_split(c, st, &co0, &grp);
+    if (grp != wgroup) set_offsets(grp, false);
   };
-  auto copy_stage = [&](const StageCopy& sc) __attribute__((always_inline)) {
+  // Loads of this wave's batches of stage st into stg[]: four channels per
+  // lane, each load reading 64 consecutive cells of one channel.
+  auto load_stage = [&](int st) __attribute__((always_inline)) {
+    const StageSrc sc = stage_src(st);
 #pragma unroll
-    for (int i = 0; i < NC; ++i)
-      if (i * NT + 64 * (NT / 64 - 1) < kStageFloats || i * NT + wave * 64 < kStageFloats)
-        copy_one(sc, i);
+    for (int j = 0; j < NJ; ++j) {
+      const int k = wave + NW * j;
+      if (k >= NB) break;
+      int block, quad;
+      batch_split(P, k, &block, &quad);
+      const bool win = block < WB;
+      const __amdgpu_buffer_rsrc_t rs = win ? sc.rg : sc.rw;
+      const uint32_t ch = win ? wch : tch;
+      const uint32_t o = off[j] + 4u * uint32_t(quad) * ch;
+      stg[j] = f32x4{load_f32(rs, o), load_f32(rs, o + ch), load_f32(rs, o + 2u * ch),
+                     load_f32(rs, o + 3u * ch)};
+    }
+  };
+  // LDS writes of stg[] into stage buffer buf (16 bytes per lane).
+  auto write_stage = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int k = wave + NW * j;
+      if (k >= NB) break;
+      int block, quad;
+      batch_split(P, k, &block, &quad);
+      const int f = batch_lds_float(P, block, quad, lane);
+      if (f >= 0) *reinterpret_cast<f32x4*>(lds + buf * kStageFloats + f) = stg[j];
+    }
   };
 
-  // First stage: each copy goes out as soon as its offset is known, so the
-  // first loads overlap the offsets still being computed.
-  {
-    const StageCopy sc0 = begin_stage_copy(0, 0);
-#pragma unroll
-    for (int i = 0; i < NC; ++i) {
-      const int f0 = i * NT + wave * 64;
-      int o;
-      if (f0 < P.wfl)
-        o = mm_window_cell_at(c, a, f0, lane);
-      else
-        o = mm_weight_cell_at<MT>(c, a, f0 - P.wfl, lane, 0);
-      off[i] = o >= 0 ? unsigned(o) * 4u : kOutOfRange;
-      if (nst > 0 && (i * NT + 64 * (NT / 64 - 1) < kStageFloats || f0 < kStageFloats))
-        copy_one(sc0, i);
-    }
-    wgroup = 0;
+  // Stage 0 is copied now; stage 1 is loaded now and written at the end of
+  // stage 0.
+  set_offsets(0, true);
+  if (nst > 0) {
+    load_stage(0);
+    write_stage(0);
+  }
+  if (nst > 1) {
+    update_weight_offsets(1);
+    load_stage(1);
   }
 
   // byte offsets within a stage buffer: block b's window cell (quad g,
@@ -252,6 +265,7 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
     const int buf = st & 1;
     int co0, grp;
     stage_split(c, st, &co0, &grp);
+    (void)co0;
     const int tap0 = grp * P.tg;
     const int ntg = imin(P.tg, c.ntaps - tap0);
     const int units = P.cg * ntg;
@@ -274,18 +288,8 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
         ++j;
       }
     };
-    auto issue_next = [&]() __attribute__((always_inline)) {
-      if (st + 1 < nst) copy_stage(begin_stage_copy(st + 1, buf ^ 1));
-    };
     if constexpr (!F16) {
-      {
-        f32x4 bv[NBW], aw[MB];
-        read_unit(Hb, Ab, wo(), ao(), bv, aw);
-        issue_next();
-        mma_f32(bv, aw);
-        advance();
-      }
-      for (int u = 1; u < units; ++u) {
+      for (int u = 0; u < units; ++u) {
         f32x4 bv[NBW], aw[MB];
         read_unit(Hb, Ab, wo(), ao(), bv, aw);
         mma_f32(bv, aw);
@@ -293,23 +297,6 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
       }
     } else {
       int u = 0;
-      if (units >= 2) {
-        f32x4 bv0[NBW], aw0[MB], bv1[NBW], aw1[MB];
-        read_unit(Hb, Ab, wo(), ao(), bv0, aw0);
-        advance();
-        read_unit(Hb, Ab, wo(), ao(), bv1, aw1);
-        advance();
-        issue_next();
-        mma_f16_pair(bv0, aw0, bv1, aw1);
-        u = 2;
-      } else {
-        f32x4 bv[NBW], aw[MB];
-        read_unit(Hb, Ab, wo(), ao(), bv, aw);
-        issue_next();
-        mma_f16_single(bv, aw);
-        advance();
-        u = 1;
-      }
       for (; u + 2 <= units; u += 2) {
         f32x4 bv0[NBW], aw0[MB], bv1[NBW], aw1[MB];
         read_unit(Hb, Ab, wo(), ao(), bv0, aw0);
@@ -326,13 +313,17 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
     }
   };
 
-  wait_vmem();
-  __syncthreads();
+  __syncthreads();   // stage 0 is in LDS
   for (int st = 0; st < nst; ++st) {
-    update_weight_offsets(st + 1);
     compute(st);
-    wait_vmem();          // this wave's copies of stage st+1 have landed
-    __syncthreads();      // ... everyone's, and buffer st&1 may be refilled
+    // stage st+1 (loaded one stage ago) into the buffer stage st-1 used, then
+    // the loads of stage st+2, which have all of stage st+1 to land
+    if (st + 1 < nst) write_stage((st + 1) & 1);
+    if (st + 2 < nst) {
+      update_weight_offsets(st + 2);
+      load_stage(st + 2);
+    }
+    __syncthreads();   // stage st+1 is in LDS, buffer st&1 may be refilled
   }
 
   // epilogue: register r of block (m, b) holds input channel

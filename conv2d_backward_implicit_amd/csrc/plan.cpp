@@ -138,12 +138,17 @@ static int finalize_divisors(PhaseDesc* d) {
   if (qp * pt4 >= lim) return CONV2D_ERR_OVERFLOW;
   if ((wb + d->ntv + 1024) * wb >= lim) return CONV2D_ERR_OVERFLOW;
   if (int64_t(d->th) * d->tw * tw >= lim) return CONV2D_ERR_OVERFLOW;
+  // copy-batch numerators: batches of a stage, weight pairs of a quad
+  if (int64_t(kStageFloats) * std::max(copy_blocks(*d), 1) >= lim) return CONV2D_ERR_OVERFLOW;
+  if ((qp + 256) * std::max(d->pt, 1) >= lim) return CONV2D_ERR_OVERFLOW;
   d->m_roww = fast_div_magic(uint32_t(roww));
   d->m_wb = fast_div_magic(uint32_t(wb));
   d->m_tw = fast_div_magic(uint32_t(tw));
   d->m_slots4 = fast_div_magic(uint32_t(slots4));
   d->m_qp = fast_div_magic(uint32_t(qp));
   d->m_pt4 = fast_div_magic(uint32_t(pt4));
+  d->m_pt = fast_div_magic(uint32_t(std::max(d->pt, 1)));
+  d->m_blocks = fast_div_magic(uint32_t(std::max(copy_blocks(*d), 1)));
   return CONV2D_OK;
 }
 
@@ -321,6 +326,7 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
       c.qp = int32_t(qp);
       c.wfl = int32_t(16 * cg * slots);
       c.used = int32_t(16 * cg * slots + wt);
+      if (stage_batches(c) > v.wm * v.wn * batches_per_wave(v)) continue;
       const double per_px = tile_cost(c, Co, v, v.half ? 2 : 1) / double(ntv);
       if (!found || per_px < best * 0.999) {
         found = true;

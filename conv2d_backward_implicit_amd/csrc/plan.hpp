@@ -71,6 +71,8 @@ struct PhaseDesc {
   uint32_t m_slots4;   // d = 4 * slots
   uint32_t m_qp;       // d = qp
   uint32_t m_pt4;      // d = 4 * pt
+  uint32_t m_pt;       // d = pt
+  uint32_t m_blocks;   // d = copy blocks of a quad (window + weight blocks)
 };
 
 // By-value kernel argument block of one launch.
@@ -101,6 +103,12 @@ struct Variant {
 
 // Floats of one stage buffer of a variant.
 constexpr int stage_floats(const Variant& v) { return v.half ? kStageFloatsHalf : kStageFloats; }
+
+// Copy batches (of 256 floats) one wave of a variant copies per stage at
+// most; a stage shape is usable only if its batches fit in the waves.
+constexpr int batches_per_wave(const Variant& v) {
+  return (stage_floats(v) / 256 + v.wm * v.wn - 1) / (v.wm * v.wn);
+}
 
 constexpr Variant kVariants[] = {
     // fp32, one workgroup per CU

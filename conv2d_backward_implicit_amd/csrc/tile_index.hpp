@@ -163,18 +163,19 @@ C2B_HD void stage_split(const TileCtx& c, int st, int* co0, int* grp) {
 //           floats apart (a multiple of 64): a lane reads the 4 channels of
 //           one (ci, tap) with one 16-byte read; pt is odd, so the 16 lanes
 //           of a group (consecutive ci) hit 16 disjoint sets of 4 banks.
-// Both are filled by buffer loads that write LDS directly: copy instruction
-// i of wave w fills floats i*threads + 64w + [0, 64) of the stage buffer.
-// wfl and used are multiples of 64, so one instruction never mixes window
-// and weights.
+// Both are filled by buffer loads that write LDS directly, 64 floats per
+// instruction (see the copy items below).
 template <int WM, int WN, int MB, int NBW, int SF>
 struct MMGeom {
   static constexpr int kThreads = 64 * WM * WN;
   static constexpr int kMT = 16 * WM * MB;            // channels per tile
   static constexpr int kNTL = 16 * NBW * WN;          // pixel lanes per tile
   static constexpr int kSF = SF;                      // floats per stage buffer
-  static constexpr int kCopies = (SF + kThreads - 1) / kThreads;
-  static_assert(SF % 64 == 0, "whole copy instructions");
+  static constexpr int kWaves = WM * WN;
+  // copy batches per wave and stage (the planner only picks stage shapes
+  // whose batches fit: at most kWaves * kBatches of them)
+  static constexpr int kBatches = (SF / 256 + kWaves - 1) / kWaves;
+  static_assert(SF % 256 == 0, "whole copy batches");
 };
 
 // Tile-local pixel of block b of pixel group ng, lane c16.
@@ -215,36 +216,80 @@ C2B_HD int mm_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp)
   return (co * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
 }
 
-// The same cells as mm_window_cell / mm_weight_cell for lane `lane` of the
-// copy instruction whose 64 floats start at f0 (window) or e0 (weights), a
-// multiple of 64: such an instruction never crosses a channel quad (4*slots
-// and qp are multiples of 64), so the quad and the instruction's first slot
-// or weight are wave-uniform and computed once, on the scalar unit.
-C2B_HD int mm_window_cell_at(const TileCtx& c, const LaunchArgs& a, int f0, int lane) {
-  const PhaseDesc& P = c.P;
-  if (c.ntaps == 0 || f0 >= P.wfl) return -1;
-  const int cq = fast_div(f0, P.m_slots4);
-  const int slot = ((f0 - cq * 4 * P.slots) >> 2) + (lane >> 2);
-  if (slot >= c.R * c.roww) return -1;
-  const int r = fast_div(slot, P.m_roww);
-  const int oh = c.oh_base + r, ow = c.ow_base + (slot - r * c.roww);
-  if ((unsigned)oh >= (unsigned)a.OH || (unsigned)ow >= (unsigned)a.OW) return -1;
-  return (4 * cq + (lane & 3)) * (a.OH * a.OW) + oh * a.OW + ow;
+// ---------------------------------------------------------------------------
+// Copy batches.  A stage buffer's window holds 4*cg channel quads of `slots`
+// slots (4 channels each); its weights hold 4*cg quads of qp/4 (ci, tap)
+// pairs (4 output channels each).  A batch fills 64 consecutive slots (a
+// window block) or pairs (a weight block) of one quad: lane l loads the 4
+// channels of slot / pair 64*block + l with 4 loads, one per channel -- the
+// 64 lanes of a load read consecutive grad_out pixels of one row segment,
+// or consecutive taps of consecutive input channels -- and stores them to
+// LDS with one 16-byte write.  Blocks [0, WB) are window blocks, [WB, WB+PB)
+// weight blocks; batch k of a stage is block k mod (WB+PB) of quad
+// k / (WB+PB), and wave w copies batches w, w + waves, w + 2*waves, ...
+// A lane's source offset depends on the quad only through a per-channel
+// constant (a grad_out plane, or a weight row), added to a per-lane offset.
+// Padding lanes (outside the image or the window, past the tap group or the
+// tile's channels) get kPadOffset: 2^31 plus any channel constant (below
+// 2^31, as the planner bounds a stage's byte ranges) stays at or beyond every
+// buffer resource's range, so such loads return 0.
+constexpr uint32_t kPadOffset = 0x80000000u;
+
+C2B_HD int window_blocks(const PhaseDesc& P) { return (P.slots + 63) / 64; }
+C2B_HD int weight_blocks(const PhaseDesc& P) { return (P.qp / 4 + 63) / 64; }
+C2B_HD int copy_blocks(const PhaseDesc& P) { return window_blocks(P) + weight_blocks(P); }
+C2B_HD int stage_batches(const PhaseDesc& P) { return 4 * P.cg * copy_blocks(P); }
+
+// Batch k -> (block, quad).
+C2B_HD void batch_split(const PhaseDesc& P, int k, int* block, int* quad) {
+  *quad = fast_div(k, P.m_blocks);
+  *block = k - *quad * copy_blocks(P);
 }
 
-template <int MT>
-C2B_HD int mm_weight_cell_at(const TileCtx& c, const LaunchArgs& a, int e0, int lane, int grp) {
+// Byte offset, within a grad_out channel plane, of the pixel of window slot
+// 64*block + lane (kPadOffset if padding).
+C2B_HD uint32_t window_lane_offset(const TileCtx& c, const LaunchArgs& a, int block, int lane) {
   const PhaseDesc& P = c.P;
-  if (c.ntaps == 0 || e0 < 0 || e0 >= 4 * P.cg * P.qp) return -1;
-  const int cq = fast_div(e0, P.m_qp);
-  const int r = e0 - cq * P.qp + lane;
-  const int ci = fast_div(r, P.m_pt4);
-  const int r2 = r - ci * 4 * P.pt;
-  const int t = r2 >> 2;
-  if (ci >= MT || t >= P.tg) return -1;
+  const int slot = 64 * block + lane;
+  if (c.ntaps == 0 || slot >= c.R * c.roww) return kPadOffset;
+  const int r = fast_div(slot, P.m_roww);
+  const int oh = c.oh_base + r, ow = c.ow_base + (slot - r * c.roww);
+  if ((unsigned)oh >= (unsigned)a.OH || (unsigned)ow >= (unsigned)a.OW) return kPadOffset;
+  return uint32_t((oh * a.OW + ow) * 4);
+}
+
+// Byte offset, within a weight row of one output channel, of weight pair
+// 64*wblock + lane of tap group `grp` (kPadOffset if padding).
+template <int MT>
+C2B_HD uint32_t weight_lane_offset(const TileCtx& c, const LaunchArgs& a, int wblock, int lane,
+                                   int grp) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0) return kPadOffset;
+  const int pr = 64 * wblock + lane;
+  const int ci = fast_div(pr, P.m_pt);
+  const int t = pr - ci * P.pt;
+  if (ci >= MT || t >= P.tg) return kPadOffset;
   const int tap = grp * P.tg + t;
-  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return -1;
-  return ((4 * cq + (r2 & 3)) * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
+  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return kPadOffset;
+  return uint32_t(((c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap)) * 4);
+}
+
+// Bytes between consecutive channels: grad_out planes, or weight rows.
+C2B_HD uint32_t window_channel_bytes(const LaunchArgs& a) { return uint32_t(4 * a.OH * a.OW); }
+C2B_HD uint32_t weight_channel_bytes(const LaunchArgs& a) {
+  return uint32_t(4 * a.Ci * a.KH * a.KW);
+}
+
+// Stage-buffer float of the 16-byte LDS write of lane `lane` of a batch, or
+// -1 if the lane is past its quad's slots / pairs (no write).
+C2B_HD int batch_lds_float(const PhaseDesc& P, int block, int quad, int lane) {
+  const int WB = window_blocks(P);
+  if (block < WB) {
+    const int slot = 64 * block + lane;
+    return slot < P.slots ? (quad * P.slots + slot) * 4 : -1;
+  }
+  const int pr = 64 * (block - WB) + lane;
+  return pr < P.qp / 4 ? P.wfl + quad * P.qp + pr * 4 : -1;
 }
 
 }  // namespace c2b
