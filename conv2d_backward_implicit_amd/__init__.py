@@ -22,7 +22,7 @@ __all__ = [
     "Conv2dParams", "Conv2dError", "PlanInfo", "grad_input", "grad_input_into",
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
     "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
-    "variant_is_f16", "conv2d_grad_input_variant",
+    "variant_is_f16", "variant_uses_column_taps", "conv2d_grad_input_variant",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -40,6 +40,7 @@ EXPORTED_SYMBOLS = (
     "conv2d_check_indexing",
     "conv2d_num_variants",
     "conv2d_variant_is_f16",
+    "conv2d_variant_uses_column_taps",
     "conv2d_grad_input_variant",
     "conv2d_check_indexing_variant",
 )
@@ -137,6 +138,8 @@ def load_library():
         lib.conv2d_num_variants.restype = ctypes.c_int
         lib.conv2d_variant_is_f16.argtypes = [ctypes.c_int]
         lib.conv2d_variant_is_f16.restype = ctypes.c_int
+        lib.conv2d_variant_uses_column_taps.argtypes = [ctypes.c_int]
+        lib.conv2d_variant_uses_column_taps.restype = ctypes.c_int
         lib.conv2d_grad_input_variant.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, P, ctypes.c_int,
                                                   ctypes.c_void_p]
@@ -204,6 +207,11 @@ def num_variants() -> int:
 def variant_is_f16(variant: int) -> int:
     """1 (f16-staged), 0 (fp32) or a negative status for a bad index."""
     return int(load_library().conv2d_variant_is_f16(int(variant)))
+
+
+def variant_uses_column_taps(variant: int) -> int:
+    """1 (column taps in the matrix rows), 0, or a negative status."""
+    return int(load_library().conv2d_variant_uses_column_taps(int(variant)))
 
 
 def conv2d_grad_input(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,

@@ -36,7 +36,7 @@ struct Failure {
     }                                                           \
   } while (0)
 
-template <int WM, int WN, int MB, int NBW, int SF>
+template <int WM, int WN, int MB, int NBW, int SF, bool CM>
 void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int kStageFloats = SF;
@@ -49,12 +49,22 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
   const int64_t HW = int64_t(a.H) * a.W;
 
   for (int bid = 0; bid < a.total_tiles; ++bid) {
-    const TileCtx c = decode_tile<MT>(a, bid);
+    const TileCtx c = decode_tile(a, bid);
     const PhaseDesc& P = c.P;
     C2B_REQUIRE(c.n >= 0 && c.n < a.N, "bid %d n %d", bid, c.n);
     C2B_REQUIRE(c.band >= 0 && c.band < P.nbands, "bid %d band %d", bid, c.band);
     C2B_REQUIRE(c.ci0 >= 0 && c.ci0 < a.Ci, "bid %d ci0 %d", bid, c.ci0);
-    C2B_REQUIRE(c.npx >= 1 && c.npx <= P.ntv && P.ntv <= G::kNTL, "bid %d npx %d", bid, c.npx);
+    C2B_REQUIRE(c.npx >= 1 && c.npx <= P.ntv && (CM || P.ntv <= G::kNTL), "bid %d npx %d", bid,
+                c.npx);
+    C2B_REQUIRE(a.cm == (CM ? 1 : 0) && (CM ? a.cit * a.twm <= MT : a.cit == MT),
+                "launch matrix rows: cm %d cit %d twm %d", a.cm, a.cit, a.twm);
+    if (CM) {
+      // whole rows of the band per tile, and one lane per window point
+      C2B_REQUIRE(c.p0 % P.wb == 0 && c.npx % P.wb == 0, "bid %d: cm tile not whole rows", bid);
+      C2B_REQUIRE(c.R - P.th + 1 == c.npx / P.wb, "bid %d: cm window rows", bid);
+      C2B_REQUIRE(c.ntaps == 0 || (cm_points(c) <= G::kNTL && P.tw <= a.twm),
+                  "bid %d: cm points %d", bid, cm_points(c));
+    }
     const int SLOTS = P.slots, QP = P.qp, PT = P.pt, TG = P.tg, CG = P.cg;
     const int CH = 16 * CG;
     if (c.ntaps > 0) {
@@ -74,12 +84,14 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
                   "stage byte range");
     }
     std::vector<unsigned char> covered(size_t(c.nstages) * size_t(c.ntaps > 0 ? P.used : 0), 0);
+    std::vector<unsigned char> qrows(CM ? size_t(16) * (16 * NBW * WN + 4) : 0, 0);
     for (int tid = 0; tid < NT; ++tid) {
       const int lane = tid & 63, wave = tid >> 6;
       const int mg = wave % WM, ng = wave / WM, g = lane >> 4, c16 = lane & 15;
       int bb[NBW], aq[MB];
       for (int b = 0; b < NBW; ++b)
-        bb[b] = (g * SLOTS + window_base(c, mm_local(b, ng, c16, WN))) * 16;
+        bb[b] = (g * SLOTS + (CM ? window_base_cm(c, mm_local(b, ng, c16, WN))
+                                 : window_base(c, mm_local(b, ng, c16, WN)))) * 16;
       for (int m = 0; m < MB; ++m) aq[m] = (g * QP + mm_channel(m, mg, c16, MB) * 4 * PT) * 4;
       for (int st = 0; st < c.nstages; ++st) {
         int co0, grp;
@@ -103,7 +115,7 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
                       "batch %d split", k);
           const bool win = block < WB;
           const uint32_t off = win ? window_lane_offset(c, a, block, lane)
-                                   : weight_lane_offset<MT>(c, a, block - WB, lane, grp);
+                                   : weight_lane_offset<MT, CM>(c, a, block - WB, lane, grp);
           const uint32_t ch = win ? window_channel_bytes(a) : weight_channel_bytes(a);
           const int64_t range = win ? int64_t(nco) * OHOW * 4 : int64_t(nco) * cstride * 4;
           C2B_REQUIRE(off == kPadOffset || off % 4 == 0, "unaligned copy offset");
@@ -138,27 +150,38 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
               C2B_REQUIRE(gi >= 0 && gi < go_size, "grad_out read %lld", (long long)gi);
             } else {
               const int e = cell - P.wfl;
-              const int o = mm_weight_cell<MT>(c, a, e, grp);
+              const int o = mm_weight_cell<MT, CM>(c, a, e, grp);
               if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) {
                 C2B_REQUIRE(!reads, "weight cell %d should read 0", e);
                 continue;
               }
               C2B_REQUIRE(reads && int64_t(o64) == int64_t(o) * 4, "weight cell %d offset", e);
-              const int cq2 = e / QP, r = e % QP, ci = r / (4 * PT), t = (r % (4 * PT)) / 4;
+              const int cq2 = e / QP, r = e % QP, m = r / (4 * PT), t = (r % (4 * PT)) / 4;
               const int co = 4 * cq2 + r % 4;
-              C2B_REQUIRE(co < nco && ci < MT && t < ntg, "weight cell %d", e);
-              const int64_t want = (int64_t(co0 + co) * a.Ci + c.ci0 + ci) * KHW +
-                                   tap_kidx(P, a, tap0 + t);
+              C2B_REQUIRE(co < nco && m < MT && t < ntg, "weight cell %d", e);
+              // matrix row m: input channel ci0 + m at tap tap0 + t of the
+              // class, or (cm) channel ci0 + m / twm at row tap tap0 + t and
+              // column tap m mod twm
+              int64_t want;
+              if (CM) {
+                const int cl = m / a.twm, l = m % a.twm, jt = tap0 + t;
+                C2B_REQUIRE(l < P.tw && cl < a.cit && jt < P.th, "cm weight cell %d", e);
+                want = (int64_t(co0 + co) * a.Ci + c.ci0 + cl) * KHW +
+                       (P.rh + a.S * jt) * a.KW + (P.rw + a.S * l);
+              } else {
+                want = (int64_t(co0 + co) * a.Ci + c.ci0 + m) * KHW + tap_kidx(P, a, tap0 + t);
+              }
               const int64_t wi = int64_t(co0) * cstride + o;
               C2B_REQUIRE(wi == want && wi >= 0 && wi < w_size, "weight element");
             }
           }
         }
-        // unit reads, in the kernel's order
-        const int j0 = tap0 / P.tw, l0 = tap0 % P.tw;
+        // unit reads, in the kernel's order (cm: row taps only)
+        const int twl = CM ? 1 : P.tw;
+        const int j0 = tap0 / twl, l0 = tap0 % twl;
         int cgi = 0, t = 0, j = j0, l = l0;
         for (int u = 0; u < CG * ntg; ++u) {
-          C2B_REQUIRE(cgi < CG && j * P.tw + l == tap0 + t, "unit order");
+          C2B_REQUIRE(cgi < CG && j * twl + l == tap0 + t, "unit order");
           const int wo = cgi * SLOTS * 64 + tap_window_offset(c, j, l) * 16;
           const int ao = cgi * QP * 16 + t * 16;
           for (int m = 0; m < MB; ++m) {
@@ -177,7 +200,16 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
             const int cell = byte / 16, cq = cell / SLOTS, slot = cell % SLOTS;
             C2B_REQUIRE(cq == 4 * cgi + g, "window quad of unit");
             const int local = mm_local(b, ng, c16, WN);
-            if (local < c.npx) {
+            if (CM) {
+              if (local < cm_points(c)) {
+                // point (r, u) at row tap j: grad_out row i' + ch - j, window column u
+                const int r = local / c.roww, uu = local % c.roww;
+                C2B_REQUIRE(slot < c.R * c.roww && l == 0, "slot beyond window");
+                C2B_REQUIRE(c.oh_base + slot / c.roww == c.i_start + r + P.ch - j &&
+                                slot % c.roww == uu,
+                            "row tap %d reads the wrong grad_out element", j);
+              }
+            } else if (local < c.npx) {
               C2B_REQUIRE(slot < c.R * c.roww, "slot beyond window");
               const int qq = c.p0 + local, ip = qq / P.wb, jj = c.band * P.wb + qq % P.wb;
               C2B_REQUIRE(c.oh_base + slot / c.roww == ip + P.ch - j &&
@@ -190,11 +222,28 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
             ++cgi;
             j = j0;
             l = l0;
-          } else if (++l == P.tw) {
+          } else if (++l == twl) {
             l = 0;
             ++j;
           }
         }
+      }
+      if (CM) {
+        // cm epilogue, part 1: matrix row 4g + r of block b goes to LDS float
+        // (4g + r) * QR + point
+        constexpr int QR = 16 * NBW * WN + 4;
+        C2B_REQUIRE(16 * QR <= 2 * SF, "cm rows exceed the stage buffers");
+        if (c.ntaps > 0)
+          for (int b = 0; b < NBW; ++b) {
+            const int local = mm_local(b, ng, c16, WN);
+            for (int r = 0; r < 4; ++r) {
+              const int f = (4 * g + r) * QR + local;
+              C2B_REQUIRE(f >= 0 && f < 16 * QR && local < QR - 4, "cm row write %d", f);
+              C2B_REQUIRE(qrows[size_t(f)] == 0, "cm row cell %d written twice", f);
+              qrows[size_t(f)] = 1;
+            }
+          }
+        continue;   // part 2 (the column-tap sums) runs per tile below
       }
       // epilogue
       for (int b = 0; b < NBW; ++b) {
@@ -218,13 +267,44 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
     for (size_t i = 0; i < covered.size(); ++i)
       C2B_REQUIRE(covered[i] == 1, "bid %d: stage %d cell %d never copied", bid,
                   int(i / size_t(P.used)), int(i % size_t(P.used)));
+    if (CM) {
+      // cm epilogue, part 2: every class pixel (i', j') of the tile, for every
+      // channel of the tile, adds matrix row cl*twm + l at point
+      // (r, j'' + tw - 1 - l) over its tw column taps l; that point's window
+      // column must be the grad_out column j' + cw - l of the gather rule,
+      // and the row must hold channel ci0 + cl at column tap l
+      constexpr int QR = 16 * NBW * WN + 4;
+      const int rows = c.R - P.th + 1;
+      for (int cl = 0; cl < a.cit && c.ci0 + cl < a.Ci; ++cl)
+        for (int q = 0; q < rows * P.wb; ++q) {
+          const int r = q / P.wb, jj = q % P.wb, col = c.band * P.wb + jj;
+          if (col >= P.wp) continue;
+          for (int l = 0; c.ntaps > 0 && l < P.tw; ++l) {
+            const int pt = r * c.roww + jj + P.tw - 1 - l, m = cl * a.twm + l;
+            C2B_REQUIRE(pt >= 0 && pt < cm_points(c) && m < MT, "cm sum point %d", pt);
+            C2B_REQUIRE(qrows[size_t(m) * QR + pt] == 1, "cm sum reads an unwritten row cell");
+            C2B_REQUIRE(c.ow_base + pt % c.roww == col + P.cw - l, "cm column tap %d", l);
+            // weight_source of row m at any row tap is channel ci0 + cl, column l
+            const int src = weight_source<MT, CM>(c, a, m, 0, 0);
+            C2B_REQUIRE(src >= 0 && src / (a.KH * a.KW) == c.ci0 + cl &&
+                            (src % (a.KH * a.KW)) % a.KW == P.rw + a.S * l,
+                        "cm row %d is not channel %d column tap %d", m, c.ci0 + cl, l);
+          }
+          const int ih = P.ih0 + a.S * (c.i_start + r), iw = P.iw0 + a.S * col;
+          C2B_REQUIRE(ih < a.H && iw < a.W, "cm pixel (%d,%d) outside the image", ih, iw);
+          const int64_t gi = int64_t(c.n) * a.Ci * HW + int64_t(c.ci0 + cl) * HW +
+                             int64_t(ih) * a.W + iw;
+          C2B_REQUIRE(written[gi] == 0, "grad_input element %lld written twice", (long long)gi);
+          written[gi] = 1;
+        }
+    }
   }
 }
 
 template <int V>
 void check_variant(const LaunchArgs& la, std::vector<unsigned char>& written) {
   constexpr Variant v = kVariants[V];
-  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v)>(la, written);
+  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v), v.cm != 0>(la, written);
 }
 
 template <int... Vs>

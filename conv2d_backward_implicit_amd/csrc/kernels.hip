@@ -71,9 +71,10 @@ __device__ __forceinline__ f16x8 join(f16x4 lo, f16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <bool F16, int WM, int WN, int MB, int NBW, int SF>
+template <bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
 __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
     const LaunchArgs a) {
+  static_assert(!CM || (WM == 1 && MB == 1 && !F16), "cm: one fp32 matrix block of rows");
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int MT = G::kMT, NW = G::kWaves, NJ = G::kBatches;
   constexpr int kStageFloats = SF;   // this instance's stage buffer
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int mg = wave % WM, ng = wave / WM;
   const int g = lane >> 4, c16 = lane & 15;
-  const TileCtx c = decode_tile<MT>(a, blockIdx.x);
+  const TileCtx c = decode_tile(a, blockIdx.x);
   const PhaseDesc& P = c.P;
   const int OHOW = a.OH * a.OW;
   const int cstride = a.Ci * a.KH * a.KW;
@@ -133,7 +134,7 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
       } else {
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        off[j] = weight_lane_offset<MT>(c, a, block - WB, ln, grp);
+        off[j] = weight_lane_offset<MT, CM>(c, a, block - WB, ln, grp);
       }
     }
     wgroup = grp;
@@ -192,7 +193,8 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
   int bb[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b)
-    bb[b] = (g * P.slots + window_base(c, mm_local(b, ng, c16, WN))) * 16;
+    bb[b] = (g * P.slots + (CM ? window_base_cm(c, mm_local(b, ng, c16, WN))
+                               : window_base(c, mm_local(b, ng, c16, WN)))) * 16;
   int aq[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) aq[m] = (g * P.qp + mm_channel(m, mg, c16, MB) * 4 * P.pt) * 4;
@@ -271,7 +273,8 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
     const int units = P.cg * ntg;
     const char* Hb = reinterpret_cast<const char*>(lds + buf * kStageFloats);
     const char* Ab = Hb + P.wfl * 4;
-    const int j0 = tap0 / P.tw, l0 = tap0 - j0 * P.tw;
+    const int twl = CM ? 1 : P.tw;   // taps per window row in the tap loop
+    const int j0 = tap0 / twl, l0 = tap0 - j0 * twl;
     int cgi = 0, t = 0, j = j0, l = l0;
     auto wo = [&]() __attribute__((always_inline)) {
       return cgi * P.slots * 64 + tap_window_offset(c, j, l) * 16;
@@ -283,7 +286,7 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
         ++cgi;
         j = j0;
         l = l0;
-      } else if (++l == P.tw) {
+      } else if (++l == twl) {
         l = 0;
         ++j;
       }
@@ -326,10 +329,55 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
     __syncthreads();   // stage st+1 is in LDS, buffer st&1 may be refilled
   }
 
-  // epilogue: register r of block (m, b) holds input channel
-  // (mg*MB + m)*16 + 4g + r, pixel (b*WN + ng)*16 + c16
   float* gi_n = a.gi + (size_t)c.n * a.Ci * (a.H * a.W);
   const size_t HW = (size_t)a.H * a.W;
+  if constexpr (CM) {
+    // cm epilogue: register r of block b holds matrix row 4g + r (input
+    // channel ci0 + row / twm, column tap row mod twm) at point
+    // (b*WN + ng)*16 + c16.  The rows go to LDS (the stage buffers are free
+    // after the last barrier), then every pixel (i', j') of the tile adds its
+    // tw column taps: tap l of the pixel sits at window column
+    // j' + tw - 1 - l of the pixel's row.
+    if (nst == 0) {
+      // a class no tap reaches: zeros
+      const int rows = c.R - P.th + 1;
+      for (int cl = 0; cl < a.cit && c.ci0 + cl < a.Ci; ++cl)
+        for (int q = tid; q < rows * P.wb; q += 64 * WM * WN) {
+          const int r = fast_div(q, P.m_wb), jj = q - r * P.wb;
+          const int col = c.band * P.wb + jj;
+          if (col >= P.wp) continue;
+          gi_n[(c.ci0 + cl) * HW + (P.ih0 + a.S * (c.i_start + r)) * a.W + P.iw0 + a.S * col] =
+              0.0f;
+        }
+      return;
+    }
+    constexpr int QP = 16 * NBW * WN + 4;   // floats per matrix row in LDS
+    static_assert(16 * QP <= 2 * SF, "cm rows fit the stage buffers");
+#pragma unroll
+    for (int b = 0; b < NBW; ++b) {
+      const int local = mm_local(b, ng, c16, WN);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lds[(4 * g + r) * QP + local] = acc[0][b][r];
+    }
+    __syncthreads();
+    const int rows = c.R - P.th + 1;
+    for (int cl = 0; cl < a.cit && c.ci0 + cl < a.Ci; ++cl) {
+      float* gi_c = gi_n + (c.ci0 + cl) * HW;
+      const float* qrow = lds + cl * a.twm * QP;
+      for (int q = tid; q < rows * P.wb; q += 64 * WM * WN) {
+        const int r = fast_div(q, P.m_wb), jj = q - r * P.wb;
+        const int col = c.band * P.wb + jj;
+        if (col >= P.wp) continue;
+        const int pt0 = r * c.roww + jj + P.tw - 1;   // column tap 0
+        float v = 0.0f;
+        for (int l = 0; l < P.tw; ++l) v += qrow[l * QP + pt0 - l];
+        gi_c[(P.ih0 + a.S * (c.i_start + r)) * a.W + P.iw0 + a.S * col] = v;
+      }
+    }
+    return;
+  }
+  // epilogue: register r of block (m, b) holds input channel
+  // (mg*MB + m)*16 + 4g + r, pixel (b*WN + ng)*16 + c16
 #pragma unroll
   for (int b = 0; b < NBW; ++b) {
     const int po = output_offset(c, a, mm_local(b, ng, c16, WN));
@@ -347,7 +395,8 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
 template <int V>
 void launch_variant(const LaunchArgs& la, hipStream_t st) {
   constexpr Variant v = kVariants[V];
-  hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw, stage_floats(v)>),
+  hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw, stage_floats(v),
+                                           v.cm != 0>),
                      dim3(la.total_tiles), dim3(64 * v.wm * v.wn), 0, st, la);
 }
 

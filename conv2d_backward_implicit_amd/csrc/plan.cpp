@@ -103,7 +103,8 @@ static void make_classes(const conv2d_params* p, std::vector<PhaseDesc>* out) {
   }
 }
 
-static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks) {
+static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks, int64_t cit, int cm,
+                                int64_t twm) {
   LaunchArgs la;
   std::memset(&la, 0, sizeof(la));
   la.N = int32_t(p->batch);
@@ -119,6 +120,9 @@ static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks) {
   la.OH = int32_t(p->out_h);
   la.OW = int32_t(p->out_w);
   la.ciblocks = int32_t(ciblocks);
+  la.cit = int32_t(cit);
+  la.cm = cm;
+  la.twm = int32_t(twm);
   return la;
 }
 
@@ -154,11 +158,11 @@ static int finalize_divisors(PhaseDesc* d) {
 
 // Split classes (already sorted heaviest first) into launches of at most
 // kMaxPhasesPerLaunch classes.
-static int emit_launches(const conv2d_params* p, int64_t ciblocks, int variant,
-                         const std::vector<PhaseDesc>& phases,
+static int emit_launches(const conv2d_params* p, int64_t ciblocks, int64_t cit, int64_t twm,
+                         int variant, const std::vector<PhaseDesc>& phases,
                          std::vector<LaunchArgs>* launches, conv2d_plan_info* info) {
   for (size_t base = 0; base < phases.size(); base += kMaxPhasesPerLaunch) {
-    LaunchArgs la = launch_header(p, ciblocks);
+    LaunchArgs la = launch_header(p, ciblocks, cit, kVariants[variant].cm, twm);
     la.variant = variant;
     int64_t total = 0;
     const size_t end = std::min(phases.size(), base + kMaxPhasesPerLaunch);
@@ -237,6 +241,22 @@ bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* 
   return false;
 }
 
+// cm tiling: a tile is `rows` whole rows of a band `wb` wide; its lanes are
+// the rows x (wb + tw - 1) window points (at most ntl), and its window of
+// rows + th - 1 rows must fit `max_slots` slots per channel.  Fills the
+// candidate for band count nb; false if nothing fits.
+bool cm_tiling(const PhaseDesc& d, int64_t nb, int64_t ntl, int64_t max_slots, int64_t* wb_out,
+               int64_t* rows_out, int64_t* slots_out) {
+  const int64_t wb = ceil_div(d.wp, nb), roww = wb + d.tw - 1;
+  int64_t rows = std::min<int64_t>({ntl / roww, int64_t(d.hp), max_slots / roww - d.th + 1});
+  if (rows < 1) return false;
+  rows = ceil_div(d.hp, ceil_div(d.hp, rows));       // equal row counts per tile
+  *wb_out = wb;
+  *rows_out = rows;
+  *slots_out = ceil_div((rows + d.th - 1) * roww, 16) * 16;
+  return *slots_out <= max_slots;
+}
+
 // Cost model of one tile, in CU cycles, with constants fitted (least squares
 // on log time) to forced-variant timings of every kernel variant on the four
 // large workloads on MI355X:
@@ -257,11 +277,12 @@ constexpr double kStageCycles = 2000.0;       // barrier, copy issue and wait pe
 constexpr double kTileCycles = 45000.0;       // set-up, first copies, epilogue
 constexpr double kCopyBytesPerCycle = 12.0;   // gathered copies into LDS, per CU
 constexpr double kSharedStageVisible = 0.4;   // stage overhead left when sharing a CU
+constexpr double kCmEpilogueCycles = 4000.0;   // cm: rows through LDS, column-tap sums
 
 double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v, int share) {
   (void)Co;
   if (d.th == 0) return kTileCycles;
-  const int64_t ntaps = int64_t(d.th) * d.tw;
+  const int64_t ntaps = v.cm ? int64_t(d.th) : int64_t(d.th) * d.tw;
   const double wps = v.wm * v.wn / 4.0;
   const double mfma = wps * v.mb * v.nbw * (v.f16 ? 8.0 : 128.0) * share;
   const double lds = 8.0 * v.wm * v.wn * (v.nbw + v.mb) * share;
@@ -269,7 +290,7 @@ double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v, int share) {
                       kUnitLatency / std::max(1.0, wps * share);
   const double copy = double(stage_floats(v)) * 4.0 / kCopyBytesPerCycle * share;
   const double stage = kStageCycles * (share == 2 ? kSharedStageVisible : 1.0);
-  double cycles = kTileCycles;
+  double cycles = kTileCycles + (v.cm ? kCmEpilogueCycles : 0.0);
   for (int64_t g = 0; g < d.ngroups; ++g) {
     const int64_t ntg = std::min<int64_t>(d.tg, ntaps - g * d.tg);
     const int64_t u = int64_t(d.cg) * ntg;
@@ -288,11 +309,13 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
     d->wb = d->wp;
     d->nbands = 1;
     d->ntv = int32_t(std::min<int64_t>(ntl, int64_t(d->hp) * d->wp));
+    if (v.cm)   // whole rows
+      d->ntv = int32_t(std::min<int64_t>(d->hp, std::max<int64_t>(1, ntl / d->wp)) * d->wp);
     d->ptiles = int32_t(ceil_div(int64_t(d->hp) * d->wp, d->ntv));
     d->cg = d->tg = d->ngroups = d->nchunks = d->slots = d->pt = d->qp = d->wfl = d->used = 0;
     return true;
   }
-  const int64_t ntaps = int64_t(d->th) * d->tw;
+  const int64_t ntaps = v.cm ? int64_t(d->th) : int64_t(d->th) * d->tw;
   const int64_t cg_useful = std::max<int64_t>(1, ceil_div(Co, 16));
   bool found = false;
   double best = 0.0;
@@ -310,9 +333,19 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
       const int64_t wt = 4 * cg * qp;
       const int64_t max_slots = (stage_floats(v) - wt) / (16 * cg) / 16 * 16;
       if (max_slots < 16) break;
+      // band candidates: the planner's own choice, or (cm) every band count
+      // up to 8
+      const int64_t ncand = v.cm ? std::min<int64_t>(8, d->wp) : 1;
+      for (int64_t nb = 1; nb <= ncand; ++nb) {
       PhaseDesc c = *d;
       int64_t wb, ntv, slots;
-      if (!choose_tiling(c, ntl, max_slots, &wb, &ntv, &slots)) continue;
+      if (v.cm) {
+        int64_t rows;
+        if (!cm_tiling(c, nb, ntl, max_slots, &wb, &rows, &slots)) continue;
+        ntv = rows * wb;
+      } else if (!choose_tiling(c, ntl, max_slots, &wb, &ntv, &slots)) {
+        continue;
+      }
       c.wb = int32_t(wb);
       c.nbands = int32_t(ceil_div(c.wp, wb));
       c.ntv = int32_t(ntv);
@@ -332,6 +365,7 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
         found = true;
         best = per_px;
         out = c;
+      }
       }
     }
   }
@@ -388,6 +422,13 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
 
   std::vector<PhaseDesc> classes;
   make_classes(p, &classes);
+  // cm variants: matrix rows per input channel (the widest class's column
+  // taps) and input channels per tile
+  const int64_t twm = ceil_div(p->kernel_w, p->stride);
+  const int64_t cm_cit = twm <= 16 ? 16 / twm : 0;
+  auto channels_per_tile = [&](const Variant& var) {
+    return var.cm ? cm_cit : 16 * int64_t(var.wm) * var.mb;
+  };
 
   int best_v = -1;
   double best_cost = 0.0;
@@ -395,7 +436,8 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   for (int v = 0; v < kNumVariants; ++v) {
     const Variant& var = kVariants[v];
     if (force_variant >= 0 ? v != force_variant : var.f16 != (f16 ? 1 : 0)) continue;
-    const int64_t vmt = 16 * int64_t(var.wm) * var.mb;
+    const int64_t vmt = channels_per_tile(var);
+    if (vmt < 1) continue;
     std::vector<PhaseDesc> phases = classes;
     bool ok = true;
     for (PhaseDesc& d : phases)
@@ -422,8 +464,9 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   if (best_v < 0) return CONV2D_ERR_UNSUPPORTED;
 
   const Variant& bv = kVariants[best_v];
-  const int64_t bmt = 16 * int64_t(bv.wm) * bv.mb;
-  const int64_t bci = ceil_div(Ci, bmt);
+  const int64_t bmt = 16 * int64_t(bv.wm) * bv.mb;   // matrix rows per tile
+  const int64_t bcit = channels_per_tile(bv);
+  const int64_t bci = ceil_div(Ci, bcit);
   for (PhaseDesc& d : best) {
     const int64_t tiles = N * d.nbands * int64_t(d.ptiles) * bci;
     if (tiles >= kI31) return CONV2D_ERR_OVERFLOW;
@@ -433,7 +476,8 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
       if (d.th == 0) info->zero_phases += 1;
       if (d.th > 0) {
         const int64_t lanes = 16 * int64_t(bv.nbw) * bv.wn;
-        const int64_t kpad = int64_t(d.nchunks) * 16 * d.cg * int64_t(d.th) * d.tw;
+        const int64_t kpad =
+            int64_t(d.nchunks) * 16 * d.cg * int64_t(d.th) * (bv.cm ? 1 : d.tw);
         info->macs += tiles * lanes * bmt * kpad;
       }
     }
@@ -441,7 +485,7 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   std::stable_sort(best.begin(), best.end(), [&](const PhaseDesc& a, const PhaseDesc& b) {
     return tile_cost(a, Co, bv, 1) > tile_cost(b, Co, bv, 1);
   });
-  return emit_launches(p, bci, best_v, best, launches, info);
+  return emit_launches(p, bci, bcit, twm, best_v, best, launches, info);
 }
 
 }  // namespace c2b
@@ -463,6 +507,11 @@ extern "C" int conv2d_num_variants(void) { return c2b::kNumVariants; }
 extern "C" int conv2d_variant_is_f16(int variant) {
   if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
   return c2b::kVariants[variant].f16;
+}
+
+extern "C" int conv2d_variant_uses_column_taps(int variant) {
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::kVariants[variant].cm;
 }
 
 extern "C" const char* conv2d_status_string(int status) {

@@ -81,7 +81,10 @@ struct LaunchArgs {
   const float* w;
   float* gi;
   int32_t N, Ci, H, W, Co, KH, KW, S, PH, PW, OH, OW;
-  int32_t ciblocks;    // ceil(Ci / channel tile)
+  int32_t ciblocks;    // ceil(Ci / cit)
+  int32_t cit;         // input channels per tile
+  int32_t cm;          // 1: column taps in the matrix rows (see Variant::cm)
+  int32_t twm;         // cm: matrix rows per input channel (widest class's tw)
   int32_t nphases;     // classes in this launch, heaviest first
   int32_t total_tiles; // workgroups in this launch
   int32_t variant;     // kernel instantiation (host side only)
@@ -92,6 +95,16 @@ struct LaunchArgs {
 // MB blocks of 16 input channels x NBW blocks of 16 pixels.  fp32 variants
 // multiply on v_mfma_f32_16x16x4_f32, f16 variants on
 // v_mfma_f32_16x16x32_f16 (pairs of units) and v_mfma_f32_16x16x16_f16.
+//
+// cm (column taps in the matrix rows, for few input channels): the 16 rows
+// of a tile's matrix block are (input channel, column tap l) pairs, twm rows
+// per channel, instead of 16 input channels; a stage's contraction runs over
+// output channels x row taps j only, and its "pixels" are the points (class
+// row, window column) of whole rows.  Each product row then holds, for one
+// channel and one column tap, the partial sum over all output channels and
+// row taps; the epilogue adds the tw partial sums of a pixel, which sit tw
+// window columns apart, through LDS.  With Ci = 3 and a 4-column class this
+// fills 12 of 16 rows, where one channel per row fills 3.
 struct Variant {
   int f16;   // 0: fp32 path, 1: f16-staged path
   int wm;    // waves along channels
@@ -99,6 +112,7 @@ struct Variant {
   int mb;    // 16-channel blocks per wave
   int nbw;   // 16-pixel blocks per wave
   int half;  // 1: half-size stage buffers, two workgroups per CU
+  int cm;    // 1: column taps in the matrix rows (wm = mb = 1, fp32)
 };
 
 // Floats of one stage buffer of a variant.
@@ -122,7 +136,10 @@ constexpr Variant kVariants[] = {
     {0, 4, 2, 1, 7, 1}, {0, 4, 2, 1, 5, 1}, {0, 4, 2, 1, 8, 1},
     // one 16-channel block per tile (few input channels)
     {0, 1, 8, 1, 7, 0}, {0, 1, 12, 1, 5, 0}, {0, 1, 16, 1, 4, 0}, {1, 1, 12, 1, 5, 0},
-    {1, 1, 8, 1, 7, 0}};
+    {1, 1, 8, 1, 7, 0},
+    // column taps in the matrix rows (few input channels)
+    {0, 1, 8, 1, 7, 0, 1}, {0, 1, 12, 1, 5, 0, 1}, {0, 1, 16, 1, 4, 0, 1},
+    {0, 1, 8, 1, 4, 1, 1}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b

@@ -59,7 +59,6 @@ C2B_HD int phase_of(const LaunchArgs& a, int bid) {
 // x mod 8 (one XCD: the dispatcher deals workgroups round-robin over the 8
 // XCDs) take one contiguous run of tiles, channel tile fastest, so tiles
 // that share grad_out rows and weights share that XCD's L2.
-template <int MT>
 C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   TileCtx c;
   c.P = a.ph[phase_of(a, bid)];
@@ -76,12 +75,12 @@ C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   t /= P.ptiles;
   c.band = t % P.nbands;
   c.n = t / P.nbands;
-  c.ci0 = ciblk * MT;
+  c.ci0 = ciblk * a.cit;
   const int bandpix = P.hp * P.wb;
   c.p0 = ptile * P.ntv;
   const int pend = imin(c.p0 + P.ntv, bandpix);
   c.npx = pend - c.p0;
-  c.ntaps = P.th * P.tw;
+  c.ntaps = a.cm ? P.th : P.th * P.tw;   // cm: row taps only
   c.nstages = c.ntaps > 0 ? P.nchunks * P.ngroups : 0;
   c.i_start = c.p0 / P.wb;
   c.R = (pend - 1) / P.wb - c.i_start + P.th;
@@ -115,6 +114,19 @@ C2B_HD int window_base(const TileCtx& c, int local) {
   const int dr = fast_div(q0, P.m_wb);
   const int jb = q0 - dr * P.wb;
   return (dr + P.th - 1) * c.roww + jb + P.tw - 1;
+}
+
+// cm (column taps in the matrix rows): the tile's lanes are the points
+// (r, u) of its class rows r < R - th + 1 and window columns u < roww, in
+// row-major order; the window slot a point reads for row tap j = 0.  Lanes
+// past the points get a slot whose row-tap offsets stay inside the window.
+C2B_HD int cm_points(const TileCtx& c) { return (c.R - c.P.th + 1) * c.roww; }
+C2B_HD int window_base_cm(const TileCtx& c, int local) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0) return 0;
+  if (local >= cm_points(c)) return (P.th - 1) * c.roww;
+  const int r = fast_div(local, P.m_roww);
+  return (r + P.th - 1) * c.roww + (local - r * c.roww);
 }
 
 // Window slot offset of tap (j, l) relative to window_base.
@@ -197,23 +209,46 @@ C2B_HD int mm_window_cell(const TileCtx& c, const LaunchArgs& a, int f) {
   return off < 0 ? -1 : ch * (a.OH * a.OW) + off;
 }
 
-// Weight cell e = cq*qp + (ci*pt + t)*4 + c (e counted from the start of the
-// weight region) of tap group `grp`: offset of weight[co = 4cq + c, ci0 + ci,
-// tap grp*tg + t] relative to the stage's first output channel, or -1 if the
-// cell is padding.
-template <int MT>
+// Offset within one output channel's weight row (ci*kH*kW + kh*kW + kw) of
+// matrix row m at tap t of tap group `grp`, or -1 if that cell is padding.
+// Matrix row m is input channel ci0 + m; with cm it is input channel
+// ci0 + m / twm at column tap m mod twm, and the taps are the row taps.
+template <int MT, bool CM>
+C2B_HD int weight_source(const TileCtx& c, const LaunchArgs& a, int m, int t, int grp) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0 || m >= MT || t >= P.tg) return -1;
+  const int tap = grp * P.tg + t;
+  if (tap >= c.ntaps) return -1;
+  int ci, kidx;
+  if (CM) {
+    const int cl = m / a.twm, l = m - cl * a.twm;
+    if (l >= P.tw || cl >= a.cit) return -1;
+    ci = c.ci0 + cl;
+    kidx = (P.rh + a.S * tap) * a.KW + (P.rw + a.S * l);
+  } else {
+    ci = c.ci0 + m;
+    kidx = tap_kidx(P, a, tap);
+  }
+  if (ci >= a.Ci) return -1;
+  return ci * (a.KH * a.KW) + kidx;
+}
+
+// Weight cell e = cq*qp + (m*pt + t)*4 + c (e counted from the start of the
+// weight region) of tap group `grp`: offset of the weight of output channel
+// 4cq + c at matrix row m, tap grp*tg + t (weight_source), relative to the
+// stage's first output channel, or -1 if the cell is padding.
+template <int MT, bool CM>
 C2B_HD int mm_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp) {
   const PhaseDesc& P = c.P;
   if (c.ntaps == 0 || e < 0 || e >= 4 * P.cg * P.qp) return -1;
   const int cq = fast_div(e, P.m_qp);
   const int r = e - cq * P.qp;
-  const int ci = fast_div(r, P.m_pt4);
-  const int r2 = r - ci * 4 * P.pt;
+  const int m = fast_div(r, P.m_pt4);
+  const int r2 = r - m * 4 * P.pt;
   const int t = r2 >> 2, co = 4 * cq + (r2 & 3);
-  if (ci >= MT || t >= P.tg) return -1;
-  const int tap = grp * P.tg + t;
-  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return -1;
-  return (co * a.Ci + c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap);
+  const int src = weight_source<MT, CM>(c, a, m, t, grp);
+  if (src < 0) return -1;
+  return co * (a.Ci * a.KH * a.KW) + src;
 }
 
 // ---------------------------------------------------------------------------
@@ -259,19 +294,17 @@ C2B_HD uint32_t window_lane_offset(const TileCtx& c, const LaunchArgs& a, int bl
 }
 
 // Byte offset, within a weight row of one output channel, of weight pair
-// 64*wblock + lane of tap group `grp` (kPadOffset if padding).
-template <int MT>
+// 64*wblock + lane (matrix row, tap) of tap group `grp` (kPadOffset if
+// padding).
+template <int MT, bool CM>
 C2B_HD uint32_t weight_lane_offset(const TileCtx& c, const LaunchArgs& a, int wblock, int lane,
                                    int grp) {
   const PhaseDesc& P = c.P;
   if (c.ntaps == 0) return kPadOffset;
   const int pr = 64 * wblock + lane;
-  const int ci = fast_div(pr, P.m_pt);
-  const int t = pr - ci * P.pt;
-  if (ci >= MT || t >= P.tg) return kPadOffset;
-  const int tap = grp * P.tg + t;
-  if (tap >= c.ntaps || c.ci0 + ci >= a.Ci) return kPadOffset;
-  return uint32_t(((c.ci0 + ci) * (a.KH * a.KW) + tap_kidx(P, a, tap)) * 4);
+  const int m = fast_div(pr, P.m_pt);
+  const int src = weight_source<MT, CM>(c, a, m, pr - m * P.pt, grp);
+  return src < 0 ? kPadOffset : uint32_t(src * 4);
 }
 
 // Bytes between consecutive channels: grad_out planes, or weight rows.

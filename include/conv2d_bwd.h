@@ -179,6 +179,14 @@ int conv2d_num_variants(void);
  * CONV2D_ERR_UNSUPPORTED if the index is out of range. */
 int conv2d_variant_is_f16(int variant);
 
+/* 1 if `variant` puts the kernel's column taps into its matrix rows next to
+ * the input channels (the few-input-channel variants: one matrix block of
+ * 16 rows holds 16 / ceil(kernel_w / stride) input channels, each with its
+ * column taps, and the column taps of a pixel are added in the epilogue),
+ * 0 if its matrix rows are input channels only, CONV2D_ERR_UNSUPPORTED if
+ * the index is out of range.  Results are the same up to summation order. */
+int conv2d_variant_uses_column_taps(int variant);
+
 /*
  * conv2d_grad_input (or conv2d_grad_input_f16, as the variant's path
  * dictates) with the kernel variant forced to `variant`.  Same contract and

@@ -55,6 +55,27 @@ VARIANT_SHAPES = [
 ]
 
 
+def _shape(name, n, ci, h, w, co, kh, kw, s, ph, pw):
+    return ConvShape(name, n, ci, h, w, co, kh, kw, s, ph, pw,
+                     (h + 2 * ph - kh) // s + 1, (w + 2 * pw - kw) // s + 1, dist="uniform")
+
+
+# Few-input-channel shapes for the variants that put column taps in the
+# matrix rows: Ci from 1 to 5, column-tap counts from 1 to 9 (several input
+# channels per 16 rows, or one), strides 1 to 4 (with classes no tap reaches),
+# asymmetric padding, ragged rows, and rows split into several bands.
+SMALL_CI_SHAPES = [
+    _shape("c_ci1_7x7_s1", 2, 1, 20, 23, 9, 7, 7, 1, 3, 2),
+    _shape("c_ci2_5x3_s2", 1, 2, 17, 30, 12, 5, 3, 2, 2, 1),
+    _shape("c_ci3_7x7_s2", 2, 3, 31, 29, 20, 7, 7, 2, 3, 3),
+    _shape("c_ci4_3x3_s3", 1, 4, 25, 26, 17, 3, 3, 3, 1, 0),
+    _shape("c_ci3_1x9_s1", 1, 3, 9, 40, 7, 1, 9, 1, 0, 4),
+    _shape("c_ci5_2x2_s2", 2, 5, 12, 13, 33, 2, 2, 2, 0, 0),
+    _shape("c_ci2_3x3_s4", 1, 2, 15, 15, 6, 3, 3, 4, 1, 1),
+    _shape("c_ci3_stem_rows", 1, 3, 120, 100, 64, 7, 7, 2, 3, 3),
+]
+
+
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     if ref.size == 0:
         return 0.0

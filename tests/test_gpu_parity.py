@@ -15,7 +15,8 @@ import oracle
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw,
                                                     draw_integers, random_shape)
-from tests.gpu_helpers import TOL, VARIANT_SHAPES, rel_err, round_f16, run_gpu
+from tests.gpu_helpers import (SMALL_CI_SHAPES, TOL, VARIANT_SHAPES, rel_err, round_f16,
+                               run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -234,5 +235,27 @@ def test_every_variant(variant):
             assert err16 <= 1e-5, (sh.name, err16)
         # integer inputs: exact on every path and in any summation order
         gi_, wi_ = draw_integers(sh, 3)
+        got_i = run_gpu(sh, gi_, wi_, variant=variant)
+        assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_)), sh.name
+
+
+# ---- variants with column taps in the matrix rows, on few-channel shapes ----
+def _cm_variants():
+    return [v for v in range(c2b.num_variants()) if c2b.variant_uses_column_taps(v) == 1]
+
+
+@pytest.mark.parametrize("variant", _cm_variants())
+def test_column_tap_variants_small_ci(variant):
+    for sh in SMALL_CI_SHAPES:
+        _say("case variant", variant, sh.name)
+        rng = np.random.default_rng(17)
+        go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+        w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+        got = run_gpu(sh, go, w, variant=variant)
+        assert not np.any(np.isnan(got)), "unwritten grad_input elements"
+        err = rel_err(got, _oracle(sh, go, w))
+        _say("  rel err", err)
+        assert err <= TOL[False], (sh.name, err)
+        gi_, wi_ = draw_integers(sh, 5)
         got_i = run_gpu(sh, gi_, wi_, variant=variant)
         assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_)), sh.name

@@ -11,7 +11,7 @@ import pytest
 
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import CONFIGS, ConvShape, random_shape
-from tests.gpu_helpers import VARIANT_SHAPES, params_of
+from tests.gpu_helpers import SMALL_CI_SHAPES, VARIANT_SHAPES, params_of
 from tests.test_gpu_parity import EDGE, RANDOM
 
 
@@ -62,3 +62,12 @@ def test_checker_rejects_bad_shape():
     p = c2b.make_params(1, 3, 8, 8, 4, 3, 3, 1, 1, 1, 7, 8)
     rc, _ = c2b.check_indexing(p)
     assert rc == -2
+
+
+def test_column_tap_variants_replay():
+    cm = [v for v in range(c2b.num_variants()) if c2b.variant_uses_column_taps(v) == 1]
+    assert cm, "no variant puts column taps in the matrix rows"
+    for v in cm:
+        for sh in SMALL_CI_SHAPES + [CONFIGS[4]]:
+            rc, msg = c2b.check_indexing_variant(params_of(sh), v)
+            assert rc == 0, (v, sh.name, rc, msg)
