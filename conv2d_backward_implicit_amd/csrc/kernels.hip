@@ -74,7 +74,7 @@ __device__ __forceinline__ f16x8 join(f16x4 lo, f16x4 hi) {
 template <bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
 __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
     const LaunchArgs a) {
-  static_assert(!CM || (WM == 1 && MB == 1 && !F16), "cm: one fp32 matrix block of rows");
+  static_assert(!CM || (WM == 1 && MB == 1), "cm: one matrix block of rows");
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int MT = G::kMT, NW = G::kWaves, NJ = G::kBatches;
   constexpr int kStageFloats = SF;   // this instance's stage buffer

@@ -112,7 +112,7 @@ struct Variant {
   int mb;    // 16-channel blocks per wave
   int nbw;   // 16-pixel blocks per wave
   int half;  // 1: half-size stage buffers, two workgroups per CU
-  int cm;    // 1: column taps in the matrix rows (wm = mb = 1, fp32)
+  int cm;    // 1: column taps in the matrix rows (wm = mb = 1)
 };
 
 // Floats of one stage buffer of a variant.
@@ -139,7 +139,8 @@ constexpr Variant kVariants[] = {
     {1, 1, 8, 1, 7, 0},
     // column taps in the matrix rows (few input channels)
     {0, 1, 8, 1, 7, 0, 1}, {0, 1, 12, 1, 5, 0, 1}, {0, 1, 16, 1, 4, 0, 1},
-    {0, 1, 8, 1, 4, 1, 1}};
+    {0, 1, 8, 1, 4, 1, 1}, {1, 1, 8, 1, 7, 0, 1}, {1, 1, 12, 1, 5, 0, 1},
+    {1, 1, 8, 1, 4, 1, 1}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b
