@@ -2,13 +2,15 @@
 """Throughput of the conv2d input-gradient HIP path on one MI355X.
 
 One step = one conv2d_grad_input call over the whole workload (all batch
-items, all stride classes), inputs already resident in HBM.  Prints one JSON
+items, all stride classes), inputs already resident in HBM.  Before the
+warm-up the kernel variant is chosen by measurement (conv2d_tune), outside
+the timed region.  Prints one JSON
 line with useful TFLOP/s (2*N*Co*out_h*out_w*Ci*kH*kW per second), the
 roofline of the kernel (timed with HIP events on the stream it runs on) and
 the CPU oracle timed on the host cores on the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--f16 | --fp32] [--no-cpu]
+                    [--f16 | --fp32] [--no-cpu] [--no-tune]
 """
 from __future__ import annotations
 
@@ -108,6 +110,8 @@ def main() -> int:
     g.add_argument("--f16", action="store_true", help="f16-staged path")
     g.add_argument("--fp32", action="store_true", help="fp32 path")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-tune", action="store_true",
+                    help="use the planner's model choice instead of tuning the variant")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run --steps plain device-to-device copies of MIB "
                          "MiB (reference kernel for HBM byte counters) and exit")
@@ -146,6 +150,14 @@ def main() -> int:
                         shape.padding_h, shape.padding_w, shape.out_h, shape.out_w)
     plan = c2b.describe_plan(p, f16)
     stream = torch.cuda.current_stream()
+    # measured variant choice for this shape, once, outside the timed region
+    # (conv2d_tune; the default entry point then uses the tuned plan)
+    if not args.no_tune:
+        plan["variant"] = c2b.tune(gi, tgo, tw, p, f16=f16, stream=stream)
+        plan["tuned"] = True
+    else:
+        plan["variant"] = c2b.planned_variant(p, f16)
+        plan["tuned"] = False
 
     def step():
         c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)

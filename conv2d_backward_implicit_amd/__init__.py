@@ -23,6 +23,7 @@ __all__ = [
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
     "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
     "variant_is_f16", "variant_uses_column_taps", "conv2d_grad_input_variant",
+    "tune", "planned_variant",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -43,6 +44,8 @@ EXPORTED_SYMBOLS = (
     "conv2d_variant_uses_column_taps",
     "conv2d_grad_input_variant",
     "conv2d_check_indexing_variant",
+    "conv2d_tune",
+    "conv2d_planned_variant",
 )
 
 CONV2D_OK = 0
@@ -140,6 +143,12 @@ def load_library():
         lib.conv2d_variant_is_f16.restype = ctypes.c_int
         lib.conv2d_variant_uses_column_taps.argtypes = [ctypes.c_int]
         lib.conv2d_variant_uses_column_taps.restype = ctypes.c_int
+        lib.conv2d_tune.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, P,
+                                    ctypes.c_int, ctypes.c_void_p,
+                                    ctypes.POINTER(ctypes.c_int)]
+        lib.conv2d_tune.restype = ctypes.c_int
+        lib.conv2d_planned_variant.argtypes = [P, ctypes.c_int, ctypes.POINTER(ctypes.c_int)]
+        lib.conv2d_planned_variant.restype = ctypes.c_int
         lib.conv2d_grad_input_variant.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
                                                   ctypes.c_void_p, P, ctypes.c_int,
                                                   ctypes.c_void_p]
@@ -279,6 +288,40 @@ def grad_input_into(grad_input, grad_out, weight, p: Conv2dParams, f16=False,
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return grad_input
+
+
+def tune(grad_input, grad_out, weight, p: Conv2dParams, f16=False, stream=None) -> int:
+    """conv2d_tune on torch tensors (checked like grad_input_into): times the
+    candidate variants of the path on these buffers and makes the fastest the
+    shape's default plan; blocks until done; returns the chosen variant."""
+    import torch
+    _check_tensor(grad_out, "grad_out", (p.batch, p.out_channels, p.out_h, p.out_w))
+    _check_tensor(weight, "weight", (p.out_channels, p.in_channels, p.kernel_h,
+                                     p.kernel_w))
+    _check_tensor(grad_input, "grad_input", (p.batch, p.in_channels, p.in_h, p.in_w))
+    if not (grad_out.device == weight.device == grad_input.device):
+        raise ValueError("all tensors must be on the same device")
+    chosen = ctypes.c_int(-1)
+    with torch.cuda.device(grad_input.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = int(load_library().conv2d_tune(
+            ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
+            ctypes.c_void_p(grad_input.data_ptr()), ctypes.byref(p), int(bool(f16)),
+            ctypes.c_void_p(int(s.cuda_stream)), ctypes.byref(chosen)))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return int(chosen.value)
+
+
+def planned_variant(p: Conv2dParams, f16: bool = False) -> int:
+    """Variant the default entry point uses for this shape now (-1: nothing
+    to launch); raises on an invalid shape."""
+    v = ctypes.c_int(-1)
+    rc = int(load_library().conv2d_planned_variant(ctypes.byref(p), int(bool(f16)),
+                                                   ctypes.byref(v)))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return int(v.value)
 
 
 def grad_input(grad_out, weight, in_h, in_w, stride=1, padding_h=0, padding_w=0,

@@ -42,6 +42,7 @@
 //    with no race between workgroups.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstring>
 #include <mutex>
@@ -425,7 +426,8 @@ int device_cus() {
 
 // Launch plans of recent shapes (host memory only), so that a repeated call
 // skips the planner's search.  Keyed by the shape, the path, the forced
-// variant and the CU count; at most kPlanCacheSize entries, oldest evicted.
+// variant (-1: the default plan, the model's choice or a tuned one) and the
+// CU count; at most kPlanCacheSize entries, oldest evicted.
 struct PlanKey {
   conv2d_params p;
   int f16, variant, cus;
@@ -436,19 +438,44 @@ struct PlanEntry {
 };
 constexpr size_t kPlanCacheSize = 64;
 
-int cached_plan(const conv2d_params* p, int f16, int variant, int cus,
-                std::vector<LaunchArgs>* out) {
+std::mutex& plan_cache_mutex() {
   static std::mutex mu;
+  return mu;
+}
+std::vector<PlanEntry>& plan_cache() {
   static std::vector<PlanEntry> cache;
+  return cache;
+}
+
+PlanKey plan_key(const conv2d_params* p, int f16, int variant, int cus) {
   PlanKey key;
   std::memset(&key, 0, sizeof(key));
   key.p = *p;
   key.f16 = f16;
   key.variant = variant;
   key.cus = cus;
+  return key;
+}
+
+// Insert or replace a plan (callers hold no lock).
+void store_plan(const PlanKey& key, const std::vector<LaunchArgs>& launches) {
+  std::lock_guard<std::mutex> lock(plan_cache_mutex());
+  std::vector<PlanEntry>& cache = plan_cache();
+  for (PlanEntry& e : cache)
+    if (std::memcmp(&e.key, &key, sizeof(key)) == 0) {
+      e.launches = launches;
+      return;
+    }
+  if (cache.size() >= kPlanCacheSize) cache.erase(cache.begin());
+  cache.push_back(PlanEntry{key, launches});
+}
+
+int cached_plan(const conv2d_params* p, int f16, int variant, int cus,
+                std::vector<LaunchArgs>* out) {
+  const PlanKey key = plan_key(p, f16, variant, cus);
   {
-    std::lock_guard<std::mutex> lock(mu);
-    for (const PlanEntry& e : cache)
+    std::lock_guard<std::mutex> lock(plan_cache_mutex());
+    for (const PlanEntry& e : plan_cache())
       if (std::memcmp(&e.key, &key, sizeof(key)) == 0) {
         *out = e.launches;
         return CONV2D_OK;
@@ -456,10 +483,21 @@ int cached_plan(const conv2d_params* p, int f16, int variant, int cus,
   }
   const int rc = build_plan(p, f16, cus, out, nullptr, variant);
   if (rc != CONV2D_OK) return rc;
-  std::lock_guard<std::mutex> lock(mu);
-  if (cache.size() >= kPlanCacheSize) cache.erase(cache.begin());
-  cache.push_back(PlanEntry{key, *out});
+  store_plan(key, *out);
   return CONV2D_OK;
+}
+
+// Enqueue a plan's launches on `st` with the caller's buffers.
+int enqueue(std::vector<LaunchArgs>& launches, const float* go, const float* w, float* gi,
+            hipStream_t st) {
+  for (LaunchArgs& la : launches) {
+    la.go = go;
+    la.w = w;
+    la.gi = gi;
+    if (la.total_tiles == 0) continue;
+    launch_dispatch(la, st, std::make_integer_sequence<int, kNumVariants>());
+  }
+  return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 
 int launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
@@ -471,15 +509,94 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, i
   std::vector<LaunchArgs> launches;
   rc = cached_plan(p, f16, variant, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  for (LaunchArgs& la : launches) {
-    la.go = go;
-    la.w = w;
-    la.gi = gi;
-    if (la.total_tiles == 0) continue;
-    launch_dispatch(la, st, std::make_integer_sequence<int, kNumVariants>());
+  return enqueue(launches, go, w, gi, static_cast<hipStream_t>(stream));
+}
+
+// Tuning: the variants of the path whose modelled makespan is within
+// kTuneSpread of the best (at most kTuneCandidates) are each run
+// kTuneReps times on the caller's buffers and stream after one warm-up run,
+// timed with events; the fastest becomes the shape's default plan.
+constexpr int kTuneCandidates = 8;
+constexpr double kTuneSpread = 1.3;
+constexpr int kTuneReps = 5;
+
+int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
+         void* stream, int* variant_out) {
+  int rc = validate_shape(p);
+  if (rc != CONV2D_OK) return rc;
+  rc = check_pointers(go, w, gi, p);
+  if (rc != CONV2D_OK) return rc;
+  const int cus = device_cus();
+  std::vector<std::pair<double, int>> cand;
+  for (int v = 0; v < kNumVariants; ++v) {
+    if (kVariants[v].f16 != f16) continue;
+    double cost = 0.0;
+    if (build_plan(p, f16, cus, nullptr, nullptr, v, &cost) == CONV2D_OK)
+      cand.push_back({cost, v});
   }
-  if (hipGetLastError() != hipSuccess) return CONV2D_ERR_HIP;
+  std::vector<LaunchArgs> launches;
+  rc = cached_plan(p, f16, -1, cus, &launches);   // the model's choice
+  if (rc != CONV2D_OK) return rc;
+  int best_v = launches.empty() ? -1 : launches[0].variant;
+  std::sort(cand.begin(), cand.end());
+  if (cand.size() > size_t(kTuneCandidates)) cand.resize(kTuneCandidates);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (!launches.empty() && cand.size() > 1) {
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+      if (e0) (void)hipEventDestroy(e0);
+      return CONV2D_ERR_HIP;
+    }
+    float best_ms = 0.0f;
+    std::vector<LaunchArgs> best_plan;
+    for (const auto& c : cand) {
+      if (c.first > kTuneSpread * cand[0].first) break;
+      std::vector<LaunchArgs> plan;
+      rc = cached_plan(p, f16, c.second, cus, &plan);
+      if (rc != CONV2D_OK) break;
+      rc = enqueue(plan, go, w, gi, st);   // warm-up
+      if (rc != CONV2D_OK) break;
+      rc = CONV2D_ERR_HIP;
+      if (hipEventRecord(e0, st) != hipSuccess) break;
+      int r = 0;
+      for (; r < kTuneReps; ++r)
+        if (enqueue(plan, go, w, gi, st) != CONV2D_OK) break;
+      if (r < kTuneReps) break;
+      float ms = 0.0f;
+      if (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
+        break;
+      rc = CONV2D_OK;
+      if (best_plan.empty() || ms < best_ms) {
+        best_ms = ms;
+        best_plan = plan;
+      }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (rc != CONV2D_OK) return rc;
+    if (!best_plan.empty()) {
+      store_plan(plan_key(p, f16, -1, cus), best_plan);
+      best_v = best_plan[0].variant;
+      // leave grad_input holding the result of the chosen plan
+      rc = enqueue(best_plan, go, w, gi, st);
+      if (rc != CONV2D_OK) return rc;
+    }
+  } else if (!launches.empty()) {
+    rc = enqueue(launches, go, w, gi, st);
+    if (rc != CONV2D_OK) return rc;
+  }
+  if (variant_out) *variant_out = best_v;
+  return CONV2D_OK;
+}
+
+// The variant the default entry point of a path uses for a shape now (-1 if
+// the shape launches nothing).
+int planned_variant(const conv2d_params* p, int f16, int* variant_out) {
+  std::vector<LaunchArgs> launches;
+  const int rc = cached_plan(p, f16, -1, device_cus(), &launches);
+  if (rc != CONV2D_OK) return rc;
+  *variant_out = launches.empty() ? -1 : launches[0].variant;
   return CONV2D_OK;
 }
 
@@ -502,4 +619,16 @@ extern "C" int conv2d_grad_input_variant(const float* grad_out, const float* wei
   if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
   return c2b::launch(grad_out, weight, grad_input, p, c2b::kVariants[variant].f16, variant,
                      stream);
+}
+
+extern "C" int conv2d_tune(const float* grad_out, const float* weight, float* grad_input,
+                           const conv2d_params* p, int f16, void* stream, int* variant_out) {
+  return c2b::tune(grad_out, weight, grad_input, p, f16 ? 1 : 0, stream, variant_out);
+}
+
+extern "C" int conv2d_planned_variant(const conv2d_params* p, int f16, int* variant_out) {
+  if (p == nullptr || variant_out == nullptr) return CONV2D_ERR_NULL_PTR;
+  const int rc = c2b::validate_shape(p);
+  if (rc != CONV2D_OK) return rc;
+  return c2b::planned_variant(p, f16 ? 1 : 0, variant_out);
 }

@@ -405,7 +405,7 @@ double lpt_makespan(const std::vector<PhaseDesc>& phases, int64_t per_class_mult
 }  // namespace
 
 int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchArgs>* launches,
-               conv2d_plan_info* info, int force_variant) {
+               conv2d_plan_info* info, int force_variant, double* model_cost) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
   if (info) std::memset(info, 0, sizeof(*info));
@@ -462,6 +462,7 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     }
   }
   if (best_v < 0) return CONV2D_ERR_UNSUPPORTED;
+  if (model_cost) *model_cost = best_cost;
 
   const Variant& bv = kVariants[best_v];
   const int64_t bmt = 16 * int64_t(bv.wm) * bv.mb;   // matrix rows per tile

@@ -160,8 +160,9 @@ int validate_shape(const conv2d_params* p);
 // appends one LaunchArgs per launch (pointers left null).  `info` may be null.
 // force_variant >= 0 plans with that variant only (CONV2D_ERR_UNSUPPORTED if
 // it belongs to the other path or cannot tile the shape).
+// `model_cost` (may be null) receives the modelled makespan of the plan.
 int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchArgs>* launches,
-               conv2d_plan_info* info, int force_variant = -1);
+               conv2d_plan_info* info, int force_variant = -1, double* model_cost = nullptr);
 
 // Pointer checks: NULL inputs of non-empty tensors and output/input overlap.
 int check_pointers(const float* go, const float* w, const float* gi,

@@ -128,6 +128,38 @@ int conv2d_check_params(const conv2d_params* p);
 const char* conv2d_status_string(int status);
 
 /*
+ * Measured choice of the kernel variant for a shape, once, before the
+ * steady-state calls (like a framework's first-call tuning).  The variants
+ * of the path (f16 != 0: the f16-staged path) whose modelled run time is
+ * within 1.3x of the best (at most 8) each run five times on the caller's
+ * buffers and `stream` after one warm-up, timed with HIP events; the fastest
+ * becomes the plan conv2d_grad_input (or conv2d_grad_input_f16) uses for
+ * this shape on devices with this many compute units, for the rest of the
+ * process (a host-side cache of at most 64 shapes, oldest evicted).
+ *   grad_out, weight, grad_input, p, stream: as for conv2d_grad_input;
+ *     grad_input is overwritten, and on success holds the input gradient
+ *     (computed by the chosen variant).
+ *   variant_out: receives the chosen variant index (may be NULL; -1 if the
+ *     shape launches nothing).
+ * Blocking: waits for `stream` (HIP events are created and destroyed here;
+ * no device memory is allocated).  Returns CONV2D_OK or a CONV2D_ERR_* code
+ * (validation errors as for conv2d_grad_input, with nothing enqueued).
+ * Thread-safe; concurrent tuning of one shape keeps the last result.
+ */
+int conv2d_tune(const float* grad_out, const float* weight, float* grad_input,
+                const conv2d_params* p, int f16, void* stream, int* variant_out);
+
+/*
+ * The variant index conv2d_grad_input (f16 == 0) or conv2d_grad_input_f16
+ * (f16 != 0) uses for this shape now, on the current device: the tuned one
+ * after conv2d_tune, else the planner's model choice.  *variant_out gets the
+ * index, or -1 if the shape launches nothing.  Returns CONV2D_OK or the
+ * CONV2D_ERR_* code of an invalid shape (CONV2D_ERR_NULL_PTR for a NULL
+ * argument).  Host code (reads the device's compute-unit count once).
+ */
+int conv2d_planned_variant(const conv2d_params* p, int f16, int* variant_out);
+
+/*
  * Launch plan of a shape, for inspection and host-side tests (pure host
  * code).  `f16` selects the plan of conv2d_grad_input_f16.  Fills `out`:
  *   out->launches      kernel launches the call would make

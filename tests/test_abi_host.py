@@ -213,3 +213,28 @@ def test_library_shares_torchs_hip_runtime():
     assert lines[0] == "1", out.stdout
     import torch
     assert os.path.dirname(torch.__file__) in lines[1], out.stdout
+
+
+def test_tune_rejects_before_any_device_call():
+    lib = c2b.load_library()
+    chosen = ctypes.c_int(7)
+
+    def tune(go, w, gi, p, f16=0):
+        return lib.conv2d_tune(ctypes.c_void_p(go), ctypes.c_void_p(w), ctypes.c_void_p(gi),
+                               ctypes.byref(p), f16, None, ctypes.byref(chosen))
+    p = _p()
+    assert tune(0x1000, 0x2000, 0x3000, _p(stride=0, out_h=1, out_w=1)) == BAD
+    assert tune(0, 0x2000, 0x100000, p) == NULL
+    assert tune(0x100000, 0x900000, 0x100000, p, 1) == ALIAS
+    assert chosen.value == 7   # untouched on a validation error
+
+
+def test_planned_variant_is_a_variant_of_the_path():
+    for f16 in (False, True):
+        v = c2b.planned_variant(_p(in_channels=40, out_channels=24), f16)
+        assert 0 <= v < c2b.num_variants() and c2b.variant_is_f16(v) == int(f16)
+    assert c2b.planned_variant(_p(batch=0)) == -1
+    with pytest.raises(c2b.Conv2dError):
+        c2b.planned_variant(_p(stride=0, out_h=1, out_w=1))
+    lib = c2b.load_library()
+    assert lib.conv2d_planned_variant(ctypes.byref(_p()), 0, None) == NULL

@@ -263,3 +263,28 @@ def test_column_tap_variants_small_ci(variant):
         gi_, wi_ = draw_integers(sh, 5)
         got_i = run_gpu(sh, gi_, wi_, variant=variant)
         assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_)), sh.name
+
+
+# ---- measured plan choice ----------------------------------------------------
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_tune_picks_a_variant_and_the_default_call_uses_it(f16):
+    import torch
+    sh = ConvShape("t_tune", 2, 24, 20, 18, 40, 3, 3, 2, 1, 1, 10, 9, dist="uniform")
+    _say("case tune", sh.name, "f16" if f16 else "fp32")
+    rng = np.random.default_rng(23)
+    go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+    ref = _oracle(sh, go, w)
+    dev = torch.device("cuda", 0)
+    tgo, tw = torch.from_numpy(go).to(dev), torch.from_numpy(w).to(dev)
+    gi = torch.full(sh.gi_shape, float("nan"), device=dev)
+    p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels,
+                        sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h, sh.padding_w)
+    v = c2b.tune(gi, tgo, tw, p, f16=f16)
+    torch.cuda.synchronize()
+    assert 0 <= v < c2b.num_variants() and c2b.variant_is_f16(v) == int(f16)
+    assert rel_err(gi.cpu().numpy(), ref) <= TOL[f16]          # tune leaves the result
+    assert c2b.planned_variant(p, f16) == v
+    got = run_gpu(sh, go, w, f16=f16)                          # default call, tuned plan
+    assert not np.any(np.isnan(got))
+    assert rel_err(got, ref) <= TOL[f16]
