@@ -23,7 +23,7 @@ __all__ = [
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
     "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
     "variant_is_f16", "variant_uses_column_taps", "conv2d_grad_input_variant",
-    "tune", "planned_variant",
+    "tune", "planned_variant", "describe_plan_variant",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -46,6 +46,7 @@ EXPORTED_SYMBOLS = (
     "conv2d_check_indexing_variant",
     "conv2d_tune",
     "conv2d_planned_variant",
+    "conv2d_describe_plan_variant",
 )
 
 CONV2D_OK = 0
@@ -131,6 +132,8 @@ def load_library():
         lib.conv2d_status_string.restype = ctypes.c_char_p
         lib.conv2d_describe_plan.argtypes = [P, ctypes.c_int, ctypes.POINTER(PlanInfo)]
         lib.conv2d_describe_plan.restype = ctypes.c_int
+        lib.conv2d_describe_plan_variant.argtypes = [P, ctypes.c_int, ctypes.POINTER(PlanInfo)]
+        lib.conv2d_describe_plan_variant.restype = ctypes.c_int
         lib.conv2d_check_indexing.argtypes = [P, ctypes.c_int, ctypes.c_char_p,
                                               ctypes.c_size_t]
         lib.conv2d_check_indexing.restype = ctypes.c_int
@@ -187,6 +190,16 @@ def describe_plan(p: Conv2dParams, f16: bool = False) -> dict:
     info = PlanInfo()
     rc = load_library().conv2d_describe_plan(ctypes.byref(p), int(bool(f16)),
                                              ctypes.byref(info))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return info.as_dict()
+
+
+def describe_plan_variant(p: Conv2dParams, variant: int) -> dict:
+    """Launch plan with the kernel variant forced (pure host code)."""
+    info = PlanInfo()
+    rc = load_library().conv2d_describe_plan_variant(ctypes.byref(p), int(variant),
+                                                     ctypes.byref(info))
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return info.as_dict()

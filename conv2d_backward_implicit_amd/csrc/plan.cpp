@@ -503,6 +503,14 @@ extern "C" int conv2d_describe_plan(const conv2d_params* p, int f16,
   return c2b::build_plan(p, f16 ? 1 : 0, c2b::kDefaultCUs, nullptr, out);
 }
 
+extern "C" int conv2d_describe_plan_variant(const conv2d_params* p, int variant,
+                                            conv2d_plan_info* out) {
+  if (p == nullptr || out == nullptr) return CONV2D_ERR_NULL_PTR;
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::build_plan(p, c2b::kVariants[variant].f16, c2b::kDefaultCUs, nullptr, out,
+                         variant);
+}
+
 extern "C" int conv2d_num_variants(void) { return c2b::kNumVariants; }
 
 extern "C" int conv2d_variant_is_f16(int variant) {

@@ -183,6 +183,15 @@ int conv2d_describe_plan(const conv2d_params* p, int f16,
                          conv2d_plan_info* out);
 
 /*
+ * conv2d_describe_plan for the plan conv2d_grad_input_variant would make
+ * with kernel variant `variant` (pure host code).  Returns as
+ * conv2d_describe_plan, or CONV2D_ERR_UNSUPPORTED if the index is out of
+ * range or the variant cannot tile the shape.
+ */
+int conv2d_describe_plan_variant(const conv2d_params* p, int variant,
+                                 conv2d_plan_info* out);
+
+/*
  * Host-side replay of the kernels' addressing for a shape (pure host code,
  * no device needed).  Walks every workgroup and thread of every launch that
  * conv2d_grad_input (f16 == 0) or conv2d_grad_input_f16 (f16 != 0) would

@@ -238,3 +238,17 @@ def test_planned_variant_is_a_variant_of_the_path():
         c2b.planned_variant(_p(stride=0, out_h=1, out_w=1))
     lib = c2b.load_library()
     assert lib.conv2d_planned_variant(ctypes.byref(_p()), 0, None) == NULL
+
+
+def test_describe_plan_variant_matches_forced_plans():
+    p = _p(in_channels=40, out_channels=24)
+    for v in range(c2b.num_variants()):
+        try:
+            info = c2b.describe_plan_variant(p, v)
+        except c2b.Conv2dError as e:
+            assert e.status == -5, (v, e.status)
+            continue
+        assert info["useful_macs"] == 1 * 24 * 8 * 8 * 40 * 9
+        assert info["macs"] >= info["useful_macs"] and info["tiles"] >= 1
+    with pytest.raises(c2b.Conv2dError):
+        c2b.describe_plan_variant(p, c2b.num_variants())
