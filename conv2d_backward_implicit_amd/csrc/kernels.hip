@@ -19,18 +19,22 @@
 //    image) into LDS once, then every tap reads that window at a fixed
 //    offset, so each grad_out element crosses from L2/HBM once per stage
 //    instead of once per tap.
-//  * Window and weights go straight from global memory into LDS with buffer
-//    loads that write LDS (no register round trip); reads past a tensor's
-//    extent return 0, which supplies the padding halo.  Copies go through
-//    registers (tile_index.hpp, copy batches): each load instruction reads
-//    64 consecutive cells of one channel, and each lane writes the 4
-//    channels of one cell to LDS with one 16-byte store.  (Loads that write
-//    LDS directly were measured to stall the matrix cores' LDS reads for the
-//    whole time they land.)  Two stage buffers: at the end of stage s the
-//    lanes write stage s+1 (loaded a stage earlier) into the buffer stage
-//    s-1 used and issue the loads of stage s+2; one barrier per stage.  The planner picks the wave shape and the stage
-//    shape (channel groups x taps) per problem from a cost model of the
-//    schedule over all CUs.
+//  * Window and weights reach LDS through registers (tile_index.hpp, copy
+//    batches): each load instruction reads 64 consecutive cells of one
+//    channel, and each lane writes the 4 channels of one cell to LDS with one
+//    16-byte store; loads past a tensor's extent return 0, which supplies the
+//    padding halo.  (Loads that write LDS directly were measured to stall the
+//    matrix cores' LDS reads for the whole time they land.)  Two stage
+//    buffers: at the end of stage s the lanes write stage s+1 (loaded a stage
+//    earlier) into the buffer stage s-1 used and issue the loads of stage
+//    s+2; one barrier per stage.
+//  * The wave shape and the stage shape (channel groups x taps) come from the
+//    planner's cost model of the schedule over all CUs, or, after
+//    conv2d_tune, from measurement.
+//  * Few input channels (cm variants, plan.hpp): the kernel's column taps
+//    join the input channels in the 16 matrix rows, the contraction runs over
+//    output channels x row taps, and the epilogue adds each pixel's
+//    column-tap partial sums through LDS.
 //  * fp32 path: v_mfma_f32_16x16x4_f32, four per (unit, block).  f16-staged
 //    path: the same fp32 data in LDS, rounded to f16 (round to nearest even)
 //    as it is read into registers -- every operand element is rounded exactly
@@ -261,9 +265,9 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
     }
   };
 
-  // Multiply stage st out of buffer st&1; the copies of stage st+1 (if any)
-  // go out into the other buffer during the first unit.  Units run channel
-  // group by channel group, taps in class order inside a group.
+  // Multiply stage st out of buffer st&1 (the copies run after it, in the
+  // stage loop below).  Units run channel group by channel group, taps in
+  // class order inside a group (cm variants: row taps only).
   auto compute = [&](int st) __attribute__((always_inline)) {
     const int buf = st & 1;
     int co0, grp;

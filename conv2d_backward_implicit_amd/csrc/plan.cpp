@@ -257,9 +257,12 @@ bool cm_tiling(const PhaseDesc& d, int64_t nb, int64_t ntl, int64_t max_slots, i
   return *slots_out <= max_slots;
 }
 
-// Cost model of one tile, in CU cycles, with constants fitted (least squares
-// on log time) to forced-variant timings of every kernel variant on the four
-// large workloads on MI355X:
+// Cost model of one tile, in CU cycles.  Its constants are a least-squares
+// fit (log time) to forced-variant timings of every kernel variant on the
+// four large workloads on MI355X, taken with an earlier copy path (loads that
+// wrote LDS directly, overlapped with the stage's products); with the
+// register-path copies it still ranks variants to within about 9%, and
+// conv2d_tune chooses among the best-ranked ones by measurement:
 //   matrix: per unit (16 k values) each wave issues MB x NBW blocks of four
 //   fp32 instructions of 32 cycles (or half an f16 pair instruction of 16
 //   cycles); the waves of a SIMD add up, at an efficiency set by how many
@@ -267,7 +270,7 @@ bool cm_tiling(const PhaseDesc& d, int64_t nb, int64_t ntl, int64_t max_slots, i
 //   copies: a stage's buffer at kCopyBytesPerCycle, overlapped with the
 //   stage's products;
 //   fixed costs per stage (barrier, copy issue and wait) and per tile (set-up,
-//   first copies, epilogue).
+//   first copies, epilogue; cm variants add the column-tap sums).
 // A two-per-CU variant that shares its CU (share = 2) gets half of every
 // SIMD, and part of its stage overheads hides behind the other workgroup.
 double simd_efficiency(int wps) { return wps >= 3 ? 1.0 : wps == 2 ? 0.9 : 0.4; }
@@ -275,7 +278,7 @@ double simd_efficiency(int wps) { return wps >= 3 ? 1.0 : wps == 2 ? 0.9 : 0.4; 
 constexpr double kUnitLatency = 500.0;        // exposed LDS latency per unit and SIMD
 constexpr double kStageCycles = 2000.0;       // barrier, copy issue and wait per stage
 constexpr double kTileCycles = 45000.0;       // set-up, first copies, epilogue
-constexpr double kCopyBytesPerCycle = 12.0;   // gathered copies into LDS, per CU
+constexpr double kCopyBytesPerCycle = 12.0;   // stage copies, per CU
 constexpr double kSharedStageVisible = 0.4;   // stage overhead left when sharing a CU
 constexpr double kCmEpilogueCycles = 4000.0;   // cm: rows through LDS, column-tap sums
 

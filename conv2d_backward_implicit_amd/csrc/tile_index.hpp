@@ -175,8 +175,8 @@ C2B_HD void stage_split(const TileCtx& c, int st, int* co0, int* grp) {
 //           floats apart (a multiple of 64): a lane reads the 4 channels of
 //           one (ci, tap) with one 16-byte read; pt is odd, so the 16 lanes
 //           of a group (consecutive ci) hit 16 disjoint sets of 4 banks.
-// Both are filled by buffer loads that write LDS directly, 64 floats per
-// instruction (see the copy items below).
+// Both are filled by copy batches (below): coalesced loads into registers,
+// then one 16-byte LDS write per lane.
 template <int WM, int WN, int MB, int NBW, int SF>
 struct MMGeom {
   static constexpr int kThreads = 64 * WM * WN;
