@@ -1,4 +1,5 @@
-"""MI355X (gfx950) convolution input-gradient as an implicit GEMM.
+"""MI355X (gfx950) convolution input-gradient as an implicit GEMM (and the
+forward convolution on the same kernels).
 
 Thin Python binding over the C ABI of ``libconv2d_bwd.so`` (declared in
 ``include/conv2d_bwd.h``).  Every step of the computation runs in the HIP
@@ -11,6 +12,7 @@ fallback.
     gi = c2b.grad_input(grad_out, weight, in_h=56, in_w=56, stride=1,
                         padding_h=1, padding_w=1)          # fp32 path
     gi = c2b.grad_input(..., f16=True)                     # f16-staged path
+    y = c2b.forward(x, weight, stride=1, padding_h=1, padding_w=1)
 """
 from __future__ import annotations
 
@@ -24,6 +26,10 @@ __all__ = [
     "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
     "variant_is_f16", "variant_uses_column_taps", "conv2d_grad_input_variant",
     "tune", "planned_variant", "describe_plan_variant",
+    "forward", "forward_into", "conv2d_forward", "conv2d_forward_f16",
+    "conv2d_forward_variant", "tune_forward", "planned_forward_variant",
+    "describe_forward_plan", "describe_forward_plan_variant",
+    "check_indexing_forward", "check_indexing_forward_variant",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -47,6 +53,15 @@ EXPORTED_SYMBOLS = (
     "conv2d_tune",
     "conv2d_planned_variant",
     "conv2d_describe_plan_variant",
+    "conv2d_forward",
+    "conv2d_forward_f16",
+    "conv2d_forward_variant",
+    "conv2d_tune_forward",
+    "conv2d_planned_forward_variant",
+    "conv2d_describe_forward_plan",
+    "conv2d_describe_forward_plan_variant",
+    "conv2d_check_indexing_forward",
+    "conv2d_check_indexing_forward_variant",
 )
 
 CONV2D_OK = 0
@@ -121,7 +136,8 @@ def load_library():
             pass
         lib = ctypes.CDLL(_LIB_PATH)
         P = ctypes.POINTER(Conv2dParams)
-        for name in ("conv2d_grad_input", "conv2d_grad_input_f16"):
+        for name in ("conv2d_grad_input", "conv2d_grad_input_f16", "conv2d_forward",
+                     "conv2d_forward_f16"):
             fn = getattr(lib, name)
             fn.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, P,
                            ctypes.c_void_p]
@@ -156,6 +172,22 @@ def load_library():
                                                   ctypes.c_void_p, P, ctypes.c_int,
                                                   ctypes.c_void_p]
         lib.conv2d_grad_input_variant.restype = ctypes.c_int
+        lib.conv2d_forward_variant.argtypes = lib.conv2d_grad_input_variant.argtypes
+        lib.conv2d_forward_variant.restype = ctypes.c_int
+        lib.conv2d_tune_forward.argtypes = lib.conv2d_tune.argtypes
+        lib.conv2d_tune_forward.restype = ctypes.c_int
+        lib.conv2d_planned_forward_variant.argtypes = lib.conv2d_planned_variant.argtypes
+        lib.conv2d_planned_forward_variant.restype = ctypes.c_int
+        lib.conv2d_describe_forward_plan.argtypes = lib.conv2d_describe_plan.argtypes
+        lib.conv2d_describe_forward_plan.restype = ctypes.c_int
+        lib.conv2d_describe_forward_plan_variant.argtypes = \
+            lib.conv2d_describe_plan_variant.argtypes
+        lib.conv2d_describe_forward_plan_variant.restype = ctypes.c_int
+        lib.conv2d_check_indexing_forward.argtypes = lib.conv2d_check_indexing.argtypes
+        lib.conv2d_check_indexing_forward.restype = ctypes.c_int
+        lib.conv2d_check_indexing_forward_variant.argtypes = \
+            lib.conv2d_check_indexing_variant.argtypes
+        lib.conv2d_check_indexing_forward_variant.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -353,3 +385,135 @@ def grad_input(grad_out, weight, in_h, in_w, stride=1, padding_h=0, padding_w=0,
         out = torch.empty((n, ci, in_h, in_w), dtype=torch.float32,
                           device=grad_out.device)
     return grad_input_into(out, grad_out, weight, p, f16=f16, stream=stream)
+
+
+# ---- forward convolution (the adjoint operator, on the same kernels) -------
+
+def describe_forward_plan(p: Conv2dParams, f16: bool = False) -> dict:
+    """Launch plan of the forward convolution of a shape (pure host code)."""
+    info = PlanInfo()
+    rc = load_library().conv2d_describe_forward_plan(ctypes.byref(p), int(bool(f16)),
+                                                     ctypes.byref(info))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return info.as_dict()
+
+
+def describe_forward_plan_variant(p: Conv2dParams, variant: int) -> dict:
+    """Forward launch plan with the kernel variant forced (pure host code)."""
+    info = PlanInfo()
+    rc = load_library().conv2d_describe_forward_plan_variant(ctypes.byref(p), int(variant),
+                                                             ctypes.byref(info))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return info.as_dict()
+
+
+def check_indexing_forward(p: Conv2dParams, f16: bool = False) -> tuple:
+    """Host replay of the forward launches' addressing (no device needed)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().conv2d_check_indexing_forward(ctypes.byref(p), int(bool(f16)), buf,
+                                                      len(buf))
+    return int(rc), buf.value.decode()
+
+
+def check_indexing_forward_variant(p: Conv2dParams, variant: int) -> tuple:
+    """check_indexing_forward with the kernel variant forced (host only)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().conv2d_check_indexing_forward_variant(ctypes.byref(p), int(variant),
+                                                              buf, len(buf))
+    return int(rc), buf.value.decode()
+
+
+def conv2d_forward(x_ptr: int, weight_ptr: int, y_ptr: int, p: Conv2dParams,
+                   stream: int = 0) -> int:
+    """Raw C-ABI call of the forward convolution; returns the status."""
+    return int(load_library().conv2d_forward(
+        ctypes.c_void_p(x_ptr), ctypes.c_void_p(weight_ptr), ctypes.c_void_p(y_ptr),
+        ctypes.byref(p), ctypes.c_void_p(stream)))
+
+
+def conv2d_forward_f16(x_ptr: int, weight_ptr: int, y_ptr: int, p: Conv2dParams,
+                       stream: int = 0) -> int:
+    """Raw C-ABI call of the f16-staged forward convolution."""
+    return int(load_library().conv2d_forward_f16(
+        ctypes.c_void_p(x_ptr), ctypes.c_void_p(weight_ptr), ctypes.c_void_p(y_ptr),
+        ctypes.byref(p), ctypes.c_void_p(stream)))
+
+
+def conv2d_forward_variant(x_ptr: int, weight_ptr: int, y_ptr: int, p: Conv2dParams,
+                           variant: int, stream: int = 0) -> int:
+    """Raw C-ABI forward call with the kernel variant forced."""
+    return int(load_library().conv2d_forward_variant(
+        ctypes.c_void_p(x_ptr), ctypes.c_void_p(weight_ptr), ctypes.c_void_p(y_ptr),
+        ctypes.byref(p), ctypes.c_int(int(variant)), ctypes.c_void_p(stream)))
+
+
+def _check_forward_tensors(y, x, weight, p):
+    _check_tensor(x, "x", (p.batch, p.in_channels, p.in_h, p.in_w))
+    _check_tensor(weight, "weight", (p.out_channels, p.in_channels, p.kernel_h,
+                                     p.kernel_w))
+    _check_tensor(y, "y", (p.batch, p.out_channels, p.out_h, p.out_w))
+    if not (x.device == weight.device == y.device):
+        raise ValueError("all tensors must be on the same device")
+
+
+def forward_into(y, x, weight, p: Conv2dParams, f16=False, stream=None, variant=None):
+    """Write the forward convolution of ``x`` with ``weight`` into ``y`` on
+    torch's current stream (or ``stream``); ``variant`` forces a kernel
+    variant.  Raises Conv2dError on a bad status."""
+    import torch
+    _check_forward_tensors(y, x, weight, p)
+    with torch.cuda.device(y.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        if variant is not None:
+            rc = conv2d_forward_variant(x.data_ptr(), weight.data_ptr(), y.data_ptr(), p,
+                                        variant, int(s.cuda_stream))
+        else:
+            fn = conv2d_forward_f16 if f16 else conv2d_forward
+            rc = fn(x.data_ptr(), weight.data_ptr(), y.data_ptr(), p, int(s.cuda_stream))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return y
+
+
+def tune_forward(y, x, weight, p: Conv2dParams, f16=False, stream=None) -> int:
+    """conv2d_tune_forward on torch tensors: the measured variant choice of
+    the forward convolution for this shape; returns the chosen variant."""
+    import torch
+    _check_forward_tensors(y, x, weight, p)
+    chosen = ctypes.c_int(-1)
+    with torch.cuda.device(y.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = int(load_library().conv2d_tune_forward(
+            ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(weight.data_ptr()),
+            ctypes.c_void_p(y.data_ptr()), ctypes.byref(p), int(bool(f16)),
+            ctypes.c_void_p(int(s.cuda_stream)), ctypes.byref(chosen)))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return int(chosen.value)
+
+
+def planned_forward_variant(p: Conv2dParams, f16: bool = False) -> int:
+    """Variant the default forward entry point uses for this shape now."""
+    v = ctypes.c_int(-1)
+    rc = int(load_library().conv2d_planned_forward_variant(ctypes.byref(p), int(bool(f16)),
+                                                           ctypes.byref(v)))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return int(v.value)
+
+
+def forward(x, weight, stride=1, padding_h=0, padding_w=0, f16=False, out=None, stream=None):
+    """Forward conv2d of NCHW ``x`` with [Co, Ci, kH, kW] ``weight`` (float32
+    GPU tensors, no bias).  Returns a new [N, Co, out_h, out_w] tensor (or
+    fills ``out``)."""
+    import torch
+    n, ci, h, w_ = (int(v) for v in x.shape)
+    co, ci2, kh, kw = (int(v) for v in weight.shape)
+    if ci2 != ci:
+        raise ValueError("x has %d channels, weight has %d" % (ci, ci2))
+    p = make_params(n, ci, h, w_, co, kh, kw, stride, padding_h, padding_w)
+    if out is None:
+        out = torch.empty((n, co, p.out_h, p.out_w), dtype=torch.float32, device=x.device)
+    return forward_into(out, x, weight, p, f16=f16, stream=stream)

@@ -37,15 +37,21 @@ struct Failure {
   } while (0)
 
 template <int WM, int WN, int MB, int NBW, int SF, bool CM>
-void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
+void check_launch(const LaunchArgs& a, const conv2d_params& prm,
+                  std::vector<unsigned char>& written) {
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int kStageFloats = SF;
   constexpr int MT = G::kMT, NT = G::kThreads, NW = G::kWaves, NJ = G::kBatches;
   const int64_t OHOW = int64_t(a.OH) * a.OW;
   const int64_t go_size = int64_t(a.N) * a.Co * OHOW;
   const int64_t KHW = int64_t(a.KH) * a.KW;
-  const int64_t cstride = int64_t(a.Ci) * KHW;
-  const int64_t w_size = int64_t(a.Co) * cstride;
+  const int64_t w_size = int64_t(a.Co) * a.Ci * KHW;   // the same product on both roles
+  // forward launches (roles exchanged, plan.hpp): their geometry is checked
+  // against the caller's stride and padding, not the launch's own fields
+  const bool fwd = a.fwd != 0;
+  C2B_REQUIRE(fwd ? (a.wsm == prm.in_channels * KHW && a.wsk == KHW && a.S == 1 && !CM)
+                  : (a.wsm == KHW && a.wsk == prm.in_channels * KHW),
+              "launch weight strides / roles");
   const int64_t HW = int64_t(a.H) * a.W;
 
   for (int bid = 0; bid < a.total_tiles; ++bid) {
@@ -80,7 +86,8 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
                       P.used <= kStageFloats && P.wfl % 64 == 0 && P.used % 64 == 0,
                   "stage buffer wfl %d used %d", P.wfl, P.used);
       C2B_REQUIRE(int64_t(CH) * OHOW * 4 < (int64_t(1) << 31) &&
-                      int64_t(CH) * cstride * 4 < (int64_t(1) << 31),
+                      int64_t(CH) * a.wsk * 4 < (int64_t(1) << 31) &&
+                      w_size * 4 < (int64_t(1) << 31),
                   "stage byte range");
     }
     std::vector<unsigned char> covered(size_t(c.nstages) * size_t(c.ntaps > 0 ? P.used : 0), 0);
@@ -117,7 +124,11 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
           const uint32_t off = win ? window_lane_offset(c, a, block, lane)
                                    : weight_lane_offset<MT, CM>(c, a, block - WB, lane, grp);
           const uint32_t ch = win ? window_channel_bytes(a) : weight_channel_bytes(a);
-          const int64_t range = win ? int64_t(nco) * OHOW * 4 : int64_t(nco) * cstride * 4;
+          // the buffer ranges of stage_src: a forward stage's weights run to
+          // the end of w, and its channels past nco are cut per load instead
+          const int64_t range = win ? int64_t(nco) * OHOW * 4
+                                    : fwd ? (w_size - int64_t(co0) * a.wsk) * 4
+                                          : int64_t(nco) * a.wsk * 4;
           C2B_REQUIRE(off == kPadOffset || off % 4 == 0, "unaligned copy offset");
           const int f = batch_lds_float(P, block, quad, lane);
           if (f < 0) continue;                               // lane writes nothing
@@ -128,9 +139,10 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
             unsigned char& cov = covered[size_t(st) * size_t(P.used) + size_t(cell)];
             C2B_REQUIRE(cov == 0, "stage %d cell %d written twice", st, cell);
             cov = 1;
-            const uint64_t o64 = uint64_t(off) + uint64_t(4 * quad + q) * ch;
+            const bool cut = fwd && !win && 4 * quad + q >= nco;   // forward channel guard
+            const uint64_t o64 = cut ? uint64_t(kPadOffset) : uint64_t(off) + uint64_t(4 * quad + q) * ch;
             C2B_REQUIRE(o64 < (uint64_t(1) << 32), "copy offset wraps");
-            const bool pad = off == kPadOffset;
+            const bool pad = off == kPadOffset || cut;
             C2B_REQUIRE(!pad || int64_t(o64) >= range, "padding cell inside the range");
             const bool reads = !pad && int64_t(o64) < range;
             if (win) {
@@ -151,7 +163,8 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
             } else {
               const int e = cell - P.wfl;
               const int o = mm_weight_cell<MT, CM>(c, a, e, grp);
-              if (o < 0 || int64_t(o) >= int64_t(nco) * cstride) {
+              const int cch = 4 * (e / QP) + (e % QP) % 4;   // the cell's contraction channel
+              if (o < 0 || cch >= nco) {
                 C2B_REQUIRE(!reads, "weight cell %d should read 0", e);
                 continue;
               }
@@ -163,7 +176,13 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
               // class, or (cm) channel ci0 + m / twm at row tap tap0 + t and
               // column tap m mod twm
               int64_t want;
-              if (CM) {
+              if (fwd) {
+                // w[co, ci, kh, kw] with co = matrix row, ci = contraction
+                // channel, and the flipped tap kh = KH-1-j, kw = KW-1-l
+                const int tap = tap0 + t, jt = tap / P.tw, lt = tap % P.tw;
+                want = ((int64_t(c.ci0 + m) * prm.in_channels + co0 + co) * a.KH +
+                        (a.KH - 1 - jt)) * a.KW + (a.KW - 1 - lt);
+              } else if (CM) {
                 const int cl = m / a.twm, l = m % a.twm, jt = tap0 + t;
                 C2B_REQUIRE(l < P.tw && cl < a.cit && jt < P.th, "cm weight cell %d", e);
                 want = (int64_t(co0 + co) * a.Ci + c.ci0 + cl) * KHW +
@@ -171,7 +190,7 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
               } else {
                 want = (int64_t(co0 + co) * a.Ci + c.ci0 + m) * KHW + tap_kidx(P, a, tap0 + t);
               }
-              const int64_t wi = int64_t(co0) * cstride + o;
+              const int64_t wi = int64_t(co0) * a.wsk + o;
               C2B_REQUIRE(wi == want && wi >= 0 && wi < w_size, "weight element");
             }
           }
@@ -212,9 +231,17 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
             } else if (local < c.npx) {
               C2B_REQUIRE(slot < c.R * c.roww, "slot beyond window");
               const int qq = c.p0 + local, ip = qq / P.wb, jj = c.band * P.wb + qq % P.wb;
-              C2B_REQUIRE(c.oh_base + slot / c.roww == ip + P.ch - j &&
-                              c.ow_base + slot % c.roww == jj + P.cw - l,
-                          "tap (%d,%d) reads the wrong grad_out element", j, l);
+              const int row = c.oh_base + slot / c.roww, col = c.ow_base + slot % c.roww;
+              if (fwd) {
+                // forward definition: output pixel (ip, jj) at kernel tap
+                // (KH-1-j, KW-1-l) reads x[s*ip - padding_h + kh, ...]
+                C2B_REQUIRE(row == int(prm.stride) * ip - int(prm.padding_h) + (a.KH - 1 - j) &&
+                                col == int(prm.stride) * jj - int(prm.padding_w) + (a.KW - 1 - l),
+                            "forward tap (%d,%d) reads the wrong x element", j, l);
+              } else {
+                C2B_REQUIRE(row == ip + P.ch - j && col == jj + P.cw - l,
+                            "tap (%d,%d) reads the wrong grad_out element", j, l);
+              }
             }
           }
           if (++t == ntg) {
@@ -250,7 +277,7 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
         const int po = output_offset(c, a, mm_local(b, ng, c16, WN));
         if (po < 0) continue;
         const int ih = po / a.W, iw = po % a.W;
-        C2B_REQUIRE(((ih + a.PH) % a.S) == P.rh && ((iw + a.PW) % a.S) == P.rw,
+        C2B_REQUIRE(fwd || (((ih + a.PH) % a.S) == P.rh && ((iw + a.PW) % a.S) == P.rw),
                     "pixel (%d,%d) outside class", ih, iw);
         for (int m = 0; m < MB; ++m)
           for (int r = 0; r < 4; ++r) {
@@ -302,26 +329,33 @@ void check_launch(const LaunchArgs& a, std::vector<unsigned char>& written) {
 }
 
 template <int V>
-void check_variant(const LaunchArgs& la, std::vector<unsigned char>& written) {
+void check_variant(const LaunchArgs& la, const conv2d_params& prm,
+                   std::vector<unsigned char>& written) {
   constexpr Variant v = kVariants[V];
-  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v), v.cm != 0>(la, written);
+  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v), v.cm != 0>(la, prm, written);
 }
 
 template <int... Vs>
-void check_dispatch(const LaunchArgs& la, std::vector<unsigned char>& written,
-                    std::integer_sequence<int, Vs...>) {
-  ((la.variant == Vs ? check_variant<Vs>(la, written) : void()), ...);
+void check_dispatch(const LaunchArgs& la, const conv2d_params& prm,
+                    std::vector<unsigned char>& written, std::integer_sequence<int, Vs...>) {
+  ((la.variant == Vs ? check_variant<Vs>(la, prm, written) : void()), ...);
 }
 
-int check_all(const conv2d_params* p, int f16, int variant, char* msg, size_t len) {
+int check_all(const conv2d_params* p, int f16, int variant, char* msg, size_t len,
+              int op = kOpGradInput) {
   std::vector<LaunchArgs> launches;
-  const int rc = build_plan(p, f16, kDefaultCUs, &launches, nullptr, variant);
+  const int rc = build_plan(p, f16, kDefaultCUs, &launches, nullptr, variant, nullptr, op);
   if (rc != CONV2D_OK) return rc;
-  const int64_t n_gi = int64_t(p->batch) * p->in_channels * p->in_h * p->in_w;
+  // elements of the output: grad_input, or y on a forward launch
+  const int64_t n_gi = op == kOpForward
+                           ? int64_t(p->batch) * p->out_channels * p->out_h * p->out_w
+                           : int64_t(p->batch) * p->in_channels * p->in_h * p->in_w;
   std::vector<unsigned char> written(size_t(n_gi), 0);
   try {
-    for (const LaunchArgs& la : launches)
-      check_dispatch(la, written, std::make_integer_sequence<int, kNumVariants>());
+    for (const LaunchArgs& la : launches) {
+      C2B_REQUIRE(la.fwd == (op == kOpForward ? 1 : 0), "launch operation");
+      check_dispatch(la, *p, written, std::make_integer_sequence<int, kNumVariants>());
+    }
     for (int64_t i = 0; i < n_gi; ++i)
       C2B_REQUIRE(written[i] == 1, "grad_input element %lld never written", (long long)i);
   } catch (const Failure& f) {
@@ -347,4 +381,15 @@ extern "C" int conv2d_check_indexing_variant(const conv2d_params* p, int variant
                                              size_t msg_len) {
   if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
   return c2b::check_all(p, c2b::kVariants[variant].f16, variant, msg, msg_len);
+}
+
+extern "C" int conv2d_check_indexing_forward(const conv2d_params* p, int f16, char* msg,
+                                             size_t msg_len) {
+  return c2b::check_all(p, f16 ? 1 : 0, -1, msg, msg_len, c2b::kOpForward);
+}
+
+extern "C" int conv2d_check_indexing_forward_variant(const conv2d_params* p, int variant,
+                                                     char* msg, size_t msg_len) {
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::check_all(p, c2b::kVariants[variant].f16, variant, msg, msg_len, c2b::kOpForward);
 }

@@ -44,6 +44,8 @@
 //  * Epilogue: masked stores straight to NCHW grad_input; every pixel of a
 //    class is owned by exactly one tile, so grad_input is overwritten once,
 //    with no race between workgroups.
+//  * The same body, with the roles of the operands exchanged (plan.hpp),
+//    runs the forward convolution (conv2d_forward_mm_kernel).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -76,10 +78,10 @@ __device__ __forceinline__ f16x8 join(f16x4 lo, f16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
-__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
-    const LaunchArgs a) {
+template <bool FWD, bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
+__device__ __forceinline__ void mm_body(const LaunchArgs& a) {
   static_assert(!CM || (WM == 1 && MB == 1), "cm: one matrix block of rows");
+  static_assert(!FWD || !CM, "forward launches have no cm variant");
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int MT = G::kMT, NW = G::kWaves, NJ = G::kBatches;
   constexpr int kStageFloats = SF;   // this instance's stage buffer
@@ -94,7 +96,6 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
   const TileCtx c = decode_tile(a, blockIdx.x);
   const PhaseDesc& P = c.P;
   const int OHOW = a.OH * a.OW;
-  const int cstride = a.Ci * a.KH * a.KW;
   const float* go_n = a.go + (size_t)c.n * a.Co * OHOW;
   const int nst = c.nstages;
   // copy batches (tile_index.hpp): batch wave + NW*j of every stage is this
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
   int wgroup = -1;    // tap group the weight offsets are for
   struct StageSrc {
     __amdgpu_buffer_rsrc_t rg, rw;
+    int nco;   // contraction channels of the stage
   };
   // (Every lambda here is forced inline: an outlined one becomes a real call
   // with its own stack frame.)
@@ -116,10 +118,16 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
     stage_split(c, st, &co0, &grp);
     const int nco = imin(16 * P.cg, a.Co - co0);
     StageSrc sc;
+    sc.nco = nco;
     sc.rg = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(go_n + (size_t)co0 * OHOW), 0,
                                               nco * OHOW * 4, kRawBufferFlags);
-    sc.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.w + (size_t)co0 * cstride), 0,
-                                              nco * cstride * 4, kRawBufferFlags);
+    // the stage's weights: its contraction channels, which on the input-
+    // gradient path are whole leading rows of w; on a forward launch they
+    // are interleaved with the other channels of every output channel, so
+    // the range runs to the end of w
+    const int wrange = FWD ? a.Ci * a.Co * a.KH * a.KW - co0 * a.wsk : nco * a.wsk;
+    sc.rw = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.w + (size_t)co0 * a.wsk), 0,
+                                              wrange * 4, kRawBufferFlags);
     return sc;
   };
   // Source offsets of this wave's batches: window blocks once per tile,
@@ -163,8 +171,17 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
       const __amdgpu_buffer_rsrc_t rs = win ? sc.rg : sc.rw;
       const uint32_t ch = win ? wch : tch;
       const uint32_t o = off[j] + 4u * uint32_t(quad) * ch;
-      stg[j] = f32x4{load_f32(rs, o), load_f32(rs, o + ch), load_f32(rs, o + 2u * ch),
-                     load_f32(rs, o + 3u * ch)};
+      uint32_t o0 = o, o1 = o + ch, o2 = o + 2u * ch, o3 = o + 3u * ch;
+      if (FWD && !win) {
+        // forward: weights of channels past the stage's last one are not
+        // cut by the buffer range (see stage_src), so they read 0 explicitly
+        const int c0 = 4 * quad;
+        if (c0 >= sc.nco) o0 = kPadOffset;
+        if (c0 + 1 >= sc.nco) o1 = kPadOffset;
+        if (c0 + 2 >= sc.nco) o2 = kPadOffset;
+        if (c0 + 3 >= sc.nco) o3 = kPadOffset;
+      }
+      stg[j] = f32x4{load_f32(rs, o0), load_f32(rs, o1), load_f32(rs, o2), load_f32(rs, o3)};
     }
   };
   // LDS writes of stg[] into stage buffer buf (16 bytes per lane).
@@ -397,9 +414,32 @@ __global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad
   }
 }
 
+// The input-gradient kernel, one instantiation per variant.
+template <bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
+__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
+    const LaunchArgs a) {
+  mm_body<false, F16, WM, WN, MB, NBW, SF, CM>(a);
+}
+
+// The forward convolution on the same body (roles exchanged, plan.hpp), one
+// instantiation per variant without cm.
+template <bool F16, int WM, int WN, int MB, int NBW, int SF>
+__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void conv2d_forward_mm_kernel(
+    const LaunchArgs a) {
+  mm_body<true, F16, WM, WN, MB, NBW, SF, false>(a);
+}
+
 template <int V>
 void launch_variant(const LaunchArgs& la, hipStream_t st) {
   constexpr Variant v = kVariants[V];
+  if constexpr (v.cm == 0) {
+    if (la.fwd) {
+      hipLaunchKernelGGL((conv2d_forward_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw,
+                                                   stage_floats(v)>),
+                         dim3(la.total_tiles), dim3(64 * v.wm * v.wn), 0, st, la);
+      return;
+    }
+  }
   hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw, stage_floats(v),
                                            v.cm != 0>),
                      dim3(la.total_tiles), dim3(64 * v.wm * v.wn), 0, st, la);
@@ -429,12 +469,12 @@ int device_cus() {
 }
 
 // Launch plans of recent shapes (host memory only), so that a repeated call
-// skips the planner's search.  Keyed by the shape, the path, the forced
-// variant (-1: the default plan, the model's choice or a tuned one) and the
-// CU count; at most kPlanCacheSize entries, oldest evicted.
+// skips the planner's search.  Keyed by the shape, the operation, the path,
+// the forced variant (-1: the default plan, the model's choice or a tuned
+// one) and the CU count; at most kPlanCacheSize entries, oldest evicted.
 struct PlanKey {
   conv2d_params p;
-  int f16, variant, cus;
+  int op, f16, variant, cus;
 };
 struct PlanEntry {
   PlanKey key;
@@ -451,10 +491,11 @@ std::vector<PlanEntry>& plan_cache() {
   return cache;
 }
 
-PlanKey plan_key(const conv2d_params* p, int f16, int variant, int cus) {
+PlanKey plan_key(const conv2d_params* p, int op, int f16, int variant, int cus) {
   PlanKey key;
   std::memset(&key, 0, sizeof(key));
   key.p = *p;
+  key.op = op;
   key.f16 = f16;
   key.variant = variant;
   key.cus = cus;
@@ -474,9 +515,9 @@ void store_plan(const PlanKey& key, const std::vector<LaunchArgs>& launches) {
   cache.push_back(PlanEntry{key, launches});
 }
 
-int cached_plan(const conv2d_params* p, int f16, int variant, int cus,
+int cached_plan(const conv2d_params* p, int op, int f16, int variant, int cus,
                 std::vector<LaunchArgs>* out) {
-  const PlanKey key = plan_key(p, f16, variant, cus);
+  const PlanKey key = plan_key(p, op, f16, variant, cus);
   {
     std::lock_guard<std::mutex> lock(plan_cache_mutex());
     for (const PlanEntry& e : plan_cache())
@@ -485,7 +526,7 @@ int cached_plan(const conv2d_params* p, int f16, int variant, int cus,
         return CONV2D_OK;
       }
   }
-  const int rc = build_plan(p, f16, cus, out, nullptr, variant);
+  const int rc = build_plan(p, f16, cus, out, nullptr, variant, nullptr, op);
   if (rc != CONV2D_OK) return rc;
   store_plan(key, *out);
   return CONV2D_OK;
@@ -505,13 +546,13 @@ int enqueue(std::vector<LaunchArgs>& launches, const float* go, const float* w, 
 }
 
 int launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
-           int variant, void* stream) {
+           int variant, void* stream, int op = kOpGradInput) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
-  rc = check_pointers(go, w, gi, p);
+  rc = check_pointers(go, w, gi, p, op);
   if (rc != CONV2D_OK) return rc;
   std::vector<LaunchArgs> launches;
-  rc = cached_plan(p, f16, variant, device_cus(), &launches);
+  rc = cached_plan(p, op, f16, variant, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
   return enqueue(launches, go, w, gi, static_cast<hipStream_t>(stream));
 }
@@ -525,21 +566,21 @@ constexpr double kTuneSpread = 1.3;
 constexpr int kTuneReps = 5;
 
 int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
-         void* stream, int* variant_out) {
+         void* stream, int* variant_out, int op = kOpGradInput) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
-  rc = check_pointers(go, w, gi, p);
+  rc = check_pointers(go, w, gi, p, op);
   if (rc != CONV2D_OK) return rc;
   const int cus = device_cus();
   std::vector<std::pair<double, int>> cand;
   for (int v = 0; v < kNumVariants; ++v) {
     if (kVariants[v].f16 != f16) continue;
     double cost = 0.0;
-    if (build_plan(p, f16, cus, nullptr, nullptr, v, &cost) == CONV2D_OK)
+    if (build_plan(p, f16, cus, nullptr, nullptr, v, &cost, op) == CONV2D_OK)
       cand.push_back({cost, v});
   }
   std::vector<LaunchArgs> launches;
-  rc = cached_plan(p, f16, -1, cus, &launches);   // the model's choice
+  rc = cached_plan(p, op, f16, -1, cus, &launches);   // the model's choice
   if (rc != CONV2D_OK) return rc;
   int best_v = launches.empty() ? -1 : launches[0].variant;
   std::sort(cand.begin(), cand.end());
@@ -556,7 +597,7 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
     for (const auto& c : cand) {
       if (c.first > kTuneSpread * cand[0].first) break;
       std::vector<LaunchArgs> plan;
-      rc = cached_plan(p, f16, c.second, cus, &plan);
+      rc = cached_plan(p, op, f16, c.second, cus, &plan);
       if (rc != CONV2D_OK) break;
       rc = enqueue(plan, go, w, gi, st);   // warm-up
       if (rc != CONV2D_OK) break;
@@ -580,9 +621,9 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
     (void)hipEventDestroy(e1);
     if (rc != CONV2D_OK) return rc;
     if (!best_plan.empty()) {
-      store_plan(plan_key(p, f16, -1, cus), best_plan);
+      store_plan(plan_key(p, op, f16, -1, cus), best_plan);
       best_v = best_plan[0].variant;
-      // leave grad_input holding the result of the chosen plan
+      // leave the output holding the result of the chosen plan
       rc = enqueue(best_plan, go, w, gi, st);
       if (rc != CONV2D_OK) return rc;
     }
@@ -596,9 +637,9 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
 
 // The variant the default entry point of a path uses for a shape now (-1 if
 // the shape launches nothing).
-int planned_variant(const conv2d_params* p, int f16, int* variant_out) {
+int planned_variant(const conv2d_params* p, int f16, int* variant_out, int op = kOpGradInput) {
   std::vector<LaunchArgs> launches;
-  const int rc = cached_plan(p, f16, -1, device_cus(), &launches);
+  const int rc = cached_plan(p, op, f16, -1, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
   *variant_out = launches.empty() ? -1 : launches[0].variant;
   return CONV2D_OK;
@@ -635,4 +676,35 @@ extern "C" int conv2d_planned_variant(const conv2d_params* p, int f16, int* vari
   const int rc = c2b::validate_shape(p);
   if (rc != CONV2D_OK) return rc;
   return c2b::planned_variant(p, f16 ? 1 : 0, variant_out);
+}
+
+extern "C" int conv2d_forward(const float* x, const float* weight, float* y,
+                              const conv2d_params* p, void* stream) {
+  return c2b::launch(x, weight, y, p, 0, -1, stream, c2b::kOpForward);
+}
+
+extern "C" int conv2d_forward_f16(const float* x, const float* weight, float* y,
+                                  const conv2d_params* p, void* stream) {
+  return c2b::launch(x, weight, y, p, 1, -1, stream, c2b::kOpForward);
+}
+
+extern "C" int conv2d_forward_variant(const float* x, const float* weight, float* y,
+                                      const conv2d_params* p, int variant, void* stream) {
+  if (p == nullptr) return CONV2D_ERR_NULL_PTR;
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::launch(x, weight, y, p, c2b::kVariants[variant].f16, variant, stream,
+                     c2b::kOpForward);
+}
+
+extern "C" int conv2d_tune_forward(const float* x, const float* weight, float* y,
+                                   const conv2d_params* p, int f16, void* stream,
+                                   int* variant_out) {
+  return c2b::tune(x, weight, y, p, f16 ? 1 : 0, stream, variant_out, c2b::kOpForward);
+}
+
+extern "C" int conv2d_planned_forward_variant(const conv2d_params* p, int f16, int* variant_out) {
+  if (p == nullptr || variant_out == nullptr) return CONV2D_ERR_NULL_PTR;
+  const int rc = c2b::validate_shape(p);
+  if (rc != CONV2D_OK) return rc;
+  return c2b::planned_variant(p, f16 ? 1 : 0, variant_out, c2b::kOpForward);
 }

@@ -50,10 +50,13 @@ int validate_shape(const conv2d_params* p) {
 }
 
 int check_pointers(const float* go, const float* w, const float* gi,
-                   const conv2d_params* p) {
+                   const conv2d_params* p, int op) {
   if (p == nullptr) return CONV2D_ERR_NULL_PTR;
-  const uint64_t n_gi = uint64_t(p->batch) * p->in_channels * p->in_h * p->in_w;
-  const uint64_t n_go = uint64_t(p->batch) * p->out_channels * p->out_h * p->out_w;
+  // input-side and output-side element counts: forward reads x and writes y
+  const uint64_t n_x = uint64_t(p->batch) * p->in_channels * p->in_h * p->in_w;
+  const uint64_t n_y = uint64_t(p->batch) * p->out_channels * p->out_h * p->out_w;
+  const uint64_t n_gi = op == kOpForward ? n_y : n_x;   // written
+  const uint64_t n_go = op == kOpForward ? n_x : n_y;   // read
   const uint64_t n_w = uint64_t(p->out_channels) * p->in_channels * p->kernel_h *
                        p->kernel_w;
   if ((n_gi && gi == nullptr) || (n_go && go == nullptr) || (n_w && w == nullptr))
@@ -92,6 +95,8 @@ static void make_classes(const conv2d_params* p, std::vector<PhaseDesc>* out) {
       d.iw0 = int32_t(iw0);
       d.hp = int32_t(hp);
       d.wp = int32_t(wp);
+      d.ss = 1;
+      d.kstep = int32_t(S);
       if (th > 0 && tw > 0) {
         d.th = int32_t(th);
         d.tw = int32_t(tw);
@@ -103,20 +108,57 @@ static void make_classes(const conv2d_params* p, std::vector<PhaseDesc>* out) {
   }
 }
 
+// The forward convolution as one class over the output plane (plan.hpp):
+// all KH x KW taps, flipped (kernel index (KH-1-j, KW-1-l)), window sampled
+// every `stride` source rows and columns.
+static void make_forward_class(const conv2d_params* p, std::vector<PhaseDesc>* out) {
+  PhaseDesc d;
+  std::memset(&d, 0, sizeof(d));
+  d.rh = int32_t(p->kernel_h) - 1;
+  d.rw = int32_t(p->kernel_w) - 1;
+  d.kstep = -1;
+  d.ss = int32_t(p->stride);
+  d.hp = int32_t(p->out_h);
+  d.wp = int32_t(p->out_w);
+  d.th = int32_t(p->kernel_h);
+  d.tw = int32_t(p->kernel_w);
+  d.ch = int32_t(p->kernel_h) - 1 - int32_t(p->padding_h);
+  d.cw = int32_t(p->kernel_w) - 1 - int32_t(p->padding_w);
+  if (d.hp > 0 && d.wp > 0) out->push_back(d);
+}
+
 static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks, int64_t cit, int cm,
-                                int64_t twm) {
+                                int64_t twm, int op) {
   LaunchArgs la;
   std::memset(&la, 0, sizeof(la));
+  const int32_t KHW = int32_t(p->kernel_h * p->kernel_w);
   la.N = int32_t(p->batch);
+  la.KH = int32_t(p->kernel_h);
+  la.KW = int32_t(p->kernel_w);
+  la.PH = int32_t(p->padding_h);
+  la.PW = int32_t(p->padding_w);
+  if (op == kOpForward) {   // roles exchanged (plan.hpp)
+    la.fwd = 1;
+    la.Ci = int32_t(p->out_channels);
+    la.H = int32_t(p->out_h);
+    la.W = int32_t(p->out_w);
+    la.Co = int32_t(p->in_channels);
+    la.S = 1;
+    la.OH = int32_t(p->in_h);
+    la.OW = int32_t(p->in_w);
+    la.wsm = int32_t(p->in_channels) * KHW;   // w[co, ci, kh, kw]: co is the row
+    la.wsk = KHW;
+    la.ciblocks = int32_t(ciblocks);
+    la.cit = int32_t(cit);
+    return la;
+  }
   la.Ci = int32_t(p->in_channels);
   la.H = int32_t(p->in_h);
   la.W = int32_t(p->in_w);
   la.Co = int32_t(p->out_channels);
-  la.KH = int32_t(p->kernel_h);
-  la.KW = int32_t(p->kernel_w);
   la.S = int32_t(p->stride);
-  la.PH = int32_t(p->padding_h);
-  la.PW = int32_t(p->padding_w);
+  la.wsm = KHW;                               // ci is the row, co the channel
+  la.wsk = int32_t(p->in_channels) * KHW;
   la.OH = int32_t(p->out_h);
   la.OW = int32_t(p->out_w);
   la.ciblocks = int32_t(ciblocks);
@@ -133,7 +175,7 @@ static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks, int64_
 // positions inside a band row plus one tile of pixels.
 static int finalize_divisors(PhaseDesc* d) {
   const int64_t lim = int64_t(1) << 31;
-  const int64_t roww = std::max<int64_t>(int64_t(d->wb) + d->tw - 1, 1);
+  const int64_t roww = std::max<int64_t>((int64_t(d->wb) - 1) * d->ss + d->tw, 1);
   const int64_t wb = d->wb, tw = std::max(d->tw, 1);
   const int64_t slots4 = std::max<int64_t>(4 * int64_t(d->slots), 1);
   const int64_t qp = std::max(d->qp, 1), pt4 = std::max<int64_t>(4 * int64_t(d->pt), 1);
@@ -160,9 +202,9 @@ static int finalize_divisors(PhaseDesc* d) {
 // kMaxPhasesPerLaunch classes.
 static int emit_launches(const conv2d_params* p, int64_t ciblocks, int64_t cit, int64_t twm,
                          int variant, const std::vector<PhaseDesc>& phases,
-                         std::vector<LaunchArgs>* launches, conv2d_plan_info* info) {
+                         std::vector<LaunchArgs>* launches, conv2d_plan_info* info, int op) {
   for (size_t base = 0; base < phases.size(); base += kMaxPhasesPerLaunch) {
-    LaunchArgs la = launch_header(p, ciblocks, cit, kVariants[variant].cm, twm);
+    LaunchArgs la = launch_header(p, ciblocks, cit, kVariants[variant].cm, twm, op);
     la.variant = variant;
     int64_t total = 0;
     const size_t end = std::min(phases.size(), base + kMaxPhasesPerLaunch);
@@ -216,17 +258,17 @@ int64_t max_rows_spanned(int64_t wb, int64_t ntv, int64_t bp) {
 // pixels, halving the tile until the window fits.
 bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* wb_out,
                    int64_t* ntv_out, int64_t* slots_out) {
-  const int64_t th = d.th, tw = d.tw, hp = d.hp, wp = d.wp;
+  const int64_t th = d.th, tw = d.tw, hp = d.hp, wp = d.wp, ss = d.ss;
   int64_t last_wb = -1;
   for (int64_t nb = 1; nb <= wp; ++nb) {
     const int64_t wb = ceil_div(wp, nb);
     if (wb == last_wb) continue;
     last_wb = wb;
     const int64_t bp = hp * wb;
-    const int64_t roww = wb + tw - 1;
+    const int64_t roww = (wb - 1) * ss + tw;
     for (int64_t cap = ntl;; cap = (cap + 1) / 2) {
       const int64_t ntv = ceil_div(bp, ceil_div(bp, cap));
-      const int64_t rows = max_rows_spanned(wb, ntv, bp) + th - 1;
+      const int64_t rows = (max_rows_spanned(wb, ntv, bp) - 1) * ss + th;
       const int64_t slots = ceil_div(rows * roww, 16) * 16;
       if (slots <= max_slots) {
         *wb_out = wb;
@@ -408,23 +450,37 @@ double lpt_makespan(const std::vector<PhaseDesc>& phases, int64_t per_class_mult
 }  // namespace
 
 int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchArgs>* launches,
-               conv2d_plan_info* info, int force_variant, double* model_cost) {
+               conv2d_plan_info* info, int force_variant, double* model_cost, int op) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
+  if (op != kOpGradInput && op != kOpForward) return CONV2D_ERR_UNSUPPORTED;
   if (info) std::memset(info, 0, sizeof(*info));
+  const bool fwd = op == kOpForward;
   const int64_t N = p->batch, Ci = p->in_channels, H = p->in_h, W = p->in_w;
   const int64_t Co = p->out_channels;
   const int64_t KHW = int64_t(p->kernel_h) * p->kernel_w;
   if (info) info->useful_macs = N * Co * p->out_h * p->out_w * Ci * KHW;
   if (force_variant >= kNumVariants || (force_variant >= 0 && kVariants[force_variant].f16 != (f16 ? 1 : 0)))
     return CONV2D_ERR_UNSUPPORTED;
-  if (N == 0 || Ci == 0 || H == 0 || W == 0) return CONV2D_OK;
+  if (force_variant >= 0 && fwd && kVariants[force_variant].cm) return CONV2D_ERR_UNSUPPORTED;
+  // nothing to write: an empty output (the forward output is empty only
+  // with no image or no output channel; Ci = 0 or an empty input still
+  // writes zeros)
+  if (fwd ? (N == 0 || Co == 0) : (N == 0 || Ci == 0 || H == 0 || W == 0)) return CONV2D_OK;
   if (num_cus < 1) num_cus = kDefaultCUs;
   const int64_t OHOW = int64_t(p->out_h) * p->out_w;
-  const int64_t cstride = Ci * KHW;
+  // roles (plan.hpp): matrix rows, contraction channels, source plane, and
+  // weight elements between contraction channels
+  const int64_t Mch = fwd ? Co : Ci;
+  const int64_t Kch = fwd ? Ci : Co;
+  const int64_t src_plane = fwd ? H * W : OHOW;
+  const int64_t cstride = fwd ? KHW : Ci * KHW;
+  // a forward stage's weight buffer reaches to the end of the tensor
+  if (fwd && Co * Ci * KHW * 4 >= kI31) return CONV2D_ERR_OVERFLOW;
 
   std::vector<PhaseDesc> classes;
-  make_classes(p, &classes);
+  if (fwd) make_forward_class(p, &classes);
+  else make_classes(p, &classes);
   // cm variants: matrix rows per input channel (the widest class's column
   // taps) and input channels per tile
   const int64_t twm = ceil_div(p->kernel_w, p->stride);
@@ -439,12 +495,13 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   for (int v = 0; v < kNumVariants; ++v) {
     const Variant& var = kVariants[v];
     if (force_variant >= 0 ? v != force_variant : var.f16 != (f16 ? 1 : 0)) continue;
+    if (fwd && var.cm) continue;
     const int64_t vmt = channels_per_tile(var);
     if (vmt < 1) continue;
     std::vector<PhaseDesc> phases = classes;
     bool ok = true;
     for (PhaseDesc& d : phases)
-      if (!tile_class(&d, var, Co, OHOW, cstride)) {
+      if (!tile_class(&d, var, Kch, src_plane, cstride)) {
         ok = false;
         break;
       }
@@ -453,11 +510,11 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     // than CUs
     int64_t ntiles = 0;
     for (const PhaseDesc& d : phases)
-      ntiles += N * d.nbands * int64_t(d.ptiles) * ceil_div(Ci, vmt);
+      ntiles += N * d.nbands * int64_t(d.ptiles) * ceil_div(Mch, vmt);
     const int share = (var.half && ntiles > num_cus) ? 2 : 1;
     std::vector<double> costs;
-    for (const PhaseDesc& d : phases) costs.push_back(tile_cost(d, Co, var, share));
-    const double cost = lpt_makespan(phases, N * ceil_div(Ci, vmt), costs, num_cus * share);
+    for (const PhaseDesc& d : phases) costs.push_back(tile_cost(d, Kch, var, share));
+    const double cost = lpt_makespan(phases, N * ceil_div(Mch, vmt), costs, num_cus * share);
     if (best_v < 0 || cost < best_cost * 0.999) {
       best_v = v;
       best_cost = cost;
@@ -470,7 +527,7 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   const Variant& bv = kVariants[best_v];
   const int64_t bmt = 16 * int64_t(bv.wm) * bv.mb;   // matrix rows per tile
   const int64_t bcit = channels_per_tile(bv);
-  const int64_t bci = ceil_div(Ci, bcit);
+  const int64_t bci = ceil_div(Mch, bcit);
   for (PhaseDesc& d : best) {
     const int64_t tiles = N * d.nbands * int64_t(d.ptiles) * bci;
     if (tiles >= kI31) return CONV2D_ERR_OVERFLOW;
@@ -487,9 +544,9 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     }
   }
   std::stable_sort(best.begin(), best.end(), [&](const PhaseDesc& a, const PhaseDesc& b) {
-    return tile_cost(a, Co, bv, 1) > tile_cost(b, Co, bv, 1);
+    return tile_cost(a, Kch, bv, 1) > tile_cost(b, Kch, bv, 1);
   });
-  return emit_launches(p, bci, bcit, twm, best_v, best, launches, info);
+  return emit_launches(p, bci, bcit, twm, best_v, best, launches, info, op);
 }
 
 }  // namespace c2b
@@ -512,6 +569,21 @@ extern "C" int conv2d_describe_plan_variant(const conv2d_params* p, int variant,
   if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
   return c2b::build_plan(p, c2b::kVariants[variant].f16, c2b::kDefaultCUs, nullptr, out,
                          variant);
+}
+
+extern "C" int conv2d_describe_forward_plan(const conv2d_params* p, int f16,
+                                            conv2d_plan_info* out) {
+  if (out == nullptr) return CONV2D_ERR_NULL_PTR;
+  return c2b::build_plan(p, f16 ? 1 : 0, c2b::kDefaultCUs, nullptr, out, -1, nullptr,
+                         c2b::kOpForward);
+}
+
+extern "C" int conv2d_describe_forward_plan_variant(const conv2d_params* p, int variant,
+                                                    conv2d_plan_info* out) {
+  if (p == nullptr || out == nullptr) return CONV2D_ERR_NULL_PTR;
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::build_plan(p, c2b::kVariants[variant].f16, c2b::kDefaultCUs, nullptr, out,
+                         variant, nullptr, c2b::kOpForward);
 }
 
 extern "C" int conv2d_num_variants(void) { return c2b::kNumVariants; }

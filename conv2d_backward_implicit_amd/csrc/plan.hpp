@@ -25,6 +25,18 @@
 // copied into one of two LDS stage buffers while the other buffer is
 // multiplied.  Stages run tap-group-major: for each tap group, every chunk of
 // 16*cg output channels.
+//
+// Forward convolution (the adjoint operator, same kernels).  With the kernel
+// taps flipped, j = KH-1-kh and l = KW-1-kw, the forward convolution
+//   y[n, co, oh, ow] = sum over ci, kh, kw of
+//       x[n, ci, s*oh - padding_h + kh, s*ow - padding_w + kw] * w[co, ci, kh, kw]
+// reads x row s*oh + ch - j with ch = KH-1-padding_h: the form of a class
+// above with the output plane as the class sub-image, all KH x KW taps, and
+// the window sampled every s rows and columns (PhaseDesc::ss).  A forward
+// launch therefore runs the same kernels with the roles exchanged: the
+// matrix rows are the output channels co, the contraction runs over the
+// input channels ci and the taps, the window is cut from x and the results
+// go to y (LaunchArgs::fwd).
 #pragma once
 
 #include <stdint.h>
@@ -48,7 +60,9 @@ struct PhaseDesc {
   int32_t ih0, iw0;    // first input row / column of the class
   int32_t hp, wp;      // rows / columns of the class sub-image
   int32_t th, tw;      // sub-kernel taps per axis (0: class gets zeros)
-  int32_t ch, cw;      // grad_out row = i' + ch - j, column = j' + cw - l
+  int32_t ch, cw;      // source row = ss*i' + ch - j, column = ss*j' + cw - l
+  int32_t ss;          // source rows / columns per pixel step (1; forward: stride)
+  int32_t kstep;       // kernel index of tap (j, l): (rh + kstep*j, rw + kstep*l)
   int32_t wb;          // band width: sub-image columns per band
   int32_t nbands;      // bands per sub-image row, ceil(wp / wb)
   int32_t ntv;         // pixels per tile (<= the kernel's lane tile)
@@ -65,7 +79,7 @@ struct PhaseDesc {
   int32_t wfl;         // window floats of a stage buffer: 16 * cg * slots
   int32_t used;        // floats of a stage buffer copied: wfl + 4 * cg * qp
   // reciprocals for per-lane division: m = ceil(2^31 / d), see fast_div
-  uint32_t m_roww;     // d = wb + tw - 1
+  uint32_t m_roww;     // d = roww = ss*(wb - 1) + tw
   uint32_t m_wb;       // d = wb
   uint32_t m_tw;       // d = tw
   uint32_t m_slots4;   // d = 4 * slots
@@ -75,12 +89,18 @@ struct PhaseDesc {
   uint32_t m_blocks;   // d = copy blocks of a quad (window + weight blocks)
 };
 
-// By-value kernel argument block of one launch.
+// By-value kernel argument block of one launch.  For a forward launch
+// (fwd = 1) the fields keep their input-gradient roles: go is x, gi is y, Ci
+// and H x W are the output channels and plane, Co and OH x OW the input
+// channels and plane, and S = 1 (the output plane is dense; the stride is the
+// classes' ss).
 struct LaunchArgs {
   const float* go;
   const float* w;
   float* gi;
   int32_t N, Ci, H, W, Co, KH, KW, S, PH, PW, OH, OW;
+  int32_t fwd;         // 1: forward convolution launch (roles above)
+  int32_t wsm, wsk;    // weight elements between matrix rows / contraction channels
   int32_t ciblocks;    // ceil(Ci / cit)
   int32_t cit;         // input channels per tile
   int32_t cm;          // 1: column taps in the matrix rows (see Variant::cm)
@@ -154,6 +174,9 @@ namespace c2b {
 // Shape checks shared by every entry point (no pointer is looked at).
 int validate_shape(const conv2d_params* p);
 
+// The two operations the kernels run.
+enum Op { kOpGradInput = 0, kOpForward = 1 };
+
 // Plan for the fp32 (f16 == 0) or f16-staged path on a device with
 // `num_cus` compute units: chooses the variant, tile sizes and stage shapes
 // per class (balancing the tiles over the compute units, heaviest first) and
@@ -161,11 +184,15 @@ int validate_shape(const conv2d_params* p);
 // force_variant >= 0 plans with that variant only (CONV2D_ERR_UNSUPPORTED if
 // it belongs to the other path or cannot tile the shape).
 // `model_cost` (may be null) receives the modelled makespan of the plan.
+// op = kOpForward plans the forward convolution (no cm variants).
 int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchArgs>* launches,
-               conv2d_plan_info* info, int force_variant = -1, double* model_cost = nullptr);
+               conv2d_plan_info* info, int force_variant = -1, double* model_cost = nullptr,
+               int op = kOpGradInput);
 
 // Pointer checks: NULL inputs of non-empty tensors and output/input overlap.
+// Input gradient: inputs go, w, output gi.  Forward (op = kOpForward):
+// inputs x (passed as go), w, output y (passed as gi).
 int check_pointers(const float* go, const float* w, const float* gi,
-                   const conv2d_params* p);
+                   const conv2d_params* p, int op = kOpGradInput);
 
 }  // namespace c2b

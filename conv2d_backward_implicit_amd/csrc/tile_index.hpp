@@ -1,8 +1,10 @@
-// Index arithmetic of the input-gradient kernel, shared by the kernel and by
-// the host-side index checker (index_check.hip), so that the checker replays
-// exactly the addresses the kernel forms.
+// Index arithmetic of the implicit-GEMM kernels, shared by the kernels and
+// by the host-side index checker (index_check.hip), so that the checker
+// replays exactly the addresses the kernels form.
 //
-// Terms (see plan.hpp for the stride-residue classes and stages):
+// Terms (see plan.hpp for the stride-residue classes, the stages and the
+// forward launches, whose roles are named here as on the input-gradient
+// path):
 //  * tile: MT input channels x up to NTL consecutive pixels of one band of
 //    one class sub-image of one image;
 //  * window: the grad_out rows/columns a tile's pixels read through all taps
@@ -83,10 +85,12 @@ C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   c.ntaps = a.cm ? P.th : P.th * P.tw;   // cm: row taps only
   c.nstages = c.ntaps > 0 ? P.nchunks * P.ngroups : 0;
   c.i_start = c.p0 / P.wb;
-  c.R = (pend - 1) / P.wb - c.i_start + P.th;
-  c.roww = P.wb + P.tw - 1;
-  c.oh_base = c.i_start + P.ch - (P.th - 1);
-  c.ow_base = c.band * P.wb + P.cw - (P.tw - 1);
+  // window: the source rows / columns of the tile's rows and band through
+  // every tap, sampled every ss (1 except on forward launches)
+  c.R = ((pend - 1) / P.wb - c.i_start) * P.ss + P.th;
+  c.roww = (P.wb - 1) * P.ss + P.tw;
+  c.oh_base = c.i_start * P.ss + P.ch - (P.th - 1);
+  c.ow_base = c.band * P.wb * P.ss + P.cw - (P.tw - 1);
   return c;
 }
 
@@ -113,7 +117,7 @@ C2B_HD int window_base(const TileCtx& c, int local) {
   const int q0 = c.p0 - c.i_start * P.wb + local;
   const int dr = fast_div(q0, P.m_wb);
   const int jb = q0 - dr * P.wb;
-  return (dr + P.th - 1) * c.roww + jb + P.tw - 1;
+  return (dr * P.ss + P.th - 1) * c.roww + jb * P.ss + P.tw - 1;
 }
 
 // cm (column taps in the matrix rows): the tile's lanes are the points
@@ -150,7 +154,7 @@ C2B_HD int output_offset(const TileCtx& c, const LaunchArgs& a, int local) {
 C2B_HD int tap_kidx(const PhaseDesc& P, const LaunchArgs& a, int tap) {
   const int j = fast_div(tap, P.m_tw);
   const int l = tap - j * P.tw;
-  return (P.rh + a.S * j) * a.KW + (P.rw + a.S * l);
+  return (P.rh + P.kstep * j) * a.KW + (P.rw + P.kstep * l);
 }
 
 // Stage st -> (first output channel, tap group); tap-group-major.
@@ -224,19 +228,19 @@ C2B_HD int weight_source(const TileCtx& c, const LaunchArgs& a, int m, int t, in
     const int cl = m / a.twm, l = m - cl * a.twm;
     if (l >= P.tw || cl >= a.cit) return -1;
     ci = c.ci0 + cl;
-    kidx = (P.rh + a.S * tap) * a.KW + (P.rw + a.S * l);
+    kidx = (P.rh + P.kstep * tap) * a.KW + (P.rw + P.kstep * l);
   } else {
     ci = c.ci0 + m;
     kidx = tap_kidx(P, a, tap);
   }
   if (ci >= a.Ci) return -1;
-  return ci * (a.KH * a.KW) + kidx;
+  return ci * a.wsm + kidx;
 }
 
 // Weight cell e = cq*qp + (m*pt + t)*4 + c (e counted from the start of the
-// weight region) of tap group `grp`: offset of the weight of output channel
-// 4cq + c at matrix row m, tap grp*tg + t (weight_source), relative to the
-// stage's first output channel, or -1 if the cell is padding.
+// weight region) of tap group `grp`: offset of the weight of contraction
+// channel 4cq + c at matrix row m, tap grp*tg + t (weight_source), relative
+// to the stage's first contraction channel, or -1 if the cell is padding.
 template <int MT, bool CM>
 C2B_HD int mm_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp) {
   const PhaseDesc& P = c.P;
@@ -248,7 +252,7 @@ C2B_HD int mm_weight_cell(const TileCtx& c, const LaunchArgs& a, int e, int grp)
   const int t = r2 >> 2, co = 4 * cq + (r2 & 3);
   const int src = weight_source<MT, CM>(c, a, m, t, grp);
   if (src < 0) return -1;
-  return co * (a.Ci * a.KH * a.KW) + src;
+  return co * a.wsk + src;
 }
 
 // ---------------------------------------------------------------------------
@@ -307,11 +311,9 @@ C2B_HD uint32_t weight_lane_offset(const TileCtx& c, const LaunchArgs& a, int wb
   return src < 0 ? kPadOffset : uint32_t(src * 4);
 }
 
-// Bytes between consecutive channels: grad_out planes, or weight rows.
+// Bytes between consecutive contraction channels: source planes, or weights.
 C2B_HD uint32_t window_channel_bytes(const LaunchArgs& a) { return uint32_t(4 * a.OH * a.OW); }
-C2B_HD uint32_t weight_channel_bytes(const LaunchArgs& a) {
-  return uint32_t(4 * a.Ci * a.KH * a.KW);
-}
+C2B_HD uint32_t weight_channel_bytes(const LaunchArgs& a) { return uint32_t(4 * a.wsk); }
 
 // Stage-buffer float of the 16-byte LDS write of lane `lane` of a batch, or
 // -1 if the lane is past its quad's slots / pairs (no write).

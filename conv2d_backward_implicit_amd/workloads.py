@@ -107,6 +107,21 @@ def draw(shape: ConvShape, seed: int):
     return go.astype(np.float32), w.astype(np.float32)
 
 
+def draw_forward(shape: ConvShape, seed: int):
+    """(x, weight) for the forward convolution of ``shape``: x [N, Ci, H, W]
+    with grad_out's distribution and weight as in ``draw`` (float32)."""
+    rng = np.random.default_rng(seed)
+    if shape.dist == "uniform":
+        x = rng.uniform(-1.0, 1.0, size=shape.gi_shape)
+        w = rng.uniform(-1.0, 1.0, size=shape.w_shape)
+    elif shape.dist == "normal":
+        x = rng.standard_normal(size=shape.gi_shape)
+        w = rng.standard_normal(size=shape.w_shape) * np.sqrt(2.0 / shape.weight_fan_in)
+    else:
+        raise ValueError(shape.dist)
+    return x.astype(np.float32), w.astype(np.float32)
+
+
 def draw_integers(shape: ConvShape, seed: int, lo: int = -4, hi: int = 4):
     """(grad_out, weight) with integer values in [lo, hi], stored as float32.
 

@@ -247,6 +247,73 @@ int conv2d_grad_input_variant(const float* grad_out, const float* weight,
 int conv2d_check_indexing_variant(const conv2d_params* p, int variant,
                                   char* msg, size_t msg_len);
 
+/*
+ * Forward convolution (the adjoint operator of the input gradient above):
+ *
+ *   y[n, co, oh, ow] = sum over ci, kh, kw with
+ *                          ih = oh * s - padding_h + kh in [0, in_h),
+ *                          iw = ow * s - padding_w + kw in [0, in_w)
+ *                      of x[n, ci, ih, iw] * weight[co, ci, kh, kw]
+ *
+ * (no bias, no kernel flip).  Source: the same shader page; its stride > 1
+ * im2col branch relates grad_out[n, co, oh, ow] to input pixel
+ * (oh * s - padding_h + kh, ow * s - padding_w + kw) through tap (kh, kw),
+ * which is the index map of this convolution, so that
+ * <grad_input(grad_out), x> = <grad_out, y(x)> for every x and grad_out.
+ *
+ * Layouts (dense, row-major, fp32 in device memory), with the same
+ * conv2d_params as above (out_h / out_w must be the forward extents):
+ *   x      [batch, in_channels, in_h, in_w]           (read)
+ *   weight [out_channels, in_channels, kernel_h, kernel_w]   (read)
+ *   y      [batch, out_channels, out_h, out_w]        (fully overwritten)
+ * Ownership, asynchrony and errors as for conv2d_grad_input; y must not
+ * overlap x or weight (CONV2D_ERR_ALIAS); an empty contraction
+ * (in_channels = 0) writes zeros.  The weight tensor must be below 2^31
+ * bytes (else CONV2D_ERR_OVERFLOW).  Runs on the kernels of the input
+ * gradient with the operand roles exchanged (the kernel variants without
+ * column taps); conv2d_forward_f16 rounds x and weight to f16 (round to
+ * nearest even) and accumulates in fp32, as conv2d_grad_input_f16 does.
+ */
+int conv2d_forward(const float* x, const float* weight, float* y,
+                   const conv2d_params* p, void* stream);
+int conv2d_forward_f16(const float* x, const float* weight, float* y,
+                       const conv2d_params* p, void* stream);
+
+/* conv2d_forward (or _f16, as the variant's path dictates) with the kernel
+ * variant forced; CONV2D_ERR_UNSUPPORTED, nothing enqueued, if the index is
+ * out of range, the variant has column taps or cannot tile the shape. */
+int conv2d_forward_variant(const float* x, const float* weight, float* y,
+                           const conv2d_params* p, int variant, void* stream);
+
+/* conv2d_tune for the forward convolution: times the best-modelled variants
+ * on the caller's buffers (x and weight read, y written, with the result of
+ * the chosen variant left in y), makes the fastest the shape's default
+ * forward plan, blocks until done, and stores it in *variant_out if that is
+ * not NULL.  Errors as conv2d_forward, or CONV2D_ERR_HIP. */
+int conv2d_tune_forward(const float* x, const float* weight, float* y,
+                        const conv2d_params* p, int f16, void* stream,
+                        int* variant_out);
+
+/* The variant conv2d_forward (f16 == 0) or conv2d_forward_f16 uses for the
+ * shape now, in *variant_out (-1 if nothing is launched).  CONV2D_OK, or
+ * the error of conv2d_check_params, or CONV2D_ERR_NULL_PTR. */
+int conv2d_planned_forward_variant(const conv2d_params* p, int f16, int* variant_out);
+
+/* conv2d_describe_plan / _variant for the forward launches (host only). */
+int conv2d_describe_forward_plan(const conv2d_params* p, int f16,
+                                 conv2d_plan_info* out);
+int conv2d_describe_forward_plan_variant(const conv2d_params* p, int variant,
+                                         conv2d_plan_info* out);
+
+/* conv2d_check_indexing / _variant for the forward launches: every access
+ * in bounds, every tap of every output pixel reading the x and weight
+ * elements of the definition above (checked against p's stride and
+ * paddings), every y element written exactly once.  Host only. */
+int conv2d_check_indexing_forward(const conv2d_params* p, int f16, char* msg,
+                                  size_t msg_len);
+int conv2d_check_indexing_forward_variant(const conv2d_params* p, int variant,
+                                          char* msg, size_t msg_len);
+
 #ifdef __cplusplus
 }
 #endif

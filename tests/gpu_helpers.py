@@ -42,6 +42,27 @@ def run_gpu(sh: ConvShape, go: np.ndarray, w: np.ndarray, f16: bool = False,
     return host[GUARD:GUARD + n].reshape(sh.gi_shape)
 
 
+def run_gpu_forward(sh: ConvShape, x: np.ndarray, w: np.ndarray, f16: bool = False,
+                    stream=None, variant=None) -> np.ndarray:
+    """Forward convolution y of the HIP path (NaN-filled, guarded output), as
+    a float32 numpy array."""
+    import torch
+    dev = torch.device("cuda", 0)
+    tx = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(dev)
+    tw = torch.from_numpy(np.ascontiguousarray(w, dtype=np.float32)).to(dev)
+    n = int(np.prod(sh.go_shape))
+    buf = torch.full((n + 2 * GUARD,), float("nan"), dtype=torch.float32, device=dev)
+    buf[:GUARD] = CANARY
+    buf[GUARD + n:] = CANARY
+    y = buf[GUARD:GUARD + n].view(sh.go_shape)
+    c2b.forward_into(y, tx, tw, params_of(sh), f16=f16, stream=stream, variant=variant)
+    torch.cuda.synchronize()
+    host = buf.cpu().numpy()
+    assert np.all(host[:GUARD] == np.float32(CANARY)), "write before y"
+    assert np.all(host[GUARD + n:] == np.float32(CANARY)), "write after y"
+    return host[GUARD:GUARD + n].reshape(sh.go_shape)
+
+
 # Shapes every kernel variant is run on (GPU) and replayed on (CPU): ragged
 # channel and pixel tiles, deep stages of a 1x1 kernel with a ragged last
 # channel chunk, stride-2 classes with 1, 2 and 4 taps, a Ci = 3 stem, a

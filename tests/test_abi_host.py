@@ -252,3 +252,72 @@ def test_describe_plan_variant_matches_forced_plans():
         assert info["macs"] >= info["useful_macs"] and info["tiles"] >= 1
     with pytest.raises(c2b.Conv2dError):
         c2b.describe_plan_variant(p, c2b.num_variants())
+
+
+# ---- forward convolution entry points ---------------------------------------
+
+@pytest.mark.parametrize("fn", [c2b.conv2d_forward, c2b.conv2d_forward_f16])
+def test_forward_entry_points_reject_before_any_device_call(fn):
+    p = _p()
+    assert _call(fn, 0x1000, 0x2000, 0x3000, _p(stride=0, out_h=1, out_w=1)) == BAD
+    # null pointers of non-empty tensors (x, weight, y)
+    assert _call(fn, 0, 0x2000, 0x100000, p) == NULL
+    assert _call(fn, 0x1000, 0, 0x100000, p) == NULL
+    assert _call(fn, 0x1000, 0x2000, 0, p) == NULL
+    # y (1 x 4 x 8 x 8 fp32) overlapping x or weight
+    y_bytes = 1 * 4 * 8 * 8 * 4
+    assert _call(fn, 0x100000, 0x900000, 0x100000, p) == ALIAS
+    assert _call(fn, 0x100000 + y_bytes - 4, 0x900000, 0x100000, p) == ALIAS
+    assert _call(fn, 0x100000, 0x900000 + 4, 0x900000, p) == ALIAS
+    # x may end where y begins
+    x_bytes = 1 * 3 * 8 * 8 * 4
+    lib = c2b.load_library()
+    assert getattr(lib, fn.__name__)(ctypes.c_void_p(1), ctypes.c_void_p(2),
+                                     ctypes.c_void_p(3), None, None) == NULL
+    assert x_bytes < y_bytes
+
+
+def test_forward_variant_and_tune_reject_before_any_device_call():
+    lib = c2b.load_library()
+    p = _p()
+    n = c2b.num_variants()
+    assert c2b.conv2d_forward_variant(0x1000, 0x2000, 0x100000, p, n) == UNSUP
+    cm = [v for v in range(n) if c2b.variant_uses_column_taps(v) == 1]
+    assert c2b.conv2d_forward_variant(0x1000, 0x2000, 0x100000, p, cm[0]) == UNSUP
+    chosen = ctypes.c_int(7)
+
+    def tune(x, w, y, q, f16=0):
+        return lib.conv2d_tune_forward(ctypes.c_void_p(x), ctypes.c_void_p(w),
+                                       ctypes.c_void_p(y), ctypes.byref(q), f16, None,
+                                       ctypes.byref(chosen))
+    assert tune(0x1000, 0x2000, 0x3000, _p(stride=0, out_h=1, out_w=1)) == BAD
+    assert tune(0, 0x2000, 0x100000, p) == NULL
+    assert tune(0x100000, 0x900000, 0x100000, p, 1) == ALIAS
+    assert chosen.value == 7
+
+
+def test_forward_plans():
+    p = _p(in_channels=40, out_channels=24)
+    for f16 in (False, True):
+        v = c2b.planned_forward_variant(p, f16)
+        assert 0 <= v < c2b.num_variants() and c2b.variant_is_f16(v) == int(f16)
+        assert c2b.variant_uses_column_taps(v) == 0
+        info = c2b.describe_forward_plan(p, f16)
+        assert info["useful_macs"] == 1 * 24 * 8 * 8 * 40 * 9
+        assert info["launches"] == 1 and info["phases"] == 1 and info["tiles"] >= 1
+    for v in range(c2b.num_variants()):
+        if c2b.variant_uses_column_taps(v) == 1:
+            with pytest.raises(c2b.Conv2dError):
+                c2b.describe_forward_plan_variant(p, v)
+            continue
+        info = c2b.describe_forward_plan_variant(p, v)
+        assert info["macs"] >= info["useful_macs"] > 0
+    # no image or no output channel: nothing to write; no input channel: y
+    # still gets its zeros
+    assert c2b.describe_forward_plan(_p(batch=0))["tiles"] == 0
+    assert c2b.describe_forward_plan(_p(out_channels=0))["tiles"] == 0
+    zero = c2b.describe_forward_plan(_p(in_channels=0))
+    assert zero["tiles"] >= 1 and zero["macs"] == 0
+    assert c2b.planned_forward_variant(_p(batch=0)) == -1
+    with pytest.raises(c2b.Conv2dError):
+        c2b.describe_forward_plan(_p(stride=0, out_h=1, out_w=1))

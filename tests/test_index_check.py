@@ -71,3 +71,51 @@ def test_column_tap_variants_replay():
         for sh in SMALL_CI_SHAPES + [CONFIGS[4]]:
             rc, msg = c2b.check_indexing_variant(params_of(sh), v)
             assert rc == 0, (v, sh.name, rc, msg)
+
+
+# ---- forward convolution launches (the same kernels, roles exchanged) ------
+# conv2d_check_indexing_forward checks every tap of every output pixel
+# against the forward definition (x[n, ci, s*oh - padding_h + kh, ...]
+# times w[co, ci, kh, kw]) with the caller's stride and paddings, and that
+# each y element is written exactly once.
+
+def _check_fwd(sh, f16):
+    rc, msg = c2b.check_indexing_forward(params_of(sh), f16)
+    assert rc == 0, (sh, f16, rc, msg)
+
+
+@pytest.mark.parametrize("sh", CONFIGS, ids=[c.name for c in CONFIGS])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_forward_workloads(sh, f16):
+    _check_fwd(sh, f16)
+
+
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_forward_test_shapes(f16):
+    for sh in EDGE + RANDOM + list(VARIANT_SHAPES) + list(SMALL_CI_SHAPES):
+        _check_fwd(sh, f16)
+
+
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_forward_random_stress(f16):
+    rng = np.random.default_rng(98)
+    for i in range(100):
+        sh = random_shape(rng, max_n=3, max_c=140, max_hw=70, max_k=9, max_s=5,
+                          name="f%d" % i)
+        _check_fwd(sh, f16)
+
+
+@pytest.mark.parametrize("variant", range(c2b.num_variants()))
+def test_forward_every_variant_replay(variant):
+    shapes = list(VARIANT_SHAPES) + [CONFIGS[0]]
+    for sh in shapes:
+        rc, msg = c2b.check_indexing_forward_variant(params_of(sh), variant)
+        if c2b.variant_uses_column_taps(variant) == 1:
+            assert rc == -5, (variant, sh.name, rc)   # no forward instance
+        else:
+            assert rc == 0, (variant, sh.name, rc, msg)
+
+
+def test_forward_checker_rejects_bad_shape():
+    p = c2b.make_params(1, 3, 8, 8, 4, 3, 3, 1, 1, 1, 7, 8)
+    assert c2b.check_indexing_forward(p)[0] == -2
