@@ -1,5 +1,6 @@
 #!/usr/bin/env python3
-"""Throughput of the conv2d input-gradient HIP path on one MI355X.
+"""Throughput of the conv2d input-gradient HIP path on one MI355X (or, with
+--op forward, of the forward convolution on the same kernels).
 
 One step = one conv2d_grad_input call over the whole workload (all batch
 items, all stride classes), inputs already resident in HBM.  Before the
@@ -10,7 +11,7 @@ roofline of the kernel (timed with HIP events on the stream it runs on) and
 the CPU oracle timed on the host cores on the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--f16 | --fp32] [--no-cpu] [--no-tune]
+                    [--f16 | --fp32] [--no-cpu] [--no-tune] [--op forward]
 """
 from __future__ import annotations
 
@@ -26,6 +27,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "conv2d grad-input useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
+METRIC_FORWARD = "conv2d forward useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}
 PEAK_HBM_GBS = 8000.0
@@ -67,8 +69,9 @@ def measured_traffic(kernel_tag: str, workload: str):
     return float(m_val.group(1))
 
 
-def cpu_baseline(shape, go, w):
-    """The oracle as it stands, on the whole workload, on this host's cores."""
+def cpu_baseline(shape, go, w, op="grad_input"):
+    """The oracle as it stands, on the whole workload, on this host's cores
+    (``go`` is x for the forward convolution)."""
     import numpy as np
     import oracle
 
@@ -76,8 +79,12 @@ def cpu_baseline(shape, go, w):
     w64 = np.ascontiguousarray(w, dtype=np.float64)
     orc = oracle.default()
     t0 = time.perf_counter()
-    orc.grad_input_gather(go64, w64, shape.in_h, shape.in_w, shape.stride,
-                          shape.padding_h, shape.padding_w)
+    if op == "forward":
+        orc.conv2d_forward(go64, w64, shape.out_h, shape.out_w, shape.stride,
+                           shape.padding_h, shape.padding_w)
+    else:
+        orc.grad_input_gather(go64, w64, shape.in_h, shape.in_w, shape.stride,
+                              shape.padding_h, shape.padding_w)
     dt = time.perf_counter() - t0
     return {"value": shape.useful_flops / dt / 1e12, "unit": "TFLOP/s",
             "cores": orc.num_threads(), "kind": "oracle",
@@ -112,6 +119,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-tune", action="store_true",
                     help="use the planner's model choice instead of tuning the variant")
+    ap.add_argument("--op", choices=("grad_input", "forward"), default="grad_input",
+                    help="the operation timed (default: the input gradient)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run --steps plain device-to-device copies of MIB "
                          "MiB (reference kernel for HBM byte counters) and exit")
@@ -132,7 +141,8 @@ def main() -> int:
     import torch
 
     import conv2d_backward_implicit_amd as c2b
-    from conv2d_backward_implicit_amd.workloads import CONFIGS, HEADLINE, by_name, draw
+    from conv2d_backward_implicit_amd.workloads import (CONFIGS, HEADLINE, by_name, draw,
+                                                        draw_forward)
 
     shape = by_name(args.workload) if args.workload else CONFIGS[HEADLINE]
     f16 = shape.f16_staged if not (args.f16 or args.fp32) else args.f16
@@ -141,28 +151,38 @@ def main() -> int:
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
-    go, w = draw(shape, seed)
+    fwd = args.op == "forward"
+    # input gradient: grad_out -> grad_input; forward: x -> y (go and gi
+    # below hold x and y)
+    go, w = draw_forward(shape, seed) if fwd else draw(shape, seed)
     tgo = torch.from_numpy(go).to(dev)
     tw = torch.from_numpy(w).to(dev)
-    gi = torch.empty(shape.gi_shape, dtype=torch.float32, device=dev)
+    gi = torch.empty(shape.go_shape if fwd else shape.gi_shape, dtype=torch.float32,
+                     device=dev)
     p = c2b.make_params(shape.batch, shape.in_channels, shape.in_h, shape.in_w,
                         shape.out_channels, shape.kernel_h, shape.kernel_w, shape.stride,
                         shape.padding_h, shape.padding_w, shape.out_h, shape.out_w)
-    plan = c2b.describe_plan(p, f16)
+    plan = c2b.describe_forward_plan(p, f16) if fwd else c2b.describe_plan(p, f16)
     stream = torch.cuda.current_stream()
     # measured variant choice for this shape, once, outside the timed region
     # (conv2d_tune; the default entry point then uses the tuned plan)
     if not args.no_tune:
-        variant = c2b.tune(gi, tgo, tw, p, f16=f16, stream=stream)
+        variant = (c2b.tune_forward(gi, tgo, tw, p, f16=f16, stream=stream) if fwd else
+                   c2b.tune(gi, tgo, tw, p, f16=f16, stream=stream))
     else:
-        variant = c2b.planned_variant(p, f16)
+        variant = (c2b.planned_forward_variant(p, f16) if fwd else
+                   c2b.planned_variant(p, f16))
     if variant >= 0:   # the plan the timed calls run
-        plan = c2b.describe_plan_variant(p, variant)
+        plan = (c2b.describe_forward_plan_variant(p, variant) if fwd else
+                c2b.describe_plan_variant(p, variant))
     plan["variant"] = variant
     plan["tuned"] = not args.no_tune
 
     def step():
-        c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
+        if fwd:
+            c2b.forward_into(gi, tgo, tw, p, f16=f16, stream=stream)
+        else:
+            c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -201,7 +221,7 @@ def main() -> int:
 
     value = shape.useful_flops * args.steps / wall / 1e12
     achieved = shape.useful_flops / ev_avg_s / 1e12
-    kernel_tag = "grad_input_%s" % dtype
+    kernel_tag = ("forward_%s" if fwd else "grad_input_%s") % dtype
     traffic = measured_traffic(kernel_tag, shape.name)
     # bound: compare the workload's arithmetic intensity (useful flops per
     # compulsory byte) with the ridge point of the path's matrix peak
@@ -217,7 +237,7 @@ def main() -> int:
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic}
     out = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_FORWARD if fwd else METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -226,7 +246,8 @@ def main() -> int:
                    "in_channels": shape.in_channels, "out_channels": shape.out_channels,
                    "in_hw": [shape.in_h, shape.in_w], "kernel": [shape.kernel_h, shape.kernel_w],
                    "stride": shape.stride, "padding": [shape.padding_h, shape.padding_w],
-                   "out_hw": [shape.out_h, shape.out_w], "path": dtype},
+                   "out_hw": [shape.out_h, shape.out_w], "path": dtype,
+                   "op": args.op},
         "pct_of_mfma_peak": round(100.0 * value / PEAK_TFLOPS[dtype], 2),
         "kernel_avg_us": round(ev_avg_s * 1e6, 3),
         "kernel_median_us": round(ev_sorted[len(ev_sorted) // 2] * 1e3, 3),
@@ -238,7 +259,7 @@ def main() -> int:
         "source_digest": source_digest(),
     }
     if not args.no_cpu:
-        out["cpu_baseline"] = cpu_baseline(shape, go, w)
+        out["cpu_baseline"] = cpu_baseline(shape, go, w, args.op)
     print(json.dumps(out), flush=True)
     return 0
 
