@@ -1,4 +1,5 @@
-"""CPU oracle for conv2d grad-input: TEST INFRASTRUCTURE ONLY.
+"""CPU oracle for conv2d grad-input (and the forward convolution and weight
+gradient beside it): TEST INFRASTRUCTURE ONLY.
 
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import this package.  The product path (the HIP library and
@@ -19,6 +20,8 @@ Functions (all take float64-convertible arrays and return float64 arrays):
 * ``grad_input_gather_at`` -- the same sum at chosen flat output indices.
 * ``grad_input_scatter``   -- independent scatter form (transpose of forward).
 * ``conv2d_forward``       -- forward cross-correlation, for the adjoint check.
+* ``grad_weight``          -- the weight gradient of the same forward
+  cross-correlation (not on the pages; its index map is the forward one).
 
 Every function is pinned by tests/test_oracle.py to facts outside the oracle
 itself (closed forms, delta inputs, a library GEMM, torch's CPU convolution
@@ -87,7 +90,7 @@ class Oracle:
         lib = ctypes.CDLL(path)
         sig = [_DP, _DP, _DP] + [_I64] * 12
         for name in ("oracle_grad_input_gather", "oracle_grad_input_scatter",
-                     "oracle_conv2d_forward"):
+                     "oracle_conv2d_forward", "oracle_grad_weight"):
             fn = getattr(lib, name)
             fn.argtypes = sig
             fn.restype = None
@@ -141,6 +144,20 @@ class Oracle:
                                         int(padding_w), int(OH), int(OW))
         return y
 
+    def grad_weight(self, grad_out, x, KH, KW, stride, padding_h, padding_w):
+        """Weight gradient [Co, Ci, KH, KW] of the forward cross-correlation
+        (float64); grad_out [N, Co, OH, OW], x [N, Ci, H, W]."""
+        go, xx = _f64(grad_out), _f64(x)
+        N, Co, OH, OW = (int(v) for v in go.shape)
+        N2, Ci, H, W = (int(v) for v in xx.shape)
+        if N2 != N:
+            raise ValueError("grad_out batch %d != x batch %d" % (N, N2))
+        gw = np.empty((Co, Ci, int(KH), int(KW)), dtype=np.float64)
+        self._lib.oracle_grad_weight(_ptr(go), _ptr(xx), _ptr(gw), N, Ci, H, W, Co,
+                                     int(KH), int(KW), int(stride), int(padding_h),
+                                     int(padding_w), OH, OW)
+        return gw
+
     def num_threads(self) -> int:
         """OpenMP threads the oracle routines use in this process."""
         return int(self._lib.oracle_num_threads())
@@ -173,6 +190,10 @@ def grad_input_scatter(*a, **k):
 
 def conv2d_forward(*a, **k):
     return default().conv2d_forward(*a, **k)
+
+
+def grad_weight(*a, **k):
+    return default().grad_weight(*a, **k)
 
 
 def num_threads() -> int:

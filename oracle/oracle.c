@@ -194,6 +194,45 @@ void oracle_conv2d_forward(const double* x, const double* w, double* y, i64 N,
   }
 }
 
+/*
+ * Gradient with respect to the weight of the same forward cross-correlation
+ * (not on the pages; it is the other half of that convolution's backward
+ * pass, and its index map is the forward one above, which is the map of the
+ * [p3] stride > 1 im2col branch read forwards):
+ *   grad_weight[co, ci, kh, kw] = sum over n, oh, ow of
+ *       grad_out[n, co, oh, ow] * x[n, ci, oh*s - ph + kh, ow*s - pw + kw],
+ * with x taken as zero outside [0,H) x [0,W).  It is the adjoint of the
+ * forward map in its weight argument: <grad_weight(go, x), V> =
+ * <go, conv2d_fwd(x, V)> for every V.  Parallel over (co, ci) pairs, each
+ * element one serial sum in the definition's loop order.
+ */
+void oracle_grad_weight(const double* go, const double* x, double* gw, i64 N,
+                        i64 Ci, i64 H, i64 W, i64 Co, i64 KH, i64 KW, i64 s,
+                        i64 ph, i64 pw, i64 OH, i64 OW) {
+  i64 total = Co * Ci * KH * KW;
+#pragma omp parallel for schedule(static)
+  for (i64 e = 0; e < total; ++e) {
+    i64 kw = e % KW;
+    i64 kh = (e / KW) % KH;
+    i64 ci = (e / (KW * KH)) % Ci;
+    i64 co = e / (KW * KH * Ci);
+    double acc = 0.0;
+    for (i64 n = 0; n < N; ++n) {
+      for (i64 oh = 0; oh < OH; ++oh) {
+        i64 ih = oh * s - ph + kh;
+        if (ih < 0 || ih >= H) continue;
+        for (i64 ow = 0; ow < OW; ++ow) {
+          i64 iw = ow * s - pw + kw;
+          if (iw < 0 || iw >= W) continue;
+          acc += go[((n * Co + co) * OH + oh) * OW + ow] *
+                 x[((n * Ci + ci) * H + ih) * W + iw];
+        }
+      }
+    }
+    gw[e] = acc;
+  }
+}
+
 /* Number of OpenMP threads the routines above will use. */
 int oracle_num_threads(void) {
   int t = 1;

@@ -7,11 +7,12 @@ committed oracle; tests/test_oracle_mutants.py runs them on mutants and
 requires that every mutant trips at least one pin.
 
 What the pins rest on:
-* torch's CPU routines ``torch.nn.grad.conv2d_input`` and
-  ``torch.nn.functional.conv2d`` in float64 (third-party library; run, not
-  copied);
-* the adjoint identity <grad_input(g), x> = <g, conv2d(x)>, which defines the
-  input gradient of a linear map;
+* torch's CPU routines ``torch.nn.grad.conv2d_input``,
+  ``torch.nn.grad.conv2d_weight`` and ``torch.nn.functional.conv2d`` in
+  float64 (third-party library; run, not copied);
+* the adjoint identities <grad_input(g), x> = <g, conv2d(x)> and
+  <grad_weight(g, x), V> = <g, conv2d(x, V)>, which define the gradients of
+  a bilinear map;
 * closed forms: all-ones inputs (tap counts from interval lengths), delta
   weights and delta grad_out (placement by strided array slicing), the 1x1
   stride-1 case as a plain matrix product (numpy matmul), exact zeros at
@@ -306,6 +307,78 @@ def pin_degenerate(orc):
     assert got.shape == sh.gi_shape and np.all(got == 0.0)
 
 
+def _gw_inputs(sh, seed):
+    rng = np.random.default_rng(seed)
+    return rng.uniform(-1, 1, size=sh.go_shape), rng.uniform(-1, 1, size=sh.gi_shape)
+
+
+def pin_torch_grad_weight(orc):
+    """The weight gradient agrees with torch.nn.grad.conv2d_weight (float64)."""
+    import torch
+    for i, sh in enumerate(_random_shapes()):
+        go, x = _gw_inputs(sh, 4000 + i)
+        ref = torch.nn.grad.conv2d_weight(
+            torch.from_numpy(x), sh.w_shape, torch.from_numpy(go), stride=sh.stride,
+            padding=(sh.padding_h, sh.padding_w)).numpy()
+        got = orc.grad_weight(go, x, sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h,
+                              sh.padding_w)
+        assert got.shape == sh.w_shape, (got.shape, sh)
+        assert _rel_err(got, ref) < 1e-12, (sh, _rel_err(got, ref))
+
+
+def pin_grad_weight_adjoint(orc):
+    """<grad_weight(g, x), V> equals <g, forward(x, V)> to float64 rounding:
+    the weight gradient of the linear map V -> forward(x, V)."""
+    for i, sh in enumerate(_random_shapes()):
+        rng = np.random.default_rng(5000 + i)
+        g = rng.uniform(-1, 1, size=sh.go_shape)
+        x = rng.uniform(-1, 1, size=sh.gi_shape)
+        v = rng.uniform(-1, 1, size=sh.w_shape)
+        gw = orc.grad_weight(g, x, sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h,
+                             sh.padding_w)
+        lhs = float(np.sum(gw * v))
+        y = orc.conv2d_forward(x, v, sh.out_h, sh.out_w, sh.stride, sh.padding_h,
+                               sh.padding_w)
+        rhs = float(np.sum(g * y))
+        scale = float(np.sum(np.abs(g)) * np.sum(np.abs(x)) + 1.0)
+        assert abs(lhs - rhs) <= 1e-12 * scale, (sh, lhs, rhs)
+
+
+def pin_grad_weight_pointwise(orc):
+    """1x1 kernel, stride 1, no padding: grad_weight[co, ci] is the plain
+    product sum_n grad_out[n] x[n]^T over pixels (numpy matmul)."""
+    sh = ConvShape("gw1x1", 3, 5, 6, 7, 4, 1, 1, 1, 0, 0, 6, 7, dist="uniform")
+    go, x = _gw_inputs(sh, 6000)
+    N = sh.batch
+    ref = sum(go[n].reshape(4, -1) @ x[n].reshape(5, -1).T for n in range(N))
+    got = orc.grad_weight(go, x, 1, 1, 1, 0, 0)[:, :, 0, 0]
+    assert _rel_err(got, ref) < 1e-12, _rel_err(got, ref)
+
+
+def _pixel_count(k, p, s, o, n):
+    """Output positions m in [0, o) whose source index m*s - p + k lies in
+    [0, n): an interval count."""
+    lo = max(0, -((-(p - k)) // s))          # ceil((p - k) / s)
+    hi = min(o - 1, (n - 1 + p - k) // s)    # floor((n - 1 + p - k) / s)
+    return max(0, hi - lo + 1)
+
+
+def pin_grad_weight_all_ones(orc):
+    """All-ones inputs: grad_weight[co, ci, kh, kw] = N * Ph(kh) * Pw(kw),
+    with Ph(kh) the output rows whose tap kh lands inside the image."""
+    for sh in _random_shapes()[:12] + [ConvShape("gwo", 2, 3, 8, 8, 5, 3, 3, 1, 1, 1, 8, 8)]:
+        go = np.ones(sh.go_shape)
+        x = np.ones(sh.gi_shape)
+        got = orc.grad_weight(go, x, sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h,
+                              sh.padding_w)
+        for kh in range(sh.kernel_h):
+            for kw in range(sh.kernel_w):
+                want = sh.batch * _pixel_count(kh, sh.padding_h, sh.stride, sh.out_h,
+                                               sh.in_h) * \
+                    _pixel_count(kw, sh.padding_w, sh.stride, sh.out_w, sh.in_w)
+                assert np.all(got[:, :, kh, kw] == want), (sh, kh, kw, want)
+
+
 ALL_PINS = [
     pin_torch_grad_input,
     pin_torch_forward,
@@ -320,4 +393,8 @@ ALL_PINS = [
     pin_gather_at,
     pin_integer_exact,
     pin_degenerate,
+    pin_torch_grad_weight,
+    pin_grad_weight_adjoint,
+    pin_grad_weight_pointwise,
+    pin_grad_weight_all_ones,
 ]

@@ -46,6 +46,16 @@ MUTANTS = [
     ("forward_flipped_kernel", "oracle_conv2d_forward",
      "w[((co * Ci + ci) * KH + kh) * KW + kw]",
      "w[((co * Ci + ci) * KH + (KH - 1 - kh)) * KW + (KW - 1 - kw)]"),
+    ("grad_weight_sign_h", "oracle_grad_weight",
+     "i64 ih = oh * s - ph + kh;", "i64 ih = oh * s + ph - kh;"),
+    ("grad_weight_padding_swapped", "oracle_grad_weight",
+     "i64 iw = ow * s - pw + kw;", "i64 iw = ow * s - ph + kw;"),
+    ("grad_weight_flipped_kernel", "oracle_grad_weight",
+     "i64 ih = oh * s - ph + kh;", "i64 ih = oh * s - ph + (KH - 1 - kh);"),
+    ("grad_weight_last_row_dropped", "oracle_grad_weight",
+     "oh < OH; ++oh", "oh < OH - 1; ++oh"),
+    ("grad_weight_bad_init", "oracle_grad_weight",
+     "double acc = 0.0;", "double acc = 1e-3;"),
 ]
 
 
