@@ -30,6 +30,8 @@ __all__ = [
     "conv2d_forward_variant", "tune_forward", "planned_forward_variant",
     "describe_forward_plan", "describe_forward_plan_variant",
     "check_indexing_forward", "check_indexing_forward_variant",
+    "grad_weight", "grad_weight_into", "conv2d_grad_weight", "grad_weight_workspace_size",
+    "check_indexing_grad_weight",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -62,6 +64,9 @@ EXPORTED_SYMBOLS = (
     "conv2d_describe_forward_plan_variant",
     "conv2d_check_indexing_forward",
     "conv2d_check_indexing_forward_variant",
+    "conv2d_grad_weight",
+    "conv2d_grad_weight_workspace_size",
+    "conv2d_check_indexing_grad_weight",
 )
 
 CONV2D_OK = 0
@@ -73,6 +78,7 @@ STATUS_NAMES = {
     -4: "CONV2D_ERR_OVERFLOW",
     -5: "CONV2D_ERR_UNSUPPORTED",
     -6: "CONV2D_ERR_HIP",
+    -7: "CONV2D_ERR_WORKSPACE",
 }
 
 
@@ -188,6 +194,14 @@ def load_library():
         lib.conv2d_check_indexing_forward_variant.argtypes = \
             lib.conv2d_check_indexing_variant.argtypes
         lib.conv2d_check_indexing_forward_variant.restype = ctypes.c_int
+        lib.conv2d_grad_weight.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                           P, ctypes.c_void_p, ctypes.c_size_t,
+                                           ctypes.c_void_p]
+        lib.conv2d_grad_weight.restype = ctypes.c_int
+        lib.conv2d_grad_weight_workspace_size.argtypes = [P, ctypes.POINTER(ctypes.c_size_t)]
+        lib.conv2d_grad_weight_workspace_size.restype = ctypes.c_int
+        lib.conv2d_check_indexing_grad_weight.argtypes = [P, ctypes.c_char_p, ctypes.c_size_t]
+        lib.conv2d_check_indexing_grad_weight.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -517,3 +531,70 @@ def forward(x, weight, stride=1, padding_h=0, padding_w=0, f16=False, out=None, 
     if out is None:
         out = torch.empty((n, co, p.out_h, p.out_w), dtype=torch.float32, device=x.device)
     return forward_into(out, x, weight, p, f16=f16, stream=stream)
+
+
+# ---- weight gradient -----------------------------------------------------------
+
+def grad_weight_workspace_size(p: Conv2dParams) -> int:
+    """Workspace bytes conv2d_grad_weight needs for this shape (current device)."""
+    n = ctypes.c_size_t(0)
+    rc = load_library().conv2d_grad_weight_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return int(n.value)
+
+
+def check_indexing_grad_weight(p: Conv2dParams) -> tuple:
+    """Host replay of the weight-gradient kernels (no device needed)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().conv2d_check_indexing_grad_weight(ctypes.byref(p), buf, len(buf))
+    return int(rc), buf.value.decode()
+
+
+def conv2d_grad_weight(grad_out_ptr: int, x_ptr: int, grad_weight_ptr: int, p: Conv2dParams,
+                       workspace_ptr: int, workspace_bytes: int, stream: int = 0) -> int:
+    """Raw C-ABI call of the weight gradient; returns the status."""
+    return int(load_library().conv2d_grad_weight(
+        ctypes.c_void_p(grad_out_ptr), ctypes.c_void_p(x_ptr), ctypes.c_void_p(grad_weight_ptr),
+        ctypes.byref(p), ctypes.c_void_p(workspace_ptr), ctypes.c_size_t(int(workspace_bytes)),
+        ctypes.c_void_p(stream)))
+
+
+def grad_weight_into(grad_weight, grad_out, x, p: Conv2dParams, workspace=None, stream=None):
+    """Write the weight gradient into ``grad_weight`` on torch's current
+    stream (or ``stream``).  ``workspace`` (a uint8 GPU tensor of at least
+    grad_weight_workspace_size bytes) is allocated here by torch if not given.
+    Raises Conv2dError on a bad status."""
+    import torch
+    _check_tensor(grad_out, "grad_out", (p.batch, p.out_channels, p.out_h, p.out_w))
+    _check_tensor(x, "x", (p.batch, p.in_channels, p.in_h, p.in_w))
+    _check_tensor(grad_weight, "grad_weight", (p.out_channels, p.in_channels, p.kernel_h,
+                                               p.kernel_w))
+    if not (grad_out.device == x.device == grad_weight.device):
+        raise ValueError("all tensors must be on the same device")
+    with torch.cuda.device(grad_weight.device):
+        need = grad_weight_workspace_size(p)
+        if workspace is None:
+            workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=grad_weight.device)
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = conv2d_grad_weight(grad_out.data_ptr(), x.data_ptr(), grad_weight.data_ptr(), p,
+                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                int(s.cuda_stream))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return grad_weight
+
+
+def grad_weight(grad_out, x, kernel_h, kernel_w, stride=1, padding_h=0, padding_w=0,
+                out=None, stream=None):
+    """Weight gradient [Co, Ci, kernel_h, kernel_w] of conv2d for NCHW
+    ``grad_out`` and ``x`` (float32 GPU tensors)."""
+    import torch
+    n, co, oh, ow = (int(v) for v in grad_out.shape)
+    n2, ci, h, w_ = (int(v) for v in x.shape)
+    if n2 != n:
+        raise ValueError("grad_out has batch %d, x has %d" % (n, n2))
+    p = make_params(n, ci, h, w_, co, kernel_h, kernel_w, stride, padding_h, padding_w, oh, ow)
+    if out is None:
+        out = torch.empty((co, ci, kernel_h, kernel_w), dtype=torch.float32, device=x.device)
+    return grad_weight_into(out, grad_out, x, p, stream=stream)

@@ -611,6 +611,7 @@ extern "C" const char* conv2d_status_string(int status) {
       return "kernel window of one stride phase too large for the staging tile, "
              "or kernel variant not available for this path";
     case CONV2D_ERR_HIP: return "HIP runtime error at launch";
+    case CONV2D_ERR_WORKSPACE: return "workspace smaller than conv2d_grad_weight_workspace_size";
     default: return "unknown status";
   }
 }

@@ -88,8 +88,10 @@ enum {
                                   (kernel_h*kernel_w / stride^2 too large),
                                   or a forced kernel variant is out of range
                                   or cannot tile the shape                  */
-  CONV2D_ERR_HIP = -6          /* the HIP runtime reported an error at
+  CONV2D_ERR_HIP = -6,         /* the HIP runtime reported an error at
                                   launch (hipGetLastError)                   */
+  CONV2D_ERR_WORKSPACE = -7    /* conv2d_grad_weight: the workspace is
+                                  smaller than its workspace size            */
 };
 
 /*
@@ -313,6 +315,54 @@ int conv2d_check_indexing_forward(const conv2d_params* p, int f16, char* msg,
                                   size_t msg_len);
 int conv2d_check_indexing_forward_variant(const conv2d_params* p, int variant,
                                           char* msg, size_t msg_len);
+
+/*
+ * Weight gradient of the same forward convolution (the other half of its
+ * backward pass):
+ *
+ *   grad_weight[co, ci, kh, kw] = sum over n, oh, ow with
+ *                                     ih = oh * s - padding_h + kh in [0, in_h),
+ *                                     iw = ow * s - padding_w + kw in [0, in_w)
+ *                                 of grad_out[n, co, oh, ow] * x[n, ci, ih, iw]
+ *
+ * Not on the source page; its index map is the forward convolution's above
+ * (the page's stride > 1 im2col branch read forwards), and it is the
+ * weight-adjoint of that map: <grad_weight(go, x), V> = <go, y(x, V)>.
+ *
+ * Layouts (dense, row-major, fp32 in device memory), same conv2d_params:
+ *   grad_out    [batch, out_channels, out_h, out_w]            (read)
+ *   x           [batch, in_channels, in_h, in_w]               (read)
+ *   grad_weight [out_channels, in_channels, kernel_h, kernel_w] (overwritten)
+ *   workspace   conv2d_grad_weight_workspace_size bytes of device memory,
+ *               owned by the caller, overwritten (partial sums of pixel
+ *               chunks; it holds nothing between calls)
+ * The contraction over all batch x out_h x out_w pixels is split into
+ * chunks; the chunks' partial sums are added in chunk order by a second
+ * kernel, so results do not depend on scheduling.  fp32 matrix cores, fp32
+ * accumulation.  Asynchronous on `stream` like conv2d_grad_input; calls that
+ * share a workspace must not overlap.
+ *
+ * Errors: as conv2d_grad_input (CONV2D_ERR_ALIAS if grad_weight or the
+ * workspace overlaps an input or each other), CONV2D_ERR_WORKSPACE if the
+ * workspace is NULL or smaller than the size below while that size is not
+ * 0, CONV2D_ERR_OVERFLOW if grad_out or x reaches 2^31 bytes.  batch = 0 (no
+ * pixel) writes zeros.
+ */
+int conv2d_grad_weight(const float* grad_out, const float* x, float* grad_weight,
+                       const conv2d_params* p, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/* Bytes of workspace conv2d_grad_weight needs for the shape on the current
+ * device, in *bytes (may be 0).  CONV2D_OK or the shape's error code. */
+int conv2d_grad_weight_workspace_size(const conv2d_params* p, size_t* bytes);
+
+/* Host replay of conv2d_grad_weight's kernels (no device needed): every
+ * copy reads the grad_out / x element of the definition above (or 0 where
+ * it has no term), every LDS cell of a stage is written once, the products
+ * pair A and B cells of one pixel, and every partial sum is stored once.
+ * Returns as conv2d_check_indexing. */
+int conv2d_check_indexing_grad_weight(const conv2d_params* p, char* msg,
+                                      size_t msg_len);
 
 #ifdef __cplusplus
 }

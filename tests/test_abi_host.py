@@ -321,3 +321,46 @@ def test_forward_plans():
     assert c2b.planned_forward_variant(_p(batch=0)) == -1
     with pytest.raises(c2b.Conv2dError):
         c2b.describe_forward_plan(_p(stride=0, out_h=1, out_w=1))
+
+
+# ---- weight gradient entry points ---------------------------------------------
+
+def test_grad_weight_rejects_before_any_device_call():
+    lib = c2b.load_library()
+    p = _p()                       # go 1x4x8x8, x 1x3x8x8, dw 4x3x3x3
+    need = c2b.grad_weight_workspace_size(p)
+    assert need > 0
+
+    def call(go, x, dw, q, ws=0x7000000, wsb=None):
+        return c2b.conv2d_grad_weight(go, x, dw, q, ws, need if wsb is None else wsb)
+    assert call(0x1000, 0x2000, 0x3000, _p(stride=0, out_h=1, out_w=1)) == BAD
+    assert call(0, 0x200000, 0x400000, p) == NULL
+    assert call(0x100000, 0, 0x400000, p) == NULL
+    assert call(0x100000, 0x200000, 0, p) == NULL
+    # workspace missing or too small
+    assert call(0x100000, 0x200000, 0x400000, p, ws=0) == -7
+    assert call(0x100000, 0x200000, 0x400000, p, wsb=need - 4) == -7
+    # grad_weight or workspace overlapping an input or each other
+    assert call(0x100000, 0x200000, 0x100000, p) == ALIAS
+    assert call(0x100000, 0x200000, 0x400000, p, ws=0x200000) == ALIAS
+    assert call(0x100000, 0x200000, 0x400000, p, ws=0x400000) == ALIAS
+    assert lib.conv2d_grad_weight(None, None, None, None, None, 0, None) == NULL
+    assert c2b.status_string(-7).startswith("workspace")
+
+
+def test_grad_weight_workspace_size():
+    lib = c2b.load_library()
+    assert lib.conv2d_grad_weight_workspace_size(ctypes.byref(_p()), None) == NULL
+    with pytest.raises(c2b.Conv2dError):
+        c2b.grad_weight_workspace_size(_p(stride=0, out_h=1, out_w=1))
+    # no pixel or no output: nothing to split
+    assert c2b.grad_weight_workspace_size(_p(batch=0)) == 0
+    assert c2b.grad_weight_workspace_size(_p(out_channels=0)) == 0
+    assert c2b.grad_weight_workspace_size(_p(in_channels=0)) == 0
+    # whole chunks of partial sums, each the size of grad_weight
+    for sh in CONFIGS:
+        p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels,
+                            sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h, sh.padding_w)
+        n = c2b.grad_weight_workspace_size(p)
+        per_chunk = sh.out_channels * sh.in_channels * sh.kernel_h * sh.kernel_w * 4
+        assert n % per_chunk == 0 and n // per_chunk >= 1, (sh.name, n)

@@ -119,3 +119,25 @@ def test_forward_every_variant_replay(variant):
 def test_forward_checker_rejects_bad_shape():
     p = c2b.make_params(1, 3, 8, 8, 4, 3, 3, 1, 1, 1, 7, 8)
     assert c2b.check_indexing_forward(p)[0] == -2
+
+
+# ---- weight gradient (conv2d_grad_weight) -------------------------------------
+
+@pytest.mark.parametrize("sh", CONFIGS, ids=[c.name for c in CONFIGS])
+def test_grad_weight_workloads(sh):
+    rc, msg = c2b.check_indexing_grad_weight(params_of(sh))
+    assert rc == 0, (sh.name, rc, msg)
+
+
+def test_grad_weight_test_shapes():
+    for sh in EDGE + RANDOM + list(VARIANT_SHAPES) + list(SMALL_CI_SHAPES):
+        rc, msg = c2b.check_indexing_grad_weight(params_of(sh))
+        assert rc == 0, (sh.name, rc, msg)
+
+
+def test_grad_weight_random_stress():
+    rng = np.random.default_rng(97)
+    for i in range(60):
+        sh = random_shape(rng, max_n=3, max_c=90, max_hw=40, max_k=7, max_s=4, name="w%d" % i)
+        rc, msg = c2b.check_indexing_grad_weight(params_of(sh))
+        assert rc == 0, (sh, rc, msg)
