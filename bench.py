@@ -1,6 +1,7 @@
 #!/usr/bin/env python3
 """Throughput of the conv2d input-gradient HIP path on one MI355X (or, with
---op forward, of the forward convolution on the same kernels).
+--op forward, of the forward convolution on the same kernels, or with
+--op grad_weight, of the weight gradient).
 
 One step = one conv2d_grad_input call over the whole workload (all batch
 items, all stride classes), inputs already resident in HBM.  Before the
@@ -11,7 +12,8 @@ roofline of the kernel (timed with HIP events on the stream it runs on) and
 the CPU oracle timed on the host cores on the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--f16 | --fp32] [--no-cpu] [--no-tune] [--op forward]
+                    [--f16 | --fp32] [--no-cpu] [--no-tune]
+                    [--op grad_input|forward|grad_weight]
 """
 from __future__ import annotations
 
@@ -28,6 +30,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "conv2d grad-input useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
 METRIC_FORWARD = "conv2d forward useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
+METRIC_GRAD_WEIGHT = "conv2d grad-weight useful TFLOP/s per MI355X and % of MFMA peak (fp32)"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}
 PEAK_HBM_GBS = 8000.0
@@ -71,7 +74,8 @@ def measured_traffic(kernel_tag: str, workload: str):
 
 def cpu_baseline(shape, go, w, op="grad_input"):
     """The oracle as it stands, on the whole workload, on this host's cores
-    (``go`` is x for the forward convolution)."""
+    (``go`` is x for the forward convolution; ``w`` is x for the weight
+    gradient)."""
     import numpy as np
     import oracle
 
@@ -82,6 +86,9 @@ def cpu_baseline(shape, go, w, op="grad_input"):
     if op == "forward":
         orc.conv2d_forward(go64, w64, shape.out_h, shape.out_w, shape.stride,
                            shape.padding_h, shape.padding_w)
+    elif op == "grad_weight":
+        orc.grad_weight(go64, w64, shape.kernel_h, shape.kernel_w, shape.stride,
+                        shape.padding_h, shape.padding_w)
     else:
         orc.grad_input_gather(go64, w64, shape.in_h, shape.in_w, shape.stride,
                               shape.padding_h, shape.padding_w)
@@ -119,7 +126,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-tune", action="store_true",
                     help="use the planner's model choice instead of tuning the variant")
-    ap.add_argument("--op", choices=("grad_input", "forward"), default="grad_input",
+    ap.add_argument("--op", choices=("grad_input", "forward", "grad_weight"),
+                    default="grad_input",
                     help="the operation timed (default: the input gradient)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead: run --steps plain device-to-device copies of MIB "
@@ -146,43 +154,65 @@ def main() -> int:
 
     shape = by_name(args.workload) if args.workload else CONFIGS[HEADLINE]
     f16 = shape.f16_staged if not (args.f16 or args.fp32) else args.f16
+    if args.op == "grad_weight":
+        if args.f16:
+            print("the weight gradient has an fp32 path only", file=sys.stderr)
+            return 2
+        f16 = False
     dtype = "f16" if f16 else "f32"
     seed = CONFIGS.index(shape)
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     dev = torch.device("cuda", 0)
     fwd = args.op == "forward"
-    # input gradient: grad_out -> grad_input; forward: x -> y (go and gi
-    # below hold x and y)
-    go, w = draw_forward(shape, seed) if fwd else draw(shape, seed)
-    tgo = torch.from_numpy(go).to(dev)
-    tw = torch.from_numpy(w).to(dev)
-    gi = torch.empty(shape.go_shape if fwd else shape.gi_shape, dtype=torch.float32,
-                     device=dev)
+    gwt = args.op == "grad_weight"
     p = c2b.make_params(shape.batch, shape.in_channels, shape.in_h, shape.in_w,
                         shape.out_channels, shape.kernel_h, shape.kernel_w, shape.stride,
                         shape.padding_h, shape.padding_w, shape.out_h, shape.out_w)
-    plan = c2b.describe_forward_plan(p, f16) if fwd else c2b.describe_plan(p, f16)
     stream = torch.cuda.current_stream()
-    # measured variant choice for this shape, once, outside the timed region
-    # (conv2d_tune; the default entry point then uses the tuned plan)
-    if not args.no_tune:
-        variant = (c2b.tune_forward(gi, tgo, tw, p, f16=f16, stream=stream) if fwd else
-                   c2b.tune(gi, tgo, tw, p, f16=f16, stream=stream))
-    else:
-        variant = (c2b.planned_forward_variant(p, f16) if fwd else
-                   c2b.planned_variant(p, f16))
-    if variant >= 0:   # the plan the timed calls run
-        plan = (c2b.describe_forward_plan_variant(p, variant) if fwd else
-                c2b.describe_plan_variant(p, variant))
-    plan["variant"] = variant
-    plan["tuned"] = not args.no_tune
+    if gwt:
+        # weight gradient: grad_out and x -> grad_weight (go, w and gi below
+        # hold grad_out, x and grad_weight); the workspace is allocated once,
+        # outside the timed region
+        go, _ = draw(shape, seed)
+        w, _ = draw_forward(shape, seed + 100)
+        tgo = torch.from_numpy(go).to(dev)
+        tw = torch.from_numpy(w).to(dev)
+        gi = torch.empty(shape.w_shape, dtype=torch.float32, device=dev)
+        need = c2b.grad_weight_workspace_size(p)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+        plan = {"workspace_bytes": need, "variant": -1, "tuned": False}
 
-    def step():
-        if fwd:
-            c2b.forward_into(gi, tgo, tw, p, f16=f16, stream=stream)
+        def step():
+            c2b.grad_weight_into(gi, tgo, tw, p, workspace=ws, stream=stream)
+    else:
+        # input gradient: grad_out -> grad_input; forward: x -> y (go and gi
+        # below hold x and y)
+        go, w = draw_forward(shape, seed) if fwd else draw(shape, seed)
+        tgo = torch.from_numpy(go).to(dev)
+        tw = torch.from_numpy(w).to(dev)
+        gi = torch.empty(shape.go_shape if fwd else shape.gi_shape, dtype=torch.float32,
+                         device=dev)
+        plan = c2b.describe_forward_plan(p, f16) if fwd else c2b.describe_plan(p, f16)
+        # measured variant choice for this shape, once, outside the timed
+        # region (conv2d_tune; the default entry point then uses the tuned plan)
+        if not args.no_tune:
+            variant = (c2b.tune_forward(gi, tgo, tw, p, f16=f16, stream=stream) if fwd else
+                       c2b.tune(gi, tgo, tw, p, f16=f16, stream=stream))
         else:
-            c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
+            variant = (c2b.planned_forward_variant(p, f16) if fwd else
+                       c2b.planned_variant(p, f16))
+        if variant >= 0:   # the plan the timed calls run
+            plan = (c2b.describe_forward_plan_variant(p, variant) if fwd else
+                    c2b.describe_plan_variant(p, variant))
+        plan["variant"] = variant
+        plan["tuned"] = not args.no_tune
+
+        def step():
+            if fwd:
+                c2b.forward_into(gi, tgo, tw, p, f16=f16, stream=stream)
+            else:
+                c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -221,7 +251,7 @@ def main() -> int:
 
     value = shape.useful_flops * args.steps / wall / 1e12
     achieved = shape.useful_flops / ev_avg_s / 1e12
-    kernel_tag = ("forward_%s" if fwd else "grad_input_%s") % dtype
+    kernel_tag = ("forward_%s" if fwd else "grad_weight_%s" if gwt else "grad_input_%s") % dtype
     traffic = measured_traffic(kernel_tag, shape.name)
     # bound: compare the workload's arithmetic intensity (useful flops per
     # compulsory byte) with the ridge point of the path's matrix peak
@@ -237,7 +267,8 @@ def main() -> int:
                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
                     "traffic": traffic}
     out = {
-        "metric": METRIC_FORWARD if fwd else METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC_FORWARD if fwd else METRIC_GRAD_WEIGHT if gwt else METRIC,
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
