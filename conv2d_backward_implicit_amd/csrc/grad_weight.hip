@@ -15,7 +15,7 @@
 //  * The contraction is split: every workgroup takes a 64 x 64 (co, c) tile
 //    and one chunk of consecutive pixels, and writes its partial tile to a
 //    caller-provided workspace; a second kernel adds the chunks' partial
-//    tiles in chunk order (deterministic) into grad_weight.  Workgroups are
+//    tiles in a fixed order (deterministic) into grad_weight.  Workgroups are
 //    dealt to the 8 XCDs in contiguous runs, so the tiles of one chunk share
 //    an L2.
 //  * A stage is 64 pixels.  Its operands go to LDS through registers:
@@ -51,7 +51,7 @@ constexpr int kPitch = kStagePx + 4;      // floats between operand rows in LDS
 constexpr int kThreads = 256;             // four waves
 constexpr int kRowsPerThread = kTile * kStagePx / kThreads;   // 16 per operand
 constexpr int kWaveRows = 32;             // each wave: 2 x 2 blocks of 16 x 16
-constexpr int kTargetGroupsPerCU = 4;     // workgroups the split aims at, per CU
+constexpr int kTargetGroupsPerCU = 2;     // workgroups the split aims at, per CU
 constexpr uint32_t kPad = 0x80000000u;    // byte offset past every buffer range
 
 // By-value kernel arguments.
@@ -109,29 +109,32 @@ C2B_HD void gw_column(const GWArgs& a, int c, int* xcol, int* khw) {
   *khw = (kh << 16) | kw;
 }
 
-// Pixel p -> (n, q = oh*OW + ow, oh, ow); false if p is past the chunk.
+// Pixel p -> (n, q = oh*OW + ow, oh, ow); false if p is past the chunk (the
+// decomposition is then that of a pixel the caller does not use).  No branch
+// (see gw_a_offset).
 C2B_HD bool gw_pixel(const GWArgs& a, int p, int p_end, int* n, int* q, int* oh, int* ow) {
-  if (p >= p_end) return false;
   *n = p / a.OHOW;
   *q = p - *n * a.OHOW;
   *oh = *q / a.OW;
   *ow = *q - *oh * a.OW;
-  return true;
+  return p < p_end;
 }
 
 // Byte offsets into grad_out / x of the A element (row co) and the B element
 // (column with xcol, khw) at pixel (n, q, oh, ow); kPad if the element is 0.
+// Computed without branches (a select at the end): a branch per element
+// would put a wait for the loads in flight at every join.
 C2B_HD uint32_t gw_a_offset(const GWArgs& a, bool pin, int n, int q, int co) {
-  if (!pin || co >= a.Co) return kPad;
-  return uint32_t(((n * a.Co + co) * a.OHOW + q) * 4);
+  const uint32_t off = uint32_t(((n * a.Co + co) * a.OHOW + q) * 4);
+  return (pin & (co < a.Co)) ? off : kPad;
 }
 C2B_HD uint32_t gw_b_offset(const GWArgs& a, bool pin, int n, int oh, int ow, int xcol,
                             int khw) {
-  if (!pin || khw < 0) return kPad;
   const int kh = khw >> 16, kw = khw & 0xffff;
   const int ih = oh * a.S + kh - a.PH, iw = ow * a.S + kw - a.PW;
-  if ((unsigned)ih >= (unsigned)a.H || (unsigned)iw >= (unsigned)a.W) return kPad;
-  return uint32_t((n * a.Ci * a.H * a.W + xcol + oh * a.S * a.W + ow * a.S) * 4);
+  const bool term = pin & (khw >= 0) & ((unsigned)ih < (unsigned)a.H) & ((unsigned)iw < (unsigned)a.W);
+  const uint32_t off = uint32_t((n * a.Ci * a.H * a.W + xcol + oh * a.S * a.W + ow * a.S) * 4);
+  return term ? off : kPad;
 }
 
 __device__ __forceinline__ float load_f32(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
@@ -161,13 +164,21 @@ __global__ __launch_bounds__(kThreads, 2) void grad_weight_mm_kernel(const GWArg
   for (int j = 0; j < kRowsPerThread; ++j) gw_column(a, T.c0 + r0 + 4 * j, &xcol[j], &khw[j]);
 
   float sa[kRowsPerThread], sb[kRowsPerThread];
+  // all offsets first, then all loads back to back
   auto load_stage = [&](int st) __attribute__((always_inline)) {
-    int n = 0, q = 0, oh = 0, ow = 0;
+    int n, q, oh, ow;
     const bool pin = gw_pixel(a, T.p_begin + st * kStagePx + cpx, T.p_end, &n, &q, &oh, &ow);
+    uint32_t oa[kRowsPerThread], ob[kRowsPerThread];
 #pragma unroll
     for (int j = 0; j < kRowsPerThread; ++j) {
-      sa[j] = load_f32(rsA, gw_a_offset(a, pin, n, q, T.co0 + r0 + 4 * j));
-      sb[j] = load_f32(rsB, gw_b_offset(a, pin, n, oh, ow, xcol[j], khw[j]));
+      oa[j] = gw_a_offset(a, pin, n, q, T.co0 + r0 + 4 * j);
+      ob[j] = gw_b_offset(a, pin, n, oh, ow, xcol[j], khw[j]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < kRowsPerThread; ++j) {
+      sa[j] = load_f32(rsA, oa[j]);
+      sb[j] = load_f32(rsB, ob[j]);
     }
   };
   auto write_stage = [&](int buf) __attribute__((always_inline)) {
@@ -238,14 +249,24 @@ __global__ __launch_bounds__(kThreads, 2) void grad_weight_mm_kernel(const GWArg
     }
 }
 
-// grad_weight[e] = sum over chunks, in chunk order, of the partial tiles.
+// grad_weight[e] = the sum over chunks of the partial tiles, in a fixed
+// order: eight interleaved partial sums (chunks k, k + 8, ...), so that eight
+// loads are in flight per thread, added pairwise at the end.
 __global__ __launch_bounds__(256) void grad_weight_reduce_kernel(const GWArgs a) {
   const int e = blockIdx.x * 256 + threadIdx.x;
   const int total = a.Co * a.NC;
   if (e >= total) return;
-  float s = 0.0f;
-  for (int k = 0; k < a.nchunks; ++k) s += a.part[(size_t)k * total + e];
-  a.dw[e] = s;
+  const float* src = a.part + e;
+  float s[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) s[i] = 0.0f;
+  int k = 0;
+  for (; k + 8 <= a.nchunks; k += 8) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) s[i] += src[(size_t)(k + i) * total];
+  }
+  for (int i = 0; k < a.nchunks; ++k, ++i) s[i] += src[(size_t)k * total];
+  a.dw[e] = ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
 // ---------------------------------------------------------------------------
