@@ -34,10 +34,13 @@ METRIC_GRAD_WEIGHT = "conv2d grad-weight useful TFLOP/s per MI355X and % of MFMA
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}
 PEAK_HBM_GBS = 8000.0
-KERNEL_SOURCES = ["conv2d_backward_implicit_amd/csrc/kernels.hip",
-                  "conv2d_backward_implicit_amd/csrc/tile_index.hpp",
-                  "conv2d_backward_implicit_amd/csrc/plan.hpp",
-                  "conv2d_backward_implicit_amd/csrc/plan.cpp"]
+_CSRC = "conv2d_backward_implicit_amd/csrc/"
+# the sources each entry point's kernels and launch set-up are built from
+KERNEL_SOURCES = {
+    "grad_input": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
+    "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
+    "grad_weight": [_CSRC + f for f in ("grad_weight.hip", "tile_index.hpp", "plan.hpp")],
+}
 
 
 def _code_only(text: str) -> str:
@@ -48,17 +51,17 @@ def _code_only(text: str) -> str:
     return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
 
 
-def source_digest() -> str:
-    """Digest of the code (not the comments) of the kernel sources: a counter
-    summary taken on other code is stale."""
+def source_digest(op: str = "grad_input") -> str:
+    """Digest of the code (not the comments) of one entry point's kernel
+    sources: a counter summary taken on other code is stale."""
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in KERNEL_SOURCES[op]:
         with open(os.path.join(ROOT, rel)) as f:
             h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_tag: str, workload: str):
+def measured_traffic(kernel_tag: str, workload: str, op: str):
     """HBM bytes per launch from a committed rocprofv3 counter summary, if it
     was taken on the current kernel sources; else None."""
     path = os.path.join(ROOT, "profiles", "traffic_%s_%s.txt" % (kernel_tag, workload))
@@ -67,7 +70,7 @@ def measured_traffic(kernel_tag: str, workload: str):
     text = open(path).read()
     m_sha = re.search(r"^source_digest:\s*(\S+)", text, re.M)
     m_val = re.search(r"^hbm_bytes_per_launch:\s*([0-9.eE+]+)", text, re.M)
-    if not m_sha or not m_val or m_sha.group(1) != source_digest():
+    if not m_sha or not m_val or m_sha.group(1) != source_digest(op):
         return None
     return float(m_val.group(1))
 
@@ -252,7 +255,7 @@ def main() -> int:
     value = shape.useful_flops * args.steps / wall / 1e12
     achieved = shape.useful_flops / ev_avg_s / 1e12
     kernel_tag = ("forward_%s" if fwd else "grad_weight_%s" if gwt else "grad_input_%s") % dtype
-    traffic = measured_traffic(kernel_tag, shape.name)
+    traffic = measured_traffic(kernel_tag, shape.name, args.op)
     # bound: compare the workload's arithmetic intensity (useful flops per
     # compulsory byte) with the ridge point of the path's matrix peak
     intensity = shape.useful_flops / shape.compulsory_bytes
@@ -287,7 +290,7 @@ def main() -> int:
         "compulsory_hbm_GBps": round(shape.compulsory_bytes / ev_avg_s / 1e9, 1),
         "plan": plan,
         "roofline": roofline,
-        "source_digest": source_digest(),
+        "source_digest": source_digest(args.op),
     }
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(shape, go, w, args.op)
