@@ -31,7 +31,8 @@ __all__ = [
     "describe_forward_plan", "describe_forward_plan_variant",
     "check_indexing_forward", "check_indexing_forward_variant",
     "grad_weight", "grad_weight_into", "conv2d_grad_weight", "grad_weight_workspace_size",
-    "check_indexing_grad_weight",
+    "check_indexing_grad_weight", "check_indexing_grad_weight_variant",
+    "conv2d_grad_weight_variant", "describe_grad_weight_plan", "GRAD_WEIGHT_VARIANTS",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -67,7 +68,14 @@ EXPORTED_SYMBOLS = (
     "conv2d_grad_weight",
     "conv2d_grad_weight_workspace_size",
     "conv2d_check_indexing_grad_weight",
+    "conv2d_grad_weight_variant",
+    "conv2d_grad_weight_variant_workspace_size",
+    "conv2d_describe_grad_weight_plan",
+    "conv2d_check_indexing_grad_weight_variant",
 )
+
+# weight-gradient column layouts: 0 flat tiles, 1..3 tap tiles of 1, 2, 4 taps
+GRAD_WEIGHT_VARIANTS = 4
 
 CONV2D_OK = 0
 STATUS_NAMES = {
@@ -202,6 +210,19 @@ def load_library():
         lib.conv2d_grad_weight_workspace_size.restype = ctypes.c_int
         lib.conv2d_check_indexing_grad_weight.argtypes = [P, ctypes.c_char_p, ctypes.c_size_t]
         lib.conv2d_check_indexing_grad_weight.restype = ctypes.c_int
+        lib.conv2d_grad_weight_variant.argtypes = lib.conv2d_grad_weight.argtypes + [ctypes.c_int]
+        lib.conv2d_grad_weight_variant.restype = ctypes.c_int
+        lib.conv2d_grad_weight_variant_workspace_size.argtypes = [
+            P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
+        lib.conv2d_grad_weight_variant_workspace_size.restype = ctypes.c_int
+        lib.conv2d_describe_grad_weight_plan.argtypes = [P, ctypes.c_int,
+                                                         ctypes.POINTER(ctypes.c_int32),
+                                                         ctypes.c_int]
+        lib.conv2d_describe_grad_weight_plan.restype = ctypes.c_int
+        lib.conv2d_check_indexing_grad_weight_variant.argtypes = [P, ctypes.c_int,
+                                                                  ctypes.c_char_p,
+                                                                  ctypes.c_size_t]
+        lib.conv2d_check_indexing_grad_weight_variant.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -535,19 +556,45 @@ def forward(x, weight, stride=1, padding_h=0, padding_w=0, f16=False, out=None, 
 
 # ---- weight gradient -----------------------------------------------------------
 
-def grad_weight_workspace_size(p: Conv2dParams) -> int:
-    """Workspace bytes conv2d_grad_weight needs for this shape (current device)."""
+def grad_weight_workspace_size(p: Conv2dParams, variant: int = -1) -> int:
+    """Workspace bytes conv2d_grad_weight (or, for variant >= 0,
+    conv2d_grad_weight_variant) needs for this shape on the current device."""
     n = ctypes.c_size_t(0)
-    rc = load_library().conv2d_grad_weight_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    lib = load_library()
+    if variant < 0:
+        rc = lib.conv2d_grad_weight_workspace_size(ctypes.byref(p), ctypes.byref(n))
+    else:
+        rc = lib.conv2d_grad_weight_variant_workspace_size(ctypes.byref(p), int(variant),
+                                                           ctypes.byref(n))
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return int(n.value)
+
+
+def describe_grad_weight_plan(p: Conv2dParams, variant: int = -1) -> dict:
+    """The weight-gradient plan (pure host code): column layout variant,
+    channels and taps of a tap tile, tile counts and the pixel split."""
+    info = (ctypes.c_int32 * 7)()
+    rc = load_library().conv2d_describe_grad_weight_plan(ctypes.byref(p), int(variant), info, 7)
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    keys = ("variant", "tile_channels", "tile_taps", "co_tiles", "column_tiles", "chunks",
+            "chunk_pixels")
+    return dict(zip(keys, (int(v) for v in info)))
 
 
 def check_indexing_grad_weight(p: Conv2dParams) -> tuple:
     """Host replay of the weight-gradient kernels (no device needed)."""
     buf = ctypes.create_string_buffer(512)
     rc = load_library().conv2d_check_indexing_grad_weight(ctypes.byref(p), buf, len(buf))
+    return int(rc), buf.value.decode()
+
+
+def check_indexing_grad_weight_variant(p: Conv2dParams, variant: int) -> tuple:
+    """Host replay of the weight-gradient kernels for a forced variant."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().conv2d_check_indexing_grad_weight_variant(ctypes.byref(p), int(variant),
+                                                                  buf, len(buf))
     return int(rc), buf.value.decode()
 
 
@@ -560,11 +607,23 @@ def conv2d_grad_weight(grad_out_ptr: int, x_ptr: int, grad_weight_ptr: int, p: C
         ctypes.c_void_p(stream)))
 
 
-def grad_weight_into(grad_weight, grad_out, x, p: Conv2dParams, workspace=None, stream=None):
+def conv2d_grad_weight_variant(grad_out_ptr: int, x_ptr: int, grad_weight_ptr: int,
+                               p: Conv2dParams, workspace_ptr: int, workspace_bytes: int,
+                               stream: int, variant: int) -> int:
+    """Raw C-ABI call of the weight gradient with a forced column layout."""
+    return int(load_library().conv2d_grad_weight_variant(
+        ctypes.c_void_p(grad_out_ptr), ctypes.c_void_p(x_ptr), ctypes.c_void_p(grad_weight_ptr),
+        ctypes.byref(p), ctypes.c_void_p(workspace_ptr), ctypes.c_size_t(int(workspace_bytes)),
+        ctypes.c_void_p(stream), int(variant)))
+
+
+def grad_weight_into(grad_weight, grad_out, x, p: Conv2dParams, workspace=None, stream=None,
+                     variant: int = -1):
     """Write the weight gradient into ``grad_weight`` on torch's current
     stream (or ``stream``).  ``workspace`` (a uint8 GPU tensor of at least
     grad_weight_workspace_size bytes) is allocated here by torch if not given.
-    Raises Conv2dError on a bad status."""
+    ``variant`` >= 0 forces a column layout (tests).  Raises Conv2dError on a
+    bad status."""
     import torch
     _check_tensor(grad_out, "grad_out", (p.batch, p.out_channels, p.out_h, p.out_w))
     _check_tensor(x, "x", (p.batch, p.in_channels, p.in_h, p.in_w))
@@ -573,13 +632,15 @@ def grad_weight_into(grad_weight, grad_out, x, p: Conv2dParams, workspace=None, 
     if not (grad_out.device == x.device == grad_weight.device):
         raise ValueError("all tensors must be on the same device")
     with torch.cuda.device(grad_weight.device):
-        need = grad_weight_workspace_size(p)
+        need = grad_weight_workspace_size(p, variant)
         if workspace is None:
             workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=grad_weight.device)
         s = stream if stream is not None else torch.cuda.current_stream()
-        rc = conv2d_grad_weight(grad_out.data_ptr(), x.data_ptr(), grad_weight.data_ptr(), p,
-                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
-                                int(s.cuda_stream))
+        args = (grad_out.data_ptr(), x.data_ptr(), grad_weight.data_ptr(), p,
+                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                int(s.cuda_stream))
+        rc = (conv2d_grad_weight(*args) if variant < 0 else
+              conv2d_grad_weight_variant(*args, variant))
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return grad_weight

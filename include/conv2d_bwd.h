@@ -337,7 +337,7 @@ int conv2d_check_indexing_forward_variant(const conv2d_params* p, int variant,
  *               owned by the caller, overwritten (partial sums of pixel
  *               chunks; it holds nothing between calls)
  * The contraction over all batch x out_h x out_w pixels is split into
- * chunks; the chunks' partial sums are added in chunk order by a second
+ * chunks; the chunks' partial sums are added in a fixed order by a second
  * kernel, so results do not depend on scheduling.  fp32 matrix cores, fp32
  * accumulation.  Asynchronous on `stream` like conv2d_grad_input; calls that
  * share a workspace must not overlap.
@@ -356,13 +356,50 @@ int conv2d_grad_weight(const float* grad_out, const float* x, float* grad_weight
  * device, in *bytes (may be 0).  CONV2D_OK or the shape's error code. */
 int conv2d_grad_weight_workspace_size(const conv2d_params* p, size_t* bytes);
 
-/* Host replay of conv2d_grad_weight's kernels (no device needed): every
- * copy reads the grad_out / x element of the definition above (or 0 where
- * it has no term), every LDS cell of a stage is written once, the products
- * pair A and B cells of one pixel, and every partial sum is stored once.
- * Returns as conv2d_check_indexing. */
+/* Host replay of conv2d_grad_weight's kernels (no device needed), through
+ * the kernels' own index functions and pixel walk: for every stored weight
+ * row and column each pixel contributes the grad_out x x product of the
+ * definition above (or 0 where it has no term), every LDS cell of a stage
+ * is written once, the products pair A and B cells of one pixel, every
+ * partial-tile element is stored once, and the reduction takes every weight
+ * element from exactly one partial element.  Returns as
+ * conv2d_check_indexing. */
 int conv2d_check_indexing_grad_weight(const conv2d_params* p, char* msg,
                                       size_t msg_len);
+
+/*
+ * Weight-gradient column layouts.  The kernel tiles the (out_channels) x
+ * (in_channels * kernel_h * kernel_w) product in 64 x 64 tiles; a variant
+ * fixes how the 64 column slots of a tile map to weight columns:
+ *   0  flat: 64 consecutive columns of the weight layout;
+ *   1, 2, 3  tap tiles: 64, 32 or 16 input channels x 1, 2 or 4 kernel taps.
+ * conv2d_grad_weight takes the planner's choice; the calls below force one
+ * (tests and measurement).  Every variant computes the same result (up to
+ * fp32 summation order); variant < -1 or > 3 gives CONV2D_ERR_UNSUPPORTED,
+ * -1 the planner's choice.
+ */
+int conv2d_grad_weight_variant(const float* grad_out, const float* x,
+                               float* grad_weight, const conv2d_params* p,
+                               void* workspace, size_t workspace_bytes,
+                               void* stream, int variant);
+
+/* Workspace bytes of conv2d_grad_weight_variant, as
+ * conv2d_grad_weight_workspace_size. */
+int conv2d_grad_weight_variant_workspace_size(const conv2d_params* p,
+                                              int variant, size_t* bytes);
+
+/* The weight-gradient plan of a shape and variant (pure host code; -1: the
+ * planner's), in info[0 .. n-1] (at most 7 values written): variant, input
+ * channels and taps of a tap tile (0, 0 for flat tiles), tiles along
+ * out_channels, column tiles, pixel chunks, pixels per chunk.  CONV2D_OK
+ * or the shape's error code. */
+int conv2d_describe_grad_weight_plan(const conv2d_params* p, int variant,
+                                     int32_t* info, int n);
+
+/* conv2d_check_indexing_grad_weight for a forced variant. */
+int conv2d_check_indexing_grad_weight_variant(const conv2d_params* p,
+                                              int variant, char* msg,
+                                              size_t msg_len);
 
 #ifdef __cplusplus
 }

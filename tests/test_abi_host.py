@@ -357,10 +357,41 @@ def test_grad_weight_workspace_size():
     assert c2b.grad_weight_workspace_size(_p(batch=0)) == 0
     assert c2b.grad_weight_workspace_size(_p(out_channels=0)) == 0
     assert c2b.grad_weight_workspace_size(_p(in_channels=0)) == 0
-    # whole chunks of partial sums, each the size of grad_weight
+    # one 64 x 64 partial tile per (chunk, co tile, column tile), enough
+    # column slots for every weight column
     for sh in CONFIGS:
         p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels,
                             sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h, sh.padding_w)
-        n = c2b.grad_weight_workspace_size(p)
-        per_chunk = sh.out_channels * sh.in_channels * sh.kernel_h * sh.kernel_w * 4
-        assert n % per_chunk == 0 and n // per_chunk >= 1, (sh.name, n)
+        for v in [-1] + list(range(c2b.GRAD_WEIGHT_VARIANTS)):
+            n = c2b.grad_weight_workspace_size(p, v)
+            d = c2b.describe_grad_weight_plan(p, v)
+            assert n == d["chunks"] * d["co_tiles"] * d["column_tiles"] * 64 * 64 * 4, (sh.name, v)
+            assert d["co_tiles"] * 64 >= sh.out_channels
+            assert d["column_tiles"] * 64 >= sh.in_channels * sh.kernel_h * sh.kernel_w
+            assert d["chunks"] * d["chunk_pixels"] >= sh.batch * sh.out_h * sh.out_w
+            if v >= 0:
+                assert d["variant"] == v
+
+
+def test_grad_weight_variants_host():
+    lib = c2b.load_library()
+    p = _p()
+    need = c2b.grad_weight_workspace_size(p, 0)
+    for v in (-2, c2b.GRAD_WEIGHT_VARIANTS):
+        assert c2b.conv2d_grad_weight_variant(0x100000, 0x200000, 0x400000, p, 0x7000000,
+                                              need, 0, v) == -5
+        with pytest.raises(c2b.Conv2dError):
+            c2b.describe_grad_weight_plan(p, v)
+        assert c2b.check_indexing_grad_weight_variant(p, v)[0] == -5
+    assert lib.conv2d_describe_grad_weight_plan(None, -1, None, 0) == NULL
+    # tap tiles: 64 (channel, tap) slots, 1, 2 or 4 taps
+    for v, taps in ((1, 1), (2, 2), (3, 4)):
+        d = c2b.describe_grad_weight_plan(p, v)
+        assert (d["tile_taps"], d["tile_channels"]) == (taps, 64 // taps)
+    # the planner: tap tiles for many channels, flat tiles for a few-channel
+    # big kernel (the 7x7 stem), the fewest slots among the tap layouts
+    assert c2b.describe_grad_weight_plan(_p(in_channels=64, out_channels=64))["variant"] == 1
+    stem = c2b.make_params(16, 3, 224, 224, 64, 7, 7, 2, 3, 3)
+    assert c2b.describe_grad_weight_plan(stem)["variant"] == 0
+    assert c2b.describe_grad_weight_plan(_p(in_channels=32))["variant"] == 2
+    assert c2b.describe_grad_weight_plan(_p(in_channels=16))["variant"] == 3

@@ -37,7 +37,7 @@ def _oracle_gw(sh, go, x):
                               sh.padding_w)
 
 
-def run_gw(sh, go, x, workspace=None):
+def run_gw(sh, go, x, workspace=None, variant=-1):
     """grad_weight of the HIP path (NaN-filled, guarded output) as numpy."""
     import torch
     dev = torch.device("cuda", 0)
@@ -48,7 +48,7 @@ def run_gw(sh, go, x, workspace=None):
     buf[:GUARD] = CANARY
     buf[GUARD + n:] = CANARY
     gw = buf[GUARD:GUARD + n].view(sh.w_shape)
-    c2b.grad_weight_into(gw, tgo, tx, params_of(sh), workspace=workspace)
+    c2b.grad_weight_into(gw, tgo, tx, params_of(sh), workspace=workspace, variant=variant)
     torch.cuda.synchronize()
     host = buf.cpu().numpy()
     assert np.all(host[:GUARD] == np.float32(CANARY)), "write before grad_weight"
@@ -63,15 +63,21 @@ def _reduced(sh: ConvShape, batch: int) -> ConvShape:
     return ConvShape(**d)
 
 
-def _check(sh, seed):
+def _check(sh, seed, variants=(-1,)):
     go, _ = draw(sh, seed)
     x, _ = draw_forward(sh, seed + 1)
     ref = _oracle_gw(sh, go, x)
-    got = run_gw(sh, go, x)
-    assert not np.any(np.isnan(got)), "unwritten grad_weight elements"
-    err = rel_err(got, ref)
-    assert err <= TOL, (sh.name, err)
-    return err
+    worst = 0.0
+    for v in variants:
+        got = run_gw(sh, go, x, variant=v)
+        assert not np.any(np.isnan(got)), ("unwritten grad_weight elements", v)
+        err = rel_err(got, ref)
+        assert err <= TOL, (sh.name, v, err)
+        worst = max(worst, err)
+    return worst
+
+
+ALL_VARIANTS = (-1,) + tuple(range(c2b.GRAD_WEIGHT_VARIANTS))
 
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
@@ -79,7 +85,7 @@ def test_grad_weight_config_reduced_batch(idx):
     cfg = CONFIGS[idx]
     sh = cfg if cfg.batch <= 2 else _reduced(cfg, 2 if idx != 2 else 1)
     _say("case grad_weight", sh.name)
-    _say("  rel err", _check(sh, 600 + idx))
+    _say("  rel err", _check(sh, 600 + idx, ALL_VARIANTS))
 
 
 @pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
@@ -90,8 +96,10 @@ def test_grad_weight_integer_inputs_bit_exact(idx):
     rng = np.random.default_rng(700 + idx)
     go = rng.integers(-4, 5, size=sh.go_shape).astype(np.float32)
     x = rng.integers(-4, 5, size=sh.gi_shape).astype(np.float32)
-    got = run_gw(sh, go, x)
-    assert np.array_equal(got.astype(np.float64), _oracle_gw(sh, go, x))
+    ref = _oracle_gw(sh, go, x)
+    for v in ALL_VARIANTS:
+        got = run_gw(sh, go, x, variant=v)
+        assert np.array_equal(got.astype(np.float64), ref), v
 
 
 GW_EXTRA = [
@@ -99,6 +107,12 @@ GW_EXTRA = [
     ConvShape("n0", 0, 3, 7, 7, 5, 3, 3, 1, 1, 1, 7, 7, dist="uniform"),
     # many chunks crossing image boundaries, columns past a 64-column tile
     ConvShape("chunks", 5, 9, 21, 17, 70, 3, 3, 1, 1, 1, 21, 17, dist="uniform"),
+    # planes of fewer than 64 pixels (a stage spans several images; the pixel
+    # walk carries into the image index), one-row and one-column images
+    ConvShape("tiny_planes", 9, 20, 4, 5, 33, 3, 3, 1, 1, 1, 4, 5, dist="uniform"),
+    ConvShape("one_pixel", 70, 17, 1, 1, 9, 1, 1, 1, 0, 0, 1, 1, dist="uniform"),
+    ConvShape("row", 3, 40, 1, 90, 20, 1, 5, 2, 0, 2, 1, 45, dist="uniform"),
+    ConvShape("column", 3, 24, 77, 1, 12, 4, 1, 3, 2, 0, 26, 1, dist="uniform"),
 ]
 
 
@@ -106,7 +120,7 @@ GW_EXTRA = [
                          ids=[s.name for s in EDGE + list(VARIANT_SHAPES) + GW_EXTRA])
 def test_grad_weight_shapes(sh):
     _say("case grad_weight", sh.name)
-    _check(sh, 31)
+    _check(sh, 31, ALL_VARIANTS)
     if sh.batch == 0:
         assert np.all(run_gw(sh, np.zeros(sh.go_shape), np.zeros(sh.gi_shape)) == 0.0)
 
@@ -114,7 +128,7 @@ def test_grad_weight_shapes(sh):
 def test_grad_weight_random_small_shapes():
     for i, sh in enumerate(RANDOM):
         _say("case grad_weight", sh)
-        _check(sh, 800 + i)
+        _check(sh, 800 + i, (-1, i % c2b.GRAD_WEIGHT_VARIANTS))
 
 
 def test_grad_weight_workspace_reuse():

@@ -129,10 +129,19 @@ def test_grad_weight_workloads(sh):
     assert rc == 0, (sh.name, rc, msg)
 
 
+@pytest.mark.parametrize("variant", range(c2b.GRAD_WEIGHT_VARIANTS))
+def test_grad_weight_workloads_every_variant(variant):
+    for sh in CONFIGS[:3]:
+        rc, msg = c2b.check_indexing_grad_weight_variant(params_of(sh), variant)
+        assert rc == 0, (sh.name, variant, rc, msg)
+
+
 def test_grad_weight_test_shapes():
     for sh in EDGE + RANDOM + list(VARIANT_SHAPES) + list(SMALL_CI_SHAPES):
-        rc, msg = c2b.check_indexing_grad_weight(params_of(sh))
-        assert rc == 0, (sh.name, rc, msg)
+        for v in [-1] + list(range(c2b.GRAD_WEIGHT_VARIANTS)):
+            rc, msg = (c2b.check_indexing_grad_weight(params_of(sh)) if v < 0 else
+                       c2b.check_indexing_grad_weight_variant(params_of(sh), v))
+            assert rc == 0, (sh.name, v, rc, msg)
 
 
 def test_grad_weight_random_stress():
@@ -141,3 +150,6 @@ def test_grad_weight_random_stress():
         sh = random_shape(rng, max_n=3, max_c=90, max_hw=40, max_k=7, max_s=4, name="w%d" % i)
         rc, msg = c2b.check_indexing_grad_weight(params_of(sh))
         assert rc == 0, (sh, rc, msg)
+        v = i % c2b.GRAD_WEIGHT_VARIANTS
+        rc, msg = c2b.check_indexing_grad_weight_variant(params_of(sh), v)
+        assert rc == 0, (sh, v, rc, msg)
