@@ -343,31 +343,49 @@ __global__ __launch_bounds__(kThreads, 4) void grad_weight_mm_kernel(const GWArg
 }
 
 // grad_weight[co, ci, t] = the sum over chunks of the partial tiles, in a
-// fixed order: eight interleaved partial sums (chunks k, k + 8, ...), so that
-// eight loads are in flight per thread, added pairwise at the end.  Thread e
-// takes partial-tile element e (tile, row, slot); rows past Co and slots with
-// no column store nothing.
+// fixed order.  A workgroup takes 16 groups of four consecutive partial-tile
+// elements (row, slots s .. s+3) and 16 chunk lanes: thread (group q, lane l)
+// adds chunks l, l + 16, ... with 16-byte loads (many in flight: the sum is
+// bandwidth-bound), then lane 0 adds the 16 lane sums in lane order.  Rows
+// past Co and slots with no column store nothing.
+constexpr int kReduceLanes = 16;
+constexpr int kReduceQuads = 256 / kReduceLanes;
+
 __global__ __launch_bounds__(256) void grad_weight_reduce_kernel(const GWArgs a) {
-  const int e = blockIdx.x * 256 + threadIdx.x;
-  const int total = a.TM * a.TN * kTileElems;
-  if (e >= total) return;
+  __shared__ f32x4 sums[kReduceLanes][kReduceQuads];
+  const int q = threadIdx.x % kReduceQuads, l = threadIdx.x / kReduceQuads;
+  const int total = a.TM * a.TN * kTileElems;   // a multiple of 4 * kReduceQuads
+  const int e = (blockIdx.x * kReduceQuads + q) * 4;
+  const f32x4* src = reinterpret_cast<const f32x4*>(a.part + e);
+  const size_t stride = size_t(total) / 4;
+  f32x4 s[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) s[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  int k = l;
+  for (; k + 3 * kReduceLanes < a.nchunks; k += 4 * kReduceLanes) {
+    f32x4 v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = src[size_t(k + i * kReduceLanes) * stride];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) s[i] += v[i];
+  }
+  for (int i = 0; k < a.nchunks; k += kReduceLanes, ++i) s[i] += src[size_t(k) * stride];
+  sums[l][q] = (s[0] + s[1]) + (s[2] + s[3]);
+  __syncthreads();
+  if (l != 0) return;
+  f32x4 t = sums[0][q];
+#pragma unroll
+  for (int i = 1; i < kReduceLanes; ++i) t += sums[i][q];
   const int tile = e / kTileElems, rs = e - tile * kTileElems;
   const int tm = tile / a.TN, tn = tile - tm * a.TN;
   const int co = tm * kTile + rs / kTile;
-  int ci, t;
-  if (!gw_slot_column(a, tn, rs % kTile, &ci, &t) || co >= a.Co) return;
-  const float* src = a.part + e;
-  float s[8];
+  if (co >= a.Co) return;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) s[i] = 0.0f;
-  int k = 0;
-  for (; k + 8 <= a.nchunks; k += 8) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) s[i] += src[size_t(k + i) * total];
+  for (int r = 0; r < 4; ++r) {
+    int ci, c;
+    if (gw_slot_column(a, tn, rs % kTile + r, &ci, &c))
+      a.dw[(co * a.Ci + ci) * a.KHW + c] = t[r];
   }
-  for (int i = 0; k < a.nchunks; ++k, ++i) s[i] += src[size_t(k) * total];
-  a.dw[(co * a.Ci + ci) * a.KHW + t] =
-      ((s[0] + s[1]) + (s[2] + s[3])) + ((s[4] + s[5]) + (s[6] + s[7]));
 }
 
 // ---------------------------------------------------------------------------
@@ -645,8 +663,9 @@ int gw_check(const conv2d_params* p, int variant, char* msg, size_t len) {
   return CONV2D_OK;
 }
 
-// Pointer checks: inputs go, x; outputs dw and the workspace, which may not
-// overlap each other or an input.
+// Pointer checks: inputs go, x; outputs dw and the workspace (16-byte
+// aligned: the reduction reads it in 16-byte loads), which may not overlap
+// each other or an input.
 int gw_check_pointers(const float* go, const float* x, const float* dw, const void* ws,
                       size_t ws_bytes, const conv2d_params* p, const GWArgs& a) {
   const uint64_t n_go = uint64_t(p->batch) * p->out_channels * p->out_h * p->out_w;
@@ -655,7 +674,8 @@ int gw_check_pointers(const float* go, const float* x, const float* dw, const vo
   const uint64_t ws_need = gw_workspace_bytes(a);
   if ((n_go && go == nullptr) || (n_x && x == nullptr) || (n_dw && dw == nullptr))
     return CONV2D_ERR_NULL_PTR;
-  if (ws_need && (ws == nullptr || ws_bytes < ws_need)) return CONV2D_ERR_WORKSPACE;
+  if (ws_need && (ws == nullptr || ws_bytes < ws_need || reinterpret_cast<uintptr_t>(ws) % 16))
+    return CONV2D_ERR_WORKSPACE;
   auto overlap = [](const void* a0, uint64_t na, const void* b0, uint64_t nb) {
     if (na == 0 || nb == 0) return false;
     const uintptr_t a = reinterpret_cast<uintptr_t>(a0), b = reinterpret_cast<uintptr_t>(b0);
@@ -700,7 +720,8 @@ int run(const float* grad_out, const float* x, float* grad_weight, const conv2d_
       hipLaunchKernelGGL(grad_weight_mm_kernel<false>, dim3(a.TM * a.TN * a.nchunks),
                          dim3(kThreads), 0, st, a);
   }
-  hipLaunchKernelGGL(grad_weight_reduce_kernel, dim3((total + 255) / 256), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(grad_weight_reduce_kernel, dim3(total / (4 * kReduceQuads)), dim3(256), 0,
+                     st, a);
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 

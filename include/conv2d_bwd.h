@@ -91,7 +91,8 @@ enum {
   CONV2D_ERR_HIP = -6,         /* the HIP runtime reported an error at
                                   launch (hipGetLastError)                   */
   CONV2D_ERR_WORKSPACE = -7    /* conv2d_grad_weight: the workspace is
-                                  smaller than its workspace size            */
+                                  smaller than its workspace size or not
+                                  16-byte aligned                            */
 };
 
 /*
@@ -334,8 +335,9 @@ int conv2d_check_indexing_forward_variant(const conv2d_params* p, int variant,
  *   x           [batch, in_channels, in_h, in_w]               (read)
  *   grad_weight [out_channels, in_channels, kernel_h, kernel_w] (overwritten)
  *   workspace   conv2d_grad_weight_workspace_size bytes of device memory,
- *               owned by the caller, overwritten (partial sums of pixel
- *               chunks; it holds nothing between calls)
+ *               16-byte aligned (hipMalloc gives 256), owned by the caller,
+ *               overwritten (partial sums of pixel chunks; it holds nothing
+ *               between calls)
  * The contraction over all batch x out_h x out_w pixels is split into
  * chunks; the chunks' partial sums are added in a fixed order by a second
  * kernel, so results do not depend on scheduling.  fp32 matrix cores, fp32
@@ -344,8 +346,8 @@ int conv2d_check_indexing_forward_variant(const conv2d_params* p, int variant,
  *
  * Errors: as conv2d_grad_input (CONV2D_ERR_ALIAS if grad_weight or the
  * workspace overlaps an input or each other), CONV2D_ERR_WORKSPACE if the
- * workspace is NULL or smaller than the size below while that size is not
- * 0, CONV2D_ERR_OVERFLOW if grad_out or x reaches 2^31 bytes.  batch = 0 (no
+ * workspace is NULL, not 16-byte aligned or smaller than the size below
+ * while that size is not 0, CONV2D_ERR_OVERFLOW if grad_out or x reaches 2^31 bytes.  batch = 0 (no
  * pixel) writes zeros.
  */
 int conv2d_grad_weight(const float* grad_out, const float* x, float* grad_weight,

@@ -340,6 +340,7 @@ def test_grad_weight_rejects_before_any_device_call():
     # workspace missing or too small
     assert call(0x100000, 0x200000, 0x400000, p, ws=0) == -7
     assert call(0x100000, 0x200000, 0x400000, p, wsb=need - 4) == -7
+    assert call(0x100000, 0x200000, 0x400000, p, ws=0x7000004) == -7   # not 16-byte aligned
     # grad_weight or workspace overlapping an input or each other
     assert call(0x100000, 0x200000, 0x100000, p) == ALIAS
     assert call(0x100000, 0x200000, 0x400000, p, ws=0x200000) == ALIAS
