@@ -343,39 +343,46 @@ __global__ __launch_bounds__(kThreads, 4) void grad_weight_mm_kernel(const GWArg
 }
 
 // grad_weight[co, ci, t] = the sum over chunks of the partial tiles, in a
-// fixed order.  A workgroup takes 16 groups of four consecutive partial-tile
-// elements (row, slots s .. s+3) and 16 chunk lanes: thread (group q, lane l)
-// adds chunks l, l + 16, ... with 16-byte loads (many in flight: the sum is
-// bandwidth-bound), then lane 0 adds the 16 lane sums in lane order.  Rows
-// past Co and slots with no column store nothing.
-constexpr int kReduceLanes = 16;
-constexpr int kReduceQuads = 256 / kReduceLanes;
+// fixed order.  A workgroup takes 256 / L groups of four consecutive
+// partial-tile elements (row, slots s .. s+3) and L chunk lanes (L = 1, 2,
+// .., 16, about nchunks / 8): thread (group q, lane l) adds chunks l, l + L,
+// ... with 16-byte loads, four in flight, then lane 0 adds the L lane sums in
+// lane order.  Rows past Co and slots with no column store nothing.
+constexpr int kReduceMaxLanes = 16;
 
-__global__ __launch_bounds__(256) void grad_weight_reduce_kernel(const GWArgs a) {
-  __shared__ f32x4 sums[kReduceLanes][kReduceQuads];
-  const int q = threadIdx.x % kReduceQuads, l = threadIdx.x / kReduceQuads;
-  const int total = a.TM * a.TN * kTileElems;   // a multiple of 4 * kReduceQuads
-  const int e = (blockIdx.x * kReduceQuads + q) * 4;
+int reduce_lanes(int nchunks) {
+  int lanes = 1;
+  while (lanes < kReduceMaxLanes && lanes * 8 < nchunks) lanes *= 2;
+  return lanes;
+}
+
+__global__ __launch_bounds__(256) void grad_weight_reduce_kernel(const GWArgs a, int lanes) {
+  __shared__ f32x4 sums[256];
+  const int quads = 256 / lanes;
+  const int q = threadIdx.x % quads, l = threadIdx.x / quads;
+  const int total = a.TM * a.TN * kTileElems;   // a multiple of 4 * 256
+  const int e = (blockIdx.x * quads + q) * 4;
   const f32x4* src = reinterpret_cast<const f32x4*>(a.part + e);
   const size_t stride = size_t(total) / 4;
   f32x4 s[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) s[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   int k = l;
-  for (; k + 3 * kReduceLanes < a.nchunks; k += 4 * kReduceLanes) {
+  for (; k + 3 * lanes < a.nchunks; k += 4 * lanes) {
     f32x4 v[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = src[size_t(k + i * kReduceLanes) * stride];
+    for (int i = 0; i < 4; ++i) v[i] = src[size_t(k + i * lanes) * stride];
 #pragma unroll
     for (int i = 0; i < 4; ++i) s[i] += v[i];
   }
-  for (int i = 0; k < a.nchunks; k += kReduceLanes, ++i) s[i] += src[size_t(k) * stride];
-  sums[l][q] = (s[0] + s[1]) + (s[2] + s[3]);
-  __syncthreads();
-  if (l != 0) return;
-  f32x4 t = sums[0][q];
-#pragma unroll
-  for (int i = 1; i < kReduceLanes; ++i) t += sums[i][q];
+  for (int i = 0; k < a.nchunks; k += lanes, ++i) s[i] += src[size_t(k) * stride];
+  f32x4 t = (s[0] + s[1]) + (s[2] + s[3]);
+  if (lanes > 1) {
+    sums[threadIdx.x] = t;
+    __syncthreads();
+    if (l != 0) return;
+    for (int i = 1; i < lanes; ++i) t += sums[i * quads + q];
+  }
   const int tile = e / kTileElems, rs = e - tile * kTileElems;
   const int tm = tile / a.TN, tn = tile - tm * a.TN;
   const int co = tm * kTile + rs / kTile;
@@ -637,7 +644,13 @@ int gw_check(const conv2d_params* p, int variant, char* msg, size_t len) {
     GW_REQUIRE(a.nchunks == 0 || (int64_t(a.nchunks - 1) * a.chunk_px < a.P &&
                                   int64_t(a.nchunks) * a.chunk_px >= a.P && a.chunk_px % kStagePx == 0),
                "chunks do not cover the pixels");
-    // the reduction writes every weight element from exactly one (row, slot)
+    // the reduction's workgroups cover the partial-tile elements in whole
+    // groups of four, and write every weight element from exactly one (row,
+    // slot)
+    const int lanes = reduce_lanes(a.nchunks);
+    GW_REQUIRE(lanes >= 1 && lanes <= kReduceMaxLanes && 256 % lanes == 0 &&
+                   (tiles * kTileElems * lanes) % (4 * 256) == 0,
+               "reduction grid");
     std::vector<unsigned char> dw_hit(size_t(int64_t(a.Co) * a.NC), 0);
     for (int64_t e = 0; e < tiles * kTileElems; ++e) {
       const int tile = int(e / kTileElems), rs = int(e % kTileElems);
@@ -720,8 +733,9 @@ int run(const float* grad_out, const float* x, float* grad_weight, const conv2d_
       hipLaunchKernelGGL(grad_weight_mm_kernel<false>, dim3(a.TM * a.TN * a.nchunks),
                          dim3(kThreads), 0, st, a);
   }
-  hipLaunchKernelGGL(grad_weight_reduce_kernel, dim3(total / (4 * kReduceQuads)), dim3(256), 0,
-                     st, a);
+  const int lanes = reduce_lanes(a.nchunks);
+  hipLaunchKernelGGL(grad_weight_reduce_kernel, dim3(total * lanes / (4 * 256)), dim3(256), 0,
+                     st, a, lanes);
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 
