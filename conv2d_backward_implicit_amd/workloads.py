@@ -157,3 +157,52 @@ def random_shape(rng: np.random.Generator, max_n=2, max_c=5, max_hw=9, max_k=5,
         if oh >= 1 and ow >= 1:
             return ConvShape(name, n, ci, h, w, co, kh, kw, s, ph, pw, oh, ow,
                              dist="uniform")
+
+
+# ---- RMSNorm-fused matrix product (C = RmsNorm(X, g) x W) ---------------------
+
+@dataclass(frozen=True)
+class RmsShape:
+    """X [m, k] tokens x hidden, g [k] norm scale, W [k, n] projection."""
+    name: str
+    m: int
+    k: int
+    n: int
+    eps: float = 1e-6
+
+    @property
+    def useful_flops(self) -> int:
+        return 2 * self.m * self.k * self.n
+
+    @property
+    def compulsory_bytes(self) -> int:
+        return 4 * (self.m * self.k + self.k + self.k * self.n + self.m * self.n)
+
+
+# The source page gives no sizes; these stand in: a ragged case the oracle
+# finishes at once, and LLM-style projections (tokens x hidden -> out).
+RMS_CONFIGS = [
+    RmsShape("rms_tiny_m7_k45_n19", 7, 45, 19),
+    RmsShape("rms_proj_m8192_k4096_n4096", 8192, 4096, 4096),
+    RmsShape("rms_mlp_up_m4096_k4096_n11008", 4096, 4096, 11008),
+    RmsShape("rms_ragged_m3000_k1000_n1500", 3000, 1000, 1500),
+]
+
+RMS_HEADLINE = 1
+
+
+def rms_by_name(name: str) -> RmsShape:
+    for c in RMS_CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+def draw_rms(shape: RmsShape, seed: int):
+    """(x, g, w) as float32: x ~ N(0, 1), g ~ 1 + 0.1 N(0, 1), w ~ N(0, 1/k),
+    drawn in that order from ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((shape.m, shape.k))
+    g = 1.0 + 0.1 * rng.standard_normal(shape.k)
+    w = rng.standard_normal((shape.k, shape.n)) / np.sqrt(shape.k)
+    return x.astype(np.float32), g.astype(np.float32), w.astype(np.float32)

@@ -22,6 +22,9 @@ Functions (all take float64-convertible arrays and return float64 arrays):
 * ``conv2d_forward``       -- forward cross-correlation, for the adjoint check.
 * ``grad_weight``          -- the weight gradient of the same forward
   cross-correlation (not on the pages; its index map is the forward one).
+* ``rms_norm_matmul``      -- C = RmsNorm(X, g) x W of the second page,
+  ``src/shaders/matmul_rms_norm.wgsl`` (header comment, per-row rsqrt
+  prologue, normalise-on-load), in that order, optionally for chosen rows.
 
 Every function is pinned by tests/test_oracle.py to facts outside the oracle
 itself (closed forms, delta inputs, a library GEMM, torch's CPU convolution
@@ -96,6 +99,9 @@ class Oracle:
             fn.restype = None
         lib.oracle_grad_input_gather_at.argtypes = [_DP, _DP, _IP, _I64, _DP] + [_I64] * 12
         lib.oracle_grad_input_gather_at.restype = None
+        lib.oracle_rms_norm_matmul.argtypes = [_DP, _DP, _DP, _DP, _I64, _I64, _I64,
+                                               ctypes.c_double, _IP, _I64]
+        lib.oracle_rms_norm_matmul.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self._lib = lib
@@ -158,6 +164,27 @@ class Oracle:
                                      int(padding_w), OH, OW)
         return gw
 
+    def rms_norm_matmul(self, x, g, w, eps, rows=None):
+        """C [M, N] = RmsNorm(x [M, K], g [K], eps) x w [K, N] (float64).  With
+        ``rows`` (indices), only those rows are computed and returned, as a
+        [len(rows), N] array."""
+        xx, gg, ww = _f64(x), _f64(g), _f64(w)
+        M, K = (int(v) for v in xx.shape)
+        K2, N = (int(v) for v in ww.shape)
+        if K2 != K or gg.shape != (K,):
+            raise ValueError("shapes x %s, g %s, w %s do not chain" % (xx.shape, gg.shape,
+                                                                     ww.shape))
+        if K < 1:
+            raise ValueError("the mean over K needs K >= 1")
+        sel = np.arange(M, dtype=np.int64) if rows is None else \
+            np.ascontiguousarray(rows, dtype=np.int64)
+        if sel.size and (sel.min() < 0 or sel.max() >= M):
+            raise IndexError("row index out of range")
+        c = np.zeros((M, N), dtype=np.float64)
+        self._lib.oracle_rms_norm_matmul(_ptr(xx), _ptr(gg), _ptr(ww), _ptr(c), M, K, N,
+                                         float(eps), sel.ctypes.data_as(_IP), int(sel.size))
+        return c if rows is None else c[sel]
+
     def num_threads(self) -> int:
         """OpenMP threads the oracle routines use in this process."""
         return int(self._lib.oracle_num_threads())
@@ -194,6 +221,10 @@ def conv2d_forward(*a, **k):
 
 def grad_weight(*a, **k):
     return default().grad_weight(*a, **k)
+
+
+def rms_norm_matmul(*a, **k):
+    return default().rms_norm_matmul(*a, **k)
 
 
 def num_threads() -> int:

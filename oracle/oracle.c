@@ -1,5 +1,7 @@
 /*
- * CPU oracle for the convolution backward pass with respect to the input.
+ * CPU oracle for the convolution backward pass with respect to the input (and
+ * the operators beside it: the forward convolution, the weight gradient, and
+ * the RMSNorm-fused matrix product of a second page).
  *
  * TEST INFRASTRUCTURE ONLY.  Only tests/, __graft_entry__.smoke() and the
  * cpu_baseline leg of bench.py may load this code.  The product path (the HIP
@@ -10,7 +12,10 @@
  * "src/shaders/conv2d_grad_input_gemm_coop.wgsl".  The sections referred to
  * are that shader's header comment, its `Params` struct, the two branches of
  * its im2col (B-tile) staging (stride 1 and stride > 1), its weight_T (A-tile)
- * staging and its final store to grad_input.
+ * staging and its final store to grad_input.  [p2] is the docs.rs source page
+ * of the same crate, "src/shaders/matmul_rms_norm.wgsl" (header comment,
+ * per-row rsqrt prologue, normalise-on-load A staging); only
+ * oracle_rms_norm_matmul follows it.
  *
  * Every routine here is a plain loop nest over the definition, accumulated in
  * double precision, with no blocking, no reordering beyond the definition and
@@ -27,6 +32,7 @@
  * still one serial sum in the definition's loop order), so results do not
  * depend on the thread count.
  */
+#include <math.h>
 #include <stdint.h>
 #include <string.h>
 #ifdef _OPENMP
@@ -230,6 +236,35 @@ void oracle_grad_weight(const double* go, const double* x, double* gw, i64 N,
       }
     }
     gw[e] = acc;
+  }
+}
+
+/* RMSNorm-fused matrix product (meganeura 0.2.0, matmul_rms_norm.wgsl: the
+ * header comment's C = RmsNorm(X, W_norm) x W_proj, the per-row prologue and
+ * the normalise-on-load step), in the page's order and in double precision:
+ *   r[i]    = 1 / sqrt(sum_k x[i, k]^2 / K + eps)
+ *   a[i, k] = x[i, k] * r[i] * g[k]
+ *   c[i, j] = sum_k a[i, k] * w[k, j]
+ * x [M, K], g [K] (the norm scale), w [K, N], c [M, N], all row-major.  Only
+ * the rows listed in rows[0 .. nrows-1] are computed (c keeps M rows).  K >=
+ * 1 is the caller's to ensure. */
+void oracle_rms_norm_matmul(const double* x, const double* g, const double* w, double* c,
+                            i64 M, i64 K, i64 N, double eps, const i64* rows, i64 nrows) {
+  (void)M;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (i64 t = 0; t < nrows; ++t) {
+    const i64 i = rows[t];
+    const double* xi = x + i * K;
+    double ss = 0.0;
+    for (i64 k = 0; k < K; ++k) ss += xi[k] * xi[k];
+    const double r = 1.0 / sqrt(ss / (double)K + eps);
+    double* ci = c + i * N;
+    for (i64 j = 0; j < N; ++j) ci[j] = 0.0;
+    for (i64 k = 0; k < K; ++k) {
+      const double a = xi[k] * r * g[k];
+      const double* wk = w + k * N;
+      for (i64 j = 0; j < N; ++j) ci[j] += a * wk[j];
+    }
   }
 }
 

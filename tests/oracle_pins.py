@@ -18,7 +18,11 @@ What the pins rest on:
   stride-1 case as a plain matrix product (numpy matmul), exact zeros at
   pixels no tap reaches (stride > kernel);
 * integer inputs, for which float64 sums are exact;
-* hand-worked tap-count tables under tests/golden/ (no program made them).
+* hand-worked tap-count tables under tests/golden/ (no program made them);
+* for the RMSNorm-fused product: torch's CPU ``rms_norm`` and matrix product
+  in float64, constant rows (normalised to their sign), the one-column case
+  written out, scale invariance at eps = 0, linearity in W and in g, and
+  zero rows.
 """
 from __future__ import annotations
 
@@ -379,6 +383,89 @@ def pin_grad_weight_all_ones(orc):
                 assert np.all(got[:, :, kh, kw] == want), (sh, kh, kw, want)
 
 
+# ---- RMSNorm-fused matrix product (second page, matmul_rms_norm.wgsl) --------
+
+_RMS_SHAPES = [(1, 1, 1), (3, 1, 4), (5, 7, 3), (9, 33, 17), (16, 64, 20), (2, 130, 5)]
+
+
+def _rms_inputs(M, K, N, seed):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((M, K)), 1.0 + 0.3 * rng.standard_normal(K),
+            rng.standard_normal((K, N)))
+
+
+def pin_torch_rms_norm_matmul(orc):
+    """torch's CPU rms_norm (float64, with the norm weight and eps) followed by
+    torch's matrix product: an implementation that is not this oracle."""
+    import torch
+    for i, (M, K, N) in enumerate(_RMS_SHAPES):
+        x, g, w = _rms_inputs(M, K, N, 300 + i)
+        for eps in (1e-6, 0.25):
+            ref = (torch.nn.functional.rms_norm(torch.from_numpy(x), (K,),
+                                                weight=torch.from_numpy(g), eps=eps)
+                   @ torch.from_numpy(w)).numpy()
+            err = _rel_err(orc.rms_norm_matmul(x, g, w, eps), ref)
+            assert err <= 1e-12, ((M, K, N), eps, err)
+
+
+def pin_rms_constant_rows(orc):
+    """Row i constant c_i != 0 and eps = 0: the mean square is c_i^2, so the
+    normalised row is sign(c_i) everywhere and C[i] = sign(c_i) * (g @ W)."""
+    rng = np.random.default_rng(41)
+    for M, K, N in [(4, 6, 5), (3, 50, 9), (2, 1, 3)]:
+        c = rng.uniform(0.5, 3.0, M) * rng.choice([-1.0, 1.0], M)
+        x = np.repeat(c[:, None], K, axis=1)
+        g = rng.standard_normal(K)
+        w = rng.standard_normal((K, N))
+        want = np.sign(c)[:, None] * (g @ w)[None, :]
+        err = _rel_err(orc.rms_norm_matmul(x, g, w, 0.0), want)
+        assert err <= 1e-13, ((M, K, N), err)
+
+
+def pin_rms_one_column(orc):
+    """K = 1: C[i, j] = x_i / sqrt(x_i^2 + eps) * g * w[0, j], written out for
+    chosen numbers (eps large enough to matter)."""
+    x = np.array([[2.0], [-0.5], [0.0]])
+    g = np.array([3.0])
+    w = np.array([[1.0, -2.0]])
+    eps = 0.25
+    got = orc.rms_norm_matmul(x, g, w, eps)
+    # 2/sqrt(4.25)*3 = 2.910427..., -0.5/sqrt(0.5)*3 = -2.121320...
+    want = np.array([[6.0 / np.sqrt(4.25), -12.0 / np.sqrt(4.25)],
+                     [-1.5 / np.sqrt(0.5), 3.0 / np.sqrt(0.5)],
+                     [0.0, 0.0]])
+    assert np.max(np.abs(got - want)) <= 1e-14, got
+
+
+def pin_rms_scale_and_linearity(orc):
+    """With eps = 0 a positive scale of a row leaves C unchanged; C is linear
+    in W and in g; the all-zero row gives a zero row for eps > 0."""
+    x, g, w = _rms_inputs(6, 40, 7, 77)
+    alpha = np.array([0.5, 1.0, 2.0, 7.5, 1e-3, 123.0])
+    assert _rel_err(orc.rms_norm_matmul(alpha[:, None] * x, g, w, 0.0),
+                    orc.rms_norm_matmul(x, g, w, 0.0)) <= 1e-13
+    _, g2, w2 = _rms_inputs(6, 40, 7, 78)
+    for eps in (0.0, 0.3):
+        a = orc.rms_norm_matmul(x, g, w + w2, eps)
+        b = orc.rms_norm_matmul(x, g, w, eps) + orc.rms_norm_matmul(x, g, w2, eps)
+        assert _rel_err(a, b) <= 1e-13
+        a = orc.rms_norm_matmul(x, g + g2, w, eps)
+        b = orc.rms_norm_matmul(x, g, w, eps) + orc.rms_norm_matmul(x, g2, w, eps)
+        assert _rel_err(a, b) <= 1e-13
+    xz = x.copy()
+    xz[2] = 0.0
+    c = orc.rms_norm_matmul(xz, g, w, 1e-6)
+    assert np.all(c[2] == 0.0) and np.all(np.isfinite(c))
+
+
+def pin_rms_rows(orc):
+    """Chosen rows alone equal the same rows of the full product."""
+    x, g, w = _rms_inputs(11, 20, 9, 5)
+    full = orc.rms_norm_matmul(x, g, w, 1e-5)
+    rows = [10, 0, 3, 3]
+    assert np.array_equal(orc.rms_norm_matmul(x, g, w, 1e-5, rows=rows), full[rows])
+
+
 ALL_PINS = [
     pin_torch_grad_input,
     pin_torch_forward,
@@ -397,4 +484,9 @@ ALL_PINS = [
     pin_grad_weight_adjoint,
     pin_grad_weight_pointwise,
     pin_grad_weight_all_ones,
+    pin_torch_rms_norm_matmul,
+    pin_rms_constant_rows,
+    pin_rms_one_column,
+    pin_rms_scale_and_linearity,
+    pin_rms_rows,
 ]

@@ -56,6 +56,22 @@ MUTANTS = [
      "oh < OH; ++oh", "oh < OH - 1; ++oh"),
     ("grad_weight_bad_init", "oracle_grad_weight",
      "double acc = 0.0;", "double acc = 1e-3;"),
+    ("rms_sum_not_mean", "oracle_rms_norm_matmul",
+     "ss / (double)K + eps", "ss + eps"),
+    ("rms_eps_dropped", "oracle_rms_norm_matmul",
+     "ss / (double)K + eps", "ss / (double)K"),
+    ("rms_sqrt_not_rsqrt", "oracle_rms_norm_matmul",
+     "1.0 / sqrt(ss / (double)K + eps)", "sqrt(ss / (double)K + eps)"),
+    ("rms_scale_dropped", "oracle_rms_norm_matmul",
+     "xi[k] * r * g[k]", "xi[k] * r"),
+    ("rms_scale_on_columns", "oracle_rms_norm_matmul",
+     "ci[j] += a * wk[j];", "ci[j] += a / g[k] * g[j % K] * wk[j];"),
+    ("rms_w_transposed", "oracle_rms_norm_matmul",
+     "const double* wk = w + k * N;", "const double* wk = w + k;"),
+    ("rms_last_k_dropped", "oracle_rms_norm_matmul",
+     "for (i64 k = 0; k < K; ++k) {", "for (i64 k = 0; k < K - 1; ++k) {"),
+    ("rms_bad_init", "oracle_rms_norm_matmul",
+     "ci[j] = 0.0;", "ci[j] = 1e-3;"),
 ]
 
 
