@@ -1,7 +1,8 @@
 #!/usr/bin/env python3
 """Throughput of the conv2d input-gradient HIP path on one MI355X (or, with
 --op forward, of the forward convolution on the same kernels, or with
---op grad_weight, of the weight gradient).
+--op grad_weight, of the weight gradient; with --op rms_norm_matmul, of the
+RMSNorm-fused matrix product of the second page).
 
 One step = one conv2d_grad_input call over the whole workload (all batch
 items, all stride classes), inputs already resident in HBM.  Before the
@@ -13,7 +14,7 @@ the CPU oracle timed on the host cores on the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--f16 | --fp32] [--no-cpu] [--no-tune]
-                    [--op grad_input|forward|grad_weight]
+                    [--op grad_input|forward|grad_weight|rms_norm_matmul]
 """
 from __future__ import annotations
 
@@ -31,6 +32,7 @@ sys.path.insert(0, ROOT)
 METRIC = "conv2d grad-input useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
 METRIC_FORWARD = "conv2d forward useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
 METRIC_GRAD_WEIGHT = "conv2d grad-weight useful TFLOP/s per MI355X and % of MFMA peak (fp32)"
+METRIC_RMS = "RMSNorm-fused matmul useful TFLOP/s per MI355X and % of MFMA peak (fp32)"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}
 PEAK_HBM_GBS = 8000.0
@@ -40,6 +42,7 @@ KERNEL_SOURCES = {
     "grad_input": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
     "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
     "grad_weight": [_CSRC + f for f in ("grad_weight.hip", "tile_index.hpp", "plan.hpp")],
+    "rms_norm_matmul": [_CSRC + "rms_matmul.hip"],
 }
 
 
@@ -117,6 +120,97 @@ def copy_calibration(mib: int, steps: int) -> int:
     return 0
 
 
+def cpu_baseline_rms(shape, x, g, w, rows):
+    """The oracle on a bounded sample of the workload's rows (every column of
+    each), scaled to useful TFLOP/s of those rows."""
+    import numpy as np
+    import oracle
+
+    orc = oracle.default()
+    sel = np.arange(rows, dtype=np.int64) * (shape.m // rows)
+    t0 = time.perf_counter()
+    orc.rms_norm_matmul(x, g, w, shape.eps, rows=sel)
+    dt = time.perf_counter() - t0
+    return {"value": 2.0 * rows * shape.k * shape.n / dt / 1e12, "unit": "TFLOP/s",
+            "cores": orc.num_threads(), "kind": "oracle",
+            "sample": "%d of %d rows (every %d-th), all %d columns, one pass, %.2f s"
+                      % (rows, shape.m, shape.m // rows, shape.n, dt)}
+
+
+def bench_rms(args) -> int:
+    """One step = one rms_norm_matmul call over the whole workload."""
+    import torch
+    import conv2d_backward_implicit_amd as c2b
+    from conv2d_backward_implicit_amd.workloads import (RMS_CONFIGS, RMS_HEADLINE, draw_rms,
+                                                        rms_by_name)
+
+    if args.f16:
+        print("the RMSNorm-fused matmul has an fp32 path only", file=sys.stderr)
+        return 2
+    shape = rms_by_name(args.workload) if args.workload else RMS_CONFIGS[RMS_HEADLINE]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    x, g, w = draw_rms(shape, RMS_CONFIGS.index(shape))
+    tx, tg, tw = (torch.from_numpy(a).to(dev) for a in (x, g, w))
+    out = torch.empty((shape.m, shape.n), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        c2b.rms_norm_matmul_into(out, tx, tg, tw, shape.eps, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+    ev_avg_s = sum(ev_ms) / len(ev_ms) / 1e3
+    value = shape.useful_flops * args.steps / wall / 1e12
+    achieved = shape.useful_flops / ev_avg_s / 1e12
+    peak = PEAK_TFLOPS["f32"]
+    out_json = {
+        "metric": METRIC_RMS, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": shape.name, "m": shape.m, "k": shape.k, "n": shape.n,
+                   "eps": shape.eps, "op": args.op},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "kernel_avg_us": round(ev_avg_s * 1e6, 3),
+        "kernel_median_us": round(ev_ms[len(ev_ms) // 2] * 1e3, 3),
+        "compulsory_hbm_GBps": round(shape.compulsory_bytes / ev_avg_s / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic("rms_norm_matmul_f32", shape.name, args.op)},
+        "source_digest": source_digest(args.op),
+    }
+    # a library fp32 product of the same shape (torch's, after an unfused
+    # RMSNorm), for context: not the oracle, not the target
+    xn = torch.nn.functional.rms_norm(tx, (shape.k,), weight=tg, eps=shape.eps)
+    torch.matmul(xn, tw)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(5):
+        torch.matmul(torch.nn.functional.rms_norm(tx, (shape.k,), weight=tg, eps=shape.eps), tw)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    lib_s = e0.elapsed_time(e1) / 5 / 1e3
+    out_json["library_unfused_us"] = round(lib_s * 1e6, 3)
+    if not args.no_cpu:
+        out_json["cpu_baseline"] = cpu_baseline_rms(shape, x, g, w, min(shape.m, 512))
+    print(json.dumps(out_json), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -129,7 +223,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-tune", action="store_true",
                     help="use the planner's model choice instead of tuning the variant")
-    ap.add_argument("--op", choices=("grad_input", "forward", "grad_weight"),
+    ap.add_argument("--op", choices=("grad_input", "forward", "grad_weight", "rms_norm_matmul"),
                     default="grad_input",
                     help="the operation timed (default: the input gradient)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -147,6 +241,8 @@ def main() -> int:
     if args.steps < 1 or args.warmup < 0:
         print("--steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
+    if args.op == "rms_norm_matmul":
+        return bench_rms(args)
 
     import numpy as np
     import torch

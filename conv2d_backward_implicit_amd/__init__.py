@@ -33,6 +33,8 @@ __all__ = [
     "grad_weight", "grad_weight_into", "conv2d_grad_weight", "grad_weight_workspace_size",
     "check_indexing_grad_weight", "check_indexing_grad_weight_variant",
     "conv2d_grad_weight_variant", "describe_grad_weight_plan", "GRAD_WEIGHT_VARIANTS",
+    "RmsMatmulParams", "make_rms_params", "rms_norm_matmul", "rms_norm_matmul_into",
+    "conv2d_rms_norm_matmul_raw", "check_indexing_rms_norm_matmul",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -72,6 +74,9 @@ EXPORTED_SYMBOLS = (
     "conv2d_grad_weight_variant_workspace_size",
     "conv2d_describe_grad_weight_plan",
     "conv2d_check_indexing_grad_weight_variant",
+    # include/rms_norm_matmul.h
+    "rms_norm_matmul",
+    "rms_norm_matmul_check_indexing",
 )
 
 # weight-gradient column layouts: 0 flat tiles, 1..3 tap tiles of 1, 2, 4 taps
@@ -102,6 +107,12 @@ class Conv2dParams(ctypes.Structure):
     def __repr__(self):
         return "Conv2dParams(%s)" % ", ".join(
             "%s=%d" % (f, getattr(self, f)) for f, _ in self._fields_)
+
+
+class RmsMatmulParams(ctypes.Structure):
+    """Mirror of ``rms_matmul_params`` (m, n, k as uint32, eps as float)."""
+    _fields_ = [("m", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
+                ("eps", ctypes.c_float)]
 
 
 class PlanInfo(ctypes.Structure):
@@ -223,6 +234,11 @@ def load_library():
                                                                   ctypes.c_char_p,
                                                                   ctypes.c_size_t]
         lib.conv2d_check_indexing_grad_weight_variant.restype = ctypes.c_int
+        R = ctypes.POINTER(RmsMatmulParams)
+        lib.rms_norm_matmul.argtypes = [ctypes.c_void_p] * 4 + [R, ctypes.c_void_p]
+        lib.rms_norm_matmul.restype = ctypes.c_int
+        lib.rms_norm_matmul_check_indexing.argtypes = [R, ctypes.c_char_p, ctypes.c_size_t]
+        lib.rms_norm_matmul_check_indexing.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -659,3 +675,54 @@ def grad_weight(grad_out, x, kernel_h, kernel_w, stride=1, padding_h=0, padding_
     if out is None:
         out = torch.empty((co, ci, kernel_h, kernel_w), dtype=torch.float32, device=x.device)
     return grad_weight_into(out, grad_out, x, p, stream=stream)
+
+
+# ---- RMSNorm-fused matrix product ------------------------------------------------
+
+def make_rms_params(m, n, k, eps=1e-6) -> RmsMatmulParams:
+    return RmsMatmulParams(int(m), int(n), int(k), float(eps))
+
+
+def check_indexing_rms_norm_matmul(p: RmsMatmulParams) -> tuple:
+    """Host replay of the RMSNorm-fused product kernel (no device needed)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().rms_norm_matmul_check_indexing(ctypes.byref(p), buf, len(buf))
+    return int(rc), buf.value.decode()
+
+
+def conv2d_rms_norm_matmul_raw(x_ptr: int, g_ptr: int, w_ptr: int, out_ptr: int,
+                               p: RmsMatmulParams, stream: int = 0) -> int:
+    """Raw C-ABI call of rms_norm_matmul; returns the status."""
+    return int(load_library().rms_norm_matmul(
+        ctypes.c_void_p(x_ptr), ctypes.c_void_p(g_ptr), ctypes.c_void_p(w_ptr),
+        ctypes.c_void_p(out_ptr), ctypes.byref(p), ctypes.c_void_p(stream)))
+
+
+def rms_norm_matmul_into(out, x, g, w, eps=1e-6, stream=None):
+    """out [m, n] = RmsNorm(x [m, k], g [k], eps) @ w [k, n] on torch's current
+    stream (or ``stream``); float32 GPU tensors.  Raises Conv2dError on a bad
+    status."""
+    import torch
+    m, k = (int(v) for v in x.shape)
+    n = int(w.shape[1])
+    _check_tensor(x, "x", (m, k))
+    _check_tensor(g, "norm_weight", (k,))
+    _check_tensor(w, "proj", (k, n))
+    _check_tensor(out, "out", (m, n))
+    if not (x.device == g.device == w.device == out.device):
+        raise ValueError("all tensors must be on the same device")
+    p = make_rms_params(m, n, k, eps)
+    with torch.cuda.device(out.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = conv2d_rms_norm_matmul_raw(x.data_ptr(), g.data_ptr(), w.data_ptr(),
+                                        out.data_ptr(), p, int(s.cuda_stream))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return out
+
+
+def rms_norm_matmul(x, g, w, eps=1e-6, stream=None):
+    """RmsNorm(x, g, eps) @ w as a new float32 tensor [m, n]."""
+    import torch
+    out = torch.empty((int(x.shape[0]), int(w.shape[1])), dtype=torch.float32, device=x.device)
+    return rms_norm_matmul_into(out, x, g, w, eps, stream)

@@ -5,6 +5,7 @@ header declares, and turn every invalid argument into its status code before
 any HIP call is made.
 """
 import ctypes
+import glob
 import os
 import re
 
@@ -19,11 +20,16 @@ HEADER = os.path.join(ROOT, "include", "conv2d_bwd.h")
 OK, NULL, BAD, ALIAS, OVF, UNSUP = 0, -1, -2, -3, -4, -5
 
 
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
+
+
 def _header_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(conv2d_\w+)\s*\(",
-                                 text, flags=re.M)))
+    names = set()
+    for path in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(path).read(), flags=re.S)
+        names |= set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text,
+                                flags=re.M))
+    return sorted(names)
 
 
 def _p(**kw):
@@ -396,3 +402,30 @@ def test_grad_weight_variants_host():
     assert c2b.describe_grad_weight_plan(stem)["variant"] == 0
     assert c2b.describe_grad_weight_plan(_p(in_channels=32))["variant"] == 2
     assert c2b.describe_grad_weight_plan(_p(in_channels=16))["variant"] == 3
+
+
+# ---- RMSNorm-fused matrix product entry point ------------------------------------
+
+def test_rms_norm_matmul_rejects_before_any_device_call():
+    lib = c2b.load_library()
+    p = c2b.make_rms_params(4, 3, 5)
+    call = c2b.conv2d_rms_norm_matmul_raw
+    assert lib.rms_norm_matmul(None, None, None, None, None, None) == NULL
+    assert call(0, 0x2000, 0x3000, 0x4000, p) == NULL
+    assert call(0x1000, 0, 0x3000, 0x4000, p) == NULL
+    assert call(0x1000, 0x2000, 0, 0x4000, p) == NULL
+    assert call(0x1000, 0x2000, 0x3000, 0, p) == NULL
+    assert call(0x1000, 0x2000, 0x3000, 0x4000, c2b.make_rms_params(4, 3, 0)) == BAD
+    assert call(0x1000, 0x2000, 0x3000, 0x4000, c2b.make_rms_params(4, 3, 5, -1e-3)) == BAD
+    # out overlapping x, the norm weight or the projection
+    assert call(0x1000, 0x2000, 0x3000, 0x1000 + 8, p) == ALIAS
+    assert call(0x1000, 0x2000, 0x3000, 0x2000 - 8, p) == ALIAS
+    assert call(0x1000, 0x2000, 0x3000, 0x3000 + 40, p) == ALIAS
+    assert call(0x1000, 0x2000, 0x3000, 0x4000, c2b.make_rms_params(1 << 16, 8, 1 << 13)) == OVF
+    # empty outputs launch nothing and succeed
+    assert call(0x1000, 0x2000, 0x3000, 0x4000, c2b.make_rms_params(0, 3, 5)) == OK
+    assert call(0x1000, 0x2000, 0x3000, 0x4000, c2b.make_rms_params(4, 0, 5)) == OK
+
+
+def test_rms_params_struct_layout():
+    assert ctypes.sizeof(c2b.RmsMatmulParams) == 16

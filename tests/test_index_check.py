@@ -153,3 +153,23 @@ def test_grad_weight_random_stress():
         v = i % c2b.GRAD_WEIGHT_VARIANTS
         rc, msg = c2b.check_indexing_grad_weight_variant(params_of(sh), v)
         assert rc == 0, (sh, v, rc, msg)
+
+
+# ---- RMSNorm-fused matrix product (rms_norm_matmul) ----------------------------
+
+RMS_REPLAY = [(1, 1, 1), (7, 19, 45), (128, 128, 32), (129, 127, 33), (300, 257, 100),
+              (5, 300, 64), (256, 130, 31), (40, 50, 2500), (3000, 1500, 1000)]
+
+
+@pytest.mark.parametrize("mnk", RMS_REPLAY, ids=lambda t: "m%d_n%d_k%d" % t)
+def test_rms_norm_matmul_replay(mnk):
+    rc, msg = c2b.check_indexing_rms_norm_matmul(c2b.make_rms_params(*mnk))
+    assert rc == 0, (mnk, rc, msg)
+
+
+def test_rms_norm_matmul_replay_rejects_bad_params():
+    for m, n, k, eps in [(4, 4, 0, 1e-6), (4, 4, 4, -1.0), (4, 4, 4, float("inf")),
+                         (4, 4, 4, float("nan"))]:
+        assert c2b.check_indexing_rms_norm_matmul(c2b.make_rms_params(m, n, k, eps))[0] == -2
+    # a tensor of 2^31 bytes
+    assert c2b.check_indexing_rms_norm_matmul(c2b.make_rms_params(1 << 16, 8, 1 << 13))[0] == -4
