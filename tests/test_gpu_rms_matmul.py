@@ -102,6 +102,19 @@ EDGE = [
 ]
 
 
+# k and n multiples of 4 take the direct-to-LDS kernel: partial tiles, a
+# single k quad, stage tails, one row, zero-padding k quads
+EDGE_DMA = [
+    RmsShape("dma_min", 1, 4, 4),
+    RmsShape("dma_partial_tiles", 129, 36, 132),
+    RmsShape("dma_one_stage", 300, 32, 260),
+    RmsShape("dma_k_tail", 77, 100, 388),
+    RmsShape("dma_tiles_exact", 256, 128, 256, eps=0.1),
+    RmsShape("dma_long_k", 40, 2504, 52),
+]
+EDGE = EDGE + EDGE_DMA
+
+
 @pytest.mark.parametrize("sh", EDGE, ids=[s.name for s in EDGE])
 def test_rms_edge_shapes(sh):
     _say("case rms", sh.name)
@@ -119,6 +132,10 @@ def test_rms_zero_and_constant_rows():
     assert np.all(got[5] == 0.0) and np.all(got[130] == 0.0)
     ref = oracle.rms_norm_matmul(x, g, w, sh.eps)
     assert rel_err(got, ref) <= TOL
+    # the same on the direct-to-LDS kernel (k and n multiples of 4)
+    got4 = run_rms(x[:, :68], g[:68], w[:68, :88], sh.eps)
+    assert np.all(got4[5] == 0.0) and np.all(got4[130] == 0.0)
+    assert rel_err(got4, oracle.rms_norm_matmul(x[:, :68], g[:68], w[:68, :88], sh.eps)) <= TOL
     # eps = 0 (no zero rows here: 0 * rsqrt(0) has no value)
     x, _, _ = draw_rms(sh, 4)
     scale = np.linspace(0.01, 50.0, sh.m, dtype=np.float32)[:, None]

@@ -157,8 +157,10 @@ def test_grad_weight_random_stress():
 
 # ---- RMSNorm-fused matrix product (rms_norm_matmul) ----------------------------
 
+# (m, n, k); k and n multiples of 4 also replay the direct-to-LDS kernel
 RMS_REPLAY = [(1, 1, 1), (7, 19, 45), (128, 128, 32), (129, 127, 33), (300, 257, 100),
-              (5, 300, 64), (256, 130, 31), (40, 50, 2500), (3000, 1500, 1000)]
+              (5, 300, 64), (256, 130, 31), (40, 50, 2500), (3000, 1500, 1000),
+              (1, 4, 4), (129, 132, 36), (300, 260, 32), (77, 388, 100), (40, 52, 2504)]
 
 
 @pytest.mark.parametrize("mnk", RMS_REPLAY, ids=lambda t: "m%d_n%d_k%d" % t)
