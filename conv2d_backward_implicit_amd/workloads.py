@@ -206,3 +206,69 @@ def draw_rms(shape: RmsShape, seed: int):
     g = 1.0 + 0.1 * rng.standard_normal(shape.k)
     w = rng.standard_normal((shape.k, shape.n)) / np.sqrt(shape.k)
     return x.astype(np.float32), g.astype(np.float32), w.astype(np.float32)
+
+
+# ---- attention dV (dV of softmax(QK^T / sqrt(D)) V, grouped kv heads) ---------
+
+@dataclass(frozen=True)
+class MhaShape:
+    """q, dO [q_seq, heads, D]; k, dV [kv_seq, kv_heads, D]; lse [q_seq, heads, 2].
+    Query pos sees key t when t <= pos (causal) and pos < t + window (window
+    > 0)."""
+    name: str
+    q_seq: int
+    kv_seq: int
+    heads: int
+    kv_heads: int
+    head_dim: int = 64
+    window: int = 0
+    causal: bool = True
+
+    def pairs(self) -> int:
+        """(query, key) pairs the mask lets through, per head."""
+        n = 0
+        for t in range(self.kv_seq):
+            start = t if self.causal else 0
+            end = min(self.q_seq, t + self.window) if self.window > 0 else self.q_seq
+            n += max(0, end - start)
+        return n
+
+    @property
+    def useful_flops(self) -> int:
+        # per visible (query, head, key): the score (2 D) and its dV term (2 D)
+        return 4 * self.head_dim * self.heads * self.pairs()
+
+    @property
+    def compulsory_bytes(self) -> int:
+        return 4 * (2 * self.q_seq * self.heads * self.head_dim + self.q_seq * self.heads * 2
+                    + 2 * self.kv_seq * self.kv_heads * self.head_dim)
+
+
+# The source page gives no sizes; these stand in: a ragged case the oracle
+# finishes at once, and LLM-style single sequences (32 query heads sharing 8
+# kv heads, head dimension 64).
+MHA_CONFIGS = [
+    MhaShape("mha_tiny_s37_h4_kv2_causal", 37, 37, 4, 2),
+    MhaShape("mha_s4096_h32_kv8_causal", 4096, 4096, 32, 8),
+    MhaShape("mha_s4096_h32_kv8_causal_window512", 4096, 4096, 32, 8, window=512),
+    MhaShape("mha_s2048_h16_kv16_full", 2048, 2048, 16, 16, causal=False),
+]
+
+MHA_HEADLINE = 1
+
+
+def mha_by_name(name: str) -> MhaShape:
+    for c in MHA_CONFIGS:
+        if c.name == name:
+            return c
+    raise KeyError(name)
+
+
+def draw_mha(shape: MhaShape, seed: int):
+    """(q, k, dout) as float32 N(0, 1), drawn in that order from
+    ``default_rng(seed)``."""
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((shape.q_seq, shape.heads, shape.head_dim))
+    k = rng.standard_normal((shape.kv_seq, shape.kv_heads, shape.head_dim))
+    g = rng.standard_normal((shape.q_seq, shape.heads, shape.head_dim))
+    return q.astype(np.float32), k.astype(np.float32), g.astype(np.float32)

@@ -22,6 +22,10 @@ Functions (all take float64-convertible arrays and return float64 arrays):
 * ``conv2d_forward``       -- forward cross-correlation, for the adjoint check.
 * ``grad_weight``          -- the weight gradient of the same forward
   cross-correlation (not on the pages; its index map is the forward one).
+* ``attention_lse``        -- the forward statistics (row max, log sum) of
+  attention under the third page's causal and window bounds.
+* ``mha_grad_v``           -- dV of multi-head attention with grouped kv
+  heads, ``src/shaders/mha_grad_v.wgsl`` (the third page).
 * ``rms_norm_matmul``      -- C = RmsNorm(X, g) x W of the second page,
   ``src/shaders/matmul_rms_norm.wgsl`` (header comment, per-row rsqrt
   prologue, normalise-on-load), in that order, optionally for chosen rows.
@@ -102,6 +106,10 @@ class Oracle:
         lib.oracle_rms_norm_matmul.argtypes = [_DP, _DP, _DP, _DP, _I64, _I64, _I64,
                                                ctypes.c_double, _IP, _I64]
         lib.oracle_rms_norm_matmul.restype = None
+        lib.oracle_attention_lse.argtypes = [_DP, _DP, _DP] + [_I64] * 7
+        lib.oracle_attention_lse.restype = None
+        lib.oracle_mha_grad_v.argtypes = [_DP] * 5 + [_I64] * 7
+        lib.oracle_mha_grad_v.restype = None
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         self._lib = lib
@@ -185,6 +193,32 @@ class Oracle:
                                          float(eps), sel.ctypes.data_as(_IP), int(sel.size))
         return c if rows is None else c[sel]
 
+    def attention_lse(self, q, k, num_kv_heads, window=0, causal=True):
+        """(max, log sum exp) per query row and head [q_seq, H, 2] (float64);
+        q [q_seq, H, D], k [kv_seq, HKV, D]."""
+        qq, kk = _f64(q), _f64(k)
+        q_seq, H, D = (int(v) for v in qq.shape)
+        kv_seq, HKV, D2 = (int(v) for v in kk.shape)
+        if D2 != D or HKV != int(num_kv_heads) or H % HKV:
+            raise ValueError("shapes q %s, k %s do not match" % (qq.shape, kk.shape))
+        lse = np.empty((q_seq, H, 2), dtype=np.float64)
+        self._lib.oracle_attention_lse(_ptr(qq), _ptr(kk), _ptr(lse), q_seq, kv_seq, H, HKV, D,
+                                       int(window), int(bool(causal)))
+        return lse
+
+    def mha_grad_v(self, dout, q, k, lse, window=0, causal=True):
+        """dV [kv_seq, HKV, D] (float64); dout, q [q_seq, H, D], k
+        [kv_seq, HKV, D], lse [q_seq, H, 2]."""
+        g, qq, kk, ll = _f64(dout), _f64(q), _f64(k), _f64(lse)
+        q_seq, H, D = (int(v) for v in qq.shape)
+        kv_seq, HKV, D2 = (int(v) for v in kk.shape)
+        if g.shape != qq.shape or D2 != D or H % HKV or ll.shape != (q_seq, H, 2):
+            raise ValueError("shapes do not match")
+        dv = np.empty((kv_seq, HKV, D), dtype=np.float64)
+        self._lib.oracle_mha_grad_v(_ptr(g), _ptr(qq), _ptr(kk), _ptr(ll), _ptr(dv), q_seq,
+                                    kv_seq, H, HKV, D, int(window), int(bool(causal)))
+        return dv
+
     def num_threads(self) -> int:
         """OpenMP threads the oracle routines use in this process."""
         return int(self._lib.oracle_num_threads())
@@ -221,6 +255,14 @@ def conv2d_forward(*a, **k):
 
 def grad_weight(*a, **k):
     return default().grad_weight(*a, **k)
+
+
+def attention_lse(*a, **k):
+    return default().attention_lse(*a, **k)
+
+
+def mha_grad_v(*a, **k):
+    return default().mha_grad_v(*a, **k)
 
 
 def rms_norm_matmul(*a, **k):

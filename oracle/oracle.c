@@ -15,7 +15,10 @@
  * staging and its final store to grad_input.  [p2] is the docs.rs source page
  * of the same crate, "src/shaders/matmul_rms_norm.wgsl" (header comment,
  * per-row rsqrt prologue, normalise-on-load A staging); only
- * oracle_rms_norm_matmul follows it.
+ * oracle_rms_norm_matmul follows it.  [p1] is the page
+ * "src/shaders/mha_grad_v.wgsl" of the same crate (its Params, the causal
+ * and window bounds of the position loop, the score recomputation and the
+ * P * dO sum); oracle_attention_lse and oracle_mha_grad_v follow it.
  *
  * Every routine here is a plain loop nest over the definition, accumulated in
  * double precision, with no blocking, no reordering beyond the definition and
@@ -266,6 +269,79 @@ void oracle_rms_norm_matmul(const double* x, const double* g, const double* w, d
       for (i64 j = 0; j < N; ++j) ci[j] += a * wk[j];
     }
   }
+}
+
+/* Attention rows for the dV routine below ([p1] = meganeura 0.2.0,
+ * src/shaders/mha_grad_v.wgsl, its kv_seq == 0 causal convention and its
+ * window bound): query pos sees key t when t <= pos (causal) and
+ * pos < t + window (window > 0).  Fills lse[(pos * H + h) * 2 + {0, 1}] =
+ * (max_t s, log sum_t exp(s - max)) over the keys pos sees, s = q . k /
+ * sqrt(D), the forward-pass statistics the dV routine takes.  A row that
+ * sees no key gets (0, 0). */
+void oracle_attention_lse(const double* q, const double* k, double* lse, i64 q_seq,
+                          i64 kv_seq, i64 H, i64 HKV, i64 D, i64 window, i64 causal) {
+  const double scale = 1.0 / sqrt((double)D);
+  const i64 group = H / HKV;
+#pragma omp parallel for collapse(2) schedule(static)
+  for (i64 pos = 0; pos < q_seq; ++pos)
+    for (i64 h = 0; h < H; ++h) {
+      const double* qp = q + (pos * H + h) * D;
+      const i64 kvh = h / group;
+      double mx = -INFINITY;
+      for (i64 t = 0; t < kv_seq; ++t) {
+        if ((causal && t > pos) || (window > 0 && pos >= t + window)) continue;
+        double s = 0.0;
+        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];
+        s *= scale;
+        if (s > mx) mx = s;
+      }
+      double sum = 0.0;
+      for (i64 t = 0; t < kv_seq; ++t) {
+        if ((causal && t > pos) || (window > 0 && pos >= t + window)) continue;
+        double s = 0.0;
+        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];
+        sum += exp(s * scale - mx);
+      }
+      lse[(pos * H + h) * 2] = sum > 0.0 ? mx : 0.0;
+      lse[(pos * H + h) * 2 + 1] = sum > 0.0 ? log(sum) : 0.0;
+    }
+}
+
+/* Gradient of multi-head attention with respect to V ([p1]): for key t of
+ * kv head kvh,
+ *   dv[t, kvh, :] = sum over pos in [causal ? t : 0, window > 0 ?
+ *                   min(q_seq, t + window) : q_seq) and heads h of the group
+ *                   of kvh (h = kvh * H / HKV + r) of P * dout[pos, h, :],
+ *   P = exp(min(s - lse[pos, h, 0], 0) - lse[pos, h, 1]),  s = q . k / sqrt(D).
+ * q, dout [q_seq, H, D]; k, dv [kv_seq, HKV, D]; lse [q_seq, H, 2]. */
+void oracle_mha_grad_v(const double* dout, const double* q, const double* k, const double* lse,
+                       double* dv, i64 q_seq, i64 kv_seq, i64 H, i64 HKV, i64 D, i64 window,
+                       i64 causal) {
+  const double scale = 1.0 / sqrt((double)D);
+  const i64 group = H / HKV;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
+  for (i64 t = 0; t < kv_seq; ++t)
+    for (i64 kvh = 0; kvh < HKV; ++kvh) {
+      const double* kt = k + (t * HKV + kvh) * D;
+      double* out = dv + (t * HKV + kvh) * D;
+      for (i64 d = 0; d < D; ++d) out[d] = 0.0;
+      const i64 start = causal ? t : 0;
+      const i64 end = window > 0 ? (q_seq < t + window ? q_seq : t + window) : q_seq;
+      for (i64 pos = start; pos < end; ++pos)
+        for (i64 r = 0; r < group; ++r) {
+          const i64 h = kvh * group + r;
+          const double* qp = q + (pos * H + h) * D;
+          double s = 0.0;
+          for (i64 d = 0; d < D; ++d) s += qp[d] * kt[d];
+          s *= scale;
+          const double* l = lse + (pos * H + h) * 2;
+          double e = s - l[0];
+          if (e > 0.0) e = 0.0;
+          const double pr = exp(e - l[1]);
+          const double* g = dout + (pos * H + h) * D;
+          for (i64 d = 0; d < D; ++d) out[d] += pr * g[d];
+        }
+    }
 }
 
 /* Number of OpenMP threads the routines above will use. */

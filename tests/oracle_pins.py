@@ -466,6 +466,115 @@ def pin_rms_rows(orc):
     assert np.array_equal(orc.rms_norm_matmul(x, g, w, 1e-5, rows=rows), full[rows])
 
 
+# ---- attention dV (third page, mha_grad_v.wgsl) ----------------------------------
+
+# (q_seq, kv_seq, H, HKV, D, window, causal)
+_MHA_CASES = [(9, 9, 4, 2, 8, 0, True), (11, 11, 6, 3, 4, 3, True), (7, 12, 2, 2, 8, 0, False),
+              (10, 6, 4, 1, 8, 2, False), (16, 16, 8, 8, 4, 5, True), (5, 5, 3, 1, 6, 1, True)]
+
+
+def _visible(q_seq, kv_seq, window, causal):
+    """[q_seq, kv_seq] mask: query pos sees key t (the page's position loop
+    read from the key side: pos in [causal ? t : 0, t + window))."""
+    pos = np.arange(q_seq)[:, None]
+    t = np.arange(kv_seq)[None, :]
+    m = np.ones((q_seq, kv_seq), dtype=bool)
+    if causal:
+        m &= t <= pos
+    if window > 0:
+        m &= pos < t + window
+    return m
+
+
+def pin_torch_mha_grad_v(orc):
+    """torch autograd of masked softmax attention in float64 (O = softmax(QK^T
+    / sqrt(D)) V per head, kv head h // (H / HKV)): dV of <O, dO>; and the
+    row statistics against torch.logsumexp."""
+    import torch
+    for i, (qs, ks, H, HKV, D, win, causal) in enumerate(_MHA_CASES):
+        rng = np.random.default_rng(500 + i)
+        q, k, v, g = (rng.standard_normal(s_) for s_ in
+                      ((qs, H, D), (ks, HKV, D), (ks, HKV, D), (qs, H, D)))
+        mask = torch.from_numpy(_visible(qs, ks, win, causal))
+        tq, tk, tg = (torch.from_numpy(a) for a in (q, k, g))
+        tv = torch.from_numpy(v).requires_grad_(True)
+        grp = H // HKV
+        out = torch.zeros(qs, H, D, dtype=torch.float64)
+        lse_ref = torch.zeros(qs, H, dtype=torch.float64)
+        seen_t = mask.any(dim=1)   # rows with no visible key attend to nothing
+        for h in range(H):
+            sc = (tq[:, h, :] @ tk[:, h // grp, :].T) / np.sqrt(D)
+            sc = sc.masked_fill(~mask, float("-inf"))
+            lse_ref[:, h] = torch.logsumexp(sc, dim=1)
+            sc = torch.where(seen_t[:, None], sc, torch.zeros_like(sc))
+            pr = torch.softmax(sc, dim=1) * seen_t[:, None]
+            out[:, h, :] = pr @ tv[:, h // grp, :]
+        (out * tg).sum().backward()
+        lse = orc.attention_lse(q, k, HKV, win, causal)
+        seen = _visible(qs, ks, win, causal).any(axis=1)   # rows that see a key
+        assert np.max(np.abs((lse[..., 0] + lse[..., 1] - lse_ref.numpy())[seen])) <= 1e-12, i
+        assert np.all(lse[~seen] == 0.0), i
+        dv = orc.mha_grad_v(g, q, k, lse, win, causal)
+        err = _rel_err(dv, tv.grad.numpy())
+        assert err <= 1e-12, (i, err)
+
+
+def pin_mha_uniform_scores(orc):
+    """K = 0: every score is 0, so P = 1 / (number of keys query pos sees)
+    and dV[t] = sum over the queries that see t and the group's heads of
+    dO / count, with the counts taken from the mask."""
+    for i, (qs, ks, H, HKV, D, win, causal) in enumerate(_MHA_CASES):
+        rng = np.random.default_rng(600 + i)
+        q, g = rng.standard_normal((qs, H, D)), rng.standard_normal((qs, H, D))
+        k = np.zeros((ks, HKV, D))
+        vis = _visible(qs, ks, win, causal)
+        cnt = vis.sum(axis=1)
+        want = np.zeros((ks, HKV, D))
+        grp = H // HKV
+        for t in range(ks):
+            for pos in range(qs):
+                if vis[pos, t]:
+                    for h in range(H):
+                        want[t, h // grp] += g[pos, h] / cnt[pos]
+        lse = orc.attention_lse(q, k, HKV, win, causal)
+        assert _rel_err(orc.mha_grad_v(g, q, k, lse, win, causal), want) <= 1e-13, i
+
+
+def pin_mha_single_dout(orc):
+    """dO nonzero at one (query, head) only: dV is nonzero only for that
+    head's kv head and the keys the query sees."""
+    qs, ks, H, HKV, D, win, causal = 12, 12, 6, 2, 4, 4, True
+    rng = np.random.default_rng(7)
+    q, k = rng.standard_normal((qs, H, D)), rng.standard_normal((ks, HKV, D))
+    g = np.zeros((qs, H, D))
+    pos0, h0 = 7, 4
+    g[pos0, h0] = rng.standard_normal(D)
+    dv = orc.mha_grad_v(g, q, k, orc.attention_lse(q, k, HKV, win, causal), win, causal)
+    vis = _visible(qs, ks, win, causal)[pos0]
+    kvh0 = h0 // (H // HKV)
+    for t in range(ks):
+        for kvh in range(HKV):
+            nz = np.any(dv[t, kvh] != 0.0)
+            assert nz == (kvh == kvh0 and vis[t]), (t, kvh)
+
+
+def pin_mha_exponent_clamp(orc):
+    """The exponent is clamped at 0: with a row max far below the scores,
+    P = exp(-log_sum) for every visible key."""
+    qs, ks, H, HKV, D = 6, 6, 2, 1, 4
+    rng = np.random.default_rng(8)
+    q, k, g = (rng.standard_normal(s_) for s_ in ((qs, H, D), (ks, HKV, D), (qs, H, D)))
+    lse = np.zeros((qs, H, 2))
+    lse[..., 0] = -1e6
+    lse[..., 1] = 0.5
+    dv = orc.mha_grad_v(g, q, k, lse, 0, True)
+    want = np.zeros((ks, HKV, D))
+    for t in range(ks):
+        for pos in range(t, qs):
+            want[t, 0] += np.exp(-0.5) * g[pos].sum(axis=0)
+    assert _rel_err(dv, want) <= 1e-13
+
+
 ALL_PINS = [
     pin_torch_grad_input,
     pin_torch_forward,
@@ -489,4 +598,8 @@ ALL_PINS = [
     pin_rms_one_column,
     pin_rms_scale_and_linearity,
     pin_rms_rows,
+    pin_torch_mha_grad_v,
+    pin_mha_uniform_scores,
+    pin_mha_single_dout,
+    pin_mha_exponent_clamp,
 ]

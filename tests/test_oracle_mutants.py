@@ -72,6 +72,23 @@ MUTANTS = [
      "for (i64 k = 0; k < K; ++k) {", "for (i64 k = 0; k < K - 1; ++k) {"),
     ("rms_bad_init", "oracle_rms_norm_matmul",
      "ci[j] = 0.0;", "ci[j] = 1e-3;"),
+    ("mha_causal_off_by_one", "oracle_mha_grad_v",
+     "const i64 start = causal ? t : 0;", "const i64 start = causal ? t + 1 : 0;"),
+    ("mha_window_off_by_one", "oracle_mha_grad_v",
+     "(q_seq < t + window ? q_seq : t + window)", "(q_seq < t + window - 1 ? q_seq : t + window - 1)"),
+    ("mha_heads_interleaved", "oracle_mha_grad_v",
+     "const i64 h = kvh * group + r;", "const i64 h = kvh + r * HKV;"),
+    ("mha_scale_dropped", "oracle_mha_grad_v",
+     "    s *= scale;\n          const double* l", "    const double* l"),
+    ("mha_clamp_dropped", "oracle_mha_grad_v",
+     "if (e > 0.0) e = 0.0;", ""),
+    ("mha_log_sum_ignored", "oracle_mha_grad_v",
+     "exp(e - l[1])", "exp(e)"),
+    ("lse_log_dropped", "oracle_attention_lse",
+     "log(sum)", "sum"),
+    ("lse_window_off_by_one", "oracle_attention_lse",
+     "pos >= t + window)) continue;\n        double s = 0.0;\n        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];\n        s *= scale;",
+     "pos > t + window)) continue;\n        double s = 0.0;\n        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];\n        s *= scale;"),
 ]
 
 
