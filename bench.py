@@ -2,7 +2,8 @@
 """Throughput of the conv2d input-gradient HIP path on one MI355X (or, with
 --op forward, of the forward convolution on the same kernels, or with
 --op grad_weight, of the weight gradient; with --op rms_norm_matmul, of the
-RMSNorm-fused matrix product of the second page).
+RMSNorm-fused matrix product of the second page; with --op mha_grad_v, of
+the attention dV of the third page).
 
 One step = one conv2d_grad_input call over the whole workload (all batch
 items, all stride classes), inputs already resident in HBM.  Before the
@@ -14,7 +15,7 @@ the CPU oracle timed on the host cores on the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
                     [--f16 | --fp32] [--no-cpu] [--no-tune]
-                    [--op grad_input|forward|grad_weight|rms_norm_matmul]
+                    [--op grad_input|forward|grad_weight|rms_norm_matmul|mha_grad_v]
 """
 from __future__ import annotations
 
@@ -33,6 +34,7 @@ METRIC = "conv2d grad-input useful TFLOP/s per MI355X and % of MFMA peak (fp32, 
 METRIC_FORWARD = "conv2d forward useful TFLOP/s per MI355X and % of MFMA peak (fp32, f16)"
 METRIC_GRAD_WEIGHT = "conv2d grad-weight useful TFLOP/s per MI355X and % of MFMA peak (fp32)"
 METRIC_RMS = "RMSNorm-fused matmul useful TFLOP/s per MI355X and % of MFMA peak (fp32)"
+METRIC_MHA = "attention dV useful TFLOP/s per MI355X and % of MFMA peak (fp32)"
 # MI355X published dense peaks (TFLOP/s) and HBM bandwidth (GB/s)
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6}
 PEAK_HBM_GBS = 8000.0
@@ -43,6 +45,7 @@ KERNEL_SOURCES = {
     "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
     "grad_weight": [_CSRC + f for f in ("grad_weight.hip", "tile_index.hpp", "plan.hpp")],
     "rms_norm_matmul": [_CSRC + "rms_matmul.hip"],
+    "mha_grad_v": [_CSRC + "mha_grad_v.hip"],
 }
 
 
@@ -211,6 +214,109 @@ def bench_rms(args) -> int:
     return 0
 
 
+def mha_lse_torch(q, k, kv_heads, window, causal):
+    """The forward's row statistics (max, log sum exp) of the scaled scores
+    under the mask, by plain torch on the device: benchmark input, not a
+    reference."""
+    import torch
+    q_seq, heads, d = q.shape
+    kv_seq = k.shape[0]
+    grp = heads // kv_heads
+    pos = torch.arange(q_seq, device=q.device)[:, None]
+    t = torch.arange(kv_seq, device=q.device)[None, :]
+    vis = torch.ones(q_seq, kv_seq, dtype=torch.bool, device=q.device)
+    if causal:
+        vis &= t <= pos
+    if window > 0:
+        vis &= pos < t + window
+    lse = torch.zeros(q_seq, heads, 2, device=q.device)
+    for h in range(heads):
+        sc = (q[:, h, :] @ k[:, h // grp, :].T.contiguous()) / float(d) ** 0.5
+        sc = sc.masked_fill(~vis, float("-inf"))
+        mx = sc.max(dim=1).values
+        mx = torch.where(torch.isfinite(mx), mx, torch.zeros_like(mx))
+        lse[:, h, 0] = mx
+        lse[:, h, 1] = torch.log(torch.exp(sc - mx[:, None]).sum(dim=1).clamp_min(1e-30))
+    return lse
+
+
+def bench_mha(args) -> int:
+    """One step = one mha_grad_v call over the whole sequence and all heads."""
+    import numpy as np
+    import torch
+    import conv2d_backward_implicit_amd as c2b
+    from conv2d_backward_implicit_amd.workloads import (MHA_CONFIGS, MHA_HEADLINE, MhaShape,
+                                                        draw_mha, mha_by_name)
+
+    if args.f16:
+        print("the attention dV kernel has an fp32 path only", file=sys.stderr)
+        return 2
+    shape = mha_by_name(args.workload) if args.workload else MHA_CONFIGS[MHA_HEADLINE]
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda", 0)
+    q, k, g = draw_mha(shape, MHA_CONFIGS.index(shape))
+    tq, tk, tg = (torch.from_numpy(a).to(dev) for a in (q, k, g))
+    tl = mha_lse_torch(tq, tk, shape.kv_heads, shape.window, shape.causal)
+    dv = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        c2b.mha_grad_v_into(dv, tg, tq, tk, tl, shape.window, shape.causal, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = sorted(s_.elapsed_time(e_) for s_, e_ in zip(starts, ends))
+    ev_avg_s = sum(ev_ms) / len(ev_ms) / 1e3
+    value = shape.useful_flops * args.steps / wall / 1e12
+    achieved = shape.useful_flops / ev_avg_s / 1e12
+    peak = PEAK_TFLOPS["f32"]
+    out = {
+        "metric": METRIC_MHA, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": shape.name, "q_seq": shape.q_seq, "kv_seq": shape.kv_seq,
+                   "heads": shape.heads, "kv_heads": shape.kv_heads,
+                   "head_dim": shape.head_dim, "window": shape.window,
+                   "causal": shape.causal, "op": args.op},
+        "pct_of_mfma_peak": round(100.0 * value / peak, 2),
+        "kernel_avg_us": round(ev_avg_s * 1e6, 3),
+        "kernel_median_us": round(ev_ms[len(ev_ms) // 2] * 1e3, 3),
+        "compulsory_hbm_GBps": round(shape.compulsory_bytes / ev_avg_s / 1e9, 1),
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                     "traffic": measured_traffic("mha_grad_v_f32", shape.name, args.op)},
+        "source_digest": source_digest(args.op),
+    }
+    if not args.no_cpu:
+        import oracle
+        orc = oracle.default()
+        sub = MhaShape("prefix", min(shape.q_seq, 512), min(shape.kv_seq, 512), shape.heads,
+                       shape.kv_heads, shape.head_dim, shape.window, shape.causal)
+        qs, ks, gs = q[:sub.q_seq], k[:sub.kv_seq], g[:sub.q_seq]
+        lse = orc.attention_lse(qs, ks, sub.kv_heads, sub.window, sub.causal)
+        t1 = time.perf_counter()
+        orc.mha_grad_v(gs, qs, ks, lse, sub.window, sub.causal)
+        dt = time.perf_counter() - t1
+        out["cpu_baseline"] = {"value": sub.useful_flops / dt / 1e12, "unit": "TFLOP/s",
+                               "cores": orc.num_threads(), "kind": "oracle",
+                               "sample": "the first %d positions and keys of the sequence, "
+                                         "all heads, one pass, %.2f s" % (sub.q_seq, dt)}
+    print(json.dumps(out), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,7 +329,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-tune", action="store_true",
                     help="use the planner's model choice instead of tuning the variant")
-    ap.add_argument("--op", choices=("grad_input", "forward", "grad_weight", "rms_norm_matmul"),
+    ap.add_argument("--op", choices=("grad_input", "forward", "grad_weight", "rms_norm_matmul",
+                                     "mha_grad_v"),
                     default="grad_input",
                     help="the operation timed (default: the input gradient)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -243,6 +350,8 @@ def main() -> int:
         return 2
     if args.op == "rms_norm_matmul":
         return bench_rms(args)
+    if args.op == "mha_grad_v":
+        return bench_mha(args)
 
     import numpy as np
     import torch

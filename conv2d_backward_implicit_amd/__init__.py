@@ -35,6 +35,8 @@ __all__ = [
     "conv2d_grad_weight_variant", "describe_grad_weight_plan", "GRAD_WEIGHT_VARIANTS",
     "RmsMatmulParams", "make_rms_params", "rms_norm_matmul", "rms_norm_matmul_into",
     "conv2d_rms_norm_matmul_raw", "check_indexing_rms_norm_matmul",
+    "MhaGradVParams", "make_mha_params", "mha_grad_v", "mha_grad_v_into", "mha_grad_v_raw",
+    "check_indexing_mha_grad_v",
     "status_string", "library_path", "load_library",
     "make_params", "EXPORTED_SYMBOLS",
 ]
@@ -77,6 +79,9 @@ EXPORTED_SYMBOLS = (
     # include/rms_norm_matmul.h
     "rms_norm_matmul",
     "rms_norm_matmul_check_indexing",
+    # include/mha_grad_v.h
+    "mha_grad_v",
+    "mha_grad_v_check_indexing",
 )
 
 # weight-gradient column layouts: 0 flat tiles, 1..3 tap tiles of 1, 2, 4 taps
@@ -113,6 +118,12 @@ class RmsMatmulParams(ctypes.Structure):
     """Mirror of ``rms_matmul_params`` (m, n, k as uint32, eps as float)."""
     _fields_ = [("m", ctypes.c_uint32), ("n", ctypes.c_uint32), ("k", ctypes.c_uint32),
                 ("eps", ctypes.c_float)]
+
+
+class MhaGradVParams(ctypes.Structure):
+    """Mirror of ``mha_grad_v_params`` (7 x uint32)."""
+    _fields_ = [(n, ctypes.c_uint32) for n in ("q_seq", "kv_seq", "heads", "kv_heads",
+                                                "head_dim", "window", "causal")]
 
 
 class PlanInfo(ctypes.Structure):
@@ -239,6 +250,11 @@ def load_library():
         lib.rms_norm_matmul.restype = ctypes.c_int
         lib.rms_norm_matmul_check_indexing.argtypes = [R, ctypes.c_char_p, ctypes.c_size_t]
         lib.rms_norm_matmul_check_indexing.restype = ctypes.c_int
+        M = ctypes.POINTER(MhaGradVParams)
+        lib.mha_grad_v.argtypes = [ctypes.c_void_p] * 5 + [M, ctypes.c_void_p]
+        lib.mha_grad_v.restype = ctypes.c_int
+        lib.mha_grad_v_check_indexing.argtypes = [M, ctypes.c_char_p, ctypes.c_size_t]
+        lib.mha_grad_v_check_indexing.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -726,3 +742,57 @@ def rms_norm_matmul(x, g, w, eps=1e-6, stream=None):
     import torch
     out = torch.empty((int(x.shape[0]), int(w.shape[1])), dtype=torch.float32, device=x.device)
     return rms_norm_matmul_into(out, x, g, w, eps, stream)
+
+
+# ---- attention dV ---------------------------------------------------------------
+
+def make_mha_params(q_seq, kv_seq, heads, kv_heads, head_dim=64, window=0,
+                    causal=True) -> MhaGradVParams:
+    return MhaGradVParams(int(q_seq), int(kv_seq), int(heads), int(kv_heads), int(head_dim),
+                          int(window), int(bool(causal)))
+
+
+def check_indexing_mha_grad_v(p: MhaGradVParams) -> tuple:
+    """Host replay of the attention-dV launch (no device needed)."""
+    buf = ctypes.create_string_buffer(512)
+    rc = load_library().mha_grad_v_check_indexing(ctypes.byref(p), buf, len(buf))
+    return int(rc), buf.value.decode()
+
+
+def mha_grad_v_raw(dout_ptr: int, q_ptr: int, k_ptr: int, lse_ptr: int, dv_ptr: int,
+                   p: MhaGradVParams, stream: int = 0) -> int:
+    """Raw C-ABI call of mha_grad_v; returns the status."""
+    return int(load_library().mha_grad_v(
+        ctypes.c_void_p(dout_ptr), ctypes.c_void_p(q_ptr), ctypes.c_void_p(k_ptr),
+        ctypes.c_void_p(lse_ptr), ctypes.c_void_p(dv_ptr), ctypes.byref(p),
+        ctypes.c_void_p(stream)))
+
+
+def mha_grad_v_into(dv, dout, q, k, lse, window=0, causal=True, stream=None):
+    """dV [kv_seq, kv_heads, 64] of attention into ``dv`` on torch's current
+    stream (or ``stream``); float32 GPU tensors dout, q [q_seq, heads, 64],
+    k [kv_seq, kv_heads, 64], lse [q_seq, heads, 2] (row max, log sum).
+    Raises Conv2dError on a bad status."""
+    import torch
+    q_seq, heads, d = (int(v) for v in q.shape)
+    kv_seq, kv_heads = int(k.shape[0]), int(k.shape[1])
+    _check_tensor(dout, "dout", (q_seq, heads, d))
+    _check_tensor(q, "q", (q_seq, heads, d))
+    _check_tensor(k, "k", (kv_seq, kv_heads, d))
+    _check_tensor(lse, "lse", (q_seq, heads, 2))
+    _check_tensor(dv, "dv", (kv_seq, kv_heads, d))
+    p = make_mha_params(q_seq, kv_seq, heads, kv_heads, d, window, causal)
+    with torch.cuda.device(dv.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = mha_grad_v_raw(dout.data_ptr(), q.data_ptr(), k.data_ptr(), lse.data_ptr(),
+                            dv.data_ptr(), p, int(s.cuda_stream))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return dv
+
+
+def mha_grad_v(dout, q, k, lse, window=0, causal=True, stream=None):
+    """dV as a new float32 tensor [kv_seq, kv_heads, 64]."""
+    import torch
+    dv = torch.empty(tuple(k.shape), dtype=torch.float32, device=k.device)
+    return mha_grad_v_into(dv, dout, q, k, lse, window, causal, stream)

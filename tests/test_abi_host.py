@@ -429,3 +429,31 @@ def test_rms_norm_matmul_rejects_before_any_device_call():
 
 def test_rms_params_struct_layout():
     assert ctypes.sizeof(c2b.RmsMatmulParams) == 16
+
+
+# ---- attention dV entry point --------------------------------------------------------
+
+def test_mha_grad_v_rejects_before_any_device_call():
+    lib = c2b.load_library()
+    p = c2b.make_mha_params(8, 8, 2, 1)        # q, dout 8 x 2 x 64; k, dv 8 x 1 x 64
+    call = c2b.mha_grad_v_raw
+    assert lib.mha_grad_v(None, None, None, None, None, None, None) == NULL
+    assert call(0, 0x100000, 0x200000, 0x300000, 0x400000, p) == NULL
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0, p) == NULL
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x400000,
+                c2b.make_mha_params(8, 8, 2, 1, 128)) == BAD          # head_dim
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x400000,
+                c2b.make_mha_params(8, 8, 3, 2)) == BAD               # groups
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x400000,
+                c2b.make_mha_params(8, 9, 2, 1)) == BAD               # causal q != kv
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x400004, p) == BAD   # unaligned dv
+    # dv overlapping an input
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x200000, p) == ALIAS
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x100000 + 64, p) == ALIAS
+    # no key: nothing to do
+    assert call(0x10000, 0x100000, 0x200000, 0x300000, 0x400000,
+                c2b.make_mha_params(8, 0, 2, 1, causal=False)) == OK
+
+
+def test_mha_params_struct_layout():
+    assert ctypes.sizeof(c2b.MhaGradVParams) == 28

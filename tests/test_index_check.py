@@ -175,3 +175,23 @@ def test_rms_norm_matmul_replay_rejects_bad_params():
         assert c2b.check_indexing_rms_norm_matmul(c2b.make_rms_params(m, n, k, eps))[0] == -2
     # a tensor of 2^31 bytes
     assert c2b.check_indexing_rms_norm_matmul(c2b.make_rms_params(1 << 16, 8, 1 << 13))[0] == -4
+
+
+# ---- attention dV (mha_grad_v) ----------------------------------------------------
+
+MHA_REPLAY = [(37, 37, 4, 2, 0, 1), (1, 1, 1, 1, 0, 1), (64, 64, 2, 1, 0, 1),
+              (65, 65, 3, 3, 5, 1), (100, 70, 4, 2, 0, 0), (100, 70, 4, 2, 9, 0),
+              (130, 130, 8, 2, 64, 1), (7, 200, 2, 1, 3, 0), (4096, 4096, 32, 8, 512, 1)]
+
+
+@pytest.mark.parametrize("case", MHA_REPLAY, ids=lambda c: "q%d_kv%d_h%d_kv%d_w%d_c%d" % c)
+def test_mha_grad_v_replay(case):
+    qs, ks, h, hkv, w, c = case
+    rc, msg = c2b.check_indexing_mha_grad_v(c2b.make_mha_params(qs, ks, h, hkv, 64, w, c))
+    assert rc == 0, (case, rc, msg)
+
+
+def test_mha_grad_v_replay_rejects_bad_params():
+    for bad in [(8, 8, 2, 1, 32, 0, 1), (8, 8, 3, 2, 64, 0, 1), (8, 9, 2, 1, 64, 0, 1),
+                (8, 8, 2, 0, 64, 0, 1)]:
+        assert c2b.check_indexing_mha_grad_v(c2b.make_mha_params(*bad))[0] == -2

@@ -86,8 +86,9 @@ MUTANTS = [
      "exp(e - l[1])", "exp(e)"),
     ("lse_log_dropped", "oracle_attention_lse",
      "log(sum)", "sum"),
-    ("lse_window_off_by_one", "oracle_attention_lse",
-     "pos >= t + window)) continue;\n        double s = 0.0;\n        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];\n        s *= scale;",
+    ("lse_sum_unscaled", "oracle_attention_lse",
+     "sum += exp(s * scale - mx);", "sum += exp(s - mx);"),
+] * k[(t * HKV + kvh) * D + d];\n        s *= scale;",
      "pos > t + window)) continue;\n        double s = 0.0;\n        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];\n        s *= scale;"),
 ]
 
