@@ -88,8 +88,6 @@ MUTANTS = [
      "log(sum)", "sum"),
     ("lse_sum_unscaled", "oracle_attention_lse",
      "sum += exp(s * scale - mx);", "sum += exp(s - mx);"),
-] * k[(t * HKV + kvh) * D + d];\n        s *= scale;",
-     "pos > t + window)) continue;\n        double s = 0.0;\n        for (i64 d = 0; d < D; ++d) s += qp[d] * k[(t * HKV + kvh) * D + d];\n        s *= scale;"),
 ]
 
 
