@@ -61,15 +61,23 @@ struct Args {
   const float* lse;
   float* dv;
   int32_t q_seq, kv_seq, H, HKV, group, window, causal;
-  int32_t nkb;   // key blocks
+  int32_t nkb;     // key blocks
+  int32_t paired;  // 1: a workgroup takes key blocks u and nkb - 1 - u
+  int32_t units;   // workgroups per kv head
   float scale;
 };
 
-// Workgroup bid -> (key block, kv head); key blocks in order (for causal
-// masks the first blocks reach the most positions, so they start first).
-MHA_HD void unit_of(const Args& a, int bid, int* kb, int* kvh) {
+// Workgroup bid -> kv head and its key blocks (1 or 2), returned count.
+// Under a causal mask without a short window, key block u reaches nkb - u
+// query blocks, so blocks u and nkb - 1 - u share a workgroup and every
+// workgroup gets about the same work.
+MHA_HD int unit_of(const Args& a, int bid, int kb[2], int* kvh) {
   *kvh = bid % a.HKV;
-  *kb = bid / a.HKV;
+  const int u = bid / a.HKV;
+  kb[0] = u;
+  if (!a.paired) return 1;
+  kb[1] = a.nkb - 1 - u;
+  return kb[1] != u ? 2 : 1;
 }
 
 // Query positions [lo, hi) that reach some key of key block kb: the union of
@@ -128,11 +136,8 @@ __global__ __launch_bounds__(kThreads, 2) void mha_grad_v_kernel(const Args a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  int kb, kvh;
-  unit_of(a, blockIdx.x, &kb, &kvh);
-  const int t0 = kb * kBK;
-  int lo, hi;
-  pos_range(a, kb, &lo, &hi);
+  int kbs[2], kvh;
+  const int nblocks = unit_of(a, blockIdx.x, kbs, &kvh);
 
   const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(a.q), 0, a.q_seq * a.H * kD * 4, 0x00020000);
@@ -143,7 +148,13 @@ __global__ __launch_bounds__(kThreads, 2) void mha_grad_v_kernel(const Args a) {
   const __amdgpu_buffer_rsrc_t rsL = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(a.lse), 0, a.q_seq * a.H * 2 * 4, 0x00020000);
 
-  // the K block, once
+  for (int ib = 0; ib < nblocks; ++ib) {
+  const int kb = kbs[ib];
+  const int t0 = kb * kBK;
+  int lo, hi;
+  pos_range(a, kb, &lo, &hi);
+  __syncthreads();   // the previous key block's reads of Kt are done
+  // the K block, once per key block
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const f32x4 v = load_f32x4(rsK, k_offset(a, t0 + row_of(tid, p), kvh, dq_of(tid)));
@@ -226,6 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void mha_grad_v_kernel(const Args a) {
 #pragma unroll
     for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4*>(out + 16 * b + 4 * g) = acc[b];
   }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -250,6 +262,8 @@ int plan(const mha_grad_v_params* p, Args* a) {
   a->window = int32_t(p->window);
   a->causal = int32_t(p->causal);
   a->nkb = int32_t((int64_t(p->kv_seq) + kBK - 1) / kBK);
+  a->paired = p->causal && (p->window == 0 || p->window >= p->q_seq / 2) ? 1 : 0;
+  a->units = a->paired ? (a->nkb + 1) / 2 : a->nkb;
   a->scale = 1.0f / std::sqrt(float(kD));
   if (int64_t(a->nkb) * a->HKV >= kI31) return CONV2D_ERR_OVERFLOW;
   return CONV2D_OK;
@@ -279,9 +293,12 @@ int check(const mha_grad_v_params* p, char* msg, size_t len) {
     const int64_t k_bytes = int64_t(a.kv_seq) * a.HKV * kD * 4;
     const int64_t l_bytes = int64_t(a.q_seq) * a.H * 2 * 4;
     std::vector<unsigned char> seen(size_t(int64_t(a.nkb) * a.HKV), 0);
-    for (int bid = 0; bid < a.nkb * a.HKV; ++bid) {
-      int kb, kvh;
-      unit_of(a, bid, &kb, &kvh);
+    for (int ub = 0; ub < 2 * a.units * a.HKV; ++ub) {
+      const int bid = ub / 2;
+      int kbs[2], kvh;
+      const int nb = unit_of(a, bid, kbs, &kvh);
+      if (ub % 2 >= nb) continue;
+      const int kb = kbs[ub % 2];
       MHA_REQUIRE(kb >= 0 && kb < a.nkb && kvh >= 0 && kvh < a.HKV &&
                       !seen[size_t(kb) * a.HKV + kvh],
                   "workgroup %d unit", bid);
@@ -336,6 +353,8 @@ int check(const mha_grad_v_params* p, char* msg, size_t len) {
                       "K element %d", t);
         }
     }
+    for (size_t i = 0; i < seen.size(); ++i)
+      MHA_REQUIRE(seen[i] == 1, "key block %zu of a kv head never taken", i / size_t(a.HKV));
     // every LDS row cell of a stage is written once: rows x quads
     std::vector<int> cnt(size_t(kBQ) * 16, 0), gcnt(size_t(kD) * 16, 0);
     for (int tid = 0; tid < kThreads; ++tid)
@@ -387,7 +406,7 @@ extern "C" int mha_grad_v(const float* dout, const float* q, const float* k, con
   a.lse = lse;
   a.dv = dv;
   // (heads == 0: the kernel's head loop is empty and it stores zeros)
-  hipLaunchKernelGGL(mhv::mha_grad_v_kernel, dim3(a.nkb * a.HKV), dim3(mhv::kThreads), 0,
+  hipLaunchKernelGGL(mhv::mha_grad_v_kernel, dim3(a.units * a.HKV), dim3(mhv::kThreads), 0,
                      static_cast<hipStream_t>(stream), a);
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
