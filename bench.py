@@ -42,7 +42,8 @@ _CSRC = "conv2d_backward_implicit_amd/csrc/"
 # the sources each entry point's kernels and launch set-up are built from
 KERNEL_SOURCES = {
     "grad_input": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
-    "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
+    "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp",
+                                     "forward_gemm.hip")],
     "grad_weight": [_CSRC + f for f in ("grad_weight.hip", "tile_index.hpp", "plan.hpp")],
     "rms_norm_matmul": [_CSRC + "rms_matmul.hip"],
     "mha_grad_v": [_CSRC + "mha_grad_v.hip"],
@@ -415,6 +416,11 @@ def main() -> int:
                     c2b.describe_plan_variant(p, variant))
         plan["variant"] = variant
         plan["tuned"] = not args.no_tune
+        if fwd and not f16 and 1 <= shape.in_channels < 16:
+            # conv2d_forward takes the im2col GEMM over (ci, kh, kw) for these
+            # shapes; the variant above belongs to the other kernel family
+            plan = {"path": "forward im2col GEMM (fewer than 16 input channels)",
+                    "variant": -1, "tuned": False}
 
         def step():
             if fwd:

@@ -16,7 +16,8 @@ LIB_NAME = "libconv2d_bwd.so"
 LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "index_check.hip"),
            os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "grad_weight.hip"),
-           os.path.join(CSRC, "rms_matmul.hip"), os.path.join(CSRC, "mha_grad_v.hip")]
+           os.path.join(CSRC, "rms_matmul.hip"), os.path.join(CSRC, "mha_grad_v.hip"),
+           os.path.join(CSRC, "forward_gemm.hip")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled on purpose: the compiler would otherwise

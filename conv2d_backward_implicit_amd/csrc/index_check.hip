@@ -383,8 +383,17 @@ extern "C" int conv2d_check_indexing_variant(const conv2d_params* p, int variant
   return c2b::check_all(p, c2b::kVariants[variant].f16, variant, msg, msg_len);
 }
 
+namespace c2b {
+namespace fg {   // forward_gemm.hip
+bool fg_applies(const conv2d_params* p, int f16);
+int fg_check(const conv2d_params* p, char* msg, size_t len);
+}  // namespace fg
+}  // namespace c2b
+
 extern "C" int conv2d_check_indexing_forward(const conv2d_params* p, int f16, char* msg,
                                              size_t msg_len) {
+  // the path conv2d_forward / conv2d_forward_f16 take for this shape
+  if (c2b::fg::fg_applies(p, f16 ? 1 : 0)) return c2b::fg::fg_check(p, msg, msg_len);
   return c2b::check_all(p, f16 ? 1 : 0, -1, msg, msg_len, c2b::kOpForward);
 }
 

@@ -678,8 +678,22 @@ extern "C" int conv2d_planned_variant(const conv2d_params* p, int f16, int* vari
   return c2b::planned_variant(p, f16 ? 1 : 0, variant_out);
 }
 
+namespace c2b {
+namespace fg {   // forward_gemm.hip: the few-input-channel forward
+bool fg_applies(const conv2d_params* p, int f16);
+int fg_launch(const float* x, const float* w, float* y, const conv2d_params* p, void* stream);
+}  // namespace fg
+}  // namespace c2b
+
 extern "C" int conv2d_forward(const float* x, const float* weight, float* y,
                               const conv2d_params* p, void* stream) {
+  // fewer than 16 input channels: the im2col GEMM over (ci, kh, kw), which
+  // pads no contraction channel (forced variants still reach this family)
+  if (c2b::fg::fg_applies(p, 0)) {
+    int rc = c2b::validate_shape(p);
+    if (rc == CONV2D_OK) rc = c2b::check_pointers(x, weight, y, p, c2b::kOpForward);
+    return rc == CONV2D_OK ? c2b::fg::fg_launch(x, weight, y, p, stream) : rc;
+  }
   return c2b::launch(x, weight, y, p, 0, -1, stream, c2b::kOpForward);
 }
 
