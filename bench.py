@@ -342,7 +342,7 @@ def main() -> int:
         return copy_calibration(args.copy_calibration, args.steps)
 
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               "(each GPU would run its own batch shard with no exchange); "
               "run with --gpus 1", file=sys.stderr)
         return 2
