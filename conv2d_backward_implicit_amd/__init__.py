@@ -25,9 +25,10 @@ __all__ = [
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
     "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
     "variant_is_f16", "variant_uses_column_taps", "conv2d_grad_input_variant",
-    "tune", "planned_variant", "describe_plan_variant",
+    "tune", "planned_variant", "select_variant", "describe_plan_variant",
     "forward", "forward_into", "conv2d_forward", "conv2d_forward_f16",
     "conv2d_forward_variant", "tune_forward", "planned_forward_variant",
+    "select_forward_variant",
     "describe_forward_plan", "describe_forward_plan_variant",
     "check_indexing_forward", "check_indexing_forward_variant",
     "grad_weight", "grad_weight_into", "conv2d_grad_weight", "grad_weight_workspace_size",
@@ -59,12 +60,14 @@ EXPORTED_SYMBOLS = (
     "conv2d_check_indexing_variant",
     "conv2d_tune",
     "conv2d_planned_variant",
+    "conv2d_select_variant",
     "conv2d_describe_plan_variant",
     "conv2d_forward",
     "conv2d_forward_f16",
     "conv2d_forward_variant",
     "conv2d_tune_forward",
     "conv2d_planned_forward_variant",
+    "conv2d_select_forward_variant",
     "conv2d_describe_forward_plan",
     "conv2d_describe_forward_plan_variant",
     "conv2d_check_indexing_forward",
@@ -214,6 +217,10 @@ def load_library():
         lib.conv2d_tune_forward.restype = ctypes.c_int
         lib.conv2d_planned_forward_variant.argtypes = lib.conv2d_planned_variant.argtypes
         lib.conv2d_planned_forward_variant.restype = ctypes.c_int
+        for name in ("conv2d_select_variant", "conv2d_select_forward_variant"):
+            fn = getattr(lib, name)
+            fn.argtypes = [P, ctypes.c_int, ctypes.c_int]
+            fn.restype = ctypes.c_int
         lib.conv2d_describe_forward_plan.argtypes = lib.conv2d_describe_plan.argtypes
         lib.conv2d_describe_forward_plan.restype = ctypes.c_int
         lib.conv2d_describe_forward_plan_variant.argtypes = \
@@ -436,6 +443,15 @@ def planned_variant(p: Conv2dParams, f16: bool = False) -> int:
     return int(v.value)
 
 
+def select_variant(p: Conv2dParams, f16: bool = False, variant: int = -1) -> None:
+    """conv2d_select_variant: make ``variant`` (-1: the model's choice) the
+    default entry point's variant for this shape; raises on a bad status."""
+    rc = int(load_library().conv2d_select_variant(ctypes.byref(p), int(bool(f16)),
+                                                  int(variant)))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+
+
 def grad_input(grad_out, weight, in_h, in_w, stride=1, padding_h=0, padding_w=0,
                f16=False, out=None, stream=None):
     """Input gradient of conv2d for NCHW ``grad_out`` and [Co, Ci, kH, kW]
@@ -569,6 +585,14 @@ def planned_forward_variant(p: Conv2dParams, f16: bool = False) -> int:
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return int(v.value)
+
+
+def select_forward_variant(p: Conv2dParams, f16: bool = False, variant: int = -1) -> None:
+    """conv2d_select_forward_variant; raises on a bad status."""
+    rc = int(load_library().conv2d_select_forward_variant(ctypes.byref(p), int(bool(f16)),
+                                                          int(variant)))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
 
 
 def forward(x, weight, stride=1, padding_h=0, padding_w=0, f16=False, out=None, stream=None):

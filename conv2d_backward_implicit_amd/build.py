@@ -36,11 +36,7 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every source into LIB_PATH (always recompiles)."""
-    tmp = LIB_PATH + ".tmp%d" % os.getpid()
-    cmd = [hipcc()] + HIPCC_FLAGS + list(extra_flags) + ["-I", INCLUDE, "-I", CSRC] \
-        + SOURCES + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,7 +48,30 @@ def build(verbose: bool = False, extra_flags=()) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
+
+
+def build(verbose: bool = False, extra_flags=()) -> str:
+    """Compile every source into LIB_PATH (always recompiles): one object per
+    source, compiled in parallel, then linked."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    obj_dir = os.path.join(ROOT, "_build", "obj%d" % os.getpid())
+    os.makedirs(obj_dir, exist_ok=True)
+    flags = [f for f in HIPCC_FLAGS if f != "-shared"] + list(extra_flags)
+    objs = [os.path.join(obj_dir, os.path.basename(src) + ".o") for src in SOURCES]
+    jobs = max(1, min(len(SOURCES), len(os.sched_getaffinity(0)), 8))
+    with ThreadPoolExecutor(jobs) as ex:
+        futs = [ex.submit(_run, [hipcc()] + flags + ["-I", INCLUDE, "-I", CSRC, "-c", src,
+                                                     "-o", obj], verbose)
+                for src, obj in zip(SOURCES, objs)]
+        for f in futs:
+            f.result()
+    tmp = LIB_PATH + ".tmp%d" % os.getpid()
+    _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
     os.replace(tmp, LIB_PATH)
+    for obj in objs:
+        os.remove(obj)
+    os.rmdir(obj_dir)
     return LIB_PATH
 
 

@@ -210,8 +210,17 @@ __global__ __launch_bounds__(kThreads, 4) void forward_gemm_kernel(const FGArgs 
 // ---------------------------------------------------------------------------
 // Host side.
 
+int fg_plan(const conv2d_params* p, FGArgs* a);
+
+// fp32 shapes with 1 to 15 input channels whose tensors fit this kernel's
+// whole-tensor 32-bit offsets (fg_plan); every other shape, including
+// larger batches of the same layer, goes to the implicit-GEMM family, which
+// offsets per image.
 bool fg_applies(const conv2d_params* p, int f16) {
-  return p != nullptr && !f16 && p->in_channels >= 1 && p->in_channels < uint32_t(kMaxChannels);
+  if (p == nullptr || f16 || p->in_channels < 1 || p->in_channels >= uint32_t(kMaxChannels))
+    return false;
+  FGArgs a;
+  return fg_plan(p, &a) == CONV2D_OK;
 }
 
 int fg_plan(const conv2d_params* p, FGArgs* a) {

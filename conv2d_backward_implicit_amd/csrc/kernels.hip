@@ -470,8 +470,9 @@ int device_cus() {
 
 // Launch plans of recent shapes (host memory only), so that a repeated call
 // skips the planner's search.  Keyed by the shape, the operation, the path,
-// the forced variant (-1: the default plan, the model's choice or a tuned
-// one) and the CU count; at most kPlanCacheSize entries, oldest evicted.
+// the variant (-1: the model's choice) and the CU count; at most
+// kPlanCacheSize entries, least recently used evicted.  A cached plan is only
+// a memo of build_plan: evicting one changes no result.
 struct PlanKey {
   conv2d_params p;
   int op, f16, variant, cus;
@@ -482,6 +483,17 @@ struct PlanEntry {
 };
 constexpr size_t kPlanCacheSize = 64;
 
+// The variant chosen for a shape by conv2d_tune or conv2d_select_variant
+// (key variant field -1): the default entry point's plan for that shape.
+// Never evicted, so a choice stays in force for the rest of the process; at
+// most kMaxSelections shapes (a further selection returns
+// CONV2D_ERR_UNSUPPORTED and leaves the model's choice in force).
+struct Selection {
+  PlanKey key;
+  int variant;
+};
+constexpr size_t kMaxSelections = 4096;
+
 std::mutex& plan_cache_mutex() {
   static std::mutex mu;
   return mu;
@@ -489,6 +501,10 @@ std::mutex& plan_cache_mutex() {
 std::vector<PlanEntry>& plan_cache() {
   static std::vector<PlanEntry> cache;
   return cache;
+}
+std::vector<Selection>& selections() {
+  static std::vector<Selection> sel;
+  return sel;
 }
 
 PlanKey plan_key(const conv2d_params* p, int op, int f16, int variant, int cus) {
@@ -502,27 +518,65 @@ PlanKey plan_key(const conv2d_params* p, int op, int f16, int variant, int cus) 
   return key;
 }
 
-// Insert or replace a plan (callers hold no lock).
+bool same_key(const PlanKey& a, const PlanKey& b) { return std::memcmp(&a, &b, sizeof(a)) == 0; }
+
+// Insert a plan as the most recently used entry (callers hold no lock).
 void store_plan(const PlanKey& key, const std::vector<LaunchArgs>& launches) {
   std::lock_guard<std::mutex> lock(plan_cache_mutex());
   std::vector<PlanEntry>& cache = plan_cache();
-  for (PlanEntry& e : cache)
-    if (std::memcmp(&e.key, &key, sizeof(key)) == 0) {
-      e.launches = launches;
-      return;
+  for (size_t i = 0; i < cache.size(); ++i)
+    if (same_key(cache[i].key, key)) {
+      cache.erase(cache.begin() + long(i));
+      break;
     }
   if (cache.size() >= kPlanCacheSize) cache.erase(cache.begin());
   cache.push_back(PlanEntry{key, launches});
 }
 
+// Selected variant of a shape's default plan, or -1 (the model's choice).
+int selected_variant(const conv2d_params* p, int op, int f16, int cus) {
+  const PlanKey key = plan_key(p, op, f16, -1, cus);
+  std::lock_guard<std::mutex> lock(plan_cache_mutex());
+  for (const Selection& s : selections())
+    if (same_key(s.key, key)) return s.variant;
+  return -1;
+}
+
+// Make `variant` the default plan's variant for a shape (-1: back to the
+// model's choice).
+int select_variant(const conv2d_params* p, int op, int f16, int cus, int variant) {
+  const PlanKey key = plan_key(p, op, f16, -1, cus);
+  std::lock_guard<std::mutex> lock(plan_cache_mutex());
+  std::vector<Selection>& sel = selections();
+  for (size_t i = 0; i < sel.size(); ++i)
+    if (same_key(sel[i].key, key)) {
+      if (variant < 0) sel.erase(sel.begin() + long(i));
+      else sel[i].variant = variant;
+      return CONV2D_OK;
+    }
+  if (variant < 0) return CONV2D_OK;
+  if (sel.size() >= kMaxSelections) return CONV2D_ERR_UNSUPPORTED;
+  sel.push_back(Selection{key, variant});
+  return CONV2D_OK;
+}
+
+// Plan of a shape with `variant` forced, or (variant -1) its default plan:
+// the selected variant if there is one, else the model's choice.
 int cached_plan(const conv2d_params* p, int op, int f16, int variant, int cus,
                 std::vector<LaunchArgs>* out) {
+  if (variant < 0) variant = selected_variant(p, op, f16, cus);
   const PlanKey key = plan_key(p, op, f16, variant, cus);
   {
     std::lock_guard<std::mutex> lock(plan_cache_mutex());
-    for (const PlanEntry& e : plan_cache())
-      if (std::memcmp(&e.key, &key, sizeof(key)) == 0) {
-        *out = e.launches;
+    std::vector<PlanEntry>& cache = plan_cache();
+    for (size_t i = 0; i < cache.size(); ++i)
+      if (same_key(cache[i].key, key)) {
+        *out = cache[i].launches;
+        if (i + 1 != cache.size()) {   // most recently used goes last
+          PlanEntry e = std::move(cache[i]);
+          cache.erase(cache.begin() + long(i));
+          cache.push_back(std::move(e));
+        }
         return CONV2D_OK;
       }
   }
@@ -579,13 +633,15 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
     if (build_plan(p, f16, cus, nullptr, nullptr, v, &cost, op) == CONV2D_OK)
       cand.push_back({cost, v});
   }
+  // the model's choice (built here, not through the selection in force)
   std::vector<LaunchArgs> launches;
-  rc = cached_plan(p, op, f16, -1, cus, &launches);   // the model's choice
+  rc = build_plan(p, f16, cus, &launches, nullptr, -1, nullptr, op);
   if (rc != CONV2D_OK) return rc;
   int best_v = launches.empty() ? -1 : launches[0].variant;
   std::sort(cand.begin(), cand.end());
   if (cand.size() > size_t(kTuneCandidates)) cand.resize(kTuneCandidates);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  std::vector<LaunchArgs> best_plan = launches;
   if (!launches.empty() && cand.size() > 1) {
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
@@ -593,11 +649,11 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
       return CONV2D_ERR_HIP;
     }
     float best_ms = 0.0f;
-    std::vector<LaunchArgs> best_plan;
+    bool timed = false;
     for (const auto& c : cand) {
       if (c.first > kTuneSpread * cand[0].first) break;
       std::vector<LaunchArgs> plan;
-      rc = cached_plan(p, op, f16, c.second, cus, &plan);
+      rc = build_plan(p, f16, cus, &plan, nullptr, c.second, nullptr, op);
       if (rc != CONV2D_OK) break;
       rc = enqueue(plan, go, w, gi, st);   // warm-up
       if (rc != CONV2D_OK) break;
@@ -612,7 +668,8 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
           hipEventElapsedTime(&ms, e0, e1) != hipSuccess)
         break;
       rc = CONV2D_OK;
-      if (best_plan.empty() || ms < best_ms) {
+      if (!timed || ms < best_ms) {
+        timed = true;
         best_ms = ms;
         best_plan = plan;
       }
@@ -620,15 +677,16 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (rc != CONV2D_OK) return rc;
-    if (!best_plan.empty()) {
-      store_plan(plan_key(p, op, f16, -1, cus), best_plan);
-      best_v = best_plan[0].variant;
-      // leave the output holding the result of the chosen plan
-      rc = enqueue(best_plan, go, w, gi, st);
-      if (rc != CONV2D_OK) return rc;
-    }
-  } else if (!launches.empty()) {
-    rc = enqueue(launches, go, w, gi, st);
+    best_v = best_plan[0].variant;
+  }
+  if (best_v >= 0) {
+    rc = select_variant(p, op, f16, cus, best_v);
+    if (rc != CONV2D_OK) return rc;
+    store_plan(plan_key(p, op, f16, best_v, cus), best_plan);
+  }
+  if (!best_plan.empty()) {
+    // leave the output holding the result of the chosen plan
+    rc = enqueue(best_plan, go, w, gi, st);
     if (rc != CONV2D_OK) return rc;
   }
   if (variant_out) *variant_out = best_v;
@@ -679,6 +737,27 @@ extern "C" int conv2d_planned_variant(const conv2d_params* p, int f16, int* vari
 }
 
 namespace c2b {
+// A variant for a shape's default plan: -1, or a variant of the path that
+// tiles the shape.
+int select_checked(const conv2d_params* p, int op, int f16, int variant) {
+  if (p == nullptr) return CONV2D_ERR_NULL_PTR;
+  int rc = validate_shape(p);
+  if (rc != CONV2D_OK) return rc;
+  if (variant < -1 || variant >= kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  const int cus = device_cus();
+  if (variant >= 0) {
+    rc = build_plan(p, f16, cus, nullptr, nullptr, variant, nullptr, op);
+    if (rc != CONV2D_OK) return rc;
+  }
+  return select_variant(p, op, f16, cus, variant);
+}
+}  // namespace c2b
+
+extern "C" int conv2d_select_variant(const conv2d_params* p, int f16, int variant) {
+  return c2b::select_checked(p, c2b::kOpGradInput, f16 ? 1 : 0, variant);
+}
+
+namespace c2b {
 namespace fg {   // forward_gemm.hip: the few-input-channel forward
 bool fg_applies(const conv2d_params* p, int f16);
 int fg_launch(const float* x, const float* w, float* y, const conv2d_params* p, void* stream);
@@ -713,6 +792,15 @@ extern "C" int conv2d_forward_variant(const float* x, const float* weight, float
 extern "C" int conv2d_tune_forward(const float* x, const float* weight, float* y,
                                    const conv2d_params* p, int f16, void* stream,
                                    int* variant_out) {
+  // shapes on the im2col GEMM have no variant to choose: run it once
+  if (c2b::fg::fg_applies(p, f16 ? 1 : 0)) {
+    const int rc = conv2d_forward(x, weight, y, p, stream);
+    if (rc != CONV2D_OK) return rc;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+      return CONV2D_ERR_HIP;
+    if (variant_out) *variant_out = -1;
+    return CONV2D_OK;
+  }
   return c2b::tune(x, weight, y, p, f16 ? 1 : 0, stream, variant_out, c2b::kOpForward);
 }
 
@@ -720,5 +808,14 @@ extern "C" int conv2d_planned_forward_variant(const conv2d_params* p, int f16, i
   if (p == nullptr || variant_out == nullptr) return CONV2D_ERR_NULL_PTR;
   const int rc = c2b::validate_shape(p);
   if (rc != CONV2D_OK) return rc;
+  if (c2b::fg::fg_applies(p, f16 ? 1 : 0)) {   // the im2col GEMM, not a variant
+    *variant_out = -1;
+    return CONV2D_OK;
+  }
   return c2b::planned_variant(p, f16 ? 1 : 0, variant_out, c2b::kOpForward);
+}
+
+extern "C" int conv2d_select_forward_variant(const conv2d_params* p, int f16, int variant) {
+  if (c2b::fg::fg_applies(p, f16 ? 1 : 0)) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::select_checked(p, c2b::kOpForward, f16 ? 1 : 0, variant);
 }

@@ -30,10 +30,23 @@
  * Ownership.  The caller owns all three device buffers and keeps them alive
  * until the work enqueued on `stream` has completed.  `p` is read during the
  * call only.  The library allocates no device memory and keeps no per-call
- * state; it keeps a small host-side cache of launch plans (at most 64
- * shapes, guarded by a mutex), so calls are reentrant and thread-safe.
- * Calls on different streams that write the same grad_input race like any
- * other kernels would.
+ * state; it keeps a host-side memo of recent launch plans (at most 64,
+ * least recently used evicted; a memo changes no result) and a table of the
+ * variants chosen per shape by conv2d_tune / conv2d_select_variant (never
+ * evicted), both guarded by a mutex, so calls are reentrant and
+ * thread-safe.  Calls on different streams that write the same grad_input
+ * race like any other kernels would.
+ *
+ * Reproducibility.  A call's result is a deterministic function of its
+ * inputs and of the kernel variant that runs it: repeated calls with one
+ * variant are bitwise identical, on any stream.  Variants differ in
+ * summation order only, so their results differ in rounding (within the
+ * fp32 / f16 tolerances), and the variant of the default entry points is
+ * the planner's model choice for the shape and the device's compute-unit
+ * count until conv2d_tune or conv2d_select_variant chooses another for the
+ * rest of the process.  For bitwise-identical results across processes,
+ * pass the variant conv2d_tune chose in one process to
+ * conv2d_select_variant in the other (or call conv2d_grad_input_variant).
  *
  * Semantics.  grad_input is fully overwritten (elements no tap reaches are
  * set to 0).  grad_out and weight are only read.  grad_input must not overlap
@@ -138,7 +151,9 @@ const char* conv2d_status_string(int status);
  * buffers and `stream` after one warm-up, timed with HIP events; the fastest
  * becomes the plan conv2d_grad_input (or conv2d_grad_input_f16) uses for
  * this shape on devices with this many compute units, for the rest of the
- * process (a host-side cache of at most 64 shapes, oldest evicted).
+ * process (as conv2d_select_variant would make it; at most 4096 shapes hold
+ * a chosen variant, after which CONV2D_ERR_UNSUPPORTED is returned and the
+ * model's choice stays in force).
  *   grad_out, weight, grad_input, p, stream: as for conv2d_grad_input;
  *     grad_input is overwritten, and on success holds the input gradient
  *     (computed by the chosen variant).
@@ -161,6 +176,19 @@ int conv2d_tune(const float* grad_out, const float* weight, float* grad_input,
  * argument).  Host code (reads the device's compute-unit count once).
  */
 int conv2d_planned_variant(const conv2d_params* p, int f16, int* variant_out);
+
+/*
+ * Choose the variant conv2d_grad_input (f16 == 0) or conv2d_grad_input_f16
+ * (f16 != 0) uses for this shape on the current device from now on, without
+ * running anything: `variant` is a variant of that path that tiles the shape
+ * (for instance the one conv2d_tune chose in another process, which makes
+ * the two processes' results bitwise identical), or -1 to return to the
+ * planner's model choice.  Returns CONV2D_OK, the shape's CONV2D_ERR_* code,
+ * CONV2D_ERR_NULL_PTR, or CONV2D_ERR_UNSUPPORTED (variant out of range, of
+ * the other path, unable to tile the shape, or 4096 shapes already chosen).
+ * Host code (reads the device's compute-unit count once).
+ */
+int conv2d_select_variant(const conv2d_params* p, int f16, int variant);
 
 /*
  * Launch plan of a shape, for inspection and host-side tests (pure host
@@ -276,6 +304,10 @@ int conv2d_check_indexing_variant(const conv2d_params* p, int variant,
  * gradient with the operand roles exchanged (the kernel variants without
  * column taps); conv2d_forward_f16 rounds x and weight to f16 (round to
  * nearest even) and accumulates in fp32, as conv2d_grad_input_f16 does.
+ * conv2d_forward with 1 to 15 input channels runs an im2col GEMM over
+ * (ci, kh, kw) instead, when x and y each stay below 2^31 bytes and
+ * batch*out_h*out_w below 2^31; larger such shapes take the variant
+ * kernels, like every other shape.
  */
 int conv2d_forward(const float* x, const float* weight, float* y,
                    const conv2d_params* p, void* stream);
@@ -292,15 +324,22 @@ int conv2d_forward_variant(const float* x, const float* weight, float* y,
  * on the caller's buffers (x and weight read, y written, with the result of
  * the chosen variant left in y), makes the fastest the shape's default
  * forward plan, blocks until done, and stores it in *variant_out if that is
- * not NULL.  Errors as conv2d_forward, or CONV2D_ERR_HIP. */
+ * not NULL.  A shape conv2d_forward runs on the im2col GEMM (above) has no
+ * variant: it is run once and *variant_out gets -1.  Errors as
+ * conv2d_forward, or CONV2D_ERR_HIP. */
 int conv2d_tune_forward(const float* x, const float* weight, float* y,
                         const conv2d_params* p, int f16, void* stream,
                         int* variant_out);
 
 /* The variant conv2d_forward (f16 == 0) or conv2d_forward_f16 uses for the
- * shape now, in *variant_out (-1 if nothing is launched).  CONV2D_OK, or
- * the error of conv2d_check_params, or CONV2D_ERR_NULL_PTR. */
+ * shape now, in *variant_out (-1 if nothing is launched or the shape runs
+ * on the im2col GEMM).  CONV2D_OK, or the error of conv2d_check_params, or
+ * CONV2D_ERR_NULL_PTR. */
 int conv2d_planned_forward_variant(const conv2d_params* p, int f16, int* variant_out);
+
+/* conv2d_select_variant for conv2d_forward / conv2d_forward_f16;
+ * CONV2D_ERR_UNSUPPORTED also for a shape on the im2col GEMM. */
+int conv2d_select_forward_variant(const conv2d_params* p, int f16, int variant);
 
 /* conv2d_describe_plan / _variant for the forward launches (host only). */
 int conv2d_describe_forward_plan(const conv2d_params* p, int f16,

@@ -519,6 +519,29 @@ def pin_torch_mha_grad_v(orc):
         assert err <= 1e-12, (i, err)
 
 
+def pin_torch_attention_row_max(orc):
+    """The statistics' first entry on its own: for a row that sees a key, the
+    maximum of the scaled scores q . k / sqrt(D) over the keys the mask lets
+    through, by torch's masked max in float64 (a row that sees none: 0).
+    Their sum with the second entry is invariant to the choice of maximum,
+    so this is pinned separately."""
+    import torch
+    for i, (qs, ks, H, HKV, D, win, causal) in enumerate(_MHA_CASES):
+        rng = np.random.default_rng(700 + i)
+        q, k = rng.standard_normal((qs, H, D)), rng.standard_normal((ks, HKV, D))
+        vis = _visible(qs, ks, win, causal)
+        mask = torch.from_numpy(vis)
+        grp = H // HKV
+        want = np.zeros((qs, H))
+        for h in range(H):
+            sc = (torch.from_numpy(q[:, h, :]) @ torch.from_numpy(k[:, h // grp, :]).T)
+            sc = (sc / np.sqrt(D)).masked_fill(~mask, float("-inf"))
+            mx = sc.max(dim=1).values.numpy()
+            want[:, h] = np.where(vis.any(axis=1), mx, 0.0)
+        lse = orc.attention_lse(q, k, HKV, win, causal)
+        assert np.max(np.abs(lse[..., 0] - want)) <= 1e-12, i
+
+
 def pin_mha_uniform_scores(orc):
     """K = 0: every score is 0, so P = 1 / (number of keys query pos sees)
     and dV[t] = sum over the queries that see t and the group's heads of
@@ -599,6 +622,7 @@ ALL_PINS = [
     pin_rms_scale_and_linearity,
     pin_rms_rows,
     pin_torch_mha_grad_v,
+    pin_torch_attention_row_max,
     pin_mha_uniform_scores,
     pin_mha_single_dout,
     pin_mha_exponent_clamp,

@@ -246,6 +246,53 @@ def test_planned_variant_is_a_variant_of_the_path():
     assert lib.conv2d_planned_variant(ctypes.byref(_p()), 0, None) == NULL
 
 
+def test_select_variant_sets_the_default_plan_and_survives_other_shapes():
+    """A chosen variant is the default plan's until changed, however many
+    other shapes are planned afterwards (the plan memo is bounded, the table
+    of chosen variants is not evicted)."""
+    p = _p(batch=3, in_channels=56, in_h=9, in_w=11, out_channels=30)
+    for f16 in (False, True):
+        model = c2b.planned_variant(p, f16)
+        others = [v for v in range(c2b.num_variants())
+                  if c2b.variant_is_f16(v) == int(f16) and v != model
+                  and _tiles(p, v)]
+        assert others
+        chosen = others[-1]
+        c2b.select_variant(p, f16, chosen)
+        assert c2b.planned_variant(p, f16) == chosen
+        assert c2b.planned_variant(p, not f16) != chosen      # per path
+        # plan 150 other shapes (more than the memo holds), each with every
+        # variant of the path forced through describe and the default plan
+        for i in range(150):
+            q = _p(batch=1 + i % 3, in_channels=8 + i, in_h=7, in_w=9, out_channels=12)
+            c2b.planned_variant(q, f16)
+        assert c2b.planned_variant(p, f16) == chosen
+        c2b.select_variant(p, f16, -1)                          # back to the model
+        assert c2b.planned_variant(p, f16) == model
+
+
+def _tiles(p, v):
+    try:
+        c2b.describe_plan_variant(p, v)
+        return True
+    except c2b.Conv2dError:
+        return False
+
+
+def test_select_variant_rejects():
+    lib = c2b.load_library()
+    p = _p(in_channels=40, out_channels=24)
+    n = c2b.num_variants()
+    fp32 = next(v for v in range(n) if c2b.variant_is_f16(v) == 0)
+    assert lib.conv2d_select_variant(ctypes.byref(p), 0, n) == UNSUP
+    assert lib.conv2d_select_variant(ctypes.byref(p), 0, -2) == UNSUP
+    assert lib.conv2d_select_variant(ctypes.byref(p), 1, fp32) == UNSUP   # other path
+    assert lib.conv2d_select_variant(None, 0, fp32) == NULL
+    assert lib.conv2d_select_variant(ctypes.byref(_p(stride=0, out_h=1, out_w=1)), 0,
+                                     fp32) == BAD
+    assert lib.conv2d_select_variant(ctypes.byref(p), 0, -1) == OK        # nothing chosen
+
+
 def test_describe_plan_variant_matches_forced_plans():
     p = _p(in_channels=40, out_channels=24)
     for v in range(c2b.num_variants()):
@@ -327,6 +374,27 @@ def test_forward_plans():
     assert c2b.planned_forward_variant(_p(batch=0)) == -1
     with pytest.raises(c2b.Conv2dError):
         c2b.describe_forward_plan(_p(stride=0, out_h=1, out_w=1))
+
+
+def test_forward_few_channel_route():
+    """fp32 forward with 1-15 input channels runs the im2col GEMM, which has
+    no variant; a batch too large for that kernel's 32-bit whole-tensor
+    offsets takes the variant kernels (which offset per image) instead of
+    failing."""
+    lib = c2b.load_library()
+    stem = c2b.make_params(16, 3, 224, 224, 64, 7, 7, 2, 3, 3)
+    assert c2b.planned_forward_variant(stem, False) == -1
+    assert lib.conv2d_select_forward_variant(ctypes.byref(stem), 0, 0) == UNSUP
+    v16 = c2b.planned_forward_variant(stem, True)            # f16: variant family
+    assert v16 >= 0 and c2b.variant_is_f16(v16) == 1
+    # x of 4000 x 3 x 224 x 224 fp32 is 2.4 GB, past 2^31 bytes
+    big = c2b.make_params(4000, 3, 224, 224, 64, 7, 7, 2, 3, 3)
+    assert c2b.check_params(big) == OK
+    v = c2b.planned_forward_variant(big, False)
+    assert v >= 0 and c2b.variant_is_f16(v) == 0 and c2b.variant_uses_column_taps(v) == 0
+    c2b.select_forward_variant(big, False, v)
+    assert c2b.planned_forward_variant(big, False) == v
+    c2b.select_forward_variant(big, False, -1)
 
 
 # ---- weight gradient entry points ---------------------------------------------

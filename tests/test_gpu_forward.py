@@ -8,6 +8,7 @@ Bar: max|gpu - oracle| / max|oracle| <= 1e-4 (fp32 path) and <= 2e-2
 element written (NaN pre-fill), nothing outside y (guard canaries).
 """
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -116,7 +117,7 @@ def test_forward_edge_shapes(sh, f16):
 def test_forward_random_small_shapes():
     for sh in RANDOM:
         _say("case forward", sh)
-        x, w = draw_forward(sh, hash(sh.name) % 2 ** 32)
+        x, w = draw_forward(sh, zlib.crc32(sh.name.encode()))
         for f16 in (False, True):
             _check(sh, x, w, f16)
 

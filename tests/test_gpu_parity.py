@@ -5,8 +5,8 @@ for the f16-staged path; integer-valued inputs must match bit for bit on both
 paths; every grad_input element is written (NaN pre-fill) and nothing outside
 it is (guard canaries).
 """
-import os
 import sys
+import zlib
 
 import numpy as np
 import pytest
@@ -77,51 +77,6 @@ def test_config_integer_inputs_bit_exact(idx, f16):
     assert np.array_equal(got.astype(np.float64), ref)
 
 
-# ---- the five workloads at full size, sampled against the oracle ------------
-def _sample_indices(sh, rng, count=3000):
-    n = int(np.prod(sh.gi_shape))
-    idx = list(rng.integers(0, n, size=count))
-    # every border row/column of the first and last image of a few channels
-    N, C, H, W = sh.gi_shape
-    for nn in (0, N - 1):
-        for cc in sorted({0, C // 2, C - 1}):
-            base = (nn * C + cc) * H * W
-            for x in range(W):
-                idx += [base + x, base + (H - 1) * W + x]
-            for y in range(H):
-                idx += [base + y * W, base + y * W + W - 1]
-    return np.unique(np.array(idx, dtype=np.int64))
-
-
-@pytest.mark.parametrize("idx", range(len(CONFIGS)), ids=[c.name for c in CONFIGS])
-def test_config_full_size_sampled(idx):
-    sh = CONFIGS[idx]
-    f16 = sh.f16_staged
-    _say("case full", sh.name, "f16" if f16 else "fp32")
-    go, w = draw(sh, idx)
-    got = run_gpu(sh, go, w, f16=f16)
-    assert not np.any(np.isnan(got)), "unwritten grad_input elements"
-    rng = np.random.default_rng(idx)
-    sel = _sample_indices(sh, rng)
-    ref = oracle.grad_input_gather_at(go, w, sh.in_h, sh.in_w, sh.stride,
-                                      sh.padding_h, sh.padding_w, sel)
-    scale = float(np.max(np.abs(ref)))
-    err = float(np.max(np.abs(got.ravel()[sel].astype(np.float64) - ref))) / scale
-    _say("  sampled rel err", err, "over", sel.size)
-    assert err <= TOL[f16], err
-    if f16:
-        ref16 = oracle.grad_input_gather_at(round_f16(go), round_f16(w), sh.in_h,
-                                            sh.in_w, sh.stride, sh.padding_h,
-                                            sh.padding_w, sel)
-        err16 = float(np.max(np.abs(got.ravel()[sel] - ref16))) / scale
-        assert err16 <= 1e-5, err16
-    # the f32 path of the f16 workload, and the f16 path of the others
-    other = run_gpu(sh, go, w, f16=not f16)
-    err2 = float(np.max(np.abs(other.ravel()[sel].astype(np.float64) - ref))) / scale
-    _say("  other path sampled rel err", err2)
-    assert err2 <= TOL[not f16], err2
-
-
 # ---- random small shapes: strides 1-3, asymmetric padding, ragged tiles ----
 RANDOM = [random_shape(np.random.default_rng(500 + i), max_n=3, max_c=9, max_hw=23,
                        max_k=7, max_s=4, name="r%d" % i) for i in range(60)]
@@ -130,7 +85,7 @@ RANDOM = [random_shape(np.random.default_rng(500 + i), max_n=3, max_c=9, max_hw=
 @pytest.mark.parametrize("sh", RANDOM, ids=[s.name for s in RANDOM])
 def test_random_small_shapes(sh):
     _say("case", sh)
-    rng = np.random.default_rng(hash(sh.name) % 2 ** 32)
+    rng = np.random.default_rng(zlib.crc32(sh.name.encode()))
     go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
     w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
     ref = _oracle(sh, go, w)
