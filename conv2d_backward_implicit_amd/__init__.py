@@ -34,6 +34,7 @@ __all__ = [
     "grad_weight", "grad_weight_into", "conv2d_grad_weight", "grad_weight_workspace_size",
     "check_indexing_grad_weight", "check_indexing_grad_weight_variant",
     "conv2d_grad_weight_variant", "describe_grad_weight_plan", "GRAD_WEIGHT_VARIANTS",
+    "grad_weight_noalloc_into",
     "RmsMatmulParams", "make_rms_params", "rms_norm_matmul", "rms_norm_matmul_into",
     "conv2d_rms_norm_matmul_raw", "check_indexing_rms_norm_matmul",
     "MhaGradVParams", "make_mha_params", "mha_grad_v", "mha_grad_v_into", "mha_grad_v_raw",
@@ -76,6 +77,7 @@ EXPORTED_SYMBOLS = (
     "conv2d_grad_weight_workspace_size",
     "conv2d_check_indexing_grad_weight",
     "conv2d_grad_weight_variant",
+    "conv2d_grad_weight_noalloc",
     "conv2d_grad_weight_variant_workspace_size",
     "conv2d_describe_grad_weight_plan",
     "conv2d_check_indexing_grad_weight_variant",
@@ -100,6 +102,7 @@ STATUS_NAMES = {
     -5: "CONV2D_ERR_UNSUPPORTED",
     -6: "CONV2D_ERR_HIP",
     -7: "CONV2D_ERR_WORKSPACE",
+    -8: "CONV2D_ERR_SCRATCH",
 }
 
 
@@ -240,6 +243,9 @@ def load_library():
         lib.conv2d_check_indexing_grad_weight.argtypes = [P, ctypes.c_char_p, ctypes.c_size_t]
         lib.conv2d_check_indexing_grad_weight.restype = ctypes.c_int
         lib.conv2d_grad_weight_variant.argtypes = lib.conv2d_grad_weight.argtypes + [ctypes.c_int]
+        lib.conv2d_grad_weight_noalloc.argtypes = [ctypes.c_void_p, ctypes.c_void_p,
+                                                   ctypes.c_void_p, P, ctypes.c_void_p]
+        lib.conv2d_grad_weight_noalloc.restype = ctypes.c_int
         lib.conv2d_grad_weight_variant.restype = ctypes.c_int
         lib.conv2d_grad_weight_variant_workspace_size.argtypes = [
             P, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)]
@@ -697,6 +703,28 @@ def grad_weight_into(grad_weight, grad_out, x, p: Conv2dParams, workspace=None, 
                 int(s.cuda_stream))
         rc = (conv2d_grad_weight(*args) if variant < 0 else
               conv2d_grad_weight_variant(*args, variant))
+    if rc != CONV2D_OK:
+        raise Conv2dError(rc)
+    return grad_weight
+
+
+def grad_weight_noalloc_into(grad_weight, grad_out, x, p: Conv2dParams, stream=None):
+    """conv2d_grad_weight_noalloc: the weight gradient into ``grad_weight``
+    with the library's own scratch instead of a workspace (nothing is
+    allocated); raises Conv2dError on a bad status."""
+    import torch
+    _check_tensor(grad_out, "grad_out", (p.batch, p.out_channels, p.out_h, p.out_w))
+    _check_tensor(x, "x", (p.batch, p.in_channels, p.in_h, p.in_w))
+    _check_tensor(grad_weight, "grad_weight", (p.out_channels, p.in_channels, p.kernel_h,
+                                               p.kernel_w))
+    if not (grad_out.device == x.device == grad_weight.device):
+        raise ValueError("all tensors must be on the same device")
+    with torch.cuda.device(grad_weight.device):
+        s = stream if stream is not None else torch.cuda.current_stream()
+        rc = int(load_library().conv2d_grad_weight_noalloc(
+            ctypes.c_void_p(grad_out.data_ptr()), ctypes.c_void_p(x.data_ptr()),
+            ctypes.c_void_p(grad_weight.data_ptr()), ctypes.byref(p),
+            ctypes.c_void_p(int(s.cuda_stream))))
     if rc != CONV2D_OK:
         raise Conv2dError(rc)
     return grad_weight

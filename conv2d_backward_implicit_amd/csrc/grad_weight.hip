@@ -46,6 +46,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -739,6 +740,54 @@ int run(const float* grad_out, const float* x, float* grad_weight, const conv2d_
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free entry point: the partial tiles go to a scratch array the
+// library holds in device memory (each device its own copy, from the load of
+// the code object until the process ends) instead of a caller's workspace.
+// The array's name is only a stand-in in host code; its device address comes
+// from hipGetSymbolAddress, once per device, with that device current.  The
+// product kernel writes every partial element it reads back, so nothing has
+// to be cleared between calls.
+
+constexpr size_t kScratchBytes = CONV2D_GRAD_WEIGHT_NOALLOC_MAX_BYTES;
+static_assert(kScratchBytes % 256 == 0, "whole 256-byte lines");
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+constexpr int kMaxScratchDevices = 64;
+
+// Device address of the current device's scratch (nullptr on a HIP error).
+void* scratch_address() {
+  static std::mutex mu;
+  static void* addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
+}
+
+int run_noalloc(const float* grad_out, const float* x, float* grad_weight,
+                const conv2d_params* p, void* stream) {
+  if (p == nullptr) return CONV2D_ERR_NULL_PTR;
+  GWArgs a;
+  int rc = gw_plan(p, device_cus_gw(), -1, &a);
+  if (rc != CONV2D_OK) return rc;
+  if (gw_workspace_bytes(a) > kScratchBytes) return CONV2D_ERR_SCRATCH;
+  // the caller's tensors first (the scratch overlaps none of them), so that
+  // every argument error is reported before any HIP call
+  GWArgs tensors_only = a;
+  tensors_only.nchunks = 0;
+  rc = gw_check_pointers(grad_out, x, grad_weight, nullptr, 0, p, tensors_only);
+  if (rc != CONV2D_OK) return rc;
+  void* ws = scratch_address();
+  if (ws == nullptr) return CONV2D_ERR_HIP;
+  return run(grad_out, x, grad_weight, p, ws, kScratchBytes, stream, -1);
+}
+
 int workspace_size(const conv2d_params* p, int variant, size_t* bytes) {
   if (p == nullptr || bytes == nullptr) return CONV2D_ERR_NULL_PTR;
   GWArgs a;
@@ -759,6 +808,12 @@ extern "C" int conv2d_grad_weight(const float* grad_out, const float* x, float* 
                                   const conv2d_params* p, void* workspace,
                                   size_t workspace_bytes, void* stream) {
   return c2b::gw::run(grad_out, x, grad_weight, p, workspace, workspace_bytes, stream, -1);
+}
+
+extern "C" int conv2d_grad_weight_noalloc(const float* grad_out, const float* x,
+                                          float* grad_weight, const conv2d_params* p,
+                                          void* stream) {
+  return c2b::gw::run_noalloc(grad_out, x, grad_weight, p, stream);
 }
 
 extern "C" int conv2d_grad_weight_variant_workspace_size(const conv2d_params* p, int variant,

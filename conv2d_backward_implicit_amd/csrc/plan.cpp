@@ -612,6 +612,9 @@ extern "C" const char* conv2d_status_string(int status) {
              "or kernel variant not available for this path";
     case CONV2D_ERR_HIP: return "HIP runtime error at launch";
     case CONV2D_ERR_WORKSPACE: return "workspace smaller than conv2d_grad_weight_workspace_size";
+    case CONV2D_ERR_SCRATCH:
+      return "shape needs more scratch than the allocation-free entry point holds "
+             "(CONV2D_GRAD_WEIGHT_NOALLOC_MAX_BYTES)";
     default: return "unknown status";
   }
 }

@@ -103,9 +103,12 @@ enum {
                                   or cannot tile the shape                  */
   CONV2D_ERR_HIP = -6,         /* the HIP runtime reported an error at
                                   launch (hipGetLastError)                   */
-  CONV2D_ERR_WORKSPACE = -7    /* conv2d_grad_weight: the workspace is
+  CONV2D_ERR_WORKSPACE = -7,   /* conv2d_grad_weight: the workspace is
                                   smaller than its workspace size or not
                                   16-byte aligned                            */
+  CONV2D_ERR_SCRATCH = -8      /* conv2d_grad_weight_noalloc: the shape needs
+                                  more than the library's scratch array
+                                  (CONV2D_GRAD_WEIGHT_NOALLOC_MAX_BYTES)     */
 };
 
 /*
@@ -423,6 +426,30 @@ int conv2d_grad_weight_variant(const float* grad_out, const float* x,
                                float* grad_weight, const conv2d_params* p,
                                void* workspace, size_t workspace_bytes,
                                void* stream, int variant);
+
+/*
+ * conv2d_grad_weight for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same operation, plan and result (bit for bit), with the
+ * partial sums in a scratch array the library holds in device memory
+ * (CONV2D_GRAD_WEIGHT_NOALLOC_MAX_BYTES per device, from the first load of
+ * the library until the process ends) instead of a caller's workspace.  The
+ * call allocates nothing.
+ *   grad_out, x, grad_weight, p, stream: as for conv2d_grad_weight.
+ * Returns what conv2d_grad_weight returns (no workspace error), or
+ * CONV2D_ERR_SCRATCH, with nothing enqueued, if
+ * conv2d_grad_weight_workspace_size reports more than
+ * CONV2D_GRAD_WEIGHT_NOALLOC_MAX_BYTES for the shape (on a 256-CU device
+ * that takes a weight of more than 2048 tiles of 64 x 64, about 8.4M
+ * elements), or CONV2D_ERR_HIP if the scratch's address cannot be taken.
+ * Every call on one device shares that device's scratch: calls that may
+ * overlap on one device (other streams, other host threads) race and must
+ * be ordered by the caller.
+ */
+#define CONV2D_GRAD_WEIGHT_NOALLOC_MAX_BYTES (32u << 20)
+int conv2d_grad_weight_noalloc(const float* grad_out, const float* x,
+                               float* grad_weight, const conv2d_params* p,
+                               void* stream);
 
 /* Workspace bytes of conv2d_grad_weight_variant, as
  * conv2d_grad_weight_workspace_size. */

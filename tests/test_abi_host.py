@@ -525,3 +525,28 @@ def test_mha_grad_v_rejects_before_any_device_call():
 
 def test_mha_params_struct_layout():
     assert ctypes.sizeof(c2b.MhaGradVParams) == 28
+
+
+def test_grad_weight_noalloc_rejects_before_any_device_call():
+    """Argument errors of the allocation-free weight gradient come back
+    before any HIP call (this machine may have no GPU), including a shape
+    whose partial sums exceed the library's scratch array."""
+    lib = c2b.load_library()
+
+    def call(go, x, dw, q):
+        return lib.conv2d_grad_weight_noalloc(ctypes.c_void_p(go), ctypes.c_void_p(x),
+                                              ctypes.c_void_p(dw), q, None)
+    p = _p()
+    assert call(1, 2, 3, None) == NULL
+    assert call(0x1000, 0x2000, 0x3000, ctypes.byref(_p(stride=0, out_h=1, out_w=1))) == BAD
+    assert call(0, 0x200000, 0x100000, ctypes.byref(p)) == NULL
+    assert call(0x300000, 0, 0x100000, ctypes.byref(p)) == NULL
+    assert call(0x300000, 0x200000, 0, ctypes.byref(p)) == NULL
+    assert call(0x100000, 0x200000, 0x100000, ctypes.byref(p)) == ALIAS   # dw on grad_out
+    # 1024 x 1024 channels, 3 x 3: 2304 tiles of 64 x 64 -> 37.7 MB of partial
+    # sums, more than the 32 MiB scratch
+    big = _p(batch=1, in_channels=1024, in_h=8, in_w=8, out_channels=1024)
+    assert call(0x1000000, 0x2000000, 0x3000000, ctypes.byref(big)) == -8
+    assert c2b.status_string(-8) != "unknown status"
+    need = c2b.grad_weight_workspace_size(big)
+    assert need > 32 << 20, need
