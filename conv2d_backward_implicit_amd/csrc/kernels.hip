@@ -227,6 +227,17 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
 #pragma unroll
     for (int b = 0; b < NBW; ++b) acc[m][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // Blocks of this wave that hold at least one of the tile's pixels (or cm
+  // points): a prefix of its NBW blocks.  A tile whose pixel count is not a
+  // multiple of the lane tile leaves the last block of some waves empty;
+  // those waves skip that block's reads and products (one uniform branch per
+  // unit; fewer empty blocks are rare and are multiplied as padding).
+  bool last_on = true;
+  {
+    const int npts = CM ? cm_points(c) : c.npx;
+    last_on = NBW == 1 || ((NBW - 1) * WN + ng) * 16 < npts;
+  }
+
   // All addresses, then all reads of one unit: the scheduling barriers keep
   // the compiler from recycling a read's target register as the next
   // address, which would serialise the reads.
@@ -242,17 +253,28 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
 #pragma unroll
     for (int m = 0; m < MB; ++m) aw[m] = *aa[m];
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) bv[b] = *ba[b];
+    for (int b = 0; b < NBW - 1; ++b) bv[b] = *ba[b];
+    if (last_on) bv[NBW - 1] = *ba[NBW - 1];
     __builtin_amdgcn_sched_barrier(0);
   };
+  // Products of one unit: blocks 0 .. NBW-2, then the last block if it holds
+  // a pixel (every accumulator still takes its four k values in order).
   auto mma_f32 = [&](const f32x4(&bv)[NBW], const f32x4(&aw)[MB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int m = 0; m < MB; ++m)
 #pragma unroll
-        for (int b = 0; b < NBW; ++b)
+        for (int b = 0; b < NBW - 1; ++b)
           acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[b][q], acc[m][b], 0, 0, 0);
+    if (last_on) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+          acc[m][NBW - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[NBW - 1][q],
+                                                                acc[m][NBW - 1], 0, 0, 0);
+    }
   };
   auto mma_f16_pair = [&](const f32x4(&bv0)[NBW], const f32x4(&aw0)[MB],
                           const f32x4(&bv1)[NBW],
@@ -262,6 +284,7 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
     for (int m = 0; m < MB; ++m) ah[m] = join(to_f16(aw0[m]), to_f16(aw1[m]));
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
+      if (b == NBW - 1 && !last_on) break;
       const f16x8 bh = join(to_f16(bv0[b]), to_f16(bv1[b]));
 #pragma unroll
       for (int m = 0; m < MB; ++m)
@@ -275,6 +298,7 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
     for (int m = 0; m < MB; ++m) ah[m] = to_f16(aw[m]);
 #pragma unroll
     for (int b = 0; b < NBW; ++b) {
+      if (b == NBW - 1 && !last_on) break;
       const f16x4 bh = to_f16(bv[b]);
 #pragma unroll
       for (int m = 0; m < MB; ++m)
@@ -337,7 +361,6 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
       }
     }
   };
-
   __syncthreads();   // stage 0 is in LDS
   for (int st = 0; st < nst; ++st) {
     compute(st);

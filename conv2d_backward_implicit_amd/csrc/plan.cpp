@@ -256,8 +256,11 @@ int64_t max_rows_spanned(int64_t wb, int64_t ntv, int64_t bp) {
 // `max_slots` slots per channel (slots rounded up to a multiple of 16).
 // Fewest bands first; for each band width, equal tiles of at most ntl
 // pixels, halving the tile until the window fits.
-bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* wb_out,
-                   int64_t* ntv_out, int64_t* slots_out) {
+// `extra` > 0 asks for that many more tiles per band than the fewest that
+// fit (smaller tiles, so that the tile count can match the CUs); false if
+// the tiles would fall below one 16-pixel block.
+bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t extra,
+                   int64_t* wb_out, int64_t* ntv_out, int64_t* slots_out) {
   const int64_t th = d.th, tw = d.tw, hp = d.hp, wp = d.wp, ss = d.ss;
   int64_t last_wb = -1;
   for (int64_t nb = 1; nb <= wp; ++nb) {
@@ -267,7 +270,11 @@ bool choose_tiling(const PhaseDesc& d, int64_t ntl, int64_t max_slots, int64_t* 
     const int64_t bp = hp * wb;
     const int64_t roww = (wb - 1) * ss + tw;
     for (int64_t cap = ntl;; cap = (cap + 1) / 2) {
-      const int64_t ntv = ceil_div(bp, ceil_div(bp, cap));
+      int64_t ntv = ceil_div(bp, ceil_div(bp, cap));
+      if (extra > 0) {
+        ntv = ceil_div(bp, ceil_div(bp, ntv) + extra);
+        if (ntv < 16) return false;
+      }
       const int64_t rows = (max_rows_spanned(wb, ntv, bp) - 1) * ss + th;
       const int64_t slots = ceil_div(rows * roww, 16) * 16;
       if (slots <= max_slots) {
@@ -323,14 +330,30 @@ constexpr double kTileCycles = 45000.0;       // set-up, first copies, epilogue
 constexpr double kCopyBytesPerCycle = 12.0;   // stage copies, per CU
 constexpr double kSharedStageVisible = 0.4;   // stage overhead left when sharing a CU
 constexpr double kCmEpilogueCycles = 4000.0;   // cm: rows through LDS, column-tap sums
+constexpr int64_t kMaxExtraTiles = 3;          // tiles per band beyond the fewest
+
+// Blocks per wave the kernel multiplies for a tile of `pts` lanes in use,
+// averaged over the waves along pixels: a wave whose last block holds no
+// lane in use runs NBW - 1 blocks, any other NBW (mm_body).
+double active_blocks(const Variant& v, int64_t pts) {
+  double sum = 0.0;
+  for (int ng = 0; ng < v.wn; ++ng) {
+    int nact = 0;
+    for (int b = 0; b < v.nbw; ++b)
+      if ((int64_t(b) * v.wn + ng) * 16 < pts) nact = b + 1;
+    sum += (v.nbw > 1 && nact == v.nbw - 1) ? v.nbw - 1 : v.nbw;
+  }
+  return sum / v.wn;
+}
 
 double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v, int share) {
   (void)Co;
   if (d.th == 0) return kTileCycles;
   const int64_t ntaps = v.cm ? int64_t(d.th) : int64_t(d.th) * d.tw;
   const double wps = v.wm * v.wn / 4.0;
-  const double mfma = wps * v.mb * v.nbw * (v.f16 ? 8.0 : 128.0) * share;
-  const double lds = 8.0 * v.wm * v.wn * (v.nbw + v.mb) * share;
+  const double nbw = v.cm ? double(v.nbw) : active_blocks(v, d.ntv);
+  const double mfma = wps * v.mb * nbw * (v.f16 ? 8.0 : 128.0) * share;
+  const double lds = 8.0 * v.wm * v.wn * (nbw + v.mb) * share;
   const double unit = std::max(mfma, lds) / simd_efficiency(int(wps * share)) +
                       kUnitLatency / std::max(1.0, wps * share);
   const double copy = double(stage_floats(v)) * 4.0 / kCopyBytesPerCycle * share;
@@ -348,7 +371,8 @@ double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v, int share) {
 // Stage shape and tiling of one class for variant v: the (taps, channel
 // groups) per stage and the band/tile sizes that fit the LDS stage buffer
 // with the lowest cost per pixel.  False if nothing fits.
-bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_t cstride) {
+bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_t cstride,
+                int64_t extra) {
   const int64_t ntl = 16 * int64_t(v.nbw) * v.wn, mt = 16 * int64_t(v.wm) * v.mb;
   if (d->th == 0) {                                   // zero class: stores only
     d->wb = d->wp;
@@ -388,7 +412,7 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
         int64_t rows;
         if (!cm_tiling(c, nb, ntl, max_slots, &wb, &rows, &slots)) continue;
         ntv = rows * wb;
-      } else if (!choose_tiling(c, ntl, max_slots, &wb, &ntv, &slots)) {
+      } else if (!choose_tiling(c, ntl, max_slots, extra, &wb, &ntv, &slots)) {
         continue;
       }
       c.wb = int32_t(wb);
@@ -498,10 +522,13 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     if (fwd && var.cm) continue;
     const int64_t vmt = channels_per_tile(var);
     if (vmt < 1) continue;
+    // the fewest tiles per band, or up to kMaxExtraTiles more (cm variants
+    // tile whole rows: fewest only)
+    for (int64_t extra = 0; extra <= (var.cm ? 0 : kMaxExtraTiles); ++extra) {
     std::vector<PhaseDesc> phases = classes;
     bool ok = true;
     for (PhaseDesc& d : phases)
-      if (!tile_class(&d, var, Kch, src_plane, cstride)) {
+      if (!tile_class(&d, var, Kch, src_plane, cstride, extra)) {
         ok = false;
         break;
       }
@@ -520,6 +547,7 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
       best_cost = cost;
       best = phases;
     }
+    }
   }
   if (best_v < 0) return CONV2D_ERR_UNSUPPORTED;
   if (model_cost) *model_cost = best_cost;
@@ -536,7 +564,10 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
       info->phases += 1;
       if (d.th == 0) info->zero_phases += 1;
       if (d.th > 0) {
-        const int64_t lanes = 16 * int64_t(bv.nbw) * bv.wn;
+        // lanes the kernel multiplies: blocks past a short wave's last one
+        // are skipped (mm_body)
+        const double blocks = bv.cm ? double(bv.nbw) : active_blocks(bv, d.ntv);
+        const int64_t lanes = int64_t(16.0 * blocks * bv.wn + 0.5);
         const int64_t kpad =
             int64_t(d.nchunks) * 16 * d.cg * int64_t(d.th) * (bv.cm ? 1 : d.tw);
         info->macs += tiles * lanes * bmt * kpad;
