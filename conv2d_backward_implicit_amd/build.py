@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(PKG, LIB_NAME)
 SOURCES = [os.path.join(CSRC, "kernels.hip"), os.path.join(CSRC, "index_check.hip"),
            os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "grad_weight.hip"),
            os.path.join(CSRC, "rms_matmul.hip"), os.path.join(CSRC, "mha_grad_v.hip"),
-           os.path.join(CSRC, "forward_gemm.hip")]
+           os.path.join(CSRC, "forward_gemm.hip"), os.path.join(CSRC, "pointwise_gemm.hip")]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are disabled on purpose: the compiler would otherwise

@@ -18,6 +18,7 @@
 #include <utility>
 #include <vector>
 
+#include "pointwise.hpp"
 #include "tile_index.hpp"
 
 namespace c2b {
@@ -374,6 +375,8 @@ int check_all(const conv2d_params* p, int f16, int variant, char* msg, size_t le
 
 extern "C" int conv2d_check_indexing(const conv2d_params* p, int f16, char* msg,
                                      size_t msg_len) {
+  // the path conv2d_grad_input / _f16 take for this shape (aligned tensors)
+  if (c2b::pw::pw_shape(p)) return c2b::pw::pw_check(p, msg, msg_len);
   return c2b::check_all(p, f16 ? 1 : 0, -1, msg, msg_len);
 }
 

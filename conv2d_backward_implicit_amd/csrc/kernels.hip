@@ -55,6 +55,7 @@
 #include <utility>
 #include <vector>
 
+#include "pointwise.hpp"
 #include "tile_index.hpp"
 
 namespace c2b {
@@ -628,6 +629,10 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, i
   if (rc != CONV2D_OK) return rc;
   rc = check_pointers(go, w, gi, p, op);
   if (rc != CONV2D_OK) return rc;
+  // 1x1, stride 1, unpadded: the GEMM over all images' pixels (forced
+  // variants still reach the kernel family)
+  if (op == kOpGradInput && variant < 0 && pw::pw_applies(p, go, w, gi))
+    return pw::pw_launch(go, w, gi, p, f16, stream);
   std::vector<LaunchArgs> launches;
   rc = cached_plan(p, op, f16, variant, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
@@ -648,6 +653,15 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
   if (rc != CONV2D_OK) return rc;
   rc = check_pointers(go, w, gi, p, op);
   if (rc != CONV2D_OK) return rc;
+  if (op == kOpGradInput && pw::pw_applies(p, go, w, gi)) {
+    // the 1x1 GEMM has no variant to choose: run it once
+    rc = pw::pw_launch(go, w, gi, p, f16, stream);
+    if (rc != CONV2D_OK) return rc;
+    if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
+      return CONV2D_ERR_HIP;
+    if (variant_out) *variant_out = -1;
+    return CONV2D_OK;
+  }
   const int cus = device_cus();
   std::vector<std::pair<double, int>> cand;
   for (int v = 0; v < kNumVariants; ++v) {
@@ -719,6 +733,10 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
 // The variant the default entry point of a path uses for a shape now (-1 if
 // the shape launches nothing).
 int planned_variant(const conv2d_params* p, int f16, int* variant_out, int op = kOpGradInput) {
+  if (op == kOpGradInput && pw::pw_shape(p)) {   // the 1x1 GEMM (aligned tensors)
+    *variant_out = -1;
+    return CONV2D_OK;
+  }
   std::vector<LaunchArgs> launches;
   const int rc = cached_plan(p, op, f16, -1, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
@@ -767,6 +785,8 @@ int select_checked(const conv2d_params* p, int op, int f16, int variant) {
   int rc = validate_shape(p);
   if (rc != CONV2D_OK) return rc;
   if (variant < -1 || variant >= kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  // the 1x1 GEMM has no variant to choose (-1 still clears a choice)
+  if (op == kOpGradInput && pw::pw_shape(p) && variant >= 0) return CONV2D_ERR_UNSUPPORTED;
   const int cus = device_cus();
   if (variant >= 0) {
     rc = build_plan(p, f16, cus, nullptr, nullptr, variant, nullptr, op);

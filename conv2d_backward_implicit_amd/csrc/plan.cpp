@@ -10,6 +10,7 @@
 #include <cstring>
 
 #include "plan.hpp"
+#include "pointwise.hpp"
 #include "tile_index.hpp"
 
 namespace c2b {
@@ -522,31 +523,54 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     if (fwd && var.cm) continue;
     const int64_t vmt = channels_per_tile(var);
     if (vmt < 1) continue;
-    // the fewest tiles per band, or up to kMaxExtraTiles more (cm variants
-    // tile whole rows: fewest only)
-    for (int64_t extra = 0; extra <= (var.cm ? 0 : kMaxExtraTiles); ++extra) {
-    std::vector<PhaseDesc> phases = classes;
-    bool ok = true;
-    for (PhaseDesc& d : phases)
-      if (!tile_class(&d, var, Kch, src_plane, cstride, extra)) {
-        ok = false;
-        break;
+    // Each class with the fewest tiles per band, or up to kMaxExtraTiles
+    // more (cm variants tile whole rows: fewest only).  Shapes with up to
+    // four classes try every combination of per-class choices (so that a
+    // light class can take smaller tiles that fill the CUs the heavy classes
+    // leave idle); others try the same choice for every class.
+    const int64_t emax = var.cm ? 0 : kMaxExtraTiles;
+    const size_t nc = classes.size();
+    std::vector<PhaseDesc> cand(nc * size_t(emax + 1));
+    std::vector<char> fits(nc * size_t(emax + 1), 0);
+    for (size_t i = 0; i < nc; ++i)
+      for (int64_t e = 0; e <= emax; ++e) {
+        PhaseDesc d = classes[i];
+        fits[i * size_t(emax + 1) + size_t(e)] =
+            tile_class(&d, var, Kch, src_plane, cstride, e) ? 1 : 0;
+        cand[i * size_t(emax + 1) + size_t(e)] = d;
       }
-    if (!ok) continue;
-    // a two-per-CU variant only shares its CU when there are more tiles
-    // than CUs
-    int64_t ntiles = 0;
-    for (const PhaseDesc& d : phases)
-      ntiles += N * d.nbands * int64_t(d.ptiles) * ceil_div(Mch, vmt);
-    const int share = (var.half && ntiles > num_cus) ? 2 : 1;
-    std::vector<double> costs;
-    for (const PhaseDesc& d : phases) costs.push_back(tile_cost(d, Kch, var, share));
-    const double cost = lpt_makespan(phases, N * ceil_div(Mch, vmt), costs, num_cus * share);
-    if (best_v < 0 || cost < best_cost * 0.999) {
-      best_v = v;
-      best_cost = cost;
-      best = phases;
-    }
+    const bool per_class = nc > 1 && nc <= 4;
+    int64_t combos = emax + 1;
+    if (per_class)
+      for (size_t i = 1; i < nc; ++i) combos *= emax + 1;
+    for (int64_t code = 0; code < combos; ++code) {
+      std::vector<PhaseDesc> phases(nc);
+      bool ok = true;
+      int64_t rest = code;
+      for (size_t i = 0; i < nc && ok; ++i) {
+        int64_t e = code;
+        if (per_class) {
+          e = rest % (emax + 1);
+          rest /= emax + 1;
+        }
+        ok = fits[i * size_t(emax + 1) + size_t(e)] != 0;
+        phases[i] = cand[i * size_t(emax + 1) + size_t(e)];
+      }
+      if (!ok) continue;
+      // a two-per-CU variant only shares its CU when there are more tiles
+      // than CUs
+      int64_t ntiles = 0;
+      for (const PhaseDesc& d : phases)
+        ntiles += N * d.nbands * int64_t(d.ptiles) * ceil_div(Mch, vmt);
+      const int share = (var.half && ntiles > num_cus) ? 2 : 1;
+      std::vector<double> costs;
+      for (const PhaseDesc& d : phases) costs.push_back(tile_cost(d, Kch, var, share));
+      const double cost = lpt_makespan(phases, N * ceil_div(Mch, vmt), costs, num_cus * share);
+      if (best_v < 0 || cost < best_cost * 0.999) {
+        best_v = v;
+        best_cost = cost;
+        best = phases;
+      }
     }
   }
   if (best_v < 0) return CONV2D_ERR_UNSUPPORTED;
@@ -591,6 +615,15 @@ extern "C" int conv2d_check_params(const conv2d_params* p) {
 extern "C" int conv2d_describe_plan(const conv2d_params* p, int f16,
                                     conv2d_plan_info* out) {
   if (out == nullptr) return CONV2D_ERR_NULL_PTR;
+  if (c2b::pw::pw_shape(p)) {   // the 1x1 GEMM over all images' pixels
+    std::memset(out, 0, sizeof(*out));
+    out->launches = 1;
+    out->phases = 1;
+    c2b::pw::pw_describe(p, &out->tiles, &out->macs);
+    out->useful_macs = int64_t(p->batch) * p->out_channels * p->out_h * p->out_w *
+                       p->in_channels;
+    return CONV2D_OK;
+  }
   return c2b::build_plan(p, f16 ? 1 : 0, c2b::kDefaultCUs, nullptr, out);
 }
 

@@ -1,0 +1,130 @@
+// Geometry and index arithmetic of the 1x1 input-gradient GEMM
+// (pointwise_gemm.hip), shared by its kernel, its host replay and the
+// planner's description of a shape's launch.
+#pragma once
+
+#include <stdint.h>
+#include <string.h>
+
+#include "plan.hpp"
+
+#if defined(__HIP__) || defined(__HIPCC__)
+#include <hip/hip_runtime.h>
+#define PW_HD __host__ __device__ __forceinline__
+#else
+#define PW_HD inline
+#endif
+
+namespace c2b {
+namespace pw {
+
+constexpr int kBM = 128, kBN = 128;   // channels x pixels per tile
+constexpr int kBK = 32;               // output channels (k) per stage
+constexpr int kBufs = 4;              // stage buffers: loads run 3 stages ahead
+constexpr int kThreads = 256;
+constexpr int kWave = 64;             // each wave 64 x 64
+constexpr int kLoads = 4;             // 16-byte loads per wave, operand and stage
+constexpr int kStageBytes = (kBK * kBM + kBK * kBN) * 4;   // A then B
+constexpr uint32_t kPad = 0x80000000u;   // byte offset past every buffer range
+constexpr int64_t kI31 = int64_t(1) << 31;
+static_assert(kLoads * 4 * 2 == kBK, "a wave's loads cover its share of both operands");
+
+struct PWArgs {
+  const float* go;
+  const float* w;
+  float* gi;
+  int32_t M;    // input channels (rows of the product)
+  int32_t K;    // output channels (contraction)
+  int32_t P;    // pixels per image, H * W
+  int32_t Q;    // pixels of all images, N * H * W
+  int32_t TM, TN;
+};
+
+PW_HD int imin(int a, int b) { return a < b ? a : b; }
+
+// Tile (channel tile tm, pixel tile tn) of workgroup bid: the workgroups of
+// one XCD (bid mod 8) take one contiguous run of tiles, channel tiles
+// fastest.
+PW_HD void tile_of(const PWArgs& a, int bid, int* tm, int* tn) {
+  const int T = a.TM * a.TN;
+  const int q = T >> 3, r = T & 7, x = bid & 7, k = bid >> 3;
+  const int t = x * q + imin(x, r) + k;
+  *tm = t % a.TM;
+  *tn = t / a.TM;
+}
+
+// Load j (0 .. 15) of an operand's stage, lane l: k row 2j + l / 32 and
+// quad l % 32 of the row's 128 elements.  It lands at byte 1024 j + 16 l of
+// the operand's region, i.e. [k row][4 * quad .. +3].
+PW_HD int load_krow(int j, int l) { return 2 * j + l / 32; }
+PW_HD int load_quad(int l) { return l % 32; }
+
+// Byte offset in weight of the A quad (k row krow of stage st, channels
+// m0 + 4 quad ..), or kPad past Co or Ci.
+PW_HD uint32_t a_offset(const PWArgs& a, int st, int m0, int krow, int quad) {
+  const int k = st * kBK + krow, m = m0 + 4 * quad;
+  if (k >= a.K || m >= a.M) return kPad;
+  return (uint32_t(k) * uint32_t(a.M) + uint32_t(m)) * 4u;
+}
+
+// Element offset n * K * P + p of grad_out pixel q (k = 0), or -1 past Q.
+PW_HD int64_t b_base(const PWArgs& a, int q) {
+  if (q >= a.Q) return -1;
+  const int n = q / a.P, p = q - n * a.P;
+  return int64_t(n) * a.K * a.P + p;
+}
+
+// Byte offset in grad_out of the B quad (k row krow of stage st, pixels
+// q0 + 4 quad ..) whose first pixel has element offset `base` (b_base).
+PW_HD uint32_t b_offset(const PWArgs& a, int st, int64_t base, int krow) {
+  const int k = st * kBK + krow;
+  if (base < 0 || k >= a.K) return kPad;
+  return uint32_t((base + int64_t(k) * a.P) * 4);
+}
+
+// Matrix instruction q of a wave's 64 rows (or columns) covers elements
+// 4 c + q of lane c = c16: the element of lane c16 in block q.
+PW_HD int strided(int c16, int q) { return 4 * c16 + q; }
+
+// The shapes this path takes: kernel 1x1, stride 1, no padding, input
+// channels and pixels per image in multiples of 4, something to write, and
+// grad_out, grad_input and weight below 2^31 bytes (32-bit buffer offsets).
+// The tensors must also be 16-byte aligned (pw_applies).
+inline bool pw_shape(const conv2d_params* p) {
+  if (p == nullptr || validate_shape(p) != CONV2D_OK) return false;
+  if (p->kernel_h != 1 || p->kernel_w != 1 || p->stride != 1 || p->padding_h != 0 ||
+      p->padding_w != 0)
+    return false;
+  const int64_t P = int64_t(p->in_h) * p->in_w, N = p->batch;
+  if (p->in_channels % 4 != 0 || P % 4 != 0) return false;
+  if (N * p->out_channels * P * 4 >= kI31 || N * p->in_channels * P * 4 >= kI31) return false;
+  if (int64_t(p->out_channels) * p->in_channels * 4 >= kI31) return false;
+  return N * P * p->in_channels > 0;
+}
+
+inline void pw_plan(const conv2d_params* p, PWArgs* a) {
+  memset(a, 0, sizeof(*a));
+  a->M = int32_t(p->in_channels);
+  a->K = int32_t(p->out_channels);
+  a->P = int32_t(int64_t(p->in_h) * p->in_w);
+  a->Q = int32_t(int64_t(p->batch) * a->P);
+  a->TM = (a->M + kBM - 1) / kBM;
+  a->TN = (a->Q + kBN - 1) / kBN;
+}
+
+// Tiles and multiply-adds issued for a shape (pw_shape must hold).
+inline void pw_describe(const conv2d_params* p, int64_t* tiles, int64_t* macs) {
+  PWArgs a;
+  pw_plan(p, &a);
+  *tiles = int64_t(a.TM) * a.TN;
+  *macs = *tiles * kBM * kBN * int64_t((a.K + kBK - 1) / kBK) * kBK;
+}
+
+// Launch and host replay (pointwise_gemm.hip).
+bool pw_applies(const conv2d_params* p, const float* go, const float* w, const float* gi);
+int pw_launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
+              void* stream);
+int pw_check(const conv2d_params* p, char* msg, size_t len);
+
+}  // namespace pw
+}  // namespace c2b

@@ -188,7 +188,8 @@ int conv2d_planned_variant(const conv2d_params* p, int f16, int* variant_out);
  * the two processes' results bitwise identical), or -1 to return to the
  * planner's model choice.  Returns CONV2D_OK, the shape's CONV2D_ERR_* code,
  * CONV2D_ERR_NULL_PTR, or CONV2D_ERR_UNSUPPORTED (variant out of range, of
- * the other path, unable to tile the shape, or 4096 shapes already chosen).
+ * the other path, unable to tile the shape, 4096 shapes already chosen, or
+ * a variant for a shape on the 1x1 GEMM, which has none).
  * Host code (reads the device's compute-unit count once).
  */
 int conv2d_select_variant(const conv2d_params* p, int f16, int variant);

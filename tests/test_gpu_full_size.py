@@ -96,6 +96,9 @@ def test_grad_input_whole_tensor_model_and_tuned_plans(idx, f16):
     assert c2b.planned_variant(p, f16) == tuned
     got = run_gpu(sh, go, w, f16=f16)
     _check(got, idx, f16, _gi_ref, "tuned plan")
+    if tuned < 0:   # a shape on the 1x1 GEMM: no variant to choose
+        assert model == -1
+        return
     assert np.array_equal(got, run_gpu(sh, go, w, variant=tuned)), \
         "default call after tuning differs from the chosen variant"
     if tuned != model:

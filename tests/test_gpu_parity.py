@@ -243,3 +243,63 @@ def test_tune_picks_a_variant_and_the_default_call_uses_it(f16):
     got = run_gpu(sh, go, w, f16=f16)                          # default call, tuned plan
     assert not np.any(np.isnan(got))
     assert rel_err(got, ref) <= TOL[f16]
+
+
+# ---- 1x1, stride 1, unpadded: the GEMM over all images' pixels --------------
+# Channel tiles of 128 with a ragged last one, pixel tiles of 128 that cross
+# image boundaries, a contraction that is not a multiple of the 32-channel
+# stage, Co = 1, images smaller than a quad row.
+PW_SHAPES = [
+    ConvShape("pw_ci4_2x2", 3, 4, 2, 2, 5, 1, 1, 1, 0, 0, 2, 2, dist="uniform"),
+    ConvShape("pw_ci36_7x4", 5, 36, 7, 4, 33, 1, 1, 1, 0, 0, 7, 4, dist="uniform"),
+    ConvShape("pw_ci132_10x20", 2, 132, 10, 20, 70, 1, 1, 1, 0, 0, 10, 20, dist="uniform"),
+    ConvShape("pw_ci256_co1", 3, 256, 14, 14, 1, 1, 1, 1, 0, 0, 14, 14, dist="uniform"),
+    ConvShape("pw_ci128_co40_12x12", 9, 128, 12, 12, 40, 1, 1, 1, 0, 0, 12, 12,
+              dist="uniform"),
+]
+
+
+@pytest.mark.parametrize("sh", PW_SHAPES, ids=[s.name for s in PW_SHAPES])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_pointwise_gemm_shapes(sh, f16):
+    _say("case pointwise", sh.name, "f16" if f16 else "fp32")
+    p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels,
+                        sh.kernel_h, sh.kernel_w, sh.stride, sh.padding_h, sh.padding_w)
+    assert c2b.planned_variant(p, f16) == -1          # the GEMM path, not a variant
+    rng = np.random.default_rng(zlib.crc32(sh.name.encode()))
+    go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+    ref = _oracle(sh, go, w)
+    got = run_gpu(sh, go, w, f16=f16)
+    assert not np.any(np.isnan(got)), "unwritten grad_input elements"
+    err = rel_err(got, ref)
+    _say("  rel err", err)
+    assert err <= TOL[f16], err
+    if f16:
+        assert rel_err(got, _oracle(sh, round_f16(go), round_f16(w))) <= 1e-5
+    gi_, wi_ = draw_integers(sh, 9)
+    got_i = run_gpu(sh, gi_, wi_, f16=f16)
+    assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_))
+
+
+def test_pointwise_gemm_misaligned_tensor_takes_the_variant_kernels():
+    """A grad_out that is not 16-byte aligned cannot use the 16-byte loads:
+    the call must still be right (it runs on the variant kernels)."""
+    import torch
+    sh = PW_SHAPES[1]
+    rng = np.random.default_rng(3)
+    go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+    dev = torch.device("cuda", 0)
+    n = go.size
+    store = torch.zeros(n + 1, dtype=torch.float32, device=dev)
+    store[1:] = torch.from_numpy(go.ravel()).to(dev)
+    tgo = store[1:].view(sh.go_shape)                   # 4 bytes past a 256-byte boundary
+    assert tgo.data_ptr() % 16 == 4
+    tw = torch.from_numpy(w).to(dev)
+    gi = torch.full(sh.gi_shape, float("nan"), device=dev)
+    p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels, 1, 1,
+                        1, 0, 0)
+    c2b.grad_input_into(gi, tgo, tw, p)
+    torch.cuda.synchronize()
+    assert rel_err(gi.cpu().numpy(), _oracle(sh, go, w)) <= TOL[False]
