@@ -188,9 +188,11 @@ class Oracle:
             np.ascontiguousarray(rows, dtype=np.int64)
         if sel.size and (sel.min() < 0 or sel.max() >= M):
             raise IndexError("row index out of range")
+        # each row once: the C routine computes its rows in parallel, in place
+        todo = np.ascontiguousarray(np.unique(sel), dtype=np.int64)
         c = np.zeros((M, N), dtype=np.float64)
         self._lib.oracle_rms_norm_matmul(_ptr(xx), _ptr(gg), _ptr(ww), _ptr(c), M, K, N,
-                                         float(eps), sel.ctypes.data_as(_IP), int(sel.size))
+                                         float(eps), todo.ctypes.data_as(_IP), int(todo.size))
         return c if rows is None else c[sel]
 
     def attention_lse(self, q, k, num_kv_heads, window=0, causal=True):
