@@ -45,7 +45,8 @@ PEAK_HBM_GBS = 8000.0
 _CSRC = "conv2d_backward_implicit_amd/csrc/"
 # the sources each entry point's kernels and launch set-up are built from
 KERNEL_SOURCES = {
-    "grad_input": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp")],
+    "grad_input": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp",
+                                        "pointwise_gemm.hip", "pointwise.hpp")],
     "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp",
                                      "forward_gemm.hip")],
     "grad_weight": [_CSRC + f for f in ("grad_weight.hip", "tile_index.hpp", "plan.hpp")],

@@ -24,7 +24,8 @@ __all__ = [
     "Conv2dParams", "Conv2dError", "PlanInfo", "grad_input", "grad_input_into",
     "conv2d_grad_input", "conv2d_grad_input_f16", "check_params",
     "describe_plan", "check_indexing", "check_indexing_variant", "num_variants",
-    "variant_is_f16", "variant_uses_column_taps", "conv2d_grad_input_variant",
+    "variant_is_f16", "variant_uses_column_taps", "variant_is_multi_class",
+    "conv2d_grad_input_variant",
     "tune", "planned_variant", "select_variant", "describe_plan_variant",
     "forward", "forward_into", "conv2d_forward", "conv2d_forward_f16",
     "conv2d_forward_variant", "tune_forward", "planned_forward_variant",
@@ -57,6 +58,7 @@ EXPORTED_SYMBOLS = (
     "conv2d_num_variants",
     "conv2d_variant_is_f16",
     "conv2d_variant_uses_column_taps",
+    "conv2d_variant_is_multi_class",
     "conv2d_grad_input_variant",
     "conv2d_check_indexing_variant",
     "conv2d_tune",
@@ -204,6 +206,8 @@ def load_library():
         lib.conv2d_variant_is_f16.restype = ctypes.c_int
         lib.conv2d_variant_uses_column_taps.argtypes = [ctypes.c_int]
         lib.conv2d_variant_uses_column_taps.restype = ctypes.c_int
+        lib.conv2d_variant_is_multi_class.argtypes = [ctypes.c_int]
+        lib.conv2d_variant_is_multi_class.restype = ctypes.c_int
         lib.conv2d_tune.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, P,
                                     ctypes.c_int, ctypes.c_void_p,
                                     ctypes.POINTER(ctypes.c_int)]
@@ -346,6 +350,12 @@ def variant_is_f16(variant: int) -> int:
 def variant_uses_column_taps(variant: int) -> int:
     """1 (column taps in the matrix rows), 0, or a negative status."""
     return int(load_library().conv2d_variant_uses_column_taps(int(variant)))
+
+
+def variant_is_multi_class(variant: int) -> int:
+    """1 (all four classes of a stride-2 shape per tile), 0, or a negative
+    status."""
+    return int(load_library().conv2d_variant_is_multi_class(int(variant)))
 
 
 def conv2d_grad_input(grad_out_ptr: int, weight_ptr: int, grad_input_ptr: int,

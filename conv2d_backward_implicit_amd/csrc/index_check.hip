@@ -37,7 +37,7 @@ struct Failure {
     }                                                           \
   } while (0)
 
-template <int WM, int WN, int MB, int NBW, int SF, bool CM>
+template <int WM, int WN, int MB, int NBW, int SF, bool CM, bool MC>
 void check_launch(const LaunchArgs& a, const conv2d_params& prm,
                   std::vector<unsigned char>& written) {
   using G = MMGeom<WM, WN, MB, NBW, SF>;
@@ -65,6 +65,10 @@ void check_launch(const LaunchArgs& a, const conv2d_params& prm,
                 c.npx);
     C2B_REQUIRE(a.cm == (CM ? 1 : 0) && (CM ? a.cit * a.twm <= MT : a.cit == MT),
                 "launch matrix rows: cm %d cit %d twm %d", a.cm, a.cit, a.twm);
+    C2B_REQUIRE(a.mc == (MC ? 1 : 0) && (MC ? a.nphases == 1 && P.mct == KHW && a.S == 2 &&
+                                                  !fwd && P.ngroups == 1 && P.tg == KHW
+                                            : P.mct == 0),
+                "multi-class launch fields");
     if (CM) {
       // whole rows of the band per tile, and one lane per window point
       C2B_REQUIRE(c.p0 % P.wb == 0 && c.npx % P.wb == 0, "bid %d: cm tile not whole rows", bid);
@@ -98,8 +102,9 @@ void check_launch(const LaunchArgs& a, const conv2d_params& prm,
       const int mg = wave % WM, ng = wave / WM, g = lane >> 4, c16 = lane & 15;
       int bb[NBW], aq[MB];
       for (int b = 0; b < NBW; ++b)
-        bb[b] = (g * SLOTS + (CM ? window_base_cm(c, mm_local(b, ng, c16, WN))
-                                 : window_base(c, mm_local(b, ng, c16, WN)))) * 16;
+        bb[b] = (g * SLOTS + (MC   ? window_pixel(c, mm_local(b, ng, c16, WN))
+                              : CM ? window_base_cm(c, mm_local(b, ng, c16, WN))
+                                   : window_base(c, mm_local(b, ng, c16, WN)))) * 16;
       for (int m = 0; m < MB; ++m) aq[m] = (g * QP + mm_channel(m, mg, c16, MB) * 4 * PT) * 4;
       for (int st = 0; st < c.nstages; ++st) {
         int co0, grp;
@@ -188,6 +193,9 @@ void check_launch(const LaunchArgs& a, const conv2d_params& prm,
                 C2B_REQUIRE(l < P.tw && cl < a.cit && jt < P.th, "cm weight cell %d", e);
                 want = (int64_t(co0 + co) * a.Ci + c.ci0 + cl) * KHW +
                        (P.rh + a.S * jt) * a.KW + (P.rw + a.S * l);
+              } else if (MC) {
+                // every kernel tap in the weight's own order
+                want = (int64_t(co0 + co) * a.Ci + c.ci0 + m) * KHW + tap0 + t;
               } else {
                 want = (int64_t(co0 + co) * a.Ci + c.ci0 + m) * KHW + tap_kidx(P, a, tap0 + t);
               }
@@ -195,6 +203,56 @@ void check_launch(const LaunchArgs& a, const conv2d_params& prm,
               C2B_REQUIRE(wi == want && wi >= 0 && wi < w_size, "weight element");
             }
           }
+        }
+        if (MC) {
+          // multi-class unit reads, in the kernel's order: for each channel
+          // group, class and class tap, the class's blocks at its window
+          // offset and the weights of kernel tap (rh + 2j, rw + 2l); the
+          // classes' taps must cover every kernel tap once
+          std::vector<int> tap_seen(size_t(KHW), 0);
+          for (int cgi = 0; cgi < CG; ++cgi)
+            for (int k = 0; k < kMCClasses; ++k) {
+              const MCClass& K = a.mcls[k];
+              for (int j = 0; j < K.th; ++j)
+                for (int l = 0; l < K.tw; ++l) {
+                  const int kh = K.rh + 2 * j, kw = K.rw + 2 * l, kidx = kh * a.KW + kw;
+                  C2B_REQUIRE(kh < a.KH && kw < a.KW, "class %d tap (%d,%d)", k, j, l);
+                  if (cgi == 0) ++tap_seen[size_t(kidx)];
+                  const int ao = cgi * QP * 16 + kidx * 16;
+                  for (int m = 0; m < MB; ++m) {
+                    const int byte = aq[m] + ao;
+                    C2B_REQUIRE(byte >= 0 && byte % 16 == 0 && byte + 16 <= 4 * CG * QP * 4,
+                                "weight read %d", byte);
+                    const int e = byte / 4, cq = e / QP, r = e % QP;
+                    C2B_REQUIRE(cq == 4 * cgi + g && r / (4 * PT) == mm_channel(m, mg, c16, MB) &&
+                                    (r % (4 * PT)) / 4 == kidx && r % 4 == 0,
+                                "weight of unit");
+                  }
+                  const int wo = cgi * SLOTS * 64 + (K.e * c.roww + K.f) * 16 +
+                                 tap_window_offset(c, j, l) * 16;
+                  for (int b = 0; b < NBW; ++b) {
+                    const int byte = bb[b] + wo;
+                    C2B_REQUIRE(byte >= 0 && byte % 16 == 0 && byte + 16 <= P.wfl * 4,
+                                "window read %d", byte);
+                    const int cell = byte / 16, cq = cell / SLOTS, slot = cell % SLOTS;
+                    C2B_REQUIRE(cq == 4 * cgi + g && slot < c.R * c.roww,
+                                "window read of class %d outside the window", k);
+                    const int local = mm_local(b, ng, c16, WN);
+                    const int po = mc_output_offset(c, a, K, local);
+                    if (po < 0) continue;
+                    // the gather rule: grad_out row (ih + padding_h - kh) / 2
+                    const int ih = po / a.W, iw = po % a.W;
+                    const int row = c.oh_base + slot / c.roww, col = c.ow_base + slot % c.roww;
+                    C2B_REQUIRE(2 * row == ih + a.PH - kh && 2 * col == iw + a.PW - kw,
+                                "class %d tap (%d,%d) reads the wrong grad_out element", k, j,
+                                l);
+                  }
+                }
+            }
+          for (int64_t t = 0; t < KHW; ++t)
+            C2B_REQUIRE(tap_seen[size_t(t)] == 1, "kernel tap %d taken %d times", int(t),
+                        tap_seen[size_t(t)]);
+          continue;
         }
         // unit reads, in the kernel's order (cm: row taps only)
         const int twl = CM ? 1 : P.tw;
@@ -273,6 +331,51 @@ void check_launch(const LaunchArgs& a, const conv2d_params& prm,
           }
         continue;   // part 2 (the column-tap sums) runs per tile below
       }
+      if (MC) {
+        // the kernel's paired stores: row class hk's two classes at a grid
+        // point write the even and odd column of one input row; each must be
+        // the pixel its class holds there (mc_output_offset) and inside it
+        for (int hk = 0; hk < 2; ++hk)
+          for (int b = 0; b < NBW; ++b) {
+            const int local = mm_local(b, ng, c16, WN);
+            int ih, col0;
+            bool even_ok, odd_ok;
+            const bool any = mc_pair_pixel(c, a, hk, local, &ih, &col0, &even_ok, &odd_ok);
+            for (int kk = 0; kk < 2; ++kk) {
+              const int k = 2 * hk + kk;
+              const int po_k = mc_output_offset(c, a, a.mcls[k], local);
+              const bool even_k = a.mcls[k].iw0 == 0;
+              const bool ok_k = any && (even_k ? even_ok : odd_ok);
+              C2B_REQUIRE(ok_k == (po_k >= 0), "class %d store mask", k);
+              if (ok_k)
+                C2B_REQUIRE(po_k == ih * a.W + col0 + (even_k ? 0 : 1) && col0 % 2 == 0,
+                            "class %d store position", k);
+            }
+          }
+        // every class's pixels at the tile's grid points
+        for (int k = 0; k < kMCClasses; ++k) {
+          const MCClass& K = a.mcls[k];
+          for (int b = 0; b < NBW; ++b) {
+            const int po = mc_output_offset(c, a, K, mm_local(b, ng, c16, WN));
+            if (po < 0) continue;
+            const int ih = po / a.W, iw = po % a.W;
+            C2B_REQUIRE(((ih + a.PH) % 2) == K.rh && ((iw + a.PW) % 2) == K.rw && ih < a.H &&
+                            iw < a.W,
+                        "pixel (%d,%d) outside class %d", ih, iw, k);
+            for (int m = 0; m < MB; ++m)
+              for (int r = 0; r < 4; ++r) {
+                const int cc = c.ci0 + (mg * MB + m) * 16 + 4 * g + r;
+                if (cc >= a.Ci) continue;
+                const int64_t gi = int64_t(c.n) * a.Ci * HW + int64_t(cc) * HW + po;
+                C2B_REQUIRE(gi >= 0 && gi < int64_t(written.size()), "grad_input write");
+                C2B_REQUIRE(written[gi] == 0, "grad_input element %lld written twice",
+                            (long long)gi);
+                written[gi] = 1;
+              }
+          }
+        }
+        continue;
+      }
       // epilogue
       for (int b = 0; b < NBW; ++b) {
         const int po = output_offset(c, a, mm_local(b, ng, c16, WN));
@@ -333,7 +436,7 @@ template <int V>
 void check_variant(const LaunchArgs& la, const conv2d_params& prm,
                    std::vector<unsigned char>& written) {
   constexpr Variant v = kVariants[V];
-  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v), v.cm != 0>(la, prm, written);
+  check_launch<v.wm, v.wn, v.mb, v.nbw, stage_floats(v), v.cm != 0, v.mc != 0>(la, prm, written);
 }
 
 template <int... Vs>

@@ -79,10 +79,11 @@ __device__ __forceinline__ f16x8 join(f16x4 lo, f16x4 hi) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <bool FWD, bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
+template <bool FWD, bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM, bool MC>
 __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
   static_assert(!CM || (WM == 1 && MB == 1), "cm: one matrix block of rows");
   static_assert(!FWD || !CM, "forward launches have no cm variant");
+  static_assert(!MC || (!FWD && !CM && !F16), "multi-class: fp32 input gradient only");
   using G = MMGeom<WM, WN, MB, NBW, SF>;
   constexpr int MT = G::kMT, NW = G::kWaves, NJ = G::kBatches;
   constexpr int kStageFloats = SF;   // this instance's stage buffer
@@ -216,17 +217,23 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
   int bb[NBW];
 #pragma unroll
   for (int b = 0; b < NBW; ++b)
-    bb[b] = (g * P.slots + (CM ? window_base_cm(c, mm_local(b, ng, c16, WN))
-                               : window_base(c, mm_local(b, ng, c16, WN)))) * 16;
+    bb[b] = (g * P.slots + (MC   ? window_pixel(c, mm_local(b, ng, c16, WN))
+                            : CM ? window_base_cm(c, mm_local(b, ng, c16, WN))
+                                 : window_base(c, mm_local(b, ng, c16, WN)))) * 16;
   int aq[MB];
 #pragma unroll
   for (int m = 0; m < MB; ++m) aq[m] = (g * P.qp + mm_channel(m, mg, c16, MB) * 4 * P.pt) * 4;
 
-  f32x4 acc[MB][NBW];
+  // one accumulator set, or (multi-class) one per class
+  constexpr int NCL = MC ? kMCClasses : 1;
+  f32x4 accs[NCL][MB][NBW];
 #pragma unroll
-  for (int m = 0; m < MB; ++m)
+  for (int k = 0; k < NCL; ++k)
 #pragma unroll
-    for (int b = 0; b < NBW; ++b) acc[m][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) accs[k][m][b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+  auto& acc = accs[0];
 
   // Blocks of this wave that hold at least one of the tile's pixels (or cm
   // points): a prefix of its NBW blocks.  A tile whose pixel count is not a
@@ -260,21 +267,22 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
   };
   // Products of one unit: blocks 0 .. NBW-2, then the last block if it holds
   // a pixel (every accumulator still takes its four k values in order).
-  auto mma_f32 = [&](const f32x4(&bv)[NBW], const f32x4(&aw)[MB]) __attribute__((always_inline)) {
+  auto mma_f32 = [&](f32x4(&ac)[MB][NBW], const f32x4(&bv)[NBW],
+                     const f32x4(&aw)[MB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int m = 0; m < MB; ++m)
 #pragma unroll
         for (int b = 0; b < NBW - 1; ++b)
-          acc[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[b][q], acc[m][b], 0, 0, 0);
+          ac[m][b] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[b][q], ac[m][b], 0, 0, 0);
     if (last_on) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
 #pragma unroll
         for (int m = 0; m < MB; ++m)
-          acc[m][NBW - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[NBW - 1][q],
-                                                                acc[m][NBW - 1], 0, 0, 0);
+          ac[m][NBW - 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(aw[m][q], bv[NBW - 1][q],
+                                                               ac[m][NBW - 1], 0, 0, 0);
     }
   };
   auto mma_f16_pair = [&](const f32x4(&bv0)[NBW], const f32x4(&aw0)[MB],
@@ -310,7 +318,37 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
   // Multiply stage st out of buffer st&1 (the copies run after it, in the
   // stage loop below).  Units run channel group by channel group, taps in
   // class order inside a group (cm variants: row taps only).
+  // Multi-class stage st: for each channel group, each class, each tap
+  // (j, l) of the class (kernel tap (rh + 2j, rw + 2l)): the class's blocks
+  // at its window offset, into its accumulator set.
+  auto compute_mc = [&](int st) __attribute__((always_inline)) {
+    const char* Hb = reinterpret_cast<const char*>(lds + (st & 1) * kStageFloats);
+    const char* Ab = Hb + P.wfl * 4;
+#pragma unroll 1
+    for (int cgi = 0; cgi < P.cg; ++cgi) {
+#pragma unroll
+      for (int k = 0; k < NCL; ++k) {
+        const MCClass& K = a.mcls[k];
+        const int wk = cgi * P.slots * 64 + (K.e * c.roww + K.f) * 16;
+        // (not unrolled: unrolled tap loops hold several units' operands)
+#pragma unroll 1
+        for (int j = 0; j < K.th; ++j)
+#pragma unroll 1
+          for (int l = 0; l < K.tw; ++l) {
+            const int kidx = (K.rh + 2 * j) * a.KW + (K.rw + 2 * l);
+            f32x4 bv[NBW], aw[MB];
+            read_unit(Hb, Ab, wk + tap_window_offset(c, j, l) * 16,
+                      cgi * P.qp * 16 + kidx * 16, bv, aw);
+            mma_f32(accs[k], bv, aw);
+          }
+      }
+    }
+  };
   auto compute = [&](int st) __attribute__((always_inline)) {
+    if constexpr (MC) {
+      compute_mc(st);
+      return;
+    }
     const int buf = st & 1;
     int co0, grp;
     stage_split(c, st, &co0, &grp);
@@ -342,7 +380,7 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
       for (int u = 0; u < units; ++u) {
         f32x4 bv[NBW], aw[MB];
         read_unit(Hb, Ab, wo(), ao(), bv, aw);
-        mma_f32(bv, aw);
+        mma_f32(acc, bv, aw);
         advance();
       }
     } else {
@@ -422,6 +460,42 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
     }
     return;
   }
+  if constexpr (MC) {
+    // register r of block (m, b) of class k holds input channel
+    // (mg*MB + m)*16 + 4g + r at the block's grid point.  The two classes of
+    // a row class hold adjacent columns there, so a lane stores them
+    // together (8 bytes) and 16 lanes fill whole lines; with an odd width
+    // (or a grad_input not 8-byte aligned) the pair is stored as two floats.
+    const bool pairs =
+        (a.W & 1) == 0 && (reinterpret_cast<uintptr_t>(a.gi) & 7) == 0;
+#pragma unroll
+    for (int hk = 0; hk < 2; ++hk)
+#pragma unroll
+      for (int b = 0; b < NBW; ++b) {
+        int ih, col0;
+        bool even_ok, odd_ok;
+        if (!mc_pair_pixel(c, a, hk, mm_local(b, ng, c16, WN), &ih, &col0, &even_ok, &odd_ok))
+          continue;
+        const bool k0_even = a.mcls[2 * hk].iw0 == 0;
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int cc = c.ci0 + (mg * MB + m) * 16 + 4 * g + r;
+            if (cc >= a.Ci) continue;
+            const float v0 = accs[2 * hk][m][b][r], v1 = accs[2 * hk + 1][m][b][r];
+            const float ve = k0_even ? v0 : v1, vo = k0_even ? v1 : v0;
+            float* dst = gi_n + cc * HW + ih * a.W + col0;
+            if (pairs && even_ok && odd_ok) {
+              *reinterpret_cast<float2*>(dst) = make_float2(ve, vo);
+            } else {
+              if (even_ok) dst[0] = ve;
+              if (odd_ok) dst[1] = vo;
+            }
+          }
+      }
+    return;
+  }
   // epilogue: register r of block (m, b) holds input channel
   // (mg*MB + m)*16 + 4g + r, pixel (b*WN + ng)*16 + c16
 #pragma unroll
@@ -439,24 +513,24 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
 }
 
 // The input-gradient kernel, one instantiation per variant.
-template <bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM>
-__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void grad_input_mm_kernel(
+template <bool F16, int WM, int WN, int MB, int NBW, int SF, bool CM, bool MC>
+__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloatsHalf ? 2 : 1) void grad_input_mm_kernel(
     const LaunchArgs a) {
-  mm_body<false, F16, WM, WN, MB, NBW, SF, CM>(a);
+  mm_body<false, F16, WM, WN, MB, NBW, SF, CM, MC>(a);
 }
 
 // The forward convolution on the same body (roles exchanged, plan.hpp), one
 // instantiation per variant without cm.
 template <bool F16, int WM, int WN, int MB, int NBW, int SF>
-__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloats ? 1 : 2) void conv2d_forward_mm_kernel(
+__global__ __launch_bounds__(64 * WM * WN, SF == kStageFloatsHalf ? 2 : 1) void conv2d_forward_mm_kernel(
     const LaunchArgs a) {
-  mm_body<true, F16, WM, WN, MB, NBW, SF, false>(a);
+  mm_body<true, F16, WM, WN, MB, NBW, SF, false, false>(a);
 }
 
 template <int V>
 void launch_variant(const LaunchArgs& la, hipStream_t st) {
   constexpr Variant v = kVariants[V];
-  if constexpr (v.cm == 0) {
+  if constexpr (v.cm == 0 && v.mc == 0) {
     if (la.fwd) {
       hipLaunchKernelGGL((conv2d_forward_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw,
                                                    stage_floats(v)>),
@@ -465,7 +539,7 @@ void launch_variant(const LaunchArgs& la, hipStream_t st) {
     }
   }
   hipLaunchKernelGGL((grad_input_mm_kernel<v.f16 != 0, v.wm, v.wn, v.mb, v.nbw, stage_floats(v),
-                                           v.cm != 0>),
+                                           v.cm != 0, v.mc != 0>),
                      dim3(la.total_tiles), dim3(64 * v.wm * v.wn), 0, st, la);
 }
 

@@ -6,6 +6,7 @@
 // out_w must equal the forward-convolution extents, so that grad_input is the
 // exact adjoint of that forward convolution.
 #include <algorithm>
+#include <climits>
 #include <cstdint>
 #include <cstring>
 
@@ -128,6 +129,47 @@ static void make_forward_class(const conv2d_params* p, std::vector<PhaseDesc>* o
   if (d.hp > 0 && d.wp > 0) out->push_back(d);
 }
 
+// The four classes of a stride-2 shape as one multi-class tiling
+// (Variant::mc): `u` describes the tiling over the grid of class pixels
+// (i', j') and the window all classes share, `mcls` each class.  Class k
+// reads grad_out row i' + ch_k - j at tap j; over the classes and their taps
+// these rows run from i' + lo to i' + max ch_k, lo = min (ch_k - th_k + 1),
+// so the union window has th = max ch_k - lo + 1 rows per grid row and class
+// k's tap j sits e_k - j rows into it, e_k = ch_k - lo (columns alike).
+// False unless the shape has stride 2, all four classes have pixels and
+// taps, and the kernel has at most kMaxStageTaps taps (one stage holds them
+// all).
+static bool make_mc_union(const conv2d_params* p, const std::vector<PhaseDesc>& classes,
+                          PhaseDesc* u, MCClass* mcls) {
+  if (p->stride != 2 || classes.size() != size_t(kMCClasses)) return false;
+  if (int64_t(p->kernel_h) * p->kernel_w > kMaxStageTaps) return false;
+  int32_t hch = INT32_MIN, hlo = INT32_MAX, wch = INT32_MIN, wlo = INT32_MAX, hp = 0, wp = 0;
+  for (const PhaseDesc& d : classes) {
+    if (d.th == 0 || d.tw == 0) return false;
+    hch = std::max(hch, d.ch);
+    hlo = std::min(hlo, d.ch - d.th + 1);
+    wch = std::max(wch, d.cw);
+    wlo = std::min(wlo, d.cw - d.tw + 1);
+    hp = std::max(hp, d.hp);
+    wp = std::max(wp, d.wp);
+  }
+  std::memset(u, 0, sizeof(*u));
+  u->hp = hp;
+  u->wp = wp;
+  u->th = hch - hlo + 1;
+  u->tw = wch - wlo + 1;
+  u->ch = hch;
+  u->cw = wch;
+  u->ss = 1;
+  u->kstep = 1;
+  u->mct = int32_t(p->kernel_h * p->kernel_w);
+  for (int k = 0; k < kMCClasses; ++k) {
+    const PhaseDesc& d = classes[size_t(k)];
+    mcls[k] = MCClass{d.ih0, d.iw0, d.hp, d.wp, d.th, d.tw, d.rh, d.rw, d.ch - hlo, d.cw - wlo};
+  }
+  return true;
+}
+
 static LaunchArgs launch_header(const conv2d_params* p, int64_t ciblocks, int64_t cit, int cm,
                                 int64_t twm, int op) {
   LaunchArgs la;
@@ -203,10 +245,15 @@ static int finalize_divisors(PhaseDesc* d) {
 // kMaxPhasesPerLaunch classes.
 static int emit_launches(const conv2d_params* p, int64_t ciblocks, int64_t cit, int64_t twm,
                          int variant, const std::vector<PhaseDesc>& phases,
-                         std::vector<LaunchArgs>* launches, conv2d_plan_info* info, int op) {
+                         std::vector<LaunchArgs>* launches, conv2d_plan_info* info, int op,
+                         const MCClass* mcls) {
   for (size_t base = 0; base < phases.size(); base += kMaxPhasesPerLaunch) {
     LaunchArgs la = launch_header(p, ciblocks, cit, kVariants[variant].cm, twm, op);
     la.variant = variant;
+    if (kVariants[variant].mc) {
+      la.mc = 1;
+      for (int k = 0; k < kMCClasses; ++k) la.mcls[k] = mcls[k];
+    }
     int64_t total = 0;
     const size_t end = std::min(phases.size(), base + kMaxPhasesPerLaunch);
     for (size_t i = base; i < end; ++i) {
@@ -347,10 +394,16 @@ double active_blocks(const Variant& v, int64_t pts) {
   return sum / v.wn;
 }
 
+// Taps of a class's contraction: row taps (cm), every kernel tap (the
+// multi-class union), or the class's taps.
+int64_t stage_taps(const PhaseDesc& d, const Variant& v) {
+  return v.cm ? int64_t(d.th) : d.mct > 0 ? int64_t(d.mct) : int64_t(d.th) * d.tw;
+}
+
 double tile_cost(const PhaseDesc& d, int64_t Co, const Variant& v, int share) {
   (void)Co;
   if (d.th == 0) return kTileCycles;
-  const int64_t ntaps = v.cm ? int64_t(d.th) : int64_t(d.th) * d.tw;
+  const int64_t ntaps = stage_taps(d, v);
   const double wps = v.wm * v.wn / 4.0;
   const double nbw = v.cm ? double(v.nbw) : active_blocks(v, d.ntv);
   const double mfma = wps * v.mb * nbw * (v.f16 ? 8.0 : 128.0) * share;
@@ -385,13 +438,14 @@ bool tile_class(PhaseDesc* d, const Variant& v, int64_t Co, int64_t OHOW, int64_
     d->cg = d->tg = d->ngroups = d->nchunks = d->slots = d->pt = d->qp = d->wfl = d->used = 0;
     return true;
   }
-  const int64_t ntaps = v.cm ? int64_t(d->th) : int64_t(d->th) * d->tw;
+  const int64_t ntaps = stage_taps(*d, v);
   const int64_t cg_useful = std::max<int64_t>(1, ceil_div(Co, 16));
   bool found = false;
   double best = 0.0;
   PhaseDesc out = *d;
   int64_t last_tg = -1;
-  for (int64_t ng = ceil_div(ntaps, kMaxStageTaps); ng <= ntaps; ++ng) {
+  // a multi-class stage holds every tap (one tap group)
+  for (int64_t ng = ceil_div(ntaps, kMaxStageTaps); ng <= (d->mct > 0 ? 1 : ntaps); ++ng) {
     const int64_t tg = ceil_div(ntaps, ng);         // fewest taps for this group count
     if (tg == last_tg) continue;
     last_tg = tg;
@@ -513,6 +567,11 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   auto channels_per_tile = [&](const Variant& var) {
     return var.cm ? cm_cit : 16 * int64_t(var.wm) * var.mb;
   };
+  // the four classes of a stride-2 input gradient as one multi-class tiling
+  std::vector<PhaseDesc> mc_union(1);
+  MCClass mcls[kMCClasses];
+  std::memset(mcls, 0, sizeof(mcls));
+  const bool mc_ok = !fwd && !f16 && make_mc_union(p, classes, &mc_union[0], mcls);
 
   int best_v = -1;
   double best_cost = 0.0;
@@ -521,6 +580,8 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     const Variant& var = kVariants[v];
     if (force_variant >= 0 ? v != force_variant : var.f16 != (f16 ? 1 : 0)) continue;
     if (fwd && var.cm) continue;
+    if (var.mc && !mc_ok) continue;
+    const std::vector<PhaseDesc>& vclasses = var.mc ? mc_union : classes;
     const int64_t vmt = channels_per_tile(var);
     if (vmt < 1) continue;
     // Each class with the fewest tiles per band, or up to kMaxExtraTiles
@@ -529,12 +590,12 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     // light class can take smaller tiles that fill the CUs the heavy classes
     // leave idle); others try the same choice for every class.
     const int64_t emax = var.cm ? 0 : kMaxExtraTiles;
-    const size_t nc = classes.size();
+    const size_t nc = vclasses.size();
     std::vector<PhaseDesc> cand(nc * size_t(emax + 1));
     std::vector<char> fits(nc * size_t(emax + 1), 0);
     for (size_t i = 0; i < nc; ++i)
       for (int64_t e = 0; e <= emax; ++e) {
-        PhaseDesc d = classes[i];
+        PhaseDesc d = vclasses[i];
         fits[i * size_t(emax + 1) + size_t(e)] =
             tile_class(&d, var, Kch, src_plane, cstride, e) ? 1 : 0;
         cand[i * size_t(emax + 1) + size_t(e)] = d;
@@ -585,15 +646,15 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
     if (tiles >= kI31) return CONV2D_ERR_OVERFLOW;
     d.tiles = int32_t(tiles);
     if (info) {
-      info->phases += 1;
+      info->phases += bv.mc ? kMCClasses : 1;
       if (d.th == 0) info->zero_phases += 1;
       if (d.th > 0) {
         // lanes the kernel multiplies: blocks past a short wave's last one
-        // are skipped (mm_body)
+        // are skipped (mm_body); a multi-class tile multiplies each class's
+        // blocks at that class's taps, kH x kW taps in all
         const double blocks = bv.cm ? double(bv.nbw) : active_blocks(bv, d.ntv);
         const int64_t lanes = int64_t(16.0 * blocks * bv.wn + 0.5);
-        const int64_t kpad =
-            int64_t(d.nchunks) * 16 * d.cg * int64_t(d.th) * (bv.cm ? 1 : d.tw);
+        const int64_t kpad = int64_t(d.nchunks) * 16 * d.cg * stage_taps(d, bv);
         info->macs += tiles * lanes * bmt * kpad;
       }
     }
@@ -601,7 +662,7 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
   std::stable_sort(best.begin(), best.end(), [&](const PhaseDesc& a, const PhaseDesc& b) {
     return tile_cost(a, Kch, bv, 1) > tile_cost(b, Kch, bv, 1);
   });
-  return emit_launches(p, bci, bcit, twm, best_v, best, launches, info, op);
+  return emit_launches(p, bci, bcit, twm, best_v, best, launches, info, op, mcls);
 }
 
 }  // namespace c2b
@@ -660,6 +721,11 @@ extern "C" int conv2d_variant_is_f16(int variant) {
 extern "C" int conv2d_variant_uses_column_taps(int variant) {
   if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
   return c2b::kVariants[variant].cm;
+}
+
+extern "C" int conv2d_variant_is_multi_class(int variant) {
+  if (variant < 0 || variant >= c2b::kNumVariants) return CONV2D_ERR_UNSUPPORTED;
+  return c2b::kVariants[variant].mc;
 }
 
 extern "C" const char* conv2d_status_string(int status) {

@@ -78,6 +78,8 @@ struct PhaseDesc {
   int32_t qp;          // weight floats per channel quad (multiple of 64)
   int32_t wfl;         // window floats of a stage buffer: 16 * cg * slots
   int32_t used;        // floats of a stage buffer copied: wfl + 4 * cg * qp
+  int32_t mct;         // multi-class union: taps of the stage contraction (kH * kW,
+                       // in the weight's own order); 0 for any other class
   // reciprocals for per-lane division: m = ceil(2^31 / d), see fast_div
   uint32_t m_roww;     // d = roww = ss*(wb - 1) + tw
   uint32_t m_wb;       // d = wb
@@ -88,6 +90,16 @@ struct PhaseDesc {
   uint32_t m_pt;       // d = pt
   uint32_t m_blocks;   // d = copy blocks of a quad (window + weight blocks)
 };
+
+// One stride-residue class of a multi-class launch (Variant::mc): its pixels
+// are (ih0 + 2 i', iw0 + 2 j') for grid points i' < hp, j' < wp, its taps
+// (rh + 2 j, rw + 2 l) for j < th, l < tw, and its pixel at window position
+// (dr, jb) of a tile reads window row dr + e - j, column jb + f - l at tap
+// (j, l).
+struct MCClass {
+  int32_t ih0, iw0, hp, wp, th, tw, rh, rw, e, f;
+};
+constexpr int kMCClasses = 4;   // multi-class launches: stride 2
 
 // By-value kernel argument block of one launch.  For a forward launch
 // (fwd = 1) the fields keep their input-gradient roles: go is x, gi is y, Ci
@@ -108,7 +120,9 @@ struct LaunchArgs {
   int32_t nphases;     // classes in this launch, heaviest first
   int32_t total_tiles; // workgroups in this launch
   int32_t variant;     // kernel instantiation (host side only)
+  int32_t mc;          // 1: multi-class launch (ph[0] is the union of mcls)
   PhaseDesc ph[kMaxPhasesPerLaunch];
+  MCClass mcls[kMCClasses];
 };
 
 // One instantiation of the kernel family: WM x WN waves; wave (mg, ng) owns
@@ -125,6 +139,14 @@ struct LaunchArgs {
 // row taps; the epilogue adds the tw partial sums of a pixel, which sit tw
 // window columns apart, through LDS.  With Ci = 3 and a 4-column class this
 // fills 12 of 16 rows, where one channel per row fills 3.
+//
+// mc (multi-class, stride 2): one tile covers the same grid points
+// (i', j') of all four stride-residue classes, so the four classes share
+// one grad_out window per stage (the union of the windows they read) and a
+// stage holds all kH x kW taps of the weights.  Every wave multiplies every
+// class: for its NBW blocks of grid points it keeps one accumulator set per
+// class, and each unit (16 output channels at one tap) updates the set of
+// the class the tap belongs to.  The epilogue stores each class's pixels.
 struct Variant {
   int f16;   // 0: fp32 path, 1: f16-staged path
   int wm;    // waves along channels
@@ -133,10 +155,17 @@ struct Variant {
   int nbw;   // 16-pixel blocks per wave
   int half;  // 1: half-size stage buffers, two workgroups per CU
   int cm;    // 1: column taps in the matrix rows (wm = mb = 1)
+  int mc;    // 1: all four classes of a stride-2 shape per tile
 };
 
-// Floats of one stage buffer of a variant.
-constexpr int stage_floats(const Variant& v) { return v.half ? kStageFloatsHalf : kStageFloats; }
+// Floats of one stage buffer of a variant.  Multi-class variants stage a
+// window shared by four classes, so their stages are smaller; 52 copy
+// batches keep each of 8 waves at 7 batches of staging registers (with
+// more, the accumulators of four classes no longer fit in registers).
+constexpr int kStageFloatsMC = 13312;
+constexpr int stage_floats(const Variant& v) {
+  return v.mc ? kStageFloatsMC : v.half ? kStageFloatsHalf : kStageFloats;
+}
 
 // Copy batches (of 256 floats) one wave of a variant copies per stage at
 // most; a stage shape is usable only if its batches fit in the waves.
@@ -160,7 +189,10 @@ constexpr Variant kVariants[] = {
     // column taps in the matrix rows (few input channels)
     {0, 1, 8, 1, 7, 0, 1}, {0, 1, 12, 1, 5, 0, 1}, {0, 1, 16, 1, 4, 0, 1},
     {0, 1, 8, 1, 4, 1, 1}, {1, 1, 8, 1, 7, 0, 1}, {1, 1, 12, 1, 5, 0, 1},
-    {1, 1, 8, 1, 4, 1, 1}};
+    {1, 1, 8, 1, 4, 1, 1},
+    // all four classes of a stride-2 shape per tile (fp32): 8 waves, whose
+    // 256 registers hold the four classes' accumulators
+    {0, 2, 4, 2, 4, 0, 0, 1}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b

@@ -82,7 +82,8 @@ C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   c.p0 = ptile * P.ntv;
   const int pend = imin(c.p0 + P.ntv, bandpix);
   c.npx = pend - c.p0;
-  c.ntaps = a.cm ? P.th : P.th * P.tw;   // cm: row taps only
+  // cm: row taps only; multi-class: every kernel tap, in the weight's order
+  c.ntaps = a.cm ? P.th : P.mct > 0 ? P.mct : P.th * P.tw;
   c.nstages = c.ntaps > 0 ? P.nchunks * P.ngroups : 0;
   c.i_start = c.p0 / P.wb;
   // window: the source rows / columns of the tile's rows and band through
@@ -131,6 +132,57 @@ C2B_HD int window_base_cm(const TileCtx& c, int local) {
   if (local >= cm_points(c)) return (P.th - 1) * c.roww;
   const int r = fast_div(local, P.m_roww);
   return (r + P.th - 1) * c.roww + (local - r * c.roww);
+}
+
+// Multi-class tiles (Variant::mc): the window position (dr, jb) of a
+// tile-local grid point, as the slot dr * roww + jb; class k's pixel there
+// reads slot + e * roww + f - (j * roww + l) at its tap (j, l).  Lanes past
+// the tile's points get slot 0, from which every class's taps stay inside
+// the window (0 <= e - j, f - l and e - j < R, f - l < roww).
+C2B_HD int window_pixel(const TileCtx& c, int local) {
+  const PhaseDesc& P = c.P;
+  if (c.ntaps == 0 || local >= c.npx) return 0;
+  const int q0 = c.p0 - c.i_start * P.wb + local;
+  const int dr = fast_div(q0, P.m_wb);
+  return dr * c.roww + (q0 - dr * P.wb);
+}
+
+// Plane offset ih*W + iw of class k's pixel at a tile-local grid point of a
+// multi-class tile, or -1 (past the tile's points or the class's extent).
+C2B_HD int mc_output_offset(const TileCtx& c, const LaunchArgs& a, const MCClass& k,
+                            int local) {
+  const PhaseDesc& P = c.P;
+  if (local >= c.npx) return -1;
+  const int q0 = c.p0 - c.i_start * P.wb + local;
+  const int dr = fast_div(q0, P.m_wb);
+  const int ip = c.i_start + dr;
+  const int jj = c.band * P.wb + (q0 - dr * P.wb);
+  if (ip >= k.hp || jj >= k.wp) return -1;
+  return (k.ih0 + 2 * ip) * a.W + k.iw0 + 2 * jj;
+}
+
+// Multi-class stores: the two classes of row class hk (mcls[2 hk] and
+// mcls[2 hk + 1], whose first columns iw0 are 0 and 1) hold, at a grid point
+// (i', j'), the two adjacent pixels (ih, 2j') and (ih, 2j' + 1) of input row
+// ih = ih0 + 2i'.  Fills the row and the even column and which of the pair
+// lie inside their class; false past the tile's points or the rows.
+C2B_HD bool mc_pair_pixel(const TileCtx& c, const LaunchArgs& a, int hk, int local, int* ih,
+                          int* col0, bool* even_ok, bool* odd_ok) {
+  const PhaseDesc& P = c.P;
+  if (local >= c.npx) return false;
+  const MCClass& k0 = a.mcls[2 * hk];
+  const MCClass& k1 = a.mcls[2 * hk + 1];
+  const int q0 = c.p0 - c.i_start * P.wb + local;
+  const int dr = fast_div(q0, P.m_wb);
+  const int ip = c.i_start + dr;
+  const int jj = c.band * P.wb + (q0 - dr * P.wb);
+  if (ip >= k0.hp) return false;
+  *ih = k0.ih0 + 2 * ip;
+  *col0 = 2 * jj;
+  const bool first_even = k0.iw0 == 0;   // which class holds the even column
+  *even_ok = jj < (first_even ? k0.wp : k1.wp);
+  *odd_ok = jj < (first_even ? k1.wp : k0.wp);
+  return *even_ok || *odd_ok;
 }
 
 // Window slot offset of tap (j, l) relative to window_base.
@@ -224,7 +276,10 @@ C2B_HD int weight_source(const TileCtx& c, const LaunchArgs& a, int m, int t, in
   const int tap = grp * P.tg + t;
   if (tap >= c.ntaps) return -1;
   int ci, kidx;
-  if (CM) {
+  if (P.mct > 0) {   // multi-class: tap t of the stage is kernel tap t
+    ci = c.ci0 + m;
+    kidx = tap;
+  } else if (CM) {
     const int cl = m / a.twm, l = m - cl * a.twm;
     if (l >= P.tw || cl >= a.cit) return -1;
     ci = c.ci0 + cl;

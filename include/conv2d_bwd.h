@@ -263,6 +263,17 @@ int conv2d_variant_is_f16(int variant);
  * the index is out of range.  Results are the same up to summation order. */
 int conv2d_variant_uses_column_taps(int variant);
 
+/* 1 if `variant` is a multi-class instance (stride 2 only: one workgroup
+ * covers the same grid points of all four stride-residue classes, which
+ * share one staged grad_out window, and the epilogue stores each class's
+ * pixels), 0 if each workgroup covers one class, CONV2D_ERR_UNSUPPORTED if
+ * the index is out of range.  Multi-class variants tile only shapes with
+ * stride 2 whose four classes all have pixels and taps and whose kernel has
+ * at most 9 taps (else CONV2D_ERR_UNSUPPORTED from the calls that force a
+ * variant); they have no forward or f16-staged instance.  Results are the
+ * same up to summation order. */
+int conv2d_variant_is_multi_class(int variant);
+
 /*
  * conv2d_grad_input (or conv2d_grad_input_f16, as the variant's path
  * dictates) with the kernel variant forced to `variant`.  Same contract and

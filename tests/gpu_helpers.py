@@ -97,6 +97,21 @@ SMALL_CI_SHAPES = [
 ]
 
 
+# Stride-2 shapes for the multi-class variants: odd extents (the four
+# classes differ in rows and columns), 2x2, 3x2 and 3x3 kernels, asymmetric,
+# zero and double padding, channels off the 64-channel tile and the stage
+# depth, and rows wide enough for several bands.
+MC_SHAPES = [
+    _shape("mc_3x3_odd", 2, 70, 13, 17, 40, 3, 3, 2, 1, 1),
+    _shape("mc_2x2", 1, 20, 12, 14, 37, 2, 2, 2, 0, 0),
+    _shape("mc_3x2_asym", 2, 33, 15, 10, 21, 3, 2, 2, 1, 0),
+    _shape("mc_3x3_pad0", 1, 64, 16, 16, 64, 3, 3, 2, 0, 0),
+    _shape("mc_3x3_pad2", 1, 17, 9, 11, 19, 3, 3, 2, 2, 2),
+    _shape("mc_3x3_wide", 1, 16, 6, 130, 24, 3, 3, 2, 1, 1),
+    _shape("mc_3x3_tiny", 3, 5, 3, 2, 6, 3, 3, 2, 1, 1),
+]
+
+
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     if ref.size == 0:
         return 0.0

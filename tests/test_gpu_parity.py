@@ -15,8 +15,8 @@ import oracle
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw,
                                                     draw_integers, random_shape)
-from tests.gpu_helpers import (SMALL_CI_SHAPES, TOL, VARIANT_SHAPES, rel_err, round_f16,
-                               run_gpu)
+from tests.gpu_helpers import (MC_SHAPES, SMALL_CI_SHAPES, TOL, VARIANT_SHAPES, params_of,
+                               rel_err, round_f16, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -175,7 +175,15 @@ def _num_variants():
 def test_every_variant(variant):
     import conv2d_backward_implicit_amd as c2b
     f16 = bool(c2b.variant_is_f16(variant))
-    for sh in VARIANT_SHAPES:
+    mc = c2b.variant_is_multi_class(variant) == 1
+    ran = 0
+    for sh in VARIANT_SHAPES + (MC_SHAPES if mc else []):
+        if mc:
+            try:
+                c2b.describe_plan_variant(params_of(sh), variant)
+            except c2b.Conv2dError:
+                continue   # not a stride-2 shape the multi-class tiles cover
+        ran += 1
         _say("case variant", variant, sh.name)
         rng = np.random.default_rng(11)
         go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
@@ -192,6 +200,7 @@ def test_every_variant(variant):
         gi_, wi_ = draw_integers(sh, 3)
         got_i = run_gpu(sh, gi_, wi_, variant=variant)
         assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_)), sh.name
+    assert ran >= 1
 
 
 # ---- variants with column taps in the matrix rows, on few-channel shapes ----

@@ -11,7 +11,7 @@ import pytest
 
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import CONFIGS, ConvShape, random_shape
-from tests.gpu_helpers import SMALL_CI_SHAPES, VARIANT_SHAPES, params_of
+from tests.gpu_helpers import MC_SHAPES, SMALL_CI_SHAPES, VARIANT_SHAPES, params_of
 from tests.test_gpu_parity import EDGE, RANDOM
 
 
@@ -41,12 +41,28 @@ def test_random_stress(f16):
         _check(sh, f16)
 
 
+def _mc_tiles(sh):
+    """Multi-class variants tile stride-2 shapes whose four classes have
+    pixels and taps, with at most 9 kernel taps."""
+    return (sh.stride == 2 and sh.kernel_h >= 2 and sh.kernel_w >= 2 and sh.in_h >= 2
+            and sh.in_w >= 2 and sh.kernel_h * sh.kernel_w <= 9)
+
+
 @pytest.mark.parametrize("variant", range(c2b.num_variants()))
 def test_every_variant_replay(variant):
     shapes = list(VARIANT_SHAPES) + [CONFIGS[0]]
+    mc = c2b.variant_is_multi_class(variant) == 1
+    if mc:
+        shapes += MC_SHAPES + [CONFIGS[2]]
+    ran = 0
     for sh in shapes:
         rc, msg = c2b.check_indexing_variant(params_of(sh), variant)
+        if mc and not _mc_tiles(sh):
+            assert rc == -5, (variant, sh.name, rc)   # not a multi-class shape
+            continue
         assert rc == 0, (variant, sh.name, rc, msg)
+        ran += 1
+    assert ran >= 1
 
 
 def test_variant_queries():
@@ -110,7 +126,7 @@ def test_forward_every_variant_replay(variant):
     shapes = list(VARIANT_SHAPES) + [CONFIGS[0]]
     for sh in shapes:
         rc, msg = c2b.check_indexing_forward_variant(params_of(sh), variant)
-        if c2b.variant_uses_column_taps(variant) == 1:
+        if c2b.variant_uses_column_taps(variant) == 1 or c2b.variant_is_multi_class(variant) == 1:
             assert rc == -5, (variant, sh.name, rc)   # no forward instance
         else:
             assert rc == 0, (variant, sh.name, rc, msg)
