@@ -500,6 +500,7 @@ extern "C" int conv2d_check_indexing_forward(const conv2d_params* p, int f16, ch
                                              size_t msg_len) {
   // the path conv2d_forward / conv2d_forward_f16 take for this shape
   if (c2b::fg::fg_applies(p, f16 ? 1 : 0)) return c2b::fg::fg_check(p, msg, msg_len);
+  if (c2b::pw::pw_shape(p)) return c2b::pw::pw_check(p, msg, msg_len, 1);
   return c2b::check_all(p, f16 ? 1 : 0, -1, msg, msg_len, c2b::kOpForward);
 }
 

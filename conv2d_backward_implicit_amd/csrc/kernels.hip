@@ -705,8 +705,9 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, i
   if (rc != CONV2D_OK) return rc;
   // 1x1, stride 1, unpadded: the GEMM over all images' pixels (forced
   // variants still reach the kernel family)
-  if (op == kOpGradInput && variant < 0 && pw::pw_applies(p, go, w, gi))
-    return pw::pw_launch(go, w, gi, p, f16, stream);
+  const int fwd = op == kOpForward ? 1 : 0;
+  if (variant < 0 && pw::pw_route(p, fwd, f16) && pw::pw_applies(p, go, w, gi))
+    return pw::pw_launch(go, w, gi, p, f16, stream, fwd);
   std::vector<LaunchArgs> launches;
   rc = cached_plan(p, op, f16, variant, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
@@ -727,9 +728,10 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
   if (rc != CONV2D_OK) return rc;
   rc = check_pointers(go, w, gi, p, op);
   if (rc != CONV2D_OK) return rc;
-  if (op == kOpGradInput && pw::pw_applies(p, go, w, gi)) {
+  const int fwd = op == kOpForward ? 1 : 0;
+  if (pw::pw_route(p, fwd, f16) && pw::pw_applies(p, go, w, gi)) {
     // the 1x1 GEMM has no variant to choose: run it once
-    rc = pw::pw_launch(go, w, gi, p, f16, stream);
+    rc = pw::pw_launch(go, w, gi, p, f16, stream, fwd);
     if (rc != CONV2D_OK) return rc;
     if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
       return CONV2D_ERR_HIP;
@@ -807,7 +809,7 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
 // The variant the default entry point of a path uses for a shape now (-1 if
 // the shape launches nothing).
 int planned_variant(const conv2d_params* p, int f16, int* variant_out, int op = kOpGradInput) {
-  if (op == kOpGradInput && pw::pw_shape(p)) {   // the 1x1 GEMM (aligned tensors)
+  if (pw::pw_route(p, op == kOpForward, f16)) {   // the 1x1 GEMM (aligned tensors)
     *variant_out = -1;
     return CONV2D_OK;
   }
@@ -860,7 +862,7 @@ int select_checked(const conv2d_params* p, int op, int f16, int variant) {
   if (rc != CONV2D_OK) return rc;
   if (variant < -1 || variant >= kNumVariants) return CONV2D_ERR_UNSUPPORTED;
   // the 1x1 GEMM has no variant to choose (-1 still clears a choice)
-  if (op == kOpGradInput && pw::pw_shape(p) && variant >= 0) return CONV2D_ERR_UNSUPPORTED;
+  if (pw::pw_route(p, op == kOpForward, f16) && variant >= 0) return CONV2D_ERR_UNSUPPORTED;
   const int cus = device_cus();
   if (variant >= 0) {
     rc = build_plan(p, f16, cus, nullptr, nullptr, variant, nullptr, op);
@@ -933,6 +935,7 @@ extern "C" int conv2d_planned_forward_variant(const conv2d_params* p, int f16, i
 }
 
 extern "C" int conv2d_select_forward_variant(const conv2d_params* p, int f16, int variant) {
-  if (c2b::fg::fg_applies(p, f16 ? 1 : 0)) return CONV2D_ERR_UNSUPPORTED;
+  // a shape on the im2col GEMM has no variant to choose (-1 still clears one)
+  if (c2b::fg::fg_applies(p, f16 ? 1 : 0) && variant >= 0) return CONV2D_ERR_UNSUPPORTED;
   return c2b::select_checked(p, c2b::kOpForward, f16 ? 1 : 0, variant);
 }

@@ -667,6 +667,18 @@ int build_plan(const conv2d_params* p, int f16, int num_cus, std::vector<LaunchA
 
 }  // namespace c2b
 
+namespace c2b {
+// Plan summary of a shape on the 1x1 GEMM (one launch, one phase).
+void describe_pw(const conv2d_params* p, int fwd, conv2d_plan_info* out) {
+  std::memset(out, 0, sizeof(*out));
+  out->launches = 1;
+  out->phases = 1;
+  pw::pw_describe(p, &out->tiles, &out->macs, fwd);
+  out->useful_macs = int64_t(p->batch) * p->out_channels * p->out_h * p->out_w *
+                     p->in_channels;
+}
+}  // namespace c2b
+
 extern "C" int conv2d_check_params(const conv2d_params* p) {
   int rc = c2b::build_plan(p, 0, c2b::kDefaultCUs, nullptr, nullptr);
   if (rc != CONV2D_OK) return rc;
@@ -676,13 +688,8 @@ extern "C" int conv2d_check_params(const conv2d_params* p) {
 extern "C" int conv2d_describe_plan(const conv2d_params* p, int f16,
                                     conv2d_plan_info* out) {
   if (out == nullptr) return CONV2D_ERR_NULL_PTR;
-  if (c2b::pw::pw_shape(p)) {   // the 1x1 GEMM over all images' pixels
-    std::memset(out, 0, sizeof(*out));
-    out->launches = 1;
-    out->phases = 1;
-    c2b::pw::pw_describe(p, &out->tiles, &out->macs);
-    out->useful_macs = int64_t(p->batch) * p->out_channels * p->out_h * p->out_w *
-                       p->in_channels;
+  if (c2b::pw::pw_route(p, 0, f16 ? 1 : 0)) {   // the 1x1 GEMM over all images' pixels
+    c2b::describe_pw(p, 0, out);
     return CONV2D_OK;
   }
   return c2b::build_plan(p, f16 ? 1 : 0, c2b::kDefaultCUs, nullptr, out);
@@ -699,6 +706,10 @@ extern "C" int conv2d_describe_plan_variant(const conv2d_params* p, int variant,
 extern "C" int conv2d_describe_forward_plan(const conv2d_params* p, int f16,
                                             conv2d_plan_info* out) {
   if (out == nullptr) return CONV2D_ERR_NULL_PTR;
+  if (c2b::pw::pw_route(p, 1, f16 ? 1 : 0)) {
+    c2b::describe_pw(p, 1, out);
+    return CONV2D_OK;
+  }
   return c2b::build_plan(p, f16 ? 1 : 0, c2b::kDefaultCUs, nullptr, out, -1, nullptr,
                          c2b::kOpForward);
 }

@@ -1,6 +1,7 @@
-// Geometry and index arithmetic of the 1x1 input-gradient GEMM
-// (pointwise_gemm.hip), shared by its kernel, its host replay and the
-// planner's description of a shape's launch.
+// Geometry and index arithmetic of the 1x1 GEMM (pointwise_gemm.hip) that
+// serves the input gradient and the forward convolution of 1x1, stride-1,
+// unpadded layers, shared by its kernel, its host replay and the planner's
+// description of a shape's launch.
 #pragma once
 
 #include <stdint.h>
@@ -16,6 +17,9 @@
 #endif
 
 namespace c2b {
+namespace fg {   // forward_gemm.hip
+bool fg_applies(const conv2d_params* p, int f16);
+}  // namespace fg
 namespace pw {
 
 constexpr int kBM = 128, kBN = 128;   // channels x pixels per tile
@@ -29,15 +33,21 @@ constexpr uint32_t kPad = 0x80000000u;   // byte offset past every buffer range
 constexpr int64_t kI31 = int64_t(1) << 31;
 static_assert(kLoads * 4 * 2 == kBK, "a wave's loads cover its share of both operands");
 
+// Operands of one launch.  Input gradient (fwd = 0): rows m are input
+// channels, k output channels, A[k][m] = weight[k, m], B = grad_out, C =
+// grad_input.  Forward convolution (fwd = 1, the same GEMM with the
+// weight's other index first): rows m are output channels, k input
+// channels, A[m][k] = weight[m, k], B = x, C = y.
 struct PWArgs {
-  const float* go;
+  const float* go;   // B: grad_out, or x
   const float* w;
-  float* gi;
-  int32_t M;    // input channels (rows of the product)
-  int32_t K;    // output channels (contraction)
+  float* gi;         // C: grad_input, or y
+  int32_t M;    // rows of the product
+  int32_t K;    // contraction
   int32_t P;    // pixels per image, H * W
   int32_t Q;    // pixels of all images, N * H * W
   int32_t TM, TN;
+  int32_t fwd;  // 1: A is [m][k] (forward)
 };
 
 PW_HD int imin(int a, int b) { return a < b ? a : b; }
@@ -65,6 +75,23 @@ PW_HD uint32_t a_offset(const PWArgs& a, int st, int m0, int krow, int quad) {
   const int k = st * kBK + krow, m = m0 + 4 * quad;
   if (k >= a.K || m >= a.M) return kPad;
   return (uint32_t(k) * uint32_t(a.M) + uint32_t(m)) * 4u;
+}
+
+// Forward (A = [m][k]): load j of the A stage, lane l: tile row 8j + l / 8
+// and LDS slot l % 8 of the row's eight k quads; the slot holds k quad
+// slot ^ a_swizzle(row), so that 16 lanes reading 16 consecutive rows at
+// one k quad hit 16 distinct 4-bank groups (rows 128 bytes apart).  The
+// swizzle is its own inverse.
+PW_HD int a_swizzle(int row) { return (row >> 1) & 7; }
+PW_HD int arow_row(int j, int l) { return 8 * j + l / 8; }
+PW_HD int arow_kq(int j, int l) { return (l % 8) ^ a_swizzle(arow_row(j, l)); }
+
+// Byte offset in weight of forward A row `row` (tile row), k quad kq of
+// stage st, or kPad past the rows or K.
+PW_HD uint32_t arow_offset(const PWArgs& a, int st, int m0, int row, int kq) {
+  const int m = m0 + row, k = st * kBK + 4 * kq;
+  if (m >= a.M || k >= a.K) return kPad;
+  return (uint32_t(m) * uint32_t(a.K) + uint32_t(k)) * 4u;
 }
 
 // Element offset n * K * P + p of grad_out pixel q (k = 0), or -1 past Q.
@@ -102,29 +129,38 @@ inline bool pw_shape(const conv2d_params* p) {
   return N * P * p->in_channels > 0;
 }
 
-inline void pw_plan(const conv2d_params* p, PWArgs* a) {
+inline void pw_plan(const conv2d_params* p, PWArgs* a, int fwd = 0) {
   memset(a, 0, sizeof(*a));
-  a->M = int32_t(p->in_channels);
-  a->K = int32_t(p->out_channels);
+  a->fwd = fwd;
+  a->M = int32_t(fwd ? p->out_channels : p->in_channels);
+  a->K = int32_t(fwd ? p->in_channels : p->out_channels);
   a->P = int32_t(int64_t(p->in_h) * p->in_w);
   a->Q = int32_t(int64_t(p->batch) * a->P);
   a->TM = (a->M + kBM - 1) / kBM;
   a->TN = (a->Q + kBN - 1) / kBN;
 }
 
+// Whether a shape's default path (input gradient, or forward with fwd = 1)
+// is this GEMM: forward shapes that the few-input-channel im2col GEMM takes
+// stay there.
+inline bool pw_route(const conv2d_params* p, int fwd, int f16) {
+  return pw_shape(p) && (!fwd || !fg::fg_applies(p, f16));
+}
+
 // Tiles and multiply-adds issued for a shape (pw_shape must hold).
-inline void pw_describe(const conv2d_params* p, int64_t* tiles, int64_t* macs) {
+inline void pw_describe(const conv2d_params* p, int64_t* tiles, int64_t* macs, int fwd = 0) {
   PWArgs a;
-  pw_plan(p, &a);
+  pw_plan(p, &a, fwd);
   *tiles = int64_t(a.TM) * a.TN;
   *macs = *tiles * kBM * kBN * int64_t((a.K + kBK - 1) / kBK) * kBK;
 }
 
-// Launch and host replay (pointwise_gemm.hip).
+// Launch and host replay (pointwise_gemm.hip); fwd = 1: the forward
+// convolution, with x in the place of grad_out and y in that of grad_input.
 bool pw_applies(const conv2d_params* p, const float* go, const float* w, const float* gi);
 int pw_launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
-              void* stream);
-int pw_check(const conv2d_params* p, char* msg, size_t len);
+              void* stream, int fwd = 0);
+int pw_check(const conv2d_params* p, char* msg, size_t len, int fwd = 0);
 
 }  // namespace pw
 }  // namespace c2b

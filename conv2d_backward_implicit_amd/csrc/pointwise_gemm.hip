@@ -54,7 +54,7 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <bool F16>
+template <bool F16, bool AROW>
 __global__ __launch_bounds__(kThreads, 1) void pointwise_gemm_kernel(const PWArgs a) {
   __shared__ f32x4 lds4[kBufs * kStageBytes / 16];
   const int tid = threadIdx.x;
@@ -84,9 +84,10 @@ __global__ __launch_bounds__(kThreads, 1) void pointwise_gemm_kernel(const PWArg
     for (int i = 0; i < kLoads; ++i) {
       const int j = kLoads * wave + i;
       const int krow = load_krow(j, lane);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rsA, (lds_void_t*)(base + j * 1024), 16, a_offset(a, st, m0, krow, load_quad(lane)),
-          0, 0, 0);
+      const uint32_t ao = AROW ? arow_offset(a, st, m0, arow_row(j, lane), arow_kq(j, lane))
+                               : a_offset(a, st, m0, krow, load_quad(lane));
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsA, (lds_void_t*)(base + j * 1024), 16, ao, 0,
+                                               0, 0);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
           rsB, (lds_void_t*)(base + kBK * kBM * 4 + j * 1024), 16,
           b_offset(a, st, bbase, krow), 0, 0, 0);
@@ -101,11 +102,62 @@ __global__ __launch_bounds__(kThreads, 1) void pointwise_gemm_kernel(const PWArg
 
   // products of stage st: acc[qa][qb] is the block of channels 4c + qa and
   // pixels 4c + qb of the wave's 64 x 64
+  // forward (AROW): block qa of the wave covers rows 16 qa + c16 (plain
+  // order); a lane reads the k quads of its row at their swizzled slots
+  auto arow_read = [&](const char* base, int qa, int kq) __attribute__((always_inline)) {
+    const int row = wm * kWave + 16 * qa + c16;
+    return *reinterpret_cast<const f32x4*>(base + row * (kBK * 4) +
+                                           16 * (kq ^ a_swizzle(row)));
+  };
   auto compute = [&](int st) __attribute__((always_inline)) {
     const char* base = buf(st);
     const float* As = reinterpret_cast<const float*>(base) + wm * kWave + 4 * c16;
     const float* Bs = reinterpret_cast<const float*>(base + kBK * kBM * 4) + wn * kWave + 4 * c16;
-    if constexpr (F16) {
+    if constexpr (AROW && F16) {
+      // lane group g: k = 8g .. 8g+7, the row's quads 2g and 2g+1
+      f32x4 bv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) bv[i] = *reinterpret_cast<const f32x4*>(Bs + (8 * g + i) * kBN);
+      f16x8 ah[4], bh[4];
+#pragma unroll
+      for (int qa = 0; qa < 4; ++qa) {
+        const f32x4 a0 = arow_read(base, qa, 2 * g), a1 = arow_read(base, qa, 2 * g + 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ah[qa][i] = _Float16(a0[i]);
+          ah[qa][4 + i] = _Float16(a1[i]);
+        }
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) bh[q][i] = _Float16(bv[i][q]);
+#pragma unroll
+      for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb)
+          acc[qa][qb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah[qa], bh[qb], acc[qa][qb], 0, 0, 0);
+    } else if constexpr (AROW) {
+      // 16-k halves h: lane group g reads its row's quad 4h + g; MFMA t of
+      // the half takes k = 16h + 4g + t from both operands
+#pragma unroll
+      for (int h = 0; h < kBK / 16; ++h) {
+        f32x4 av[4], bv[4];
+#pragma unroll
+        for (int qa = 0; qa < 4; ++qa) av[qa] = arow_read(base, qa, 4 * h + g);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          bv[t] = *reinterpret_cast<const f32x4*>(Bs + (16 * h + 4 * g + t) * kBN);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+          for (int qa = 0; qa < 4; ++qa)
+#pragma unroll
+            for (int qb = 0; qb < 4; ++qb)
+              acc[qa][qb] =
+                  __builtin_amdgcn_mfma_f32_16x16x4f32(av[qa][t], bv[t][qb], acc[qa][qb], 0, 0, 0);
+      }
+    } else if constexpr (F16) {
       f32x4 av[8], bv[8];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -171,7 +223,8 @@ __global__ __launch_bounds__(kThreads, 1) void pointwise_gemm_kernel(const PWArg
   for (int qa = 0; qa < 4; ++qa)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * kWave + 16 * g + 4 * r + qa;
+      // product row 4g + r of block qa: strided (input gradient) or plain
+      const int m = m0 + wm * kWave + (AROW ? 16 * qa + 4 * g + r : 16 * g + 4 * r + qa);
       if (m < a.M)
         *reinterpret_cast<f32x4*>(gi_n + (size_t)m * a.P) =
             f32x4{acc[qa][0][r], acc[qa][1][r], acc[qa][2][r], acc[qa][3][r]};
@@ -191,18 +244,22 @@ bool pw_applies(const conv2d_params* p, const float* go, const float* w, const f
 
 // Launch (shape and pointers already validated, pw_applies true).
 int pw_launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
-              void* stream) {
+              void* stream, int fwd) {
   PWArgs a;
-  pw_plan(p, &a);
+  pw_plan(p, &a, fwd);
   a.go = go;
   a.w = w;
   a.gi = gi;
   const dim3 grid(a.TM * a.TN), block(kThreads);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (f16)
-    hipLaunchKernelGGL(pointwise_gemm_kernel<true>, grid, block, 0, st, a);
+  if (f16 && fwd)
+    hipLaunchKernelGGL((pointwise_gemm_kernel<true, true>), grid, block, 0, st, a);
+  else if (f16)
+    hipLaunchKernelGGL((pointwise_gemm_kernel<true, false>), grid, block, 0, st, a);
+  else if (fwd)
+    hipLaunchKernelGGL((pointwise_gemm_kernel<false, true>), grid, block, 0, st, a);
   else
-    hipLaunchKernelGGL(pointwise_gemm_kernel<false>, grid, block, 0, st, a);
+    hipLaunchKernelGGL((pointwise_gemm_kernel<false, false>), grid, block, 0, st, a);
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 
@@ -226,9 +283,9 @@ struct Failure {
 // the pixels; the product reads of every block pair the same k in A and B,
 // each k of the stage once; every grad_input element stored once, by the
 // lane holding its channel and pixel.
-int pw_check(const conv2d_params* p, char* msg, size_t len) {
+int pw_check(const conv2d_params* p, char* msg, size_t len, int fwd) {
   PWArgs a;
-  pw_plan(p, &a);
+  pw_plan(p, &a, fwd);
   try {
     const int64_t a_bytes = int64_t(a.K) * a.M * 4, b_bytes = int64_t(a.Q) * a.K * 4;
     const int nst = (a.K + kBK - 1) / kBK;
@@ -238,6 +295,11 @@ int pw_check(const conv2d_params* p, char* msg, size_t len) {
     auto a_src = [&](int st, int m0, int krow, int col) -> int64_t {
       const int k = st * kBK + krow, m = m0 + col;
       return (k < a.K && m < a.M) ? (int64_t(k) * a.M + m) * 4 : -1;
+    };
+    // forward: A[m][k] = weight[m * K + k]
+    auto arow_src = [&](int st, int m0, int row, int kk) -> int64_t {
+      const int k = st * kBK + kk, m = m0 + row;
+      return (k < a.K && m < a.M) ? (int64_t(m) * a.K + k) * 4 : -1;
     };
     auto b_src = [&](int st, int q0, int krow, int col) -> int64_t {
       const int k = st * kBK + krow, q = q0 + col;
@@ -257,31 +319,83 @@ int pw_check(const conv2d_params* p, char* msg, size_t len) {
       for (int st : {0, 1, nst - 1}) {
         if (st < 0 || st >= nst) continue;
         std::vector<int64_t> cellA(kBK * kBM, -2), cellB(kBK * kBN, -2);
+        if (fwd) {
+          // A stage as [row][slot][4]: slot s of row r holds k quad
+          // s ^ a_swizzle(r); kept in cellA[r * kBK + k]
+          for (int wave = 0; wave < kThreads / 64; ++wave)
+            for (int lane = 0; lane < 64; ++lane)
+              for (int i = 0; i < kLoads; ++i) {
+                const int j = kLoads * wave + i, row = arow_row(j, lane), kq = arow_kq(j, lane);
+                const int byte = j * 1024 + 16 * lane;   // M0 + 16 lane
+                PW_REQUIRE(byte / (kBK * 4) == row && (byte % (kBK * 4)) / 16 == (lane % 8),
+                           "forward A lane layout");
+                PW_REQUIRE((lane % 8) == (kq ^ a_swizzle(row)), "swizzle not an involution");
+                const uint32_t oa = arow_offset(a, st, m0, row, kq);
+                PW_REQUIRE(oa == kPad || int64_t(oa) + 16 <= a_bytes, "A load in range");
+                for (int e = 0; e < 4; ++e) {
+                  const int cell = row * kBK + 4 * kq + e;
+                  PW_REQUIRE(cellA[cell] == -2, "A cell written twice");
+                  const int64_t ea = arow_src(st, m0, row, 4 * kq + e);
+                  const int64_t ga = oa == kPad ? -1 : int64_t(oa) + 4 * e;
+                  PW_REQUIRE(ga == ea, "A cell (%d, %d) of tile %d stage %d", row, 4 * kq + e,
+                             bid, st);
+                  cellA[cell] = ea;
+                }
+              }
+          // reads: block qa of wave row wm, lane (c16, g) reads its row's
+          // k quads (f16: 2g and 2g + 1; fp32: 4h + g) at slot kq ^ swizzle
+          for (int wm = 0; wm < 2; ++wm)
+            for (int qa = 0; qa < 4; ++qa)
+              for (int c16 = 0; c16 < 16; ++c16) {
+                const int row = wm * kWave + 16 * qa + c16;
+                for (int kq = 0; kq < kBK / 4; ++kq) {
+                  const int slot = kq ^ a_swizzle(row);
+                  PW_REQUIRE(slot >= 0 && slot < kBK / 4, "read slot");
+                  for (int e = 0; e < 4; ++e)
+                    PW_REQUIRE(cellA[row * kBK + 4 * kq + e] != -2, "read of an unwritten cell");
+                }
+              }
+          // bank spread of one read instruction: the 16 lanes of a group
+          // (consecutive rows, one k quad) cover 16 distinct 4-bank groups
+          for (int qa = 0; qa < 4; ++qa)
+            for (int kq = 0; kq < kBK / 4; ++kq) {
+              unsigned used = 0;
+              for (int c16 = 0; c16 < 16; ++c16) {
+                const int row = 16 * qa + c16;
+                const int grp = ((row * kBK * 4 + 16 * (kq ^ a_swizzle(row))) / 16) % 16;
+                used |= 1u << grp;
+              }
+              PW_REQUIRE(used == 0xffffu, "forward A read conflicts (quad %d)", kq);
+            }
+        }
         for (int wave = 0; wave < kThreads / 64; ++wave)
           for (int lane = 0; lane < 64; ++lane) {
             const int64_t bbase = b_base(a, q0 + 4 * load_quad(lane));
             for (int i = 0; i < kLoads; ++i) {
               const int j = kLoads * wave + i, krow = load_krow(j, lane);
               const int quad = load_quad(lane);
-              const uint32_t oa = a_offset(a, st, m0, krow, quad);
+              const uint32_t oa = fwd ? 0u : a_offset(a, st, m0, krow, quad);
               const uint32_t ob = b_offset(a, st, bbase, krow);
               for (int e = 0; e < 4; ++e) {
                 const int byte = j * 1024 + 16 * lane + 4 * e;   // M0 + 16 lane
                 const int cell = byte / 4, row = cell / kBM, col = cell % kBM;
                 PW_REQUIRE(row == krow && col == 4 * quad + e, "lane layout");
-                PW_REQUIRE(cellA[cell] == -2 && cellB[cell] == -2, "cell written twice");
-                const int64_t ea = a_src(st, m0, row, col), eb = b_src(st, q0, row, col);
-                const int64_t ga = oa >= uint32_t(a_bytes) ? -1 : int64_t(oa) + 4 * e;
+                PW_REQUIRE(cellB[cell] == -2, "cell written twice");
+                const int64_t eb = b_src(st, q0, row, col);
+                cellB[cell] = eb;
                 const int64_t gb = ob >= uint32_t(b_bytes) ? -1 : int64_t(ob) + 4 * e;
+                PW_REQUIRE(gb == eb, "B cell (%d, %d) of tile %d stage %d", row, col, bid, st);
+                PW_REQUIRE(ob == kPad || int64_t(ob) + 16 <= b_bytes, "B load in range");
+                if (fwd) continue;
+                PW_REQUIRE(cellA[cell] == -2, "cell written twice");
+                const int64_t ea = a_src(st, m0, row, col);
+                const int64_t ga = oa >= uint32_t(a_bytes) ? -1 : int64_t(oa) + 4 * e;
                 // 16-byte loads are whole: an in-range load must hold the
                 // definition's element, padding only where it has none
                 PW_REQUIRE(ga == ea || (ga >= 0 && ea < 0 && m0 + col >= a.M),
                            "A cell (%d, %d) of tile %d stage %d", row, col, bid, st);
-                PW_REQUIRE(gb == eb, "B cell (%d, %d) of tile %d stage %d", row, col, bid, st);
-                PW_REQUIRE(ob == kPad || int64_t(ob) + 16 <= b_bytes, "B load in range");
                 PW_REQUIRE(oa == kPad || int64_t(oa) + 16 <= a_bytes, "A load in range");
                 cellA[cell] = ea;
-                cellB[cell] = eb;
               }
             }
           }
@@ -309,11 +423,14 @@ int pw_check(const conv2d_params* p, char* msg, size_t len) {
           if (q >= a.Q) continue;
           for (int qa = 0; qa < 4; ++qa)
             for (int r = 0; r < 4; ++r) {
-              const int m = m0 + wm * kWave + 16 * g + 4 * r + qa;
+              const int m = m0 + wm * kWave + (fwd ? 16 * qa + 4 * g + r : 16 * g + 4 * r + qa);
               // the accumulator row 4g + r of block qa is channel
-              // strided(4g + r, qa); its column c16 of block qb is pixel
-              // strided(c16, qb)
-              PW_REQUIRE(m == m0 + wm * kWave + strided(4 * g + r, qa), "store row");
+              // strided(4g + r, qa) (input gradient) or row 16 qa + 4g + r
+              // (forward: block qa read rows 16 qa + c16); its column c16
+              // of block qb is pixel strided(c16, qb)
+              PW_REQUIRE(m == m0 + wm * kWave +
+                                  (fwd ? 16 * qa + 4 * g + r : strided(4 * g + r, qa)),
+                         "store row");
               if (m >= a.M) continue;
               for (int qb = 0; qb < 4; ++qb) {
                 PW_REQUIRE(q + qb == q0 + wn * kWave + strided(c16, qb), "store column");

@@ -136,6 +136,18 @@ int conv2d_grad_input_f16(const float* grad_out, const float* weight,
                           void* stream);
 
 /*
+ * Route of 1x1, stride-1, unpadded shapes (both paths above, and
+ * conv2d_forward / conv2d_forward_f16 below): with in_channels and
+ * in_h*in_w multiples of 4, each tensor below 2^31 bytes and all three
+ * pointers 16-byte aligned, the call is one GEMM over the pixels of all
+ * images (grad_input[n, :, p] = weight^T grad_out[n, :, p]; forward:
+ * y[n, :, p] = weight x[n, :, p]), with the same rounding contract.  Such
+ * a shape has no kernel variant (conv2d_tune runs it once and reports -1;
+ * conv2d_select_variant refuses a variant for it).  Other pointers take
+ * the variant kernels.
+ */
+
+/*
  * Validate a shape without touching any device or pointer (pure host code).
  * Returns CONV2D_OK, CONV2D_ERR_NULL_PTR (p == NULL), CONV2D_ERR_BAD_SHAPE,
  * CONV2D_ERR_OVERFLOW or CONV2D_ERR_UNSUPPORTED, exactly as the compute entry
@@ -322,7 +334,8 @@ int conv2d_check_indexing_variant(const conv2d_params* p, int variant,
  * conv2d_forward with 1 to 15 input channels runs an im2col GEMM over
  * (ci, kh, kw) instead, when x and y each stay below 2^31 bytes and
  * batch*out_h*out_w below 2^31; larger such shapes take the variant
- * kernels, like every other shape.
+ * kernels, like every other shape.  Other 1x1, stride-1, unpadded shapes
+ * take the 1x1 GEMM (described after conv2d_grad_input_f16).
  */
 int conv2d_forward(const float* x, const float* weight, float* y,
                    const conv2d_params* p, void* stream);
@@ -339,8 +352,9 @@ int conv2d_forward_variant(const float* x, const float* weight, float* y,
  * on the caller's buffers (x and weight read, y written, with the result of
  * the chosen variant left in y), makes the fastest the shape's default
  * forward plan, blocks until done, and stores it in *variant_out if that is
- * not NULL.  A shape conv2d_forward runs on the im2col GEMM (above) has no
- * variant: it is run once and *variant_out gets -1.  Errors as
+ * not NULL.  A shape conv2d_forward runs on the im2col GEMM or the 1x1
+ * GEMM (above) has no variant: it is run once and *variant_out gets -1.
+ * Errors as
  * conv2d_forward, or CONV2D_ERR_HIP. */
 int conv2d_tune_forward(const float* x, const float* weight, float* y,
                         const conv2d_params* p, int f16, void* stream,
@@ -348,12 +362,13 @@ int conv2d_tune_forward(const float* x, const float* weight, float* y,
 
 /* The variant conv2d_forward (f16 == 0) or conv2d_forward_f16 uses for the
  * shape now, in *variant_out (-1 if nothing is launched or the shape runs
- * on the im2col GEMM).  CONV2D_OK, or the error of conv2d_check_params, or
+ * on the im2col GEMM or the 1x1 GEMM).  CONV2D_OK, or the error of conv2d_check_params, or
  * CONV2D_ERR_NULL_PTR. */
 int conv2d_planned_forward_variant(const conv2d_params* p, int f16, int* variant_out);
 
 /* conv2d_select_variant for conv2d_forward / conv2d_forward_f16;
- * CONV2D_ERR_UNSUPPORTED also for a shape on the im2col GEMM. */
+ * CONV2D_ERR_UNSUPPORTED also for a variant of a shape on the im2col GEMM
+ * or the 1x1 GEMM. */
 int conv2d_select_forward_variant(const conv2d_params* p, int f16, int variant);
 
 /* conv2d_describe_plan / _variant for the forward launches (host only). */

@@ -385,6 +385,7 @@ def test_forward_few_channel_route():
     stem = c2b.make_params(16, 3, 224, 224, 64, 7, 7, 2, 3, 3)
     assert c2b.planned_forward_variant(stem, False) == -1
     assert lib.conv2d_select_forward_variant(ctypes.byref(stem), 0, 0) == UNSUP
+    assert lib.conv2d_select_forward_variant(ctypes.byref(stem), 0, -1) == OK
     v16 = c2b.planned_forward_variant(stem, True)            # f16: variant family
     assert v16 >= 0 and c2b.variant_is_f16(v16) == 1
     # x of 4000 x 3 x 224 x 224 fp32 is 2.4 GB, past 2^31 bytes
@@ -395,6 +396,28 @@ def test_forward_few_channel_route():
     c2b.select_forward_variant(big, False, v)
     assert c2b.planned_forward_variant(big, False) == v
     c2b.select_forward_variant(big, False, -1)
+
+
+def test_forward_pointwise_route():
+    """1x1, stride-1, unpadded forward shapes run on the 1x1 GEMM (no
+    variant), except those with fewer than 16 input channels on the fp32
+    path, which the im2col GEMM takes; the plan description reports one
+    launch of ceil(Co/128) x ceil(N H W/128) tiles."""
+    lib = c2b.load_library()
+    p = c2b.make_params(64, 256, 14, 14, 1024, 1, 1, 1, 0, 0)
+    for f16 in (False, True):
+        assert c2b.planned_forward_variant(p, f16) == -1
+        assert lib.conv2d_select_forward_variant(ctypes.byref(p), int(f16), 0) == UNSUP
+        assert lib.conv2d_select_forward_variant(ctypes.byref(p), int(f16), -1) == OK
+        info = c2b.describe_forward_plan(p, f16)
+        assert info["launches"] == 1 and info["phases"] == 1
+        assert info["tiles"] == 8 * ((64 * 14 * 14 + 127) // 128)
+        assert info["useful_macs"] == 64 * 14 * 14 * 256 * 1024
+    # the input gradient of the same shape: ceil(Ci/128) row tiles
+    assert c2b.describe_plan(p, False)["tiles"] == 2 * ((64 * 14 * 14 + 127) // 128)
+    # a 1x1 stride-2 shape is not on the GEMM: a variant runs it
+    p2 = c2b.make_params(4, 64, 14, 14, 32, 1, 1, 2, 0, 0)
+    assert c2b.planned_forward_variant(p2, False) >= 0
 
 
 # ---- weight gradient entry points ---------------------------------------------

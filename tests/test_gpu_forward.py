@@ -19,7 +19,7 @@ from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw, dr
                                                     draw_integers)
 from tests.gpu_helpers import (TOL, VARIANT_SHAPES, rel_err, round_f16, run_gpu,
                                run_gpu_forward)
-from tests.test_gpu_parity import EDGE, RANDOM
+from tests.test_gpu_parity import EDGE, PW_SHAPES, RANDOM
 
 pytestmark = pytest.mark.gpu
 
@@ -122,6 +122,46 @@ def test_forward_random_small_shapes():
         x, w = draw_forward(sh, zlib.crc32(sh.name.encode()))
         for f16 in (False, True):
             _check(sh, x, w, f16)
+
+
+# ---- 1x1, stride 1, unpadded: the forward on the 1x1 GEMM --------------------
+@pytest.mark.parametrize("sh", PW_SHAPES, ids=[s.name for s in PW_SHAPES])
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_forward_pointwise_gemm_shapes(sh, f16):
+    """Ragged 128-row output-channel tiles, pixel tiles across images, a
+    contraction that is not a multiple of the 32-deep stage; integer inputs
+    bit-exact."""
+    _say("case forward pointwise", sh.name, "f16" if f16 else "fp32")
+    p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels, 1, 1,
+                        1, 0, 0)
+    few = sh.in_channels < 16 and not f16           # the im2col GEMM takes these
+    assert c2b.planned_forward_variant(p, f16) == -1
+    x, w = draw_forward(sh, zlib.crc32(sh.name.encode()))
+    _say("  rel err", _check(sh, x, w, f16), "(im2col GEMM)" if few else "")
+    rng = np.random.default_rng(zlib.crc32(sh.name.encode()) + 1)
+    xi = rng.integers(-4, 5, size=sh.gi_shape).astype(np.float32)
+    wi = rng.integers(-4, 5, size=sh.w_shape).astype(np.float32)
+    got = run_gpu_forward(sh, xi, wi, f16=f16)
+    assert np.array_equal(got.astype(np.float64), _oracle_fwd(sh, xi, wi))
+
+
+def test_forward_pointwise_misaligned_input_takes_the_variant_kernels():
+    """An x that is not 16-byte aligned cannot use the 16-byte loads: the
+    call must still be right (it runs on the variant kernels)."""
+    import torch
+    sh = PW_SHAPES[2]
+    x, w = draw_forward(sh, 5)
+    dev = torch.device("cuda", 0)
+    store = torch.zeros(x.size + 1, dtype=torch.float32, device=dev)
+    store[1:] = torch.from_numpy(x.ravel()).to(dev)
+    tx = store[1:].view(sh.gi_shape)
+    assert tx.data_ptr() % 16 == 4
+    y = torch.full(sh.go_shape, float("nan"), device=dev)
+    p = c2b.make_params(sh.batch, sh.in_channels, sh.in_h, sh.in_w, sh.out_channels, 1, 1,
+                        1, 0, 0)
+    c2b.forward_into(y, tx, torch.from_numpy(w).to(dev), p)
+    torch.cuda.synchronize()
+    assert rel_err(y.cpu().numpy(), _oracle_fwd(sh, x, w)) <= TOL[False]
 
 
 @pytest.mark.parametrize("idx", range(1, len(CONFIGS)), ids=[c.name for c in CONFIGS[1:]])

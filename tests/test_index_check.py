@@ -12,7 +12,7 @@ import pytest
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import CONFIGS, ConvShape, random_shape
 from tests.gpu_helpers import MC_SHAPES, SMALL_CI_SHAPES, VARIANT_SHAPES, params_of
-from tests.test_gpu_parity import EDGE, RANDOM
+from tests.test_gpu_parity import EDGE, PW_SHAPES, RANDOM
 
 
 def _check(sh, f16):
@@ -130,6 +130,34 @@ def test_forward_every_variant_replay(variant):
             assert rc == -5, (variant, sh.name, rc)   # no forward instance
         else:
             assert rc == 0, (variant, sh.name, rc, msg)
+
+
+# ---- the 1x1 GEMM, both directions ------------------------------------------
+def _pw_random(rng, count, name):
+    out = []
+    for i in range(count):
+        n = int(rng.integers(1, 5))
+        h, w = int(rng.integers(1, 20)), 4 * int(rng.integers(1, 6))   # H W % 4 == 0
+        if i % 2:
+            h, w = w, h
+        ci = 4 * int(rng.integers(1, 80))
+        co = int(rng.integers(1, 300))
+        out.append(ConvShape("%s%d" % (name, i), n, ci, h, w, co, 1, 1, 1, 0, 0, h, w,
+                             dist="uniform"))
+    return out
+
+
+@pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
+def test_pointwise_replay_both_directions(f16):
+    """Every stage load, LDS cell, read and store of the 1x1 GEMM, as the
+    input gradient and as the forward convolution, on channel counts that
+    leave ragged 128-row tiles and 32-deep stages."""
+    shapes = PW_SHAPES + _pw_random(np.random.default_rng(97), 40, "pw")
+    for sh in shapes:
+        assert (sh.in_h * sh.in_w) % 4 == 0, sh
+        _check(sh, f16)
+        if sh.in_channels >= 16 or f16:   # fewer: the im2col forward GEMM
+            _check_fwd(sh, f16)
 
 
 def test_forward_checker_rejects_bad_shape():
