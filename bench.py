@@ -48,7 +48,7 @@ KERNEL_SOURCES = {
     "grad_input": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp",
                                         "pointwise_gemm.hip", "pointwise.hpp")],
     "forward": [_CSRC + f for f in ("kernels.hip", "tile_index.hpp", "plan.hpp", "plan.cpp",
-                                     "forward_gemm.hip")],
+                                     "forward_gemm.hip", "pointwise_gemm.hip", "pointwise.hpp")],
     "grad_weight": [_CSRC + f for f in ("grad_weight.hip", "tile_index.hpp", "plan.hpp")],
     "rms_norm_matmul": [_CSRC + "rms_matmul.hip"],
     "mha_grad_v": [_CSRC + "mha_grad_v.hip"],
