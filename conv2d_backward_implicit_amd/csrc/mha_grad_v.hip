@@ -22,7 +22,11 @@
 //  * accumulates dV^T[d, t] += dO^T[d, pos] P[pos, t]: register r of the S
 //    block of positions 16b + 4 g' + r is exactly the B operand MFMA r needs
 //    (lane group g' supplies position 4 g' + r), so P never leaves registers.
-// The last stores write dV rows as 16-byte pieces.
+// The last stores write dV rows as 16-byte pieces.  When the causal pairing
+// below leaves fewer workgroups than two per CU, each unit is split over two
+// workgroups by the heads of the group; each adds its partial dV onto a
+// zeroed dv, and since exactly two terms meet on zero (0 + a + b equals
+// 0 + b + a in fp32), the result does not depend on their order.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -63,7 +67,8 @@ struct Args {
   int32_t q_seq, kv_seq, H, HKV, group, window, causal;
   int32_t nkb;     // key blocks
   int32_t paired;  // 1: a workgroup takes key blocks u and nkb - 1 - u
-  int32_t units;   // workgroups per kv head
+  int32_t units;   // units (1 or 2 key blocks) per kv head
+  int32_t hsplit;  // workgroups per unit, each taking group / hsplit heads
   float scale;
 };
 
@@ -71,7 +76,12 @@ struct Args {
 // Under a causal mask without a short window, key block u reaches nkb - u
 // query blocks, so blocks u and nkb - 1 - u share a workgroup and every
 // workgroup gets about the same work.
-MHA_HD int unit_of(const Args& a, int bid, int kb[2], int* kvh) {
+// Workgroups [part * units * HKV, (part + 1) * units * HKV) take heads
+// [part * group / hsplit, (part + 1) * group / hsplit) of their group.
+MHA_HD int unit_of(const Args& a, int bid, int kb[2], int* kvh, int* part) {
+  const int per = a.units * a.HKV;
+  *part = bid / per;
+  bid -= *part * per;
   *kvh = bid % a.HKV;
   const int u = bid / a.HKV;
   kb[0] = u;
@@ -136,8 +146,9 @@ __global__ __launch_bounds__(kThreads, 2) void mha_grad_v_kernel(const Args a) {
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 4, c16 = lane & 15;
-  int kbs[2], kvh;
-  const int nblocks = unit_of(a, blockIdx.x, kbs, &kvh);
+  int kbs[2], kvh, part;
+  const int nblocks = unit_of(a, blockIdx.x, kbs, &kvh, &part);
+  const int hper = a.group / a.hsplit;
 
   const __amdgpu_buffer_rsrc_t rsQ = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<float*>(a.q), 0, a.q_seq * a.H * kD * 4, 0x00020000);
@@ -166,10 +177,13 @@ __global__ __launch_bounds__(kThreads, 2) void mha_grad_v_kernel(const Args a) {
   for (int b = 0; b < 4; ++b) acc[b] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
   const int tk = 16 * wave + c16;   // this lane's key within the block
 
-  const int qb0 = lo / kBQ * kBQ;
-  for (int r = 0; r < a.group; ++r) {
+  // Query blocks run from the last down: under a causal mask every key
+  // block's range ends at the sequence's end, so the workgroups resident
+  // together start on the same blocks and share them in L2.
+  const int qb0 = lo / kBQ * kBQ, qlast = (hi - 1) / kBQ * kBQ;
+  for (int r = part * hper; r < (part + 1) * hper; ++r) {
     const int h = kvh * a.group + r;
-    for (int pos0 = qb0; pos0 < hi; pos0 += kBQ) {
+    for (int pos0 = qlast; pos0 >= qb0 && hi > lo; pos0 -= kBQ) {
       __syncthreads();   // the previous block's reads are done
       f32x4 qv[4];
       float gv[4][4], lv = 0.0f;
@@ -234,10 +248,23 @@ __global__ __launch_bounds__(kThreads, 2) void mha_grad_v_kernel(const Args a) {
   const int t = t0 + tk;
   if (t < a.kv_seq) {
     float* out = a.dv + (size_t(t) * a.HKV + kvh) * kD;
+    if (a.hsplit == 1) {
 #pragma unroll
-    for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4*>(out + 16 * b + 4 * g) = acc[b];
+      for (int b = 0; b < 4; ++b) *reinterpret_cast<f32x4*>(out + 16 * b + 4 * g) = acc[b];
+    } else {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) unsafeAtomicAdd(out + 16 * b + 4 * g + j, acc[b][j]);
+    }
   }
   }
+}
+
+// dv = 0 ahead of a split launch's two partial sums.
+__global__ __launch_bounds__(256) void mha_zero_kernel(f32x4* dv, uint32_t n4) {
+  for (uint32_t i = blockIdx.x * 256u + threadIdx.x; i < n4; i += gridDim.x * 256u)
+    dv[i] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 }
 
 // ---------------------------------------------------------------------------
@@ -264,6 +291,10 @@ int plan(const mha_grad_v_params* p, Args* a) {
   a->nkb = int32_t((int64_t(p->kv_seq) + kBK - 1) / kBK);
   a->paired = p->causal && (p->window == 0 || p->window >= p->q_seq / 2) ? 1 : 0;
   a->units = a->paired ? (a->nkb + 1) / 2 : a->nkb;
+  // fewer units than two per CU of the largest MI355X part: split each over
+  // two workgroups by heads (an even group of at least two)
+  a->hsplit =
+      a->paired && a->group >= 2 && a->group % 2 == 0 && int64_t(a->units) * a->HKV < 2 * 256 ? 2 : 1;
   a->scale = 1.0f / std::sqrt(float(kD));
   if (int64_t(a->nkb) * a->HKV >= kI31) return CONV2D_ERR_OVERFLOW;
   return CONV2D_OK;
@@ -292,17 +323,27 @@ int check(const mha_grad_v_params* p, char* msg, size_t len) {
     const int64_t q_bytes = int64_t(a.q_seq) * a.H * kD * 4;
     const int64_t k_bytes = int64_t(a.kv_seq) * a.HKV * kD * 4;
     const int64_t l_bytes = int64_t(a.q_seq) * a.H * 2 * 4;
-    std::vector<unsigned char> seen(size_t(int64_t(a.nkb) * a.HKV), 0);
-    for (int ub = 0; ub < 2 * a.units * a.HKV; ++ub) {
+    MHA_REQUIRE(a.hsplit >= 1 && a.group % a.hsplit == 0, "head split %d of %d", a.hsplit,
+                a.group);
+    MHA_REQUIRE(a.hsplit == 1 || a.paired, "only paired units are split");
+    // (key block, kv head, head of the group) -> times covered
+    std::vector<unsigned char> seen(size_t(int64_t(a.nkb) * a.HKV * (a.group ? a.group : 1)), 0);
+    for (int ub = 0; ub < 2 * a.units * a.HKV * a.hsplit; ++ub) {
       const int bid = ub / 2;
-      int kbs[2], kvh;
-      const int nb = unit_of(a, bid, kbs, &kvh);
+      int kbs[2], kvh, part;
+      const int nb = unit_of(a, bid, kbs, &kvh, &part);
       if (ub % 2 >= nb) continue;
       const int kb = kbs[ub % 2];
-      MHA_REQUIRE(kb >= 0 && kb < a.nkb && kvh >= 0 && kvh < a.HKV &&
-                      !seen[size_t(kb) * a.HKV + kvh],
+      MHA_REQUIRE(kb >= 0 && kb < a.nkb && kvh >= 0 && kvh < a.HKV && part >= 0 &&
+                      part < a.hsplit,
                   "workgroup %d unit", bid);
-      seen[size_t(kb) * a.HKV + kvh] = 1;
+      const int hper = a.group / a.hsplit;
+      for (int r = part * hper; r < (part + 1) * hper; ++r) {
+        const size_t e = (size_t(kb) * a.HKV + kvh) * a.group + r;
+        MHA_REQUIRE(!seen[e], "key block %d, kv head %d, head %d taken twice", kb, kvh, r);
+        seen[e] = 1;
+      }
+      if (a.group == 0) seen[size_t(kb) * a.HKV + kvh] = 1;
       int lo, hi;
       pos_range(a, kb, &lo, &hi);
       const int qb0 = lo / kBQ * kBQ;
@@ -320,8 +361,9 @@ int check(const mha_grad_v_params* p, char* msg, size_t len) {
         }
       }
       // staged elements of one query block at each visited block start
-      // (position roles, 0 past the sequence), and the K block
-      for (int pos0 = qb0; pos0 < hi; pos0 += kBQ) {
+      // (position roles, 0 past the sequence), and the K block; with no
+      // heads the head loop stages nothing
+      for (int pos0 = qb0; pos0 < hi && a.group > 0; pos0 += kBQ) {
         for (int tid = 0; tid < kThreads; ++tid)
           for (int pq = 0; pq < 4; ++pq) {
             const int pos = pos0 + row_of(tid, pq), dq = dq_of(tid);
@@ -354,7 +396,7 @@ int check(const mha_grad_v_params* p, char* msg, size_t len) {
         }
     }
     for (size_t i = 0; i < seen.size(); ++i)
-      MHA_REQUIRE(seen[i] == 1, "key block %zu of a kv head never taken", i / size_t(a.HKV));
+      MHA_REQUIRE(seen[i] == 1, "(key block, kv head, head) %zu never taken", i);
     // every LDS row cell of a stage is written once: rows x quads
     std::vector<int> cnt(size_t(kBQ) * 16, 0), gcnt(size_t(kD) * 16, 0);
     for (int tid = 0; tid < kThreads; ++tid)
@@ -406,8 +448,14 @@ extern "C" int mha_grad_v(const float* dout, const float* q, const float* k, con
   a.lse = lse;
   a.dv = dv;
   // (heads == 0: the kernel's head loop is empty and it stores zeros)
-  hipLaunchKernelGGL(mhv::mha_grad_v_kernel, dim3(a.units * a.HKV), dim3(mhv::kThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (a.hsplit > 1) {
+    const uint32_t n4 = uint32_t(nk / 4);   // nk = kv_seq * kv_heads * 64
+    hipLaunchKernelGGL(mhv::mha_zero_kernel, dim3((n4 + 255) / 256 < 1024 ? (n4 + 255) / 256 : 1024),
+                       dim3(256), 0, st, reinterpret_cast<mhv::f32x4*>(dv), n4);
+  }
+  hipLaunchKernelGGL(mhv::mha_grad_v_kernel, dim3(a.units * a.HKV * a.hsplit),
+                     dim3(mhv::kThreads), 0, st, a);
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 

@@ -25,7 +25,12 @@
  *
  * fp32 operands on the fp32 matrix cores (v_mfma_f32_16x16x4_f32), fp32
  * accumulation.  Asynchronous on `stream` (a hipStream_t; NULL: the null
- * stream).  Status codes are the CONV2D_* codes of conv2d_bwd.h:
+ * stream).  Causal launches with too few units of work to give every
+ * compute unit two workgroups (and an even number of heads per kv head)
+ * split each unit's heads over two workgroups: dv is first zeroed by a fill
+ * kernel on `stream`, then each workgroup adds its partial sum with an fp32
+ * atomic add.  Exactly two terms meet on zero, so the result is the same on
+ * every run (0 + a + b = 0 + b + a in IEEE arithmetic).  Status codes are the CONV2D_* codes of conv2d_bwd.h:
  *   CONV2D_ERR_NULL_PTR   p, or a pointer of a non-empty tensor, is NULL;
  *   CONV2D_ERR_BAD_SHAPE  head_dim != 64 (the page's 64-lane workgroup),
  *                         kv_heads == 0, heads not a multiple of kv_heads,

@@ -76,6 +76,10 @@ EDGE = [
     MhaShape("window_block", 130, 130, 8, 2, window=64),
     MhaShape("q_lt_kv", 7, 200, 2, 1, window=3, causal=False),
     MhaShape("mqa", 200, 200, 6, 1),
+    # causal units split over two workgroups by heads (group 2), and an odd
+    # group that stays whole
+    MhaShape("split_heads_causal", 130, 130, 4, 2),
+    MhaShape("odd_group_causal", 100, 100, 3, 1),
 ]
 
 
@@ -83,6 +87,19 @@ EDGE = [
 def test_mha_grad_v_edges(sh):
     _say("case mha", sh.name)
     _check(sh, 5)
+
+
+def test_mha_grad_v_causal_split_is_deterministic():
+    """The causal config's units are split over two workgroups whose partial
+    dV meet on a zeroed dv by exactly two atomic adds: repeated calls must
+    agree bit for bit."""
+    sh = next(c for c in MHA_CONFIGS if c.causal and c.window == 0)
+    _say("case mha determinism", sh.name)
+    q, k, g = draw_mha(sh, 71)
+    lse = oracle.attention_lse(q, k, sh.kv_heads, sh.window, sh.causal).astype(np.float32)
+    first = run_dv(sh, q, k, g, lse)
+    for _ in range(2):
+        assert np.array_equal(run_dv(sh, q, k, g, lse), first)
 
 
 def test_mha_grad_v_errors_and_empty():

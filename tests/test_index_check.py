@@ -225,7 +225,9 @@ def test_rms_norm_matmul_replay_rejects_bad_params():
 
 MHA_REPLAY = [(37, 37, 4, 2, 0, 1), (1, 1, 1, 1, 0, 1), (64, 64, 2, 1, 0, 1),
               (65, 65, 3, 3, 5, 1), (100, 70, 4, 2, 0, 0), (100, 70, 4, 2, 9, 0),
-              (130, 130, 8, 2, 64, 1), (7, 200, 2, 1, 3, 0), (4096, 4096, 32, 8, 512, 1)]
+              (130, 130, 8, 2, 64, 1), (7, 200, 2, 1, 3, 0), (4096, 4096, 32, 8, 512, 1),
+              (4096, 4096, 32, 8, 0, 1), (130, 130, 4, 2, 0, 1), (100, 100, 3, 1, 0, 1),
+              (200, 200, 6, 1, 0, 1), (8, 8, 0, 1, 0, 1)]
 
 
 @pytest.mark.parametrize("case", MHA_REPLAY, ids=lambda c: "q%d_kv%d_h%d_kv%d_w%d_c%d" % c)
