@@ -707,7 +707,7 @@ int launch(const float* go, const float* w, float* gi, const conv2d_params* p, i
   // variants still reach the kernel family)
   const int fwd = op == kOpForward ? 1 : 0;
   if (variant < 0 && pw::pw_route(p, fwd, f16) && pw::pw_applies(p, go, w, gi))
-    return pw::pw_launch(go, w, gi, p, f16, stream, fwd);
+    return pw::pw_launch(go, w, gi, p, f16, stream, fwd, device_cus());
   std::vector<LaunchArgs> launches;
   rc = cached_plan(p, op, f16, variant, device_cus(), &launches);
   if (rc != CONV2D_OK) return rc;
@@ -731,7 +731,7 @@ int tune(const float* go, const float* w, float* gi, const conv2d_params* p, int
   const int fwd = op == kOpForward ? 1 : 0;
   if (pw::pw_route(p, fwd, f16) && pw::pw_applies(p, go, w, gi)) {
     // the 1x1 GEMM has no variant to choose: run it once
-    rc = pw::pw_launch(go, w, gi, p, f16, stream, fwd);
+    rc = pw::pw_launch(go, w, gi, p, f16, stream, fwd, device_cus());
     if (rc != CONV2D_OK) return rc;
     if (hipStreamSynchronize(static_cast<hipStream_t>(stream)) != hipSuccess)
       return CONV2D_ERR_HIP;

@@ -25,6 +25,7 @@ namespace pw {
 constexpr int kBM = 128, kBN = 128;   // channels x pixels per tile
 constexpr int kBK = 32;               // output channels (k) per stage
 constexpr int kBufs = 4;              // stage buffers: loads run 3 stages ahead
+constexpr int kBufsShared = 2;        // ... or 1 ahead, two workgroups per CU
 constexpr int kThreads = 256;
 constexpr int kWave = 64;             // each wave 64 x 64
 constexpr int kLoads = 4;             // 16-byte loads per wave, operand and stage
@@ -158,8 +159,10 @@ inline void pw_describe(const conv2d_params* p, int64_t* tiles, int64_t* macs, i
 // Launch and host replay (pointwise_gemm.hip); fwd = 1: the forward
 // convolution, with x in the place of grad_out and y in that of grad_input.
 bool pw_applies(const conv2d_params* p, const float* go, const float* w, const float* gi);
+// `cus`: compute units of the device; with more tiles than that, the
+// launch uses two-buffer workgroups that share a CU two at a time.
 int pw_launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
-              void* stream, int fwd = 0);
+              void* stream, int fwd, int cus);
 int pw_check(const conv2d_params* p, char* msg, size_t len, int fwd = 0);
 
 }  // namespace pw

@@ -54,8 +54,13 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
-template <bool F16, bool AROW>
-__global__ __launch_bounds__(kThreads, 1) void pointwise_gemm_kernel(const PWArgs a) {
+// BUFS stage buffers: 4 (loads three stages ahead, one workgroup per CU)
+// or 2 (one stage ahead; 64 KiB, so two workgroups share a CU and cover
+// each other's waits, which pays when there are more tiles than CUs).
+template <bool F16, bool AROW, int BUFS>
+__global__ __launch_bounds__(kThreads, BUFS == kBufsShared ? 2 : 1) void pointwise_gemm_kernel(
+    const PWArgs a) {
+  constexpr int kBufs = BUFS;
   __shared__ f32x4 lds4[kBufs * kStageBytes / 16];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -192,10 +197,10 @@ __global__ __launch_bounds__(kThreads, 1) void pointwise_gemm_kernel(const PWArg
     }
   };
 
-  // stages 0 .. 2 in flight; at stage st a wave waits for its own loads of
-  // st (2 * kLoads loads per later stage may stay outstanding), the barrier
-  // then covers every wave's loads of st and every read of stage st - 1,
-  // whose buffer stage st + 3 refills
+  // stages 0 .. kBufs - 2 in flight; at stage st a wave waits for its own
+  // loads of st (2 * kLoads loads per later stage may stay outstanding), the
+  // barrier then covers every wave's loads of st and every read of stage
+  // st - 1, whose buffer stage st + kBufs - 1 refills
   for (int st = 0; st < kBufs - 1 && st < nst; ++st) issue(st);
   for (int st = 0; st < nst; ++st) {
     const int ahead = imin(nst - 1 - st, kBufs - 2);
@@ -243,23 +248,31 @@ bool pw_applies(const conv2d_params* p, const float* go, const float* w, const f
 }
 
 // Launch (shape and pointers already validated, pw_applies true).
+template <int BUFS>
+void pw_launch_bufs(const PWArgs& a, int f16, int fwd, hipStream_t st) {
+  const dim3 grid(a.TM * a.TN), block(kThreads);
+  if (f16 && fwd)
+    hipLaunchKernelGGL((pointwise_gemm_kernel<true, true, BUFS>), grid, block, 0, st, a);
+  else if (f16)
+    hipLaunchKernelGGL((pointwise_gemm_kernel<true, false, BUFS>), grid, block, 0, st, a);
+  else if (fwd)
+    hipLaunchKernelGGL((pointwise_gemm_kernel<false, true, BUFS>), grid, block, 0, st, a);
+  else
+    hipLaunchKernelGGL((pointwise_gemm_kernel<false, false, BUFS>), grid, block, 0, st, a);
+}
+
 int pw_launch(const float* go, const float* w, float* gi, const conv2d_params* p, int f16,
-              void* stream, int fwd) {
+              void* stream, int fwd, int cus) {
   PWArgs a;
   pw_plan(p, &a, fwd);
   a.go = go;
   a.w = w;
   a.gi = gi;
-  const dim3 grid(a.TM * a.TN), block(kThreads);
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (f16 && fwd)
-    hipLaunchKernelGGL((pointwise_gemm_kernel<true, true>), grid, block, 0, st, a);
-  else if (f16)
-    hipLaunchKernelGGL((pointwise_gemm_kernel<true, false>), grid, block, 0, st, a);
-  else if (fwd)
-    hipLaunchKernelGGL((pointwise_gemm_kernel<false, true>), grid, block, 0, st, a);
+  if (int64_t(a.TM) * a.TN > cus)
+    pw_launch_bufs<kBufsShared>(a, f16, fwd, st);
   else
-    hipLaunchKernelGGL((pointwise_gemm_kernel<false, false>), grid, block, 0, st, a);
+    pw_launch_bufs<kBufs>(a, f16, fwd, st);
   return hipGetLastError() == hipSuccess ? CONV2D_OK : CONV2D_ERR_HIP;
 }
 

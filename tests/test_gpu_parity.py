@@ -265,6 +265,12 @@ PW_SHAPES = [
     ConvShape("pw_ci256_co1", 3, 256, 14, 14, 1, 1, 1, 1, 0, 0, 14, 14, dist="uniform"),
     ConvShape("pw_ci128_co40_12x12", 9, 128, 12, 12, 40, 1, 1, 1, 0, 0, 12, 12,
               dist="uniform"),
+    # 294 tiles, more than the CUs: the two-buffer form, two workgroups per
+    # CU (input gradient of the first, forward of the second)
+    ConvShape("pw_ci700_co64_28x28", 8, 700, 28, 28, 64, 1, 1, 1, 0, 0, 28, 28,
+              dist="uniform"),
+    ConvShape("pw_ci64_co700_28x28", 8, 64, 28, 28, 700, 1, 1, 1, 0, 0, 28, 28,
+              dist="uniform"),
 ]
 
 
