@@ -30,7 +30,10 @@
  * split each unit's heads over two workgroups: dv is first zeroed by a fill
  * kernel on `stream`, then each workgroup adds its partial sum with an fp32
  * atomic add.  Exactly two terms meet on zero, so the result is the same on
- * every run (0 + a + b = 0 + b + a in IEEE arithmetic).  Status codes are the CONV2D_* codes of conv2d_bwd.h:
+ * every run (0 + a + b = 0 + b + a in IEEE arithmetic).  dv must then be
+ * ordinary (coarse-grained) device memory, as hipMalloc and torch return:
+ * the adds use the device's fp32 atomic instruction, which fine-grained or
+ * host-coherent memory does not support.  Status codes are the CONV2D_* codes of conv2d_bwd.h:
  *   CONV2D_ERR_NULL_PTR   p, or a pointer of a non-empty tensor, is NULL;
  *   CONV2D_ERR_BAD_SHAPE  head_dim != 64 (the page's 64-lane workgroup),
  *                         kv_heads == 0, heads not a multiple of kv_heads,
