@@ -161,10 +161,14 @@ struct Variant {
 // Floats of one stage buffer of a variant.  Multi-class variants stage a
 // window shared by four classes, so their stages are smaller; 52 copy
 // batches keep each of 8 waves at 7 batches of staging registers (with
-// more, the accumulators of four classes no longer fit in registers).
+// more, the accumulators of four classes no longer fit in registers).  The
+// one-block-row form (32 channels, 7 pixel blocks per wave) holds 8 operand
+// reads per unit and stays at 46 batches (6 per wave).
 constexpr int kStageFloatsMC = 13312;
+constexpr int kStageFloatsMC1 = 11776;
 constexpr int stage_floats(const Variant& v) {
-  return v.mc ? kStageFloatsMC : v.half ? kStageFloatsHalf : kStageFloats;
+  return v.mc ? (v.mb == 1 ? kStageFloatsMC1 : kStageFloatsMC)
+              : v.half ? kStageFloatsHalf : kStageFloats;
 }
 
 // Copy batches (of 256 floats) one wave of a variant copies per stage at
@@ -191,8 +195,10 @@ constexpr Variant kVariants[] = {
     {0, 1, 8, 1, 4, 1, 1}, {1, 1, 8, 1, 7, 0, 1}, {1, 1, 12, 1, 5, 0, 1},
     {1, 1, 8, 1, 4, 1, 1},
     // all four classes of a stride-2 shape per tile (fp32): 8 waves, whose
-    // 256 registers hold the four classes' accumulators
-    {0, 2, 4, 2, 4, 0, 0, 1}};
+    // 256 registers hold the four classes' accumulators; 64 channels x 4
+    // blocks per wave, or 32 channels x 7 blocks (pixel blocks then split
+    // 13 : 12 rather than 14 : 12 between the SIMDs on 196-pixel tiles)
+    {0, 2, 4, 2, 4, 0, 0, 1}, {0, 2, 4, 1, 7, 0, 0, 1}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b
