@@ -468,13 +468,18 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
     // (or a grad_input not 8-byte aligned) the pair is stored as two floats.
     const bool pairs =
         (a.W & 1) == 0 && (reinterpret_cast<uintptr_t>(a.gi) & 7) == 0;
+    // (an opaque copy of the lane's column, so that the store addresses are
+    // formed here rather than hoisted above the stage loop, where they
+    // would hold registers the accumulators need)
+    int c16e = c16;
+    asm volatile("" : "+v"(c16e));
 #pragma unroll
     for (int hk = 0; hk < 2; ++hk)
 #pragma unroll
       for (int b = 0; b < NBW; ++b) {
         int ih, col0;
         bool even_ok, odd_ok;
-        if (!mc_pair_pixel(c, a, hk, mm_local(b, ng, c16, WN), &ih, &col0, &even_ok, &odd_ok))
+        if (!mc_pair_pixel(c, a, hk, mm_local(b, ng, c16e, WN), &ih, &col0, &even_ok, &odd_ok))
           continue;
         const bool k0_even = a.mcls[2 * hk].iw0 == 0;
 #pragma unroll
