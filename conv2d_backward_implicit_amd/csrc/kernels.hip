@@ -329,7 +329,11 @@ __device__ __forceinline__ void mm_body(const LaunchArgs& a) {
 #pragma unroll
       for (int k = 0; k < NCL; ++k) {
         const MCClass& K = a.mcls[k];
-        const int wk = cgi * P.slots * 64 + (K.e * c.roww + K.f) * 16;
+        // (opaque: otherwise the compiler keeps every class's window offset
+        // added to every block's read base, in registers, across the stage
+        // loop)
+        int wk = cgi * P.slots * 64 + (K.e * c.roww + K.f) * 16;
+        asm volatile("" : "+s"(wk));
         // (not unrolled: unrolled tap loops hold several units' operands)
 #pragma unroll 1
         for (int j = 0; j < K.th; ++j)

@@ -194,11 +194,12 @@ constexpr Variant kVariants[] = {
     {0, 1, 8, 1, 7, 0, 1}, {0, 1, 12, 1, 5, 0, 1}, {0, 1, 16, 1, 4, 0, 1},
     {0, 1, 8, 1, 4, 1, 1}, {1, 1, 8, 1, 7, 0, 1}, {1, 1, 12, 1, 5, 0, 1},
     {1, 1, 8, 1, 4, 1, 1},
-    // all four classes of a stride-2 shape per tile (fp32): 8 waves, whose
-    // 256 registers hold the four classes' accumulators; 64 channels x 4
-    // blocks per wave, or 32 channels x 7 blocks (pixel blocks then split
-    // 13 : 12 rather than 14 : 12 between the SIMDs on 196-pixel tiles)
-    {0, 2, 4, 2, 4, 0, 0, 1}, {0, 2, 4, 1, 7, 0, 0, 1}};
+    // all four classes of a stride-2 shape per tile (fp32), the four
+    // classes' accumulators in registers: 8 waves of 64 channels x 4 blocks
+    // or 32 channels x 7 blocks (pixel blocks then split 13 : 12 rather than
+    // 14 : 12 between the SIMDs on 196-pixel tiles), or 12 waves of 32
+    // channels x 5 blocks (three waves per SIMD, 13 : 12 as well)
+    {0, 2, 4, 2, 4, 0, 0, 1}, {0, 2, 4, 1, 7, 0, 0, 1}, {0, 2, 6, 1, 5, 0, 0, 1}};
 constexpr int kNumVariants = int(sizeof(kVariants) / sizeof(kVariants[0]));
 
 }  // namespace c2b
