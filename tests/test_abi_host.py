@@ -398,6 +398,31 @@ def test_forward_few_channel_route():
     c2b.select_forward_variant(big, False, -1)
 
 
+def test_multi_class_planning():
+    """Multi-class variants tile only fp32 stride-2 input gradients whose four
+    residue classes all have pixels and taps (kernel of at most 9 taps); on
+    such a layer every class is in the one launch, and the model picks a
+    multi-class variant for the strided workload.  They issue fewer MACs
+    than a per-class plan would pad, never fewer than the useful ones."""
+    mc = [v for v in range(c2b.num_variants()) if c2b.variant_is_multi_class(v) == 1]
+    assert len(mc) == 3 and all(c2b.variant_is_f16(v) == 0 for v in mc)
+    strided = c2b.make_params(32, 128, 56, 56, 256, 3, 3, 2, 1, 1)
+    assert c2b.planned_variant(strided, False) in mc
+    for v in mc:
+        info = c2b.describe_plan_variant(strided, v)
+        assert info["launches"] == 1 and info["phases"] == 4 and info["zero_phases"] == 0
+        assert info["useful_macs"] <= info["macs"] <= 1.07 * info["useful_macs"]
+    for bad in (c2b.make_params(4, 16, 20, 20, 8, 3, 3, 1, 1, 1),    # stride 1
+                c2b.make_params(4, 16, 20, 20, 8, 5, 5, 2, 2, 2),    # 25 taps
+                c2b.make_params(4, 16, 20, 20, 8, 1, 1, 2, 0, 0),    # three classes without taps
+                c2b.make_params(4, 16, 20, 20, 8, 3, 3, 3, 1, 1)):   # stride 3
+        for v in mc:
+            with pytest.raises(c2b.Conv2dError):
+                c2b.describe_plan_variant(bad, v)
+    # the f16-staged path has no multi-class variant
+    assert c2b.planned_variant(strided, True) not in mc
+
+
 def test_forward_pointwise_route():
     """1x1, stride-1, unpadded forward shapes run on the 1x1 GEMM (no
     variant), except those with fewer than 16 input channels on the fp32
