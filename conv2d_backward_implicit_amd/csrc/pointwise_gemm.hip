@@ -268,6 +268,7 @@ int pw_launch(const float* go, const float* w, float* gi, const conv2d_params* p
   a.go = go;
   a.w = w;
   a.gi = gi;
+  if (a.TM == 0 || a.TN == 0) return CONV2D_OK;   // no output channel: nothing to write
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (int64_t(a.TM) * a.TN > cus)
     pw_launch_bufs<kBufsShared>(a, f16, fwd, st);

@@ -113,8 +113,10 @@ EDGE = [
     ConvShape("k11", 1, 5, 20, 20, 9, 11, 11, 1, 5, 5, 20, 20, dist="uniform"),
     # output channels not a multiple of the stage depth
     ConvShape("co13", 1, 7, 12, 12, 13, 3, 3, 1, 1, 1, 12, 12, dist="uniform"),
-    # zero output channels: grad_input must be all zeros
+    # zero output channels: grad_input must be all zeros (a 3x3 layer, and a
+    # 1x1 one on the 1x1 GEMM, whose forward then has no tile to launch)
     ConvShape("co0", 2, 5, 7, 7, 0, 3, 3, 1, 1, 1, 7, 7, dist="uniform"),
+    ConvShape("pw_co0", 2, 20, 6, 6, 0, 1, 1, 1, 0, 0, 6, 6, dist="uniform"),
 ]
 
 
