@@ -7,14 +7,15 @@ the attention dV of the third page).
 
 One step = one conv2d_grad_input call over the whole workload (all batch
 items, all stride classes), inputs already resident in HBM.  Before the
-warm-up the kernel variant is chosen by measurement (conv2d_tune), outside
-the timed region.  Prints one JSON
+warm-up the kernel variant is chosen by measurement (conv2d_tune), and the
+step runs untimed for 40 ms of GPU time (--clock-warmup-ms) so that the
+timed steps see the steady shader clock, not its ramp.  Prints one JSON
 line with useful TFLOP/s (2*N*Co*out_h*out_w*Ci*kH*kW per second), the
 roofline of the kernel (timed with HIP events on the stream it runs on) and
 the CPU oracle timed on the host cores on the same workload.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                    [--f16 | --fp32] [--no-cpu] [--no-tune]
+                    [--f16 | --fp32] [--no-cpu] [--no-tune] [--clock-warmup-ms MS]
                     [--op grad_input|forward|grad_weight|rms_norm_matmul|mha_grad_v]
 """
 from __future__ import annotations
@@ -129,6 +130,26 @@ def copy_calibration(mib: int, steps: int) -> int:
     return 0
 
 
+def clock_warmup(step, stream, ms: float):
+    """Run `step` untimed, in batches of 10, until `ms` milliseconds of GPU
+    time have passed on `stream` (at most 5000 steps).  MI355X raises its
+    shader clock over the first ~15 ms of sustained matrix work, so a short
+    warmup leaves the timed steps partly on the ramp; a training loop runs
+    at the steady clock.  Returns (steps run, GPU ms)."""
+    import torch
+    done, total = 0, 0.0
+    while total < ms and done < 5000:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            step()
+        e1.record(stream)
+        e1.synchronize()
+        total += e0.elapsed_time(e1)
+        done += 10
+    return done, total
+
+
 def cpu_baseline_rms(shape, x, g, w, rows):
     """The oracle on a bounded sample of the workload's rows (every column of
     each), scaled to useful TFLOP/s of those rows."""
@@ -167,6 +188,7 @@ def bench_rms(args) -> int:
     def step():
         c2b.rms_norm_matmul_into(out, tx, tg, tw, shape.eps, stream=stream)
 
+    cw_steps, cw_ms = clock_warmup(step, stream, args.clock_warmup_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -188,6 +210,7 @@ def bench_rms(args) -> int:
     out_json = {
         "metric": METRIC_RMS, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
+        "clock_warmup": {"steps": cw_steps, "gpu_ms": round(cw_ms, 1)},
         "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": shape.name, "m": shape.m, "k": shape.k, "n": shape.n,
@@ -270,6 +293,7 @@ def bench_mha(args) -> int:
     def step():
         c2b.mha_grad_v_into(dv, tg, tq, tk, tl, shape.window, shape.causal, stream=stream)
 
+    cw_steps, cw_ms = clock_warmup(step, stream, args.clock_warmup_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -291,6 +315,7 @@ def bench_mha(args) -> int:
     out = {
         "metric": METRIC_MHA, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
+        "clock_warmup": {"steps": cw_steps, "gpu_ms": round(cw_ms, 1)},
         "ms_per_step": round(wall / args.steps * 1e3, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": shape.name, "q_seq": shape.q_seq, "kv_seq": shape.kv_seq,
@@ -330,6 +355,10 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--clock-warmup-ms", type=float, default=40.0,
+                    help="untimed steps before the warmup steps until this much GPU time "
+                         "has passed, so that the timed steps run at the steady shader "
+                         "clock (0: none)")
     ap.add_argument("--workload", default=None, help="workload name (default: headline)")
     g = ap.add_mutually_exclusive_group()
     g.add_argument("--f16", action="store_true", help="f16-staged path")
@@ -435,6 +464,7 @@ def main() -> int:
             else:
                 c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
 
+    cw_steps, cw_ms = clock_warmup(step, stream, args.clock_warmup_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -491,6 +521,7 @@ def main() -> int:
         "metric": METRIC_FORWARD if fwd else METRIC_GRAD_WEIGHT if gwt else METRIC,
         "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup,
+        "clock_warmup": {"steps": cw_steps, "gpu_ms": round(cw_ms, 1)},
         "ms_per_step": round(wall / args.steps * 1e3, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": dtype, "data": "synthetic",
