@@ -7,9 +7,10 @@ the attention dV of the third page).
 
 One step = one conv2d_grad_input call over the whole workload (all batch
 items, all stride classes), inputs already resident in HBM.  Before the
-warm-up the kernel variant is chosen by measurement (conv2d_tune), and the
-step runs untimed for 40 ms of GPU time (--clock-warmup-ms) so that the
-timed steps see the steady shader clock, not its ramp.  Prints one JSON
+warm-up the step runs untimed for 40 ms of GPU time (--clock-warmup-ms), so
+that the tuning and the timed steps see the steady shader clock, not its
+ramp, and the kernel variant is chosen by measurement (conv2d_tune), outside
+the timed region.  Prints one JSON
 line with useful TFLOP/s (2*N*Co*out_h*out_w*Ci*kH*kW per second), the
 roofline of the kernel (timed with HIP events on the stream it runs on) and
 the CPU oracle timed on the host cores on the same workload.
@@ -135,9 +136,14 @@ def clock_warmup(step, stream, ms: float):
     time have passed on `stream` (at most 5000 steps).  MI355X raises its
     shader clock over the first ~15 ms of sustained matrix work, so a short
     warmup leaves the timed steps partly on the ramp; a training loop runs
-    at the steady clock.  Returns (steps run, GPU ms)."""
+    at the steady clock.  The first call (which plans the shape on the host)
+    runs before the timed batches.  Returns (steps run, GPU ms)."""
     import torch
-    done, total = 0, 0.0
+    if ms <= 0:
+        return 0, 0.0
+    step()                    # the first call plans the shape on the host
+    torch.cuda.synchronize()
+    done, total = 1, 0.0
     while total < ms and done < 5000:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -439,6 +445,16 @@ def main() -> int:
         gi = torch.empty(shape.go_shape if fwd else shape.gi_shape, dtype=torch.float32,
                          device=dev)
         plan = c2b.describe_forward_plan(p, f16) if fwd else c2b.describe_plan(p, f16)
+
+        def step():
+            if fwd:
+                c2b.forward_into(gi, tgo, tw, p, f16=f16, stream=stream)
+            else:
+                c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
+
+        # the clock warm-up first, so that the tuning below times its
+        # candidates at the steady clock
+        cw_steps, cw_ms = clock_warmup(step, stream, args.clock_warmup_ms)
         # measured variant choice for this shape, once, outside the timed
         # region (conv2d_tune; the default entry point then uses the tuned plan)
         if not args.no_tune:
@@ -458,13 +474,8 @@ def main() -> int:
             plan = {"path": "forward im2col GEMM (fewer than 16 input channels)",
                     "variant": -1, "tuned": False}
 
-        def step():
-            if fwd:
-                c2b.forward_into(gi, tgo, tw, p, f16=f16, stream=stream)
-            else:
-                c2b.grad_input_into(gi, tgo, tw, p, f16=f16, stream=stream)
-
-    cw_steps, cw_ms = clock_warmup(step, stream, args.clock_warmup_ms)
+    if gwt:
+        cw_steps, cw_ms = clock_warmup(step, stream, args.clock_warmup_ms)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()

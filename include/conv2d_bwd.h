@@ -162,8 +162,9 @@ const char* conv2d_status_string(int status);
  * Measured choice of the kernel variant for a shape, once, before the
  * steady-state calls (like a framework's first-call tuning).  The variants
  * of the path (f16 != 0: the f16-staged path) whose modelled run time is
- * within 1.3x of the best (at most 8) each run five times on the caller's
- * buffers and `stream` after one warm-up, timed with HIP events; the fastest
+ * within 1.3x of the best (at most 8) each run once as a warm-up, then
+ * three rounds time two runs of each in turn on the caller's buffers and
+ * `stream` with HIP events; the one whose fastest round is fastest
  * becomes the plan conv2d_grad_input (or conv2d_grad_input_f16) uses for
  * this shape on devices with this many compute units, for the rest of the
  * process (as conv2d_select_variant would make it; at most 4096 shapes hold
