@@ -112,6 +112,28 @@ MC_SHAPES = [
 ]
 
 
+def pw_random_shapes(rng: np.random.Generator, count: int, name: str) -> list:
+    """Random shapes the 1x1 GEMM takes (1x1 kernel, stride 1, no padding,
+    Ci and H*W multiples of 4): Ci up to 316 and Co up to 299 leave ragged
+    128-row tiles and 32-deep stages; H*W from 4 to 380 pixels, so pixel
+    tiles cross image boundaries."""
+    out = []
+    for i in range(count):
+        n = int(rng.integers(1, 5))
+        h, w = int(rng.integers(1, 20)), 4 * int(rng.integers(1, 6))   # H W % 4 == 0
+        if i % 2:
+            h, w = w, h
+        ci = 4 * int(rng.integers(1, 80))
+        co = int(rng.integers(1, 300))
+        out.append(ConvShape("%s%d" % (name, i), n, ci, h, w, co, 1, 1, 1, 0, 0, h, w,
+                             dist="uniform"))
+    return out
+
+
+# Replayed on the host (every access of both directions) and run on the GPU.
+PW_RANDOM = pw_random_shapes(np.random.default_rng(97), 40, "pw")
+
+
 def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
     if ref.size == 0:
         return 0.0

@@ -17,8 +17,8 @@ import oracle
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw, draw_forward,
                                                     draw_integers)
-from tests.gpu_helpers import (TOL, VARIANT_SHAPES, rel_err, round_f16, run_gpu,
-                               run_gpu_forward)
+from tests.gpu_helpers import (PW_RANDOM, TOL, VARIANT_SHAPES, params_of, rel_err,
+                               round_f16, run_gpu, run_gpu_forward)
 from tests.test_gpu_parity import EDGE, PW_SHAPES, RANDOM
 
 pytestmark = pytest.mark.gpu
@@ -143,6 +143,17 @@ def test_forward_pointwise_gemm_shapes(sh, f16):
     wi = rng.integers(-4, 5, size=sh.w_shape).astype(np.float32)
     got = run_gpu_forward(sh, xi, wi, f16=f16)
     assert np.array_equal(got.astype(np.float64), _oracle_fwd(sh, xi, wi))
+
+
+@pytest.mark.parametrize("sh", PW_RANDOM, ids=[s.name for s in PW_RANDOM])
+def test_forward_pointwise_random_shapes(sh):
+    """Random 1x1 shapes (the ones the host replay walks) as forward
+    convolutions, on both paths, against the oracle."""
+    _say("case forward pointwise random", sh)
+    x, w = draw_forward(sh, zlib.crc32(sh.name.encode()) + 2)
+    for f16 in (False, True):
+        assert c2b.planned_forward_variant(params_of(sh), f16) == -1
+        _check(sh, x, w, f16)
 
 
 def test_forward_pointwise_misaligned_input_takes_the_variant_kernels():

@@ -15,8 +15,8 @@ import oracle
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import (CONFIGS, ConvShape, draw,
                                                     draw_integers, random_shape)
-from tests.gpu_helpers import (MC_SHAPES, SMALL_CI_SHAPES, TOL, VARIANT_SHAPES, params_of,
-                               rel_err, round_f16, run_gpu)
+from tests.gpu_helpers import (MC_SHAPES, PW_RANDOM, SMALL_CI_SHAPES, TOL, VARIANT_SHAPES,
+                               params_of, rel_err, round_f16, run_gpu)
 
 pytestmark = pytest.mark.gpu
 
@@ -297,6 +297,23 @@ def test_pointwise_gemm_shapes(sh, f16):
     gi_, wi_ = draw_integers(sh, 9)
     got_i = run_gpu(sh, gi_, wi_, f16=f16)
     assert np.array_equal(got_i.astype(np.float64), _oracle(sh, gi_, wi_))
+
+
+@pytest.mark.parametrize("sh", PW_RANDOM, ids=[s.name for s in PW_RANDOM])
+def test_pointwise_gemm_random_shapes(sh):
+    """Random shapes on the 1x1 GEMM (the ones the host replay walks), on
+    both paths, against the oracle."""
+    _say("case pointwise random", sh)
+    p = params_of(sh)
+    rng = np.random.default_rng(zlib.crc32(sh.name.encode()))
+    go = rng.uniform(-1, 1, size=sh.go_shape).astype(np.float32)
+    w = rng.uniform(-1, 1, size=sh.w_shape).astype(np.float32)
+    ref = _oracle(sh, go, w)
+    for f16 in (False, True):
+        assert c2b.planned_variant(p, f16) == -1
+        got = run_gpu(sh, go, w, f16=f16)
+        assert not np.any(np.isnan(got)), ("unwritten grad_input elements", f16)
+        assert rel_err(got, ref) <= TOL[f16], (f16, rel_err(got, ref))
 
 
 def test_pointwise_gemm_misaligned_tensor_takes_the_variant_kernels():

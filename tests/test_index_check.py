@@ -11,7 +11,8 @@ import pytest
 
 import conv2d_backward_implicit_amd as c2b
 from conv2d_backward_implicit_amd.workloads import CONFIGS, ConvShape, random_shape
-from tests.gpu_helpers import MC_SHAPES, SMALL_CI_SHAPES, VARIANT_SHAPES, params_of
+from tests.gpu_helpers import (MC_SHAPES, PW_RANDOM, SMALL_CI_SHAPES, VARIANT_SHAPES,
+                               params_of)
 from tests.test_gpu_parity import EDGE, PW_SHAPES, RANDOM
 
 
@@ -133,26 +134,12 @@ def test_forward_every_variant_replay(variant):
 
 
 # ---- the 1x1 GEMM, both directions ------------------------------------------
-def _pw_random(rng, count, name):
-    out = []
-    for i in range(count):
-        n = int(rng.integers(1, 5))
-        h, w = int(rng.integers(1, 20)), 4 * int(rng.integers(1, 6))   # H W % 4 == 0
-        if i % 2:
-            h, w = w, h
-        ci = 4 * int(rng.integers(1, 80))
-        co = int(rng.integers(1, 300))
-        out.append(ConvShape("%s%d" % (name, i), n, ci, h, w, co, 1, 1, 1, 0, 0, h, w,
-                             dist="uniform"))
-    return out
-
-
 @pytest.mark.parametrize("f16", [False, True], ids=["fp32", "f16"])
 def test_pointwise_replay_both_directions(f16):
     """Every stage load, LDS cell, read and store of the 1x1 GEMM, as the
     input gradient and as the forward convolution, on channel counts that
     leave ragged 128-row tiles and 32-deep stages."""
-    shapes = PW_SHAPES + _pw_random(np.random.default_rng(97), 40, "pw")
+    shapes = PW_SHAPES + PW_RANDOM
     for sh in shapes:
         assert (sh.in_h * sh.in_w) % 4 == 0, sh
         _check(sh, f16)
