@@ -254,18 +254,32 @@ static int emit_launches(const conv2d_params* p, int64_t ciblocks, int64_t cit, 
       la.mc = 1;
       for (int k = 0; k < kMCClasses; ++k) la.mcls[k] = mcls[k];
     }
-    int64_t total = 0;
+    int64_t total = 0, per_image = 0;
     const size_t end = std::min(phases.size(), base + kMaxPhasesPerLaunch);
     for (size_t i = base; i < end; ++i) {
       PhaseDesc d = phases[i];
       const int rc = finalize_divisors(&d);
       if (rc != CONV2D_OK) return rc;
-      d.tile_begin = int32_t(total);
       total += d.tiles;
       if (total >= kI31) return CONV2D_ERR_OVERFLOW;
+      // a class's tiles run image by image (tile_class: N x bands x pixel
+      // tiles x channel blocks)
+      d.img_tiles = p->batch > 0 ? int32_t(d.tiles / p->batch) : 0;
+      d.img_begin = int32_t(per_image);
+      per_image += d.img_tiles;
       la.ph[la.nphases++] = d;
     }
     la.total_tiles = int32_t(total);
+    la.img_total = int32_t(per_image);
+    // Interleave the classes image by image when their tiles run the same
+    // number of stages.  With unequal stage counts the heaviest-first class
+    // order is kept: interleaved, a late image's heavy tiles would set the
+    // launch's tail.
+    bool same_stages = la.nphases > 1 && per_image > 0;
+    for (int i = 1; i < la.nphases; ++i)
+      same_stages = same_stages && la.ph[i].nchunks * la.ph[i].ngroups ==
+                                       la.ph[0].nchunks * la.ph[0].ngroups;
+    la.ilv = same_stages ? 1 : 0;
     if (launches) launches->push_back(la);
     if (info) {
       info->launches += 1;

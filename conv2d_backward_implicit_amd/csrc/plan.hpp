@@ -68,7 +68,9 @@ struct PhaseDesc {
   int32_t ntv;         // pixels per tile (<= the kernel's lane tile)
   int32_t ptiles;      // tiles per (image, band): ceil(hp * wb / ntv)
   int32_t tiles;       // tiles of this class in the launch
-  int32_t tile_begin;  // first workgroup index of this class in the launch
+  int32_t img_tiles;   // tiles of this class per image: tiles / N
+  int32_t img_begin;   // first tile of this class in an image's run (see
+                       // decode_tile): img_tiles of the classes before it
   int32_t cg;          // 16-channel groups per stage
   int32_t tg;          // taps per stage
   int32_t ngroups;     // tap groups, ceil(th * tw / tg)
@@ -119,6 +121,8 @@ struct LaunchArgs {
   int32_t twm;         // cm: matrix rows per input channel (widest class's tw)
   int32_t nphases;     // classes in this launch, heaviest first
   int32_t total_tiles; // workgroups in this launch
+  int32_t ilv;         // 1: classes interleaved image by image (decode_tile)
+  int32_t img_total;   // tiles per image over the launch's classes
   int32_t variant;     // kernel instantiation (host side only)
   int32_t mc;          // 1: multi-class launch (ph[0] is the union of mcls)
   PhaseDesc ph[kMaxPhasesPerLaunch];

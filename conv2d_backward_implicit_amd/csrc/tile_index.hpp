@@ -49,28 +49,40 @@ C2B_HD uint32_t fast_div_magic(uint32_t d) {
   return uint32_t(((uint64_t(1) << 31) + d - 1) / d);
 }
 
-// Index of the class of workgroup `bid` within the launch.
-C2B_HD int phase_of(const LaunchArgs& a, int bid) {
-  int pi = 0;
-  for (int i = 1; i < a.nphases; ++i)
-    if (bid >= a.ph[i].tile_begin) pi = i;
-  return pi;
+// Contiguous runs per XCD: the dispatcher deals workgroups round-robin over
+// the 8 XCDs, so of `count` workgroups the ones with l = x mod 8 (one XCD)
+// take the x-th of 8 contiguous runs of the tiles.
+C2B_HD int xcd_run(int l, int count) {
+  const int q = count >> 3, r = count & 7, x = l & 7, k = l >> 3;
+  return x * q + imin(x, r) + k;
 }
 
-// Tile of a workgroup.  Inside a class, the workgroups whose index is
-// x mod 8 (one XCD: the dispatcher deals workgroups round-robin over the 8
-// XCDs) take one contiguous run of tiles, channel tile fastest, so tiles
-// that share grad_out rows and weights share that XCD's L2.
+// Tile of a workgroup.  Each XCD takes contiguous runs of tiles, channel
+// tile fastest, so that tiles that share grad_out rows and weights share
+// that XCD's L2.  Classes (stride > 1) occupy consecutive workgroup ranges,
+// heaviest first, and each class's range is dealt over the XCDs on its own.
+// With `ilv` (classes of equal stage counts) the whole launch is dealt at
+// once, image by image and inside an image class by class: the classes of
+// one image read the same grad_out planes, which then stay in the XCD's L2
+// while they all run, instead of coming back from memory once per class.
 C2B_HD TileCtx decode_tile(const LaunchArgs& a, int bid) {
   TileCtx c;
-  c.P = a.ph[phase_of(a, bid)];
-  const PhaseDesc& P = c.P;
-  int t;
-  {
-    const int l = bid - P.tile_begin, T = P.tiles;
-    const int q = T >> 3, r = T & 7, x = l & 7, k = l >> 3;
-    t = x * q + imin(x, r) + k;
+  int pi = 0, t;
+  if (a.ilv) {
+    const int u = xcd_run(bid, a.total_tiles);
+    const int n = u / a.img_total, v = u - n * a.img_total;
+    for (int i = 1; i < a.nphases; ++i)
+      if (v >= a.ph[i].img_begin) pi = i;
+    t = n * a.ph[pi].img_tiles + (v - a.ph[pi].img_begin);
+  } else {
+    // class pi's workgroups start at N * img_begin (its tiles run image by
+    // image)
+    for (int i = 1; i < a.nphases; ++i)
+      if (bid >= a.N * a.ph[i].img_begin) pi = i;
+    t = xcd_run(bid - a.N * a.ph[pi].img_begin, a.ph[pi].tiles);
   }
+  c.P = a.ph[pi];
+  const PhaseDesc& P = c.P;
   const int ciblk = t % a.ciblocks;
   t /= a.ciblocks;
   const int ptile = t % P.ptiles;
