@@ -156,6 +156,21 @@ def test_deterministic_and_on_side_stream():
     assert np.array_equal(a, b)
 
 
+def test_call_without_stream_runs_on_torchs_current_stream():
+    """With no stream given, a call goes to torch's current stream, also
+    inside a ``torch.cuda.stream`` context, and gives the same result."""
+    import torch
+    sh = _reduced(CONFIGS[2], 1)
+    go, w = draw(sh, 2)
+    ref = run_gpu(sh, go, w)
+    assert c2b._stream_id(None) == torch.cuda.current_stream().cuda_stream
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        assert c2b._stream_id(None) == side.cuda_stream
+        got = run_gpu(sh, go, w)
+    assert np.array_equal(ref, got)
+
+
 def test_bad_status_raises():
     import torch
     import conv2d_backward_implicit_amd as c2b
