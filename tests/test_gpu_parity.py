@@ -117,6 +117,10 @@ EDGE = [
     # 1x1 one on the 1x1 GEMM, whose forward then has no tile to launch)
     ConvShape("co0", 2, 5, 7, 7, 0, 3, 3, 1, 1, 1, 7, 7, dist="uniform"),
     ConvShape("pw_co0", 2, 20, 6, 6, 0, 1, 1, 1, 0, 0, 6, 6, dist="uniform"),
+    # stride 5: 25 classes in two launches; one tap each (classes of equal
+    # stage counts, dealt image by image), and 7x7 taps (unequal classes)
+    ConvShape("s5_k5", 2, 5, 23, 23, 6, 5, 5, 5, 2, 2, 5, 5, dist="uniform"),
+    ConvShape("s5_k7", 3, 4, 21, 19, 3, 7, 7, 5, 3, 3, 5, 4, dist="uniform"),
 ]
 
 
