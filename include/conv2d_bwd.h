@@ -52,7 +52,10 @@
  * set to 0).  grad_out and weight are only read.  grad_input must not overlap
  * either input.  The call is asynchronous on `stream` (a hipStream_t; NULL
  * means the null stream); execution faults surface at the caller's next
- * synchronisation.
+ * synchronisation.  A call enqueues kernel launches only (no memset, no
+ * allocation, no host synchronisation; conv2d_tune excepted), so once a shape
+ * has been planned by one call, later calls on a stream under HIP graph
+ * capture are recorded and replay to the same bits.
  *
  * Errors.  Every entry point returns an int status: CONV2D_OK (0) or a
  * negative CONV2D_ERR_* code.  On any validation error nothing is enqueued and
